@@ -1,0 +1,209 @@
+"""ctypes binding of libglq.so (include/glq.h). Argument marshalling only.
+
+Every computation happens in the library: the GPU entry points take device
+pointers from torch tensors and the current HIP stream; the CPU entry points
+(codebook tables, reference encoder) take numpy arrays. There is no fallback:
+if the library is missing, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libglq.so")
+
+GLQ_OK, GLQ_ERR_ARG, GLQ_ERR_UNSUPPORTED, GLQ_ERR_HIP, GLQ_ERR_WORKSPACE = 0, -1, -2, -3, -4
+GLQ_F32, GLQ_BF16 = 0, 1
+GLQ_CB_INT8_2X, GLQ_CB_DEVICE = 0, 1
+FLAG_NO_INPUT_RHT, FLAG_NO_OUTPUT_RHT = 1, 2
+
+EXPORTS = ("glq_build_codebook", "glq_encode_ref", "glq_rht_apply", "glq_decode_weights",
+           "glq_fused_linear_workspace", "glq_fused_linear", "glq_status_string", "glq_version")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libglq.so not built at {LIB_PATH}: run python -m dequant_e8_codebook_amd.build")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i64, _i32, _u32, _f32, _sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                    ctypes.c_uint32, ctypes.c_float, ctypes.c_size_t)
+
+
+class GlqLayerStruct(ctypes.Structure):
+    _fields_ = [("n", _i64), ("k", _i64), ("bpw", _i32), ("resid_shift", _i32), ("scale", _f32),
+                ("idx1", _vp), ("idx2", _vp), ("sign_k", _vp), ("sign_n", _vp), ("cb", _vp)]
+
+
+_lib.glq_build_codebook.argtypes = [_i32, _vp, _sz, ctypes.POINTER(_sz)]
+_lib.glq_encode_ref.argtypes = [_vp, _i64, _i64, _i32, _vp, _vp, _f32, ctypes.POINTER(_f32), _vp, _vp, _i32]
+_lib.glq_rht_apply.argtypes = [_vp, _i32, _vp, _i32, _i64, _i64, _vp, _i32, _vp]
+_lib.glq_decode_weights.argtypes = [ctypes.POINTER(GlqLayerStruct), _vp, _i32, _vp]
+_lib.glq_fused_linear_workspace.argtypes = [ctypes.POINTER(GlqLayerStruct), _i64]
+_lib.glq_fused_linear_workspace.restype = _sz
+_lib.glq_fused_linear.argtypes = [ctypes.POINTER(GlqLayerStruct), _vp, _i32, _i64, _vp, _i32, _vp, _sz,
+                                  _u32, _vp]
+_lib.glq_status_string.argtypes = [_i32]
+_lib.glq_status_string.restype = ctypes.c_char_p
+_lib.glq_version.restype = _u32
+for _name in ("glq_build_codebook", "glq_encode_ref", "glq_rht_apply", "glq_decode_weights",
+              "glq_fused_linear"):
+    getattr(_lib, _name).restype = ctypes.c_int
+
+
+class GlqError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+        self.status = status
+
+
+def _check(rc: int, what: str):
+    if rc != GLQ_OK:
+        raise GlqError(rc, what)
+
+
+def raw():
+    """The ctypes library object (for tests of the C ABI itself)."""
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return _lib.glq_status_string(status).decode()
+
+
+def version() -> int:
+    return int(_lib.glq_version())
+
+
+# ------------------------------------------------------------------ CPU calls
+
+def build_codebook(form: int) -> bytes:
+    need = _sz(0)
+    _check(_lib.glq_build_codebook(form, None, 0, ctypes.byref(need)), "glq_build_codebook")
+    buf = ctypes.create_string_buffer(need.value)
+    _check(_lib.glq_build_codebook(form, buf, need.value, None), "glq_build_codebook")
+    return buf.raw
+
+
+def codebook_doubled() -> np.ndarray:
+    """int8 [65536, 8] doubled coordinates 2*C[i]."""
+    return np.frombuffer(build_codebook(GLQ_CB_INT8_2X), dtype=np.int8).reshape(65536, 8).copy()
+
+
+def encode_ref(w: np.ndarray, bpw: int, sign_n: np.ndarray, sign_k: np.ndarray,
+               scale: float = 0.0, nthreads: int = 0):
+    """CPU encoder: returns (idx1 uint16 [n, k/8], idx2 or None, scale)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    n, k = w.shape
+    sn = np.ascontiguousarray(sign_n, dtype=np.int8)
+    sk = np.ascontiguousarray(sign_k, dtype=np.int8)
+    i1 = np.empty((n, max(k // 8, 0)), dtype=np.uint16)
+    i2 = None
+    if bpw in (3, 4):
+        i2 = np.empty((n, k // 8), dtype=np.uint8 if bpw == 3 else np.uint16)
+    s = _f32(0.0)
+    rc = _lib.glq_encode_ref(w.ctypes.data, n, k, bpw, sn.ctypes.data, sk.ctypes.data, float(scale),
+                             ctypes.byref(s), i1.ctypes.data, None if i2 is None else i2.ctypes.data,
+                             nthreads)
+    _check(rc, "glq_encode_ref")
+    return i1, i2, np.float32(s.value)
+
+
+# ------------------------------------------------------------------ GPU calls
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return GLQ_F32
+    if t.dtype == torch.bfloat16:
+        return GLQ_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def device_codebook(device="cuda"):
+    """The GLQ_CB_DEVICE tables copied into a device uint8 tensor."""
+    torch = _torch()
+    blob = np.frombuffer(build_codebook(GLQ_CB_DEVICE), dtype=np.uint8).copy()
+    return torch.from_numpy(blob).to(device)
+
+
+@dataclass
+class Layer:
+    """Device tensors of one compressed layer, and its glq_layer struct."""
+    n: int
+    k: int
+    bpw: int
+    scale: float
+    idx1: object                # torch uint16-compatible tensor [n, k/8] (stored as int16)
+    idx2: object                # torch [n, k/8] uint8 / int16, or None
+    sign_k: object              # torch int8 [k]
+    sign_n: object              # torch int8 [n]
+    cb: object                  # torch uint8 device tables
+
+    def struct(self) -> GlqLayerStruct:
+        return GlqLayerStruct(
+            self.n, self.k, self.bpw, {2: 0, 3: 1, 4: 2}[self.bpw], float(self.scale),
+            self.idx1.data_ptr(), 0 if self.idx2 is None else self.idx2.data_ptr(),
+            0 if self.sign_k is None else self.sign_k.data_ptr(),
+            0 if self.sign_n is None else self.sign_n.data_ptr(), self.cb.data_ptr())
+
+    @staticmethod
+    def from_numpy(idx1, idx2, scale, sign_n, sign_k, cb, device="cuda") -> "Layer":
+        torch = _torch()
+        idx1 = np.ascontiguousarray(idx1, dtype=np.uint16)
+        n, g = idx1.shape
+        bpw = 2 if idx2 is None else (3 if np.asarray(idx2).dtype == np.uint8 else 4)
+        t1 = torch.from_numpy(idx1.view(np.int16)).to(device)
+        t2 = None
+        if idx2 is not None:
+            a2 = np.ascontiguousarray(idx2)
+            t2 = torch.from_numpy(a2 if bpw == 3 else a2.astype(np.uint16).view(np.int16)).to(device)
+        sk = None if sign_k is None else torch.from_numpy(np.ascontiguousarray(sign_k, np.int8)).to(device)
+        sn = None if sign_n is None else torch.from_numpy(np.ascontiguousarray(sign_n, np.int8)).to(device)
+        return Layer(n, 8 * g, bpw, float(scale), t1, t2, sk, sn, cb)
+
+
+def rht_apply(inp, out, signs, transpose: bool, stream=None):
+    """out = RHT(inp) along the last axis (glq_rht_apply)."""
+    n = inp.shape[-1]
+    rows = inp.numel() // n if n else 0
+    rc = _lib.glq_rht_apply(inp.data_ptr(), _dtype_code(inp), out.data_ptr(), _dtype_code(out), rows, n,
+                            signs.data_ptr(), int(bool(transpose)), _stream_ptr(stream))
+    _check(rc, "glq_rht_apply")
+    return out
+
+
+def decode_weights(layer: Layer, out, stream=None):
+    st = layer.struct()
+    _check(_lib.glq_decode_weights(ctypes.byref(st), out.data_ptr(), _dtype_code(out), _stream_ptr(stream)),
+           "glq_decode_weights")
+    return out
+
+
+def workspace_bytes(layer: Layer, m: int) -> int:
+    st = layer.struct()
+    return int(_lib.glq_fused_linear_workspace(ctypes.byref(st), m))
+
+
+def fused_linear(layer: Layer, x, y, workspace, flags: int = 0, stream=None):
+    """y = U^T (s W^) (V x) (glq_fused_linear); x [m, k], y [m, n]."""
+    st = layer.struct()
+    m = x.shape[0]
+    rc = _lib.glq_fused_linear(ctypes.byref(st), x.data_ptr(), _dtype_code(x), m, y.data_ptr(),
+                               _dtype_code(y), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                               flags, _stream_ptr(stream))
+    _check(rc, "glq_fused_linear")
+    return y

@@ -1,0 +1,171 @@
+/*
+ * glq.h -- C ABI of the E8-lattice-codebook linear layer for MI355X (gfx950).
+ *
+ * What the library computes (the method of "glq 0.1.1", PyPI project page,
+ * section "How it works", items 1-2, and section "Bit widths"):
+ *
+ *   Every group of 8 consecutive weights of a rotated weight matrix
+ *   W~ = U W V^T  [n, k]  is stored as a 16-bit index into a 65,536-entry
+ *   E8 lattice codebook C, optionally plus an 8-bit (3 bpw) or 16-bit
+ *   (4 bpw) index into a residual codebook, with one global float32 scale s
+ *   per layer:   W^[r, 8g:8g+8] = s * ( C[i1] + 2^-k * C_r[i2] ).
+ *   U and V are randomized Hadamard transforms: random sign flips followed
+ *   by a (block-diagonal) fast Walsh-Hadamard transform, normalised by
+ *   1/sqrt(b).  At run time a layer computes
+ *
+ *       y = U^T ( s W^ ) ( V x )
+ *
+ *   reconstructing W^ inside the matrix product ("EntroPack" news item:
+ *   the GPU fuses symbol decoding and weight reconstruction; storage rate is
+ *   kept separate from compute precision).
+ *
+ * Format decisions the pages leave open (all stated in the library's design
+ * notes): standard E8 coordinates; the origin counts as shell 0; codebook
+ * order = ascending (|x|^2, -orbit size, max|x_i|, |x| lexicographic, sign
+ * counter); C_r = the first 2^8 (3 bpw) or 2^16 (4 bpw) codebook entries
+ * with k = 1 (3 bpw) or k = 2 (4 bpw); groups run along k; Sylvester
+ * Hadamard in natural order, block b(n) = largest power of two dividing n.
+ *
+ * Conventions for every call:
+ *  - All memory is owned and allocated by the caller. No call allocates or
+ *    frees memory, device or host (glq_encode_ref allocates host scratch).
+ *  - Device pointers are HIP device pointers; "host" marks host pointers.
+ *  - Every call returns a glq_status. Arguments are validated before any
+ *    launch; no error aborts the process or escapes as an exception.
+ *  - GPU calls are asynchronous on the given HIP stream (NULL = default
+ *    stream), never synchronise the host, and keep no state between calls:
+ *    calls on different streams may run concurrently.
+ *  - Layouts are dense row-major with no padding.
+ */
+#ifndef GLQ_H
+#define GLQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GLQ_OK = 0,
+    GLQ_ERR_ARG = -1,          /* invalid argument (null pointer, bad size, bad enum) */
+    GLQ_ERR_UNSUPPORTED = -2,  /* valid but unsupported shape (e.g. Hadamard block > 32768) */
+    GLQ_ERR_HIP = -3,          /* a HIP launch or runtime call failed */
+    GLQ_ERR_WORKSPACE = -4     /* workspace missing or smaller than required */
+} glq_status;
+
+typedef enum { GLQ_F32 = 0, GLQ_BF16 = 1 } glq_dtype;
+
+/* codebook forms for glq_build_codebook */
+enum {
+    GLQ_CB_INT8_2X = 0,  /* host table int8 [65536][8] holding 2*C[i] (doubled coordinates) */
+    GLQ_CB_DEVICE = 1    /* opaque decode tables; copy the bytes to device memory unchanged */
+};
+
+/* flags for glq_fused_linear */
+enum {
+    GLQ_FLAG_NO_INPUT_RHT = 1u,   /* x is already rotated: use x~ = x */
+    GLQ_FLAG_NO_OUTPUT_RHT = 2u   /* return z = s W^ x~ (rotated basis) instead of y = U^T z */
+};
+
+/* One compressed linear layer. The struct itself lives in host memory; the
+ * pointers in it are device pointers owned by the caller. */
+typedef struct {
+    int64_t n;                /* out features (rows of W), >= 1 */
+    int64_t k;                /* in features, >= 8 and k % 8 == 0 */
+    int32_t bpw;              /* 2, 3 or 4 */
+    int32_t resid_shift;      /* residual scale 2^-resid_shift: must be 1 at 3 bpw, 2 at 4 bpw; ignored at 2 bpw */
+    float scale;              /* the global scale s (finite, > 0) */
+    const uint16_t *idx1;     /* [n][k/8] stage-1 codebook indices */
+    const void *idx2;         /* [n][k/8] residual indices: uint8 (3 bpw), uint16 (4 bpw), NULL (2 bpw) */
+    const int8_t *sign_k;     /* [k] input-side signs, each +1 or -1 */
+    const int8_t *sign_n;     /* [n] output-side signs, each +1 or -1 */
+    const void *cb;           /* device copy of the GLQ_CB_DEVICE tables */
+} glq_layer;
+
+/*
+ * glq_build_codebook -- write the codebook ("glq 0.1.1", "How it works",
+ * item 1: 65,536 E8 vectors from the first 7 shells) in the stated order.
+ *   form       GLQ_CB_INT8_2X or GLQ_CB_DEVICE
+ *   out        host buffer of out_bytes bytes, or NULL to query the size
+ *   needed     host; if not NULL receives the size in bytes of the form
+ * Returns GLQ_ERR_ARG for an unknown form and GLQ_ERR_WORKSPACE when out is
+ * not NULL and out_bytes is too small (nothing is written then).
+ */
+int glq_build_codebook(int32_t form, void *out, size_t out_bytes, size_t *needed);
+
+/*
+ * glq_encode_ref -- CPU encoder ("glq 0.1.1", "How it works", items 1-2;
+ * "Bit widths"): W~ = U W V^T in float64, s = fp32(sqrt(mean(W~^2))) unless
+ * given, X = W~/s in groups of 8 along k, i1 = nearest codebook entry (float64
+ * squared distance, lowest index on ties), and for 3/4 bpw i2 = nearest entry
+ * of 2^-k C_r to the residual X - C[i1]. Nearest-neighbour rounding only
+ * (the page's LDLQ error feedback needs calibration data and is not done).
+ *   w          host float [n][k], original (unrotated) basis, finite
+ *   sign_n     host int8 [n] (+1/-1),  sign_k  host int8 [k] (+1/-1)
+ *   scale_in   > 0: use as s;  <= 0: compute s as above
+ *   scale_out  host, receives s (may be NULL)
+ *   idx1_out   host uint16 [n][k/8]
+ *   idx2_out   host uint8 (3 bpw) / uint16 (4 bpw) [n][k/8]; NULL at 2 bpw
+ *   nthreads   worker threads (<= 0: hardware concurrency)
+ * Returns GLQ_ERR_ARG for bad sizes/bpw, non-finite weights or signs not +-1.
+ */
+int glq_encode_ref(const float *w, int64_t n, int64_t k, int32_t bpw,
+                   const int8_t *sign_n, const int8_t *sign_k,
+                   float scale_in, float *scale_out,
+                   uint16_t *idx1_out, void *idx2_out, int32_t nthreads);
+
+/*
+ * glq_rht_apply -- randomized Hadamard transform along the last axis of a
+ * [rows][n] array ("glq 0.1.1", "How it works", item 2), b = largest power of
+ * two dividing n (<= 32768), computed in float32:
+ *   transpose = 0:  out = (I (x) H_b) diag(signs) in / sqrt(b)   (signs, then FWHT)
+ *   transpose = 1:  out = diag(signs) (I (x) H_b) in / sqrt(b)   (FWHT, then signs)
+ *   in, out    device, dtype in_dt / out_dt; may be the same buffer when
+ *              in_dt == out_dt
+ *   signs      device int8 [n]
+ * rows == 0 is a successful no-op.
+ */
+int glq_rht_apply(const void *in, glq_dtype in_dt, void *out, glq_dtype out_dt,
+                  int64_t rows, int64_t n, const int8_t *signs,
+                  int32_t transpose, void *hip_stream);
+
+/*
+ * glq_decode_weights -- expand the index planes into the rotated-basis
+ * weights W^ [n][k] (the reconstruction the fused kernels do on the fly):
+ * v = C[i1] + 2^-k C_r[i2] exactly, w = fl32(s * v) (one float32 multiply),
+ * bf16 output = round-to-nearest-even of w.
+ *   w_out      device [n][k] of out_dt
+ */
+int glq_decode_weights(const glq_layer *L, void *w_out, glq_dtype out_dt, void *hip_stream);
+
+/* Bytes of device workspace glq_fused_linear needs for m rows (any dtype, any flags). */
+size_t glq_fused_linear_workspace(const glq_layer *L, int64_t m);
+
+/*
+ * glq_fused_linear -- y = U^T (s W^) (V x) for x [m][k], y [m][n], with the
+ * weights reconstructed inside the product and never written to memory.
+ *   x_dt = GLQ_F32:  float32 path (float32 x~, exact float32 weights, float32
+ *                    accumulation)
+ *   x_dt = GLQ_BF16: bf16 matrix-core path (x~ rounded to bf16, weights exact
+ *                    in bf16, float32 accumulation, scale in the epilogue)
+ *   y_dt             GLQ_F32 or GLQ_BF16 (round-to-nearest-even)
+ *   workspace        device, >= glq_fused_linear_workspace(L, m) bytes, 256-byte aligned
+ *   flags            GLQ_FLAG_* (0 = the full layer)
+ * m == 0 is a successful no-op. x and y must not overlap the workspace.
+ */
+int glq_fused_linear(const glq_layer *L, const void *x, glq_dtype x_dt, int64_t m,
+                     void *y, glq_dtype y_dt, void *workspace, size_t ws_bytes,
+                     uint32_t flags, void *hip_stream);
+
+/* Static text for a status code. */
+const char *glq_status_string(int status);
+
+/* Library and codebook-format version, e.g. 0x00010000. */
+uint32_t glq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GLQ_H */

@@ -1,0 +1,178 @@
+"""C-ABI tests that need no GPU: the library loads and exports every symbol
+include/glq.h declares, the CPU entry points match the oracle, and argument
+validation of the GPU entry points returns a status before touching a GPU."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import e8, glq as og, rht
+import workloads
+
+glq = pytest.importorskip("dequant_e8_codebook_amd.glq")
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "glq.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(glq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert set(names) == set(glq.EXPORTS)
+    lib = ctypes.CDLL(glq.LIB_PATH)
+    for nm in names:
+        assert getattr(lib, nm) is not None
+
+
+def test_status_strings_and_version():
+    assert glq.status_string(0) == "ok"
+    for s in (-1, -2, -3, -4):
+        assert glq.status_string(s) != "unknown status"
+    assert glq.status_string(7) == "unknown status"
+    assert glq.version() == 0x00010000
+
+
+def test_codebook_equals_oracle():
+    assert np.array_equal(glq.codebook_doubled(), e8.codebook())
+
+
+def test_build_codebook_size_queries():
+    lib = glq.raw()
+    need = ctypes.c_size_t(0)
+    assert lib.glq_build_codebook(glq.GLQ_CB_INT8_2X, None, 0, ctypes.byref(need)) == 0
+    assert need.value == 65536 * 8
+    small = ctypes.create_string_buffer(16)
+    assert lib.glq_build_codebook(glq.GLQ_CB_INT8_2X, small, 16, None) == glq.GLQ_ERR_WORKSPACE
+    assert lib.glq_build_codebook(7, None, 0, ctypes.byref(need)) == glq.GLQ_ERR_ARG
+
+
+def _walk_blob(blob: bytes):
+    """Decode all 65536 indices through the device tables, written from the
+    table format description (numpy, vectorised), into doubled coordinates."""
+    b = np.frombuffer(blob, dtype=np.uint8)
+    ct = b[256:256 + 8192].view(np.uint16).astype(np.int64)
+    ot = b[8448:8448 + 1472 * 16].view(np.uint32).reshape(-1, 4).astype(np.int64)
+    a3 = b[8448 + 1472 * 16 + 2368 * 8: 8448 + 1472 * 16 + 2 * 2368 * 8].view(np.int16)
+    i = np.arange(65536, dtype=np.int64)
+    ip = (i - 1) & 0xFFFF
+    e = ct[ip >> 4]
+    rec = (e >> 5) + ((ip & 15) >> (e & 31))
+    r = ot[rec]
+    lo = r[:, 1] + 8 * (ip & ((1 << r[:, 0]) - 1))
+    qsrc = ip & ((1 << r[:, 3]) - 1)
+    q = np.array([bin(v).count("1") & 1 for v in qsrc])
+    hi = (r[:, 2] + 8 * (ip >> r[:, 0]) + 64 * q) & 0xFFFFFFFF
+    out = np.zeros((65536, 8), dtype=np.int64)
+    for t in range(4):
+        out[:, t] = a3[(lo + 2 * t) // 2] // 2
+        out[:, 4 + t] = a3[(hi + 2 * t) // 2] // 2
+    return out
+
+
+def test_device_tables_decode_every_index():
+    blob = glq.build_codebook(glq.GLQ_CB_DEVICE)
+    assert np.array_equal(_walk_blob(blob), e8.codebook().astype(np.int64))
+    b = np.frombuffer(blob, dtype=np.uint8)
+    # value formats agree with each other: bf16 = y/2, A4 = 2 * A3, B4 = 0x4340 + y
+    base = 8448 + 1472 * 16
+    hb = b[base: base + 2368 * 8].view(np.uint16)
+    a3 = b[base + 2368 * 8: base + 2 * 2368 * 8].view(np.int16).astype(np.int64)
+    a4 = b[base + 2 * 2368 * 8: base + 3 * 2368 * 8].view(np.int16).astype(np.int64)
+    b4 = b[base + 3 * 2368 * 8: base + 4 * 2368 * 8].view(np.uint16).astype(np.int64)
+    used = int(np.frombuffer(blob[12:16], np.uint32)[0]) * 4
+    y = a3[:used] // 2
+    assert np.array_equal(a4[:used], 4 * y)
+    assert np.array_equal(b4[:used], 0x4340 + y)
+    f = (hb[:used].astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(f, (y / 2.0).astype(np.float32))
+    r3 = b[base + 4 * 2368 * 8: base + 4 * 2368 * 8 + 4096].view(np.uint16).astype(np.int64).reshape(256, 8)
+    assert np.array_equal(r3 - 0x4340, e8.codebook()[:256].astype(np.int64))
+
+
+@pytest.mark.parametrize("bpw", [2, 3, 4])
+def test_encode_ref_matches_oracle(bpw):
+    spec = workloads.LayerSpec("t", 40, 192, bpw, 1, "student_t", "f32", "f32", 0, 777)
+    w = workloads.weights(spec).astype(np.float32)
+    sn, sk = workloads.sign_n(spec), workloads.sign_k(spec)
+    a1, a2, s = glq.encode_ref(w, bpw, sn, sk, nthreads=4)
+    b1, b2, so = og.encode(w.astype(np.float64), bpw, sn, sk)
+    assert s == so
+    assert np.array_equal(a1, b1)
+    if bpw > 2:
+        assert np.array_equal(a2, b2) and a2.dtype == b2.dtype
+
+
+def test_encode_ref_explicit_scale_codebook_exact():
+    # W = U^T (s C[idx]) V: with the same s, the encoder returns idx
+    rng = np.random.default_rng(5)
+    n, k = 24, 64
+    idx = rng.integers(0, 65536, (n, k // 8)).astype(np.uint16)
+    s = np.float32(0.031)
+    sn, sk = workloads.signs(n, 3), workloads.signs(k, 4)
+    w = rht.unrotate_weights(np.float64(s) * og.decode_values(idx, None, 2), sn, sk)
+    a1, _, s_out = glq.encode_ref(w.astype(np.float32), 2, sn, sk, scale=float(s))
+    assert s_out == s
+    # float32 rounding of W may move a group only if it sits within ~1e-6 of a
+    # Voronoi boundary; random lattice points are never that close
+    assert np.array_equal(a1, idx)
+
+
+def test_encode_ref_errors():
+    lib = glq.raw()
+    w = np.zeros((4, 16), np.float32)
+    s = np.ones(16, np.int8)
+    i1 = np.zeros((4, 2), np.uint16)
+    f = ctypes.c_float(0)
+    call = lambda w_, n, k, bpw, sn, sk, i2=None: lib.glq_encode_ref(
+        w_.ctypes.data, n, k, bpw, sn.ctypes.data, sk.ctypes.data, 0.0, ctypes.byref(f),
+        i1.ctypes.data, i2, 1)
+    assert call(w, 4, 16, 5, s, s) == glq.GLQ_ERR_ARG          # bpw
+    assert call(w, 4, 12, 2, s, s) == glq.GLQ_ERR_ARG          # k % 8
+    assert call(w, 4, 16, 3, s, s) == glq.GLQ_ERR_ARG          # idx2 missing
+    bad = s.copy()
+    bad[3] = 0
+    assert call(w, 4, 16, 2, s, bad) == glq.GLQ_ERR_ARG        # sign not +-1
+    wn = w.copy()
+    wn[1, 1] = np.inf
+    assert call(wn, 4, 16, 2, s, s) == glq.GLQ_ERR_ARG         # non-finite
+    assert call(w, 4, 16, 2, s, s) == glq.GLQ_OK
+    zero_i1 = i1.copy()
+    assert np.array_equal(i1, zero_i1)                         # all-zero W -> origin (s = 1)
+
+
+def test_gpu_entry_points_validate_before_launch():
+    lib = glq.raw()
+    L = glq.GlqLayerStruct(0, 64, 2, 0, 1.0, 1, 0, 1, 1, 1)   # n = 0
+    p = ctypes.byref(L)
+    assert lib.glq_decode_weights(p, ctypes.c_void_p(1), 0, None) == glq.GLQ_ERR_ARG
+    assert lib.glq_decode_weights(None, ctypes.c_void_p(1), 0, None) == glq.GLQ_ERR_ARG
+    L2 = glq.GlqLayerStruct(16, 60, 2, 0, 1.0, 1, 0, 1, 1, 1)  # k % 8
+    assert lib.glq_fused_linear(ctypes.byref(L2), 1, 0, 1, 1, 0, 1, 1 << 20, 0, None) == glq.GLQ_ERR_ARG
+    L3 = glq.GlqLayerStruct(16, 64, 3, 2, 1.0, 1, 1, 1, 1, 1)  # wrong resid_shift for 3 bpw
+    assert lib.glq_fused_linear(ctypes.byref(L3), 1, 0, 1, 1, 0, 1, 1 << 20, 0, None) == glq.GLQ_ERR_ARG
+    L4 = glq.GlqLayerStruct(16, 64, 4, 2, 1.0, 1, 0, 1, 1, 1)  # idx2 missing
+    assert lib.glq_fused_linear(ctypes.byref(L4), 1, 0, 1, 1, 0, 1, 1 << 20, 0, None) == glq.GLQ_ERR_ARG
+    L5 = glq.GlqLayerStruct(16, 64, 2, 0, float("nan"), 1, 0, 1, 1, 1)
+    assert lib.glq_fused_linear(ctypes.byref(L5), 1, 0, 1, 1, 0, 1, 1 << 20, 0, None) == glq.GLQ_ERR_ARG
+    ok = glq.GlqLayerStruct(16, 64, 2, 0, 1.0, 1, 0, 1, 1, 1)
+    po = ctypes.byref(ok)
+    need = lib.glq_fused_linear_workspace(po, 4)
+    assert need >= 4 * 64 * 4 + 4 * 16 * 4
+    assert lib.glq_fused_linear(po, 1, 0, 4, 1, 0, 256, need - 1, 0, None) == glq.GLQ_ERR_WORKSPACE
+    assert lib.glq_fused_linear(po, 1, 0, 4, 1, 0, 0, need, 0, None) == glq.GLQ_ERR_WORKSPACE
+    assert lib.glq_fused_linear(po, 1, 0, 4, 1, 0, 257, need, 0, None) == glq.GLQ_ERR_WORKSPACE  # alignment
+    assert lib.glq_fused_linear(po, 1, 5, 4, 1, 0, 256, need, 0, None) == glq.GLQ_ERR_ARG        # dtype
+    assert lib.glq_fused_linear(po, 1, 0, 4, 1, 0, 256, need, 8, None) == glq.GLQ_ERR_ARG        # flags
+    assert lib.glq_fused_linear(po, 1, 0, 0, 1, 0, 256, need, 0, None) == glq.GLQ_OK             # m == 0
+    assert lib.glq_rht_apply(1, 0, 1, 0, 0, 64, 1, 0, None) == glq.GLQ_OK                       # rows == 0
+    assert lib.glq_rht_apply(1, 0, 1, 0, 4, 64, 1, 2, None) == glq.GLQ_ERR_ARG                  # transpose
+    assert lib.glq_rht_apply(1, 0, 1, 1, 4, 64, 1, 0, None) == glq.GLQ_ERR_ARG                  # in place, dtype change
+    big = glq.GlqLayerStruct(16, 65536 * 2, 2, 0, 1.0, 1, 0, 1, 1, 1)                          # Hadamard block 131072
+    nb = lib.glq_fused_linear_workspace(ctypes.byref(big), 1)
+    assert lib.glq_fused_linear(ctypes.byref(big), 1, 0, 1, 1, 0, 256, nb, 0, None) == glq.GLQ_ERR_UNSUPPORTED
