@@ -27,6 +27,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
 
 #include "glq.h"
 #include "glq_tables.h"
@@ -465,7 +466,13 @@ gemv_f32(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const floa
 }
 
 // ---------------------------------------------------------------- host helpers
-int hip_status(hipError_t e) { return e == hipSuccess ? GLQ_OK : GLQ_ERR_HIP; }
+thread_local char g_last_error[256] = "";
+
+int hip_status(hipError_t e, const char *where = "launch") {
+  if (e == hipSuccess) return GLQ_OK;
+  snprintf(g_last_error, sizeof g_last_error, "%s: %s (%d)", where, hipGetErrorString(e), (int)e);
+  return GLQ_ERR_HIP;
+}
 
 constexpr int kMaxLogBlock = 14;   // Hadamard block <= 16384 (64 KiB of float32 in LDS)
 
@@ -509,7 +516,8 @@ template <class K>
 int allow_lds(K kernel, size_t bytes) {
   if (bytes <= 60 * 1024) return GLQ_OK;
   return hip_status(hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes));
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes),
+                    "hipFuncSetAttribute");
 }
 
 bool valid_dtype(int dt) { return dt == GLQ_F32 || dt == GLQ_BF16; }
@@ -631,6 +639,8 @@ extern "C" int glq_decode_weights(const glq_layer *L, void *w_out, glq_dtype out
     default: return launch_decode<4>(L, w_out, out_dt, st);
   }
 }
+
+extern "C" const char *glq_last_error(void) { return g_last_error; }
 
 extern "C" size_t glq_fused_linear_workspace(const glq_layer *L, int64_t m) {
   if (!L || m <= 0 || L->n < 1 || L->k < 8) return 0;

@@ -22,7 +22,14 @@ GLQ_CB_INT8_2X, GLQ_CB_DEVICE = 0, 1
 FLAG_NO_INPUT_RHT, FLAG_NO_OUTPUT_RHT = 1, 2
 
 EXPORTS = ("glq_build_codebook", "glq_encode_ref", "glq_rht_apply", "glq_decode_weights",
-           "glq_fused_linear_workspace", "glq_fused_linear", "glq_status_string", "glq_version")
+           "glq_fused_linear_workspace", "glq_fused_linear", "glq_status_string", "glq_last_error",
+           "glq_version")
+
+# torch's wheel bundles its own HIP runtime (libamdhip64.so, same soname as
+# /opt/rocm's). Load torch first so libglq.so binds to that one runtime:
+# loaded the other way round the process ends up with two HIP/HSA runtimes
+# and neither sees the device.
+import torch  # noqa: E402,F401
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"libglq.so not built at {LIB_PATH}: run python -m dequant_e8_codebook_amd.build")
@@ -48,6 +55,7 @@ _lib.glq_fused_linear.argtypes = [ctypes.POINTER(GlqLayerStruct), _vp, _i32, _i6
 _lib.glq_status_string.argtypes = [_i32]
 _lib.glq_status_string.restype = ctypes.c_char_p
 _lib.glq_version.restype = _u32
+_lib.glq_last_error.restype = ctypes.c_char_p
 for _name in ("glq_build_codebook", "glq_encode_ref", "glq_rht_apply", "glq_decode_weights",
               "glq_fused_linear"):
     getattr(_lib, _name).restype = ctypes.c_int
@@ -55,7 +63,8 @@ for _name in ("glq_build_codebook", "glq_encode_ref", "glq_rht_apply", "glq_deco
 
 class GlqError(RuntimeError):
     def __init__(self, status: int, what: str):
-        super().__init__(f"{what}: {status_string(status)} ({status})")
+        detail = _lib.glq_last_error().decode() if status == GLQ_ERR_HIP else ""
+        super().__init__(f"{what}: {status_string(status)} ({status}) {detail}".rstrip())
         self.status = status
 
 

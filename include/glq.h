@@ -162,6 +162,11 @@ int glq_fused_linear(const glq_layer *L, const void *x, glq_dtype x_dt, int64_t 
 /* Static text for a status code. */
 const char *glq_status_string(int status);
 
+/* Text of the last HIP failure seen by a GPU call on this thread ("" if none):
+ * the HIP call or launch, its error string and code. Static storage, valid
+ * until the next GPU call on the same thread. */
+const char *glq_last_error(void);
+
 /* Library and codebook-format version, e.g. 0x00010000. */
 uint32_t glq_version(void);
 
