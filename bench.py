@@ -1,0 +1,349 @@
+"""Benchmark of the fused E8-decode linear layer on one MI355X.
+
+Default workload: the 4096x4096, 2 bpw, batch-1 layer (bf16 activations with
+8 outlier channels at 20x, Student-t(5) weights of std 0.02). One step is one
+full layer forward y = U^T (s W^) (V x): input RHT, fused decode-GEMV, output
+RHT, all in libglq.so. Steps rotate through --layers distinct copies of the
+layer's index planes (128 x 4 MiB = 512 MiB, twice the 256 MB Infinity
+Cache), so each step streams its compressed weights from HBM.
+
+value = compressed-weight bytes moved per second (GB/s) over the timed steps.
+roofline = the dominant kernel (the fused decode-GEMV) timed alone with HIP
+events around each launch on the launch stream: compressed bytes per launch /
+mean launch duration, against 8 TB/s HBM. traffic = HBM bytes per launch from
+rocprofv3 FETCH_SIZE + WRITE_SIZE counters (profiles/), scaled by what the
+counters read for a plain copy of known size; null if the kernel source has
+changed since those counters were taken.
+cpu_baseline = the oracle's layer forward on the host (float64), on a bounded
+sample of layer forwards of the same workload.
+
+Other modes (profiling helpers, not bench lines):
+  --workload batch16|prefill_up|dit_block|small   time another workload
+  --copy-calibration                              a plain device copy of known size
+  --pmc-summary DIR                               turn rocprofv3 counter CSVs into a profile file
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+KERNEL_SRC = os.path.join(ROOT, "dequant_e8_codebook_amd", "csrc", "glq_kernels.hip")
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+COPY_BYTES = 256 << 20
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _profile_path(workload):
+    return os.path.join(PROFILE_DIR, f"pmc_traffic_{workload}.txt")
+
+
+def read_traffic(workload, dominant):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    profile, or None if absent or taken on a different kernel source."""
+    p = _profile_path(workload)
+    if not os.path.exists(p):
+        return None
+    kv = {}
+    for line in open(p):
+        if ":" in line and not line.startswith("#"):
+            a, b = line.split(":", 1)
+            kv[a.strip()] = b.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash() or kv.get("kernel") != dominant:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------------ workload
+
+def build_layers(workload, n_layers, device):
+    import numpy as np
+    import torch
+    from dequant_e8_codebook_amd import glq
+    import workloads as wl
+
+    specs = wl.layer_specs(workload)
+    cb = glq.device_codebook(device)
+    built = []
+    for spec in specs:
+        w = wl.weights(spec).astype(np.float32)
+        sn, sk = wl.sign_n(spec), wl.sign_k(spec)
+        i1, i2, s = glq.encode_ref(w, spec.bpw, sn, sk)
+        base = glq.Layer.from_numpy(i1, i2, s, sn, sk, cb, device=device)
+        copies = [base]
+        for _ in range(n_layers - 1):
+            copies.append(glq.Layer(base.n, base.k, base.bpw, base.scale, base.idx1.clone(),
+                                    None if base.idx2 is None else base.idx2.clone(),
+                                    base.sign_k, base.sign_n, cb))
+        x = wl.activations(spec)
+        xdt = torch.float32 if spec.x_dtype == "f32" else torch.bfloat16
+        ydt = torch.float32 if spec.y_dtype == "f32" else torch.bfloat16
+        xt = torch.from_numpy(x).to(device=device, dtype=xdt)
+        y = torch.empty((spec.m, spec.n), device=device, dtype=ydt)
+        ws = torch.empty(glq.workspace_bytes(base, spec.m), device=device, dtype=torch.uint8)
+        built.append(dict(spec=spec, layers=copies, x=xt, y=y, ws=ws, idx=(i1, i2, s, sn, sk), xnp=x))
+    return built
+
+
+def dominant_kernel(spec):
+    if spec.x_dtype == "f32":
+        return f"gemv_f32<{spec.bpw}>"
+    return f"gemv_bf16<{spec.bpw}>" if spec.m <= 16 else f"gemm_bf16<{spec.bpw}>"
+
+
+def run_bench(args):
+    import numpy as np
+    import torch
+    from dequant_e8_codebook_amd import glq
+    from workloads import layer_specs
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    specs = layer_specs(args.workload)
+    per_step_layers = len(specs)
+    n_rot = args.layers if per_step_layers == 1 else max(1, args.layers // 16)
+    built = build_layers(args.workload, n_rot, dev)
+    comp_bytes = sum(b["layers"][0].idx1.numel() * 2 + (0 if b["layers"][0].idx2 is None else
+                     b["layers"][0].idx2.numel() * b["layers"][0].idx2.element_size()) for b in built)
+    flops = sum(2.0 * b["spec"].m * b["spec"].n * b["spec"].k for b in built)
+
+    def step(i):
+        for b in built:
+            L = b["layers"][i % len(b["layers"])]
+            glq.fused_linear(L, b["x"], b["y"], b["ws"])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t0.elapsed_time(t1)
+    ms_step = ms / args.steps
+    gbs = comp_bytes * args.steps / (ms * 1e-3) / 1e9
+    tflops = flops * args.steps / (ms * 1e-3) / 1e12
+
+    # dominant kernel alone: x pre-rotated, output left in the rotated basis
+    b0 = built[0]
+    spec0 = b0["spec"]
+    xr = b0["x"].clone()
+    sk = b0["layers"][0].sign_k
+    glq.rht_apply(b0["x"], xr, sk, False)
+    z = torch.empty_like(b0["y"])
+    n_k = max(args.kernel_launches, len(b0["layers"]))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_k)]
+    for i in range(len(b0["layers"])):       # warm the rotation
+        glq.fused_linear(b0["layers"][i], xr, z, b0["ws"], glq.FLAG_NO_INPUT_RHT | glq.FLAG_NO_OUTPUT_RHT)
+    torch.cuda.synchronize()
+    for i in range(n_k):
+        L = b0["layers"][i % len(b0["layers"])]
+        evs[i][0].record()
+        glq.fused_linear(L, xr, z, b0["ws"], glq.FLAG_NO_INPUT_RHT | glq.FLAG_NO_OUTPUT_RHT)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    durs = np.array([a.elapsed_time(c) for a, c in evs]) * 1e-3      # seconds
+    k_mean = float(durs.mean())
+    L0 = b0["layers"][0]
+    k_bytes = L0.idx1.numel() * 2 + (0 if L0.idx2 is None else L0.idx2.numel() * L0.idx2.element_size())
+    k_flops = 2.0 * spec0.m * spec0.n * spec0.k
+    dom = dominant_kernel(spec0)
+    hbm_bound = spec0.m <= 16
+    if hbm_bound:
+        achieved = k_bytes / k_mean / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 2), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4))
+    else:
+        achieved = k_flops / k_mean / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / MFMA_BF16_PEAK_TFLOPS, 4))
+    traffic = read_traffic(args.workload, dom)
+    roof["traffic"] = traffic
+    roof["kernel"] = dom
+    roof["kernel_mean_us"] = round(k_mean * 1e6, 3)
+    roof["kernel_median_us"] = round(float(np.median(durs)) * 1e6, 3)
+    roof["algorithmic_bytes_per_launch"] = k_bytes
+    roof["algorithmic_flops_per_launch"] = k_flops
+
+    out = {
+        "metric": "fused E8-decode linear TFLOP/s + compressed-weight GB/s (% roofline), 1 MI355X",
+        "value": round(gbs, 2) if hbm_bound else round(tflops, 3),
+        "unit": "GB/s" if hbm_bound else "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload,
+                   "layers": [f"{b['spec'].n}x{b['spec'].k}" for b in built],
+                   "bpw": spec0.bpw, "m": spec0.m, "x_dtype": spec0.x_dtype,
+                   "distinct_layer_copies": len(b0["layers"]),
+                   "step": "full layer forward: input RHT + fused decode-matmul + output RHT"},
+        "tflops": round(tflops, 4), "compressed_gbs": round(gbs, 2),
+        "wall_s_timed": round(wall, 4),
+        "roofline": roof,
+    }
+    return out, built
+
+
+def cpu_baseline(built, budget_s):
+    """The oracle's float64 layer forward on the host, timed on a bounded sample."""
+    import numpy as np
+    from oracle import glq as og
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    b = built[0]
+    spec = b["spec"]
+    i1, i2, s, sn, sk = b["idx"]
+    x = b["xnp"]
+    rows = min(spec.m, 4)
+    n_done = 0
+    t0 = time.perf_counter()
+    while True:
+        og.layer_reference(x[:rows], i1, i2, spec.bpw, s, sn, sk)
+        n_done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    comp = i1.size * 2 + (0 if i2 is None else i2.size * i2.itemsize)
+    gbs = n_done * comp / dt / 1e9
+    return {"value": round(gbs, 5), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n_done} layer forwards of {spec.n}x{spec.k} at {spec.bpw} bpw, {rows} activation row(s) "
+                      f"each (decode + float64 RHTs + matmul), {dt:.1f} s; compressed bytes per second",
+            "cpu_model": _cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# ------------------------------------------------------------------ profiling helpers
+
+def copy_calibration():
+    """A plain device-to-device copy of COPY_BYTES (for counter calibration)."""
+    import torch
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 5}))
+
+
+def _read_counters(d):
+    """{(kernel_name, counter): [values per dispatch]} from rocprofv3 counter CSVs."""
+    vals = {}
+    for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(p) as f:
+            for row in csv.DictReader(f):
+                key = (row.get("Kernel_Name", ""), row.get("Counter_Name", ""))
+                try:
+                    vals.setdefault(key, []).append(float(row.get("Counter_Value", "nan")))
+                except ValueError:
+                    pass
+    return vals
+
+
+def pmc_summary(args):
+    """Write profiles/pmc_traffic_<workload>.txt from four counter runs:
+    copy FETCH, copy WRITE, bench FETCH, bench WRITE (directories given)."""
+    cf, cw, bf, bw = args.pmc_summary
+    kernel_pat = args.pmc_kernel
+    def pick(d, counter, pat):
+        v = _read_counters(d)
+        sel = [x for (k, c), xs in v.items() if c == counter and pat in k for x in xs]
+        if not sel:
+            raise SystemExit(f"no {counter} values for kernels matching {pat!r} in {d}")
+        return sel
+    copy_kib = COPY_BYTES / 1024.0
+    cfetch = pick(cf, "FETCH_SIZE", args.copy_kernel)
+    cwrite = pick(cw, "WRITE_SIZE", args.copy_kernel)
+    f_fac = copy_kib / max(cfetch)          # the largest dispatch is the full copy
+    w_fac = copy_kib / max(cwrite)
+    kf = pick(bf, "FETCH_SIZE", kernel_pat)
+    kw = pick(bw, "WRITE_SIZE", kernel_pat)
+    import statistics
+    mf, mw = statistics.median(kf), statistics.median(kw)
+    hbm = (mf * f_fac + mw * w_fac) * 1024.0
+    os.makedirs(PROFILE_DIR, exist_ok=True)
+    with open(_profile_path(args.workload), "w") as f:
+        f.write("# HBM traffic of the dominant kernel from rocprofv3 counters (KiB per dispatch),\n"
+                "# scaled by copy_bytes / counter reading of a plain device copy of known size.\n")
+        f.write(f"# commands: {args.pmc_commands}\n" if args.pmc_commands else "")
+        f.write(f"workload: {args.workload}\nkernel: {args.pmc_kernel_label}\n")
+        f.write(f"kernel_source_sha256_16: {kernel_source_hash()}\n")
+        f.write(f"dispatches_fetch: {len(kf)}\ndispatches_write: {len(kw)}\n")
+        f.write(f"fetch_kib_per_dispatch_median: {mf:.1f}\nwrite_kib_per_dispatch_median: {mw:.1f}\n")
+        f.write(f"copy_fetch_factor: {f_fac:.4f}\ncopy_write_factor: {w_fac:.4f}\n")
+        f.write(f"hbm_bytes_per_dispatch: {hbm:.0f}\n")
+    print(open(_profile_path(args.workload)).read())
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1024)
+    ap.add_argument("--warmup", type=int, default=128)
+    ap.add_argument("--workload", default="gemv", choices=["small", "gemv", "batch16", "prefill_up", "dit_block"])
+    ap.add_argument("--layers", type=int, default=128, help="distinct copies of the index planes rotated through")
+    ap.add_argument("--kernel-launches", type=int, default=512)
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("COPY_FETCH", "COPY_WRITE", "BENCH_FETCH", "BENCH_WRITE"))
+    ap.add_argument("--pmc-kernel", default="gemv_bf16")
+    ap.add_argument("--pmc-kernel-label", default="gemv_bf16<2>")
+    ap.add_argument("--copy-kernel", default="")
+    ap.add_argument("--pmc-commands", default="")
+    args = ap.parse_args()
+
+    if args.pmc_summary:
+        pmc_summary(args)
+        return 0
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(rows of x or output features would shard with no exchange; see the design notes).",
+              file=sys.stderr)
+        return 2
+    if args.copy_calibration:
+        copy_calibration()
+        return 0
+    out, built = run_bench(args)
+    out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(built, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
