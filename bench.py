@@ -129,44 +129,75 @@ def run_bench(args):
             L = b["layers"][i % len(b["layers"])]
             glq.fused_linear(L, b["x"], b["y"], b["ws"])
 
-    for i in range(args.warmup):
+    # The timed steps replay a HIP graph holding one step per distinct layer
+    # copy (captured through torch's CUDA-graph API, on its capture stream), so
+    # the measurement sees GPU time, not Python/ctypes launch overhead.
+    per_graph = len(built[0]["layers"])
+    for i in range(max(args.warmup, 1)):
         step(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(per_graph):
+            step(i)
+    replays = max(1, args.steps // per_graph)
+    steps_timed = replays * per_graph
+    for _ in range(max(1, args.warmup // per_graph)):
+        graph.replay()
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record()
-    for i in range(args.steps):
-        step(args.warmup + i)
+    for _ in range(replays):
+        graph.replay()
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms = t0.elapsed_time(t1)
-    ms_step = ms / args.steps
-    gbs = comp_bytes * args.steps / (ms * 1e-3) / 1e9
-    tflops = flops * args.steps / (ms * 1e-3) / 1e12
+    ms_step = ms / steps_timed
+    gbs = comp_bytes * steps_timed / (ms * 1e-3) / 1e9
+    tflops = flops * steps_timed / (ms * 1e-3) / 1e12
 
-    # dominant kernel alone: x pre-rotated, output left in the rotated basis
+    # eager (no graph) rate of the same steps, for reference
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    n_eager = min(steps_timed, 256)
+    e0.record()
+    for i in range(n_eager):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    eager_ms_step = e0.elapsed_time(e1) / n_eager
+
+    # dominant kernel alone (x pre-rotated, output left rotated): a graph of
+    # one launch per layer copy, replayed; mean launch = time / launches
     b0 = built[0]
     spec0 = b0["spec"]
     xr = b0["x"].clone()
     sk = b0["layers"][0].sign_k
     glq.rht_apply(b0["x"], xr, sk, False)
     z = torch.empty_like(b0["y"])
-    n_k = max(args.kernel_launches, len(b0["layers"]))
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_k)]
-    for i in range(len(b0["layers"])):       # warm the rotation
-        glq.fused_linear(b0["layers"][i], xr, z, b0["ws"], glq.FLAG_NO_INPUT_RHT | glq.FLAG_NO_OUTPUT_RHT)
+    flags = glq.FLAG_NO_INPUT_RHT | glq.FLAG_NO_OUTPUT_RHT
+    for L in b0["layers"]:
+        glq.fused_linear(L, xr, z, b0["ws"], flags)
     torch.cuda.synchronize()
-    for i in range(n_k):
-        L = b0["layers"][i % len(b0["layers"])]
-        evs[i][0].record()
-        glq.fused_linear(L, xr, z, b0["ws"], glq.FLAG_NO_INPUT_RHT | glq.FLAG_NO_OUTPUT_RHT)
-        evs[i][1].record()
+    kgraph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(kgraph):
+        for L in b0["layers"]:
+            glq.fused_linear(L, xr, z, b0["ws"], flags)
+    krep = max(1, args.kernel_launches // len(b0["layers"]))
+    kgraph.replay()
     torch.cuda.synchronize()
-    durs = np.array([a.elapsed_time(c) for a, c in evs]) * 1e-3      # seconds
-    k_mean = float(durs.mean())
+    k0 = torch.cuda.Event(enable_timing=True)
+    k1 = torch.cuda.Event(enable_timing=True)
+    k0.record()
+    for _ in range(krep):
+        kgraph.replay()
+    k1.record()
+    torch.cuda.synchronize()
+    k_mean = k0.elapsed_time(k1) * 1e-3 / (krep * len(b0["layers"]))
+    # rotated-basis launches of 3/4 bpw also run a small row-sum kernel
     L0 = b0["layers"][0]
     k_bytes = L0.idx1.numel() * 2 + (0 if L0.idx2 is None else L0.idx2.numel() * L0.idx2.element_size())
     k_flops = 2.0 * spec0.m * spec0.n * spec0.k
@@ -184,7 +215,7 @@ def run_bench(args):
     roof["traffic"] = traffic
     roof["kernel"] = dom
     roof["kernel_mean_us"] = round(k_mean * 1e6, 3)
-    roof["kernel_median_us"] = round(float(np.median(durs)) * 1e6, 3)
+    roof["timing"] = f"HIP events around {krep} replays of a graph of {len(b0['layers'])} launches"
     roof["algorithmic_bytes_per_launch"] = k_bytes
     roof["algorithmic_flops_per_launch"] = k_flops
 
@@ -192,7 +223,7 @@ def run_bench(args):
         "metric": "fused E8-decode linear TFLOP/s + compressed-weight GB/s (% roofline), 1 MI355X",
         "value": round(gbs, 2) if hbm_bound else round(tflops, 3),
         "unit": "GB/s" if hbm_bound else "TFLOP/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "n_gpus": 1, "steps": steps_timed, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": args.workload,
@@ -201,6 +232,7 @@ def run_bench(args):
                    "distinct_layer_copies": len(b0["layers"]),
                    "step": "full layer forward: input RHT + fused decode-matmul + output RHT"},
         "tflops": round(tflops, 4), "compressed_gbs": round(gbs, 2),
+        "eager_ms_per_step": round(eager_ms_step, 5),
         "wall_s_timed": round(wall, 4),
         "roofline": roof,
     }
@@ -317,7 +349,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=128)
     ap.add_argument("--workload", default="gemv", choices=["small", "gemv", "batch16", "prefill_up", "dit_block"])
     ap.add_argument("--layers", type=int, default=128, help="distinct copies of the index planes rotated through")
-    ap.add_argument("--kernel-launches", type=int, default=512)
+    ap.add_argument("--kernel-launches", type=int, default=1024)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")

@@ -13,11 +13,11 @@
 //                   optionally rounds to bf16 and records each row's sum of the
 //                   rounded values (needed by the biased 3/4 bpw operands).
 //   decode_weights  indices -> W^ (rotated basis) as float32 or bf16.
-//   gemv_bf16       m <= 16: one 16-row weight tile per workgroup, 4 waves split
+//   gemv_bf16       m <= 16: one 16-row weight tile per workgroup, 16 waves split
 //                   k, bf16 MFMA 16x16x32 with x~ rows as the M side (the few
 //                   activation rows are padded to 16) and weights decoded
 //                   straight into the B operand registers.
-//   gemm_bf16       m > 16: 128 x 128 output tiles, x~ staged through LDS,
+//   gemm_bf16       m > 16: 256 x 256 output tiles, x~ double-buffered in LDS,
 //                   weights decoded per wave straight into MFMA B operands.
 //   gemv_f32        float32 path: exact float32 weights, float32 FMAs.
 //
@@ -25,6 +25,7 @@
 // the caller's GLQ_CB_DEVICE buffer into LDS.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -54,21 +55,31 @@ template <> struct TabCfg<4> { static constexpr uint32_t ht1 = kHtA4Off, ht2 = k
 template <int BPW>
 constexpr uint32_t lds_table_bytes() { return kLdsHt2 + TabCfg<BPW>::ht2_bytes; }
 
-// Copy CT + OT + the two value tables of this bit width into LDS.
-template <int BPW>
+// Copy CT + OT + the two value tables of this bit width into LDS. Each
+// thread first issues all of its 16-byte loads (clamped addresses, no
+// branches) and only then writes LDS, so the global-memory latency is paid
+// once per workgroup instead of once per chunk.
+template <int BPW, int NT = 256>
 __device__ __forceinline__ void load_tables(uint8_t *lds, const uint8_t *blob) {
-  const uint32_t tid = threadIdx.x, nt = blockDim.x;
-  // CT and OT are contiguous in the blob and in LDS
-  const uint4 *src0 = reinterpret_cast<const uint4 *>(blob + kCtOff);
-  uint4 *dst0 = reinterpret_cast<uint4 *>(lds + kLdsCt);
-  for (uint32_t i = tid; i < (kCtBytes + kOtBytes) / 16; i += nt) dst0[i] = src0[i];
-  const uint4 *src1 = reinterpret_cast<const uint4 *>(blob + TabCfg<BPW>::ht1);
-  uint4 *dst1 = reinterpret_cast<uint4 *>(lds + kLdsHt1);
-  for (uint32_t i = tid; i < kHtBytes / 16; i += nt) dst1[i] = src1[i];
-  if constexpr (TabCfg<BPW>::ht2_bytes > 0) {
-    const uint4 *src2 = reinterpret_cast<const uint4 *>(blob + TabCfg<BPW>::ht2);
-    uint4 *dst2 = reinterpret_cast<uint4 *>(lds + kLdsHt2);
-    for (uint32_t i = tid; i < TabCfg<BPW>::ht2_bytes / 16; i += nt) dst2[i] = src2[i];
+  constexpr uint32_t c01 = (kCtBytes + kOtBytes) / 16;          // CT + OT (contiguous in both)
+  constexpr uint32_t c2 = c01 + kHtBytes / 16;                   // + stage-1 half table
+  constexpr uint32_t total = lds_table_bytes<BPW>() / 16;
+  constexpr uint32_t per = (total + NT - 1) / NT;
+  static_assert(kLdsCt == 0 && kLdsOt == kCtBytes && kLdsHt1 == kCtBytes + kOtBytes, "LDS table order");
+  const uint32_t tid = threadIdx.x;       // blockDim.x == NT
+  uint4 v[per];
+#pragma unroll
+  for (uint32_t r = 0; r < per; ++r) {
+    const uint32_t i = min(tid + NT * r, total - 1);
+    const uint32_t src = i < c01 ? kCtOff + 16 * i
+                       : i < c2  ? TabCfg<BPW>::ht1 + 16 * (i - c01)
+                                 : TabCfg<BPW>::ht2 + 16 * (i - c2);
+    v[r] = *reinterpret_cast<const uint4 *>(blob + src);
+  }
+#pragma unroll
+  for (uint32_t r = 0; r < per; ++r) {
+    const uint32_t i = tid + NT * r;
+    if (i < total) reinterpret_cast<uint4 *>(lds)[i] = v[r];
   }
 }
 
@@ -235,6 +246,119 @@ rht_rows(const void *in, glq_dtype in_dt, void *out, glq_dtype out_dt, int64_t r
   }
 }
 
+// Vectorised RHT: one workgroup (256 threads) per row, the whole row in LDS
+// as float32 (n % 8 == 0, n <= 32768). Each thread moves 8-element pieces
+// with 16-byte loads, issued 4 at a time before any LDS write; the row sum of
+// the (rounded) outputs is reduced in the workgroup, so it is deterministic.
+constexpr int RV_MAX = 32768;
+
+template <bool IN_BF16>
+__device__ __forceinline__ void rv_load_piece(const void *in, size_t e0, float (&v)[8]) {
+  if constexpr (IN_BF16) {
+    const uint4 u = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(in) + e0);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      v[2 * t] = __uint_as_float(w[t] << 16);
+      v[2 * t + 1] = __uint_as_float(w[t] & 0xFFFF0000u);
+    }
+  } else {
+    const float4 a = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(in) + e0);
+    const float4 b = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(in) + e0 + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+__device__ __forceinline__ void rv_signs(const int8_t *signs, int64_t i0, float (&sg)[8]) {
+  const uint2 u = *reinterpret_cast<const uint2 *>(signs + i0);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) sg[t] = (float)(int8_t)(((t < 4 ? u.x : u.y) >> (8 * (t & 3))) & 0xFF);
+}
+
+template <bool IN_BF16, bool OUT_BF16, bool TRANSPOSE>
+__global__ void __launch_bounds__(256)
+rht_rows_vec(const void *in, void *out, int64_t rows, int64_t n, int logb, const int8_t *signs,
+             float *rowsum) {
+  extern __shared__ float buf[];
+  __shared__ float red[4];
+  const int b = 1 << logb;
+  const float inv = 1.0f / sqrtf((float)b);   // exact for even logb
+  const int pieces = (int)(n >> 3);
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    const size_t base = (size_t)row * n;
+    __syncthreads();                           // previous row's readers are done with buf
+    for (int p0 = threadIdx.x; p0 < pieces; p0 += 4 * 256) {
+      float v[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int pc = min(p0 + 256 * u, pieces - 1);
+        rv_load_piece<IN_BF16>(in, base + 8 * (size_t)pc, v[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int pc = p0 + 256 * u;
+        if (pc < pieces) {
+          if (!TRANSPOSE) {
+            float sg[8];
+            rv_signs(signs, 8 * (int64_t)pc, sg);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) v[u][t] *= sg[t];
+          }
+          float4 *d = reinterpret_cast<float4 *>(buf + 8 * pc);
+          d[0] = make_float4(v[u][0], v[u][1], v[u][2], v[u][3]);
+          d[1] = make_float4(v[u][4], v[u][5], v[u][6], v[u][7]);
+        }
+      }
+    }
+    __syncthreads();
+    int lo = 0;
+    for (; lo + 4 <= logb; lo += 4) { fwht_pass<16>(buf, (int)n, lo); __syncthreads(); }
+    switch (logb - lo) {
+      case 1: fwht_pass<2>(buf, (int)n, lo); break;
+      case 2: fwht_pass<4>(buf, (int)n, lo); break;
+      case 3: fwht_pass<8>(buf, (int)n, lo); break;
+      default: break;
+    }
+    __syncthreads();
+    float rs = 0.0f;
+    for (int pc = threadIdx.x; pc < pieces; pc += 256) {
+      const float4 a = reinterpret_cast<const float4 *>(buf + 8 * pc)[0];
+      const float4 c = reinterpret_cast<const float4 *>(buf + 8 * pc)[1];
+      float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+      float sg[8];
+      if (TRANSPOSE) rv_signs(signs, 8 * (int64_t)pc, sg);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        v[t] *= inv;
+        if (TRANSPOSE) v[t] *= sg[t];
+      }
+      if constexpr (OUT_BF16) {
+        uint32_t w[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint16_t h0 = f32_to_bf16_rne(v[2 * t]), h1 = f32_to_bf16_rne(v[2 * t + 1]);
+          w[t] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+          rs += __uint_as_float((uint32_t)h0 << 16) + __uint_as_float((uint32_t)h1 << 16);
+        }
+        *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(out) + base + 8 * (size_t)pc) =
+            make_uint4(w[0], w[1], w[2], w[3]);
+      } else {
+        float *o = reinterpret_cast<float *>(out) + base + 8 * (size_t)pc;
+        reinterpret_cast<float4 *>(o)[0] = make_float4(v[0], v[1], v[2], v[3]);
+        reinterpret_cast<float4 *>(o)[1] = make_float4(v[4], v[5], v[6], v[7]);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) rs += v[t];
+      }
+    }
+    if (rowsum) {
+      for (int off = 32; off > 0; off >>= 1) rs += __shfl_xor(rs, off);
+      if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = rs;
+      __syncthreads();
+      if (threadIdx.x == 0) rowsum[row] = red[0] + red[1] + red[2] + red[3];
+    }
+  }
+}
+
 // row sums of a bf16 [rows][n] array (x already rotated, biased operands need them)
 __global__ void __launch_bounds__(256)
 row_sums_bf16(const uint16_t *x, int64_t rows, int64_t n, float *rowsum) {
@@ -286,140 +410,271 @@ decode_weights_k(const uint16_t *idx1, const void *idx2, const uint8_t *blob, fl
 }
 
 // ---------------------------------------------------------------- GEMV (m <= 16)
-// Workgroup = 4 waves, one 16-row weight tile n0..n0+15. The k axis is cut in
-// chunks of 32 groups (256 inputs); wave w takes chunks w, w+4, ... In a chunk,
-// lane l (row j = l & 15, k-slot q = l >> 4) owns groups 32c + 8q .. 32c + 8q + 7
-// of weight row n0 + j, and MFMA step s contracts group 32c + 8q + s of every
-// slot: A = x~ rows (m = l & 15, zero-padded beyond m), B = decoded weights.
-template <int BPW>
-__global__ void __launch_bounds__(256)
+// Workgroup = 16 waves (4 per SIMD, so the SIMDs switch waves while loads are
+// in flight), one 16-row weight tile n0 .. n0 + 15. The k axis is cut in
+// chunks of 32 groups (256 inputs); wave w takes chunks w, w + 16, ... In a
+// chunk, lane l (weight row j = l & 15, k-slot q = l >> 4) owns groups
+// 32c + 8q .. 32c + 8q + 7 of row n0 + j (one 16-byte index load), and MFMA
+// 16x16x32 step s contracts group 32c + 8q + s of every slot: A = x~ rows
+// (m = l & 15, zero beyond m; the M side of the tile is the activation rows),
+// B = decoded weights. All loads of a chunk are issued before its first
+// decode. Partial sums of the 16 waves meet in LDS.
+constexpr int GV_WAVES = 16;
+
+template <int BPW, bool G8>
+__device__ __forceinline__ void gv_load_idx(const uint16_t *idx1, const void *idx2, int64_t row, int64_t G,
+                                            int64_t g0, uint32_t (&i1)[8], uint32_t (&i2)[8]) {
+  // row is clamped to the layer; groups past G are clamped (they meet zero x~)
+  if constexpr (G8) {
+    const int64_t off = row * G + min(g0, G - 8);
+    const uint4 a = *reinterpret_cast<const uint4 *>(idx1 + off);
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) { i1[2 * u] = w[u] & 0xFFFFu; i1[2 * u + 1] = w[u] >> 16; }
+    if constexpr (BPW == 3) {
+      const uint2 b = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint8_t *>(idx2) + off);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) { i2[u] = (b.x >> (8 * u)) & 0xFFu; i2[4 + u] = (b.y >> (8 * u)) & 0xFFu; }
+    } else if constexpr (BPW == 4) {
+      const uint4 b = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(idx2) + off);
+      const uint32_t x[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) { i2[2 * u] = x[u] & 0xFFFFu; i2[2 * u + 1] = x[u] >> 16; }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) i2[u] = 0;
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t o = row * G + min(g0 + u, G - 1);
+      i1[u] = idx1[o];
+      i2[u] = BPW > 2 ? load_idx2(idx2, o, BPW) : 0u;
+    }
+  }
+}
+
+template <int BPW, bool G8>
+__global__ void __launch_bounds__(64 * GV_WAVES, 1)
 gemv_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uint16_t *xt,
           const float *rowsum, int64_t m, int64_t n, int64_t k, float post, void *out,
           glq_dtype out_dt) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   float *red = reinterpret_cast<float *>(lds + lds_table_bytes<BPW>());
-  load_tables<BPW>(lds, blob);
-  __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 15, q = lane >> 4;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
-  const int64_t row = n0 + j;
-  const bool row_ok = row < n;
+  const int64_t row = min(n0 + j, n - 1);
   const int64_t G = k / 8;
   const int64_t chunks = (G + 31) / 32;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int64_t c = wave; c < chunks; c += 4) {
-    const int64_t g0 = 32 * c + 8 * q;
-    uint32_t i1s[8], i2s[8];
+  const bool a_row = j < m;
+  const uint16_t *xrow = xt + (size_t)min((int64_t)j, m - 1) * k;
+
+  // the first chunk's loads go out before the table copy; later chunks (k >
+  // 4096) are loaded one at a time: the other waves of the SIMD hide the wait
+  int64_t c = wave;
+  uint32_t i1[8], i2[8];
+  uint4 av[8];
+  auto load_chunk = [&](int64_t cc) {
+    const int64_t g0 = 32 * cc + 8 * q;
+    gv_load_idx<BPW, G8>(idx1, idx2, row, G, g0, i1, i2);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int64_t g = g0 + s;
-      const bool ok = row_ok && g < G;
-      i1s[s] = ok ? idx1[row * G + g] : 0u;
-      i2s[s] = (BPW > 2 && ok) ? load_idx2(idx2, row * G + g, BPW) : 0u;
+      const uint4 v = *reinterpret_cast<const uint4 *>(xrow + 8 * min(g, G - 1));
+      av[s] = (a_row && g < G) ? v : make_uint4(0, 0, 0, 0);
     }
+  };
+  if (c < chunks) load_chunk(c);
+  load_tables<BPW, 64 * GV_WAVES>(lds, blob);
+  __syncthreads();
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  while (c < chunks) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const int64_t g = g0 + s;
-      uint4 av = make_uint4(0, 0, 0, 0);
-      if (j < m && g < G) av = *reinterpret_cast<const uint4 *>(xt + (size_t)j * k + 8 * g);
-      const uint4 bv = decode_group<BPW>(i1s[s], i2s[s], lds);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+      const uint4 bv = decode_group<BPW>(i1[s], i2[s], lds);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[s]),
                                                     __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
     }
+    c += GV_WAVES;
+    if (c < chunks) load_chunk(c);
   }
-  // D[r][c]: lane holds rows 4*(lane>>4)+t (activation row), column lane&15 (weight row)
+  // D[r][col]: lane holds rows 4 (lane >> 4) + t (activation row), column lane & 15 (weight row)
 #pragma unroll
   for (int t = 0; t < 4; ++t) red[(wave * 16 + 4 * q + t) * 16 + j] = acc[t];
   __syncthreads();
-  if (wave == 0) {
+  if (threadIdx.x < 256) {
+    const int r = threadIdx.x >> 4, col = threadIdx.x & 15;
+    float v = 0.0f;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int r = 4 * q + t;
-      float v = red[(0 * 16 + r) * 16 + j] + red[(1 * 16 + r) * 16 + j] +
-                red[(2 * 16 + r) * 16 + j] + red[(3 * 16 + r) * 16 + j];
-      if (r < m && row_ok) {
-        if (Epi<BPW>::bias != 0.0f) v -= Epi<BPW>::bias * rowsum[r];
-        store_out(out, out_dt, (size_t)r * n + row, post * v);
-      }
+    for (int w = 0; w < GV_WAVES; ++w) v += red[(w * 16 + r) * 16 + col];
+    const int64_t nrow = n0 + col;
+    if (r < m && nrow < n) {
+      if (Epi<BPW>::bias != 0.0f) v -= Epi<BPW>::bias * rowsum[r];
+      store_out(out, out_dt, (size_t)r * n + nrow, post * v);
     }
   }
 }
 
 // ---------------------------------------------------------------- GEMM (m > 16)
-// Tile 128 (m) x 128 (n), 4 waves; wave w owns weight rows n0 + 32w .. +31 for
-// all 128 activation rows (8 x 2 MFMA 16x16 tiles). Per k-step of 32 inputs
-// the workgroup stages x~[128][32] in LDS; every wave decodes its own 32 x 4
-// groups straight into B operands (two per lane).
-constexpr int GM_BM = 128, GM_BN = 128, GM_LDA = 40;   // LDA in bf16 (row of 32 + pad 8)
+// Workgroup tile 256 (activation rows) x 256 (weight rows), 4 waves; wave w
+// owns weight rows n0 + 64w .. +63 for all 256 activation rows: 8 x 2 tiles of
+// MFMA 32x32x16 (bf16) whose B operands it decodes itself, straight into
+// registers (no weight tile goes through LDS). A k-step covers 64 inputs =
+// 8 groups; MFMA sub-step u (0..3) contracts, in k-slot p = lane >> 5,
+// group 8s + 4p + u, so lane (c = lane & 31, p) needs groups 8s + 4p .. +3 of
+// weight rows n0 + 32t + c: one 8-byte index load per tile. x~ is staged
+// through a double-buffered LDS tile [256][64 + 8] (one barrier per k-step),
+// fetched from global memory one step ahead into registers.
+//   MFMA 32x32x16 operand layout: A lane l = row l & 31, k 8(l >> 5) .. +7;
+//   B lane l = column l & 31, k 8(l >> 5) .. +7; D register i of lane l =
+//   row 8(i >> 2) + 4(l >> 5) + (i & 3), column l & 31.
+constexpr int GM_BM = 256, GM_BN = 256, GM_BK = 64, GM_LDA = GM_BK + 8;
+constexpr size_t GM_A_BYTES = (size_t)GM_BM * GM_LDA * 2;   // one buffer
 
-template <int BPW>
-__global__ void __launch_bounds__(256)
-gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uint16_t *xt,
-          const float *rowsum, int64_t m, int64_t n, int64_t k, float post, void *out,
-          glq_dtype out_dt) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  uint16_t *As = reinterpret_cast<uint16_t *>(lds + lds_table_bytes<BPW>());
-  load_tables<BPW>(lds, blob);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int j = lane & 15, q = lane >> 4;
-  const int64_t m0 = (int64_t)blockIdx.y * GM_BM;
-  const int64_t n0 = (int64_t)blockIdx.x * GM_BN + 32 * wave;
-  const int64_t G = k / 8;
-  f32x4 acc[8][2];
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Index planes for k-step s: rows nrow0 + 32 t + c (t = 0, 1), groups
+// 8 s + 4 p .. +3. Addresses are clamped into the planes instead of
+// branching: out-of-range rows are never stored, out-of-range groups meet
+// zero activations, and any index decodes to finite values. G4: k/8 is a
+// multiple of 4, so the 4 indices are one aligned 8-byte load.
+template <int BPW, bool G4>
+__device__ __forceinline__ void gm_load_idx(const uint16_t *idx1, const void *idx2, int64_t n,
+                                            int64_t G, int64_t nrow0, int c, int p, int64_t s,
+                                            uint2 (&i1)[2], uint2 (&i2)[2]) {
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
+  for (int t = 0; t < 2; ++t) {
+    const int64_t row = min(nrow0 + 32 * t + c, n - 1);
+    if constexpr (G4) {
+      const int64_t off = row * G + min(8 * s + 4 * p, G - 4);
+      i1[t] = *reinterpret_cast<const uint2 *>(idx1 + off);
+      if constexpr (BPW == 3) i2[t] = make_uint2(*reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint8_t *>(idx2) + off), 0u);
+      if constexpr (BPW == 4) i2[t] = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(idx2) + off);
+      if constexpr (BPW == 2) i2[t] = make_uint2(0u, 0u);
+    } else {
+      uint32_t w1[4], w2[4];
 #pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2) acc[a][b2] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int64_t ksteps = (G + 3) / 4;
-  for (int64_t ks = 0; ks < ksteps; ++ks) {
-    __syncthreads();
-    // stage x~[m0 .. m0+127][32 ks .. 32 ks + 31]: 512 16-byte pieces, 2 per thread
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int piece = threadIdx.x + 256 * p;
-      const int r = piece >> 2, cq = piece & 3;
-      const int64_t gm = m0 + r, g = 4 * ks + cq;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (gm < m && g < G) v = *reinterpret_cast<const uint4 *>(xt + (size_t)gm * k + 8 * g);
-      *reinterpret_cast<uint4 *>(As + r * GM_LDA + 8 * cq) = v;
-    }
-    // decode this wave's B operands: columns n0 + 16 t + j, group 4 ks + q
-    uint4 bv[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int64_t rowi = n0 + 16 * t + j, g = 4 * ks + q;
-      const bool ok = rowi < n && g < G;
-      const uint32_t i1 = ok ? idx1[rowi * G + g] : 0u;
-      const uint32_t i2 = (BPW > 2 && ok) ? load_idx2(idx2, rowi * G + g, BPW) : 0u;
-      bv[t] = decode_group<BPW>(i1, i2, lds);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int a = 0; a < 8; ++a) {
-      const uint4 av = *reinterpret_cast<const uint4 *>(As + (16 * a + j) * GM_LDA + 8 * q);
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-        acc[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
-                                                            __builtin_bit_cast(bf16x8, bv[t]),
-                                                            acc[a][t], 0, 0, 0);
+      for (int u = 0; u < 4; ++u) {
+        const int64_t o = row * G + min(8 * s + 4 * p + u, G - 1);
+        w1[u] = idx1[o];
+        w2[u] = BPW > 2 ? load_idx2(idx2, o, BPW) : 0u;
+      }
+      i1[t] = make_uint2(w1[0] | (w1[1] << 16), w1[2] | (w1[3] << 16));
+      if constexpr (BPW == 3) i2[t] = make_uint2(w2[0] | (w2[1] << 8) | (w2[2] << 16) | (w2[3] << 24), 0u);
+      else i2[t] = make_uint2(w2[0] | (w2[1] << 16), w2[2] | (w2[3] << 16));
     }
   }
+}
+
+// x~ tile of k-step s: 256 rows x 64 inputs (128 B per row); piece
+// pc = tid + 256 u is row pc >> 3, 16-byte column pc & 7. Clamped loads,
+// zeroed outside [0, m) x [0, k).
+__device__ __forceinline__ void gm_load_a(const uint16_t *xt, int64_t m, int64_t k, int64_t m0, int64_t s,
+                                          uint4 (&ra)[8]) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int pc = threadIdx.x + 256 * u;
+    const int64_t r = m0 + (pc >> 3);
+    const int64_t kk = GM_BK * s + 8 * (pc & 7);
+    const bool ok = r < m && kk < k;
+    const uint4 v = *reinterpret_cast<const uint4 *>(xt + (size_t)min(r, m - 1) * k + min(kk, k - 8));
+    ra[u] = ok ? v : make_uint4(0, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void gm_store_a(uint16_t *As, const uint4 (&ra)[8]) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int pc = threadIdx.x + 256 * u;
+    *reinterpret_cast<uint4 *>(As + (pc >> 3) * GM_LDA + 8 * (pc & 7)) = ra[u];
+  }
+}
+
+template <int BPW>
+__device__ __forceinline__ uint4 gm_decode_one(const uint2 (&i1)[2], const uint2 (&i2)[2], int t, int u,
+                                               const uint8_t *lds) {
+  const uint32_t w1 = u < 2 ? i1[t].x : i1[t].y;
+  const uint32_t a1 = (w1 >> (16 * (u & 1))) & 0xFFFFu;
+  uint32_t a2 = 0;
+  if constexpr (BPW == 3) a2 = (i2[t].x >> (8 * u)) & 0xFFu;
+  if constexpr (BPW == 4) a2 = ((u < 2 ? i2[t].x : i2[t].y) >> (16 * (u & 1))) & 0xFFFFu;
+  return decode_group<BPW>(a1, a2, lds);
+}
+
+template <int BPW, bool G4>
+__global__ void __launch_bounds__(256, 1)
+gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uint16_t *xt,
+          const float *rowsum, int64_t m, int64_t n, int64_t k, float post, void *out,
+          glq_dtype out_dt, int64_t mblocks, int64_t tiles) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  uint16_t *As0 = reinterpret_cast<uint16_t *>(lds + lds_table_bytes<BPW>());
+  uint16_t *As1 = As0 + GM_BM * GM_LDA;
+  // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs; give each
+  // XCD a contiguous range of tiles (m-block fastest) so the workgroups that
+  // share an L2 share weight rows and walk the same x~ k-window together.
+  int64_t tile = blockIdx.x;
+  if (tiles % 8 == 0) tile = (blockIdx.x % 8) * (tiles / 8) + blockIdx.x / 8;
+  const int64_t m0 = (tile % mblocks) * GM_BM;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 31, p = lane >> 5;
+  const int64_t n0 = (tile / mblocks) * GM_BN + 64 * wave;
+  const int64_t G = k / 8;
+  const int64_t S = (k + GM_BK - 1) / GM_BK;
+
+  load_tables<BPW>(lds, blob);
+  uint4 ra[8];
+  gm_load_a(xt, m, k, m0, 0, ra);
+  uint2 i1[2], i2[2];
+  gm_load_idx<BPW, G4>(idx1, idx2, n, G, n0, c, p, 0, i1, i2);
+  gm_store_a(As0, ra);
+  gm_load_a(xt, m, k, m0, min((int64_t)1, S - 1), ra);
+  __syncthreads();                                   // tables and x~ tile 0 in LDS
+
+  f32x16 acc[8][2];
 #pragma unroll
   for (int a = 0; a < 8; ++a)
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int64_t col = n0 + 16 * t + j;
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t r = m0 + 16 * a + 4 * q + e;
-        if (r < m && col < n) {
-          float v = acc[a][t][e];
-          if (Epi<BPW>::bias != 0.0f) v -= Epi<BPW>::bias * rowsum[r];
-          store_out(out, out_dt, (size_t)r * n + col, post * v);
-        }
+      for (int e = 0; e < 16; ++e) acc[a][t][e] = 0.f;
+
+  for (int64_t s = 0; s < S; ++s) {
+    const uint16_t *Acur = (s & 1) ? As1 : As0;
+    const uint2 c1[2] = {i1[0], i1[1]}, c2[2] = {i2[0], i2[1]};
+    gm_load_idx<BPW, G4>(idx1, idx2, n, G, n0, c, p, min(s + 1, S - 1), i1, i2);
+    // decode and MFMAs in one basic block so the scheduler overlaps them
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint4 b0 = gm_decode_one<BPW>(c1, c2, 0, u, lds);
+      const uint4 b1 = gm_decode_one<BPW>(c1, c2, 1, u, lds);
+#pragma unroll
+      for (int a = 0; a < 8; ++a) {
+        const uint4 av = *reinterpret_cast<const uint4 *>(Acur + (32 * a + c) * GM_LDA + 32 * p + 8 * u);
+        acc[a][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+                                                            __builtin_bit_cast(bf16x8, b0), acc[a][0], 0, 0, 0);
+        acc[a][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+                                                            __builtin_bit_cast(bf16x8, b1), acc[a][1], 0, 0, 0);
       }
     }
+    gm_store_a((s & 1) ? As0 : As1, ra);             // tile s + 1 (harmless past the end)
+    gm_load_a(xt, m, k, m0, min(s + 2, S - 1), ra);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int a = 0; a < 8; ++a) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int64_t r = m0 + 32 * a + 8 * (i >> 2) + 4 * p + (i & 3);
+      if (r >= m) continue;
+      const float bias = Epi<BPW>::bias != 0.0f ? Epi<BPW>::bias * rowsum[r] : 0.0f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int64_t col = n0 + 32 * t + c;
+        if (col < n) store_out(out, out_dt, (size_t)r * n + col, post * (acc[a][t][i] - bias));
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------- float32 path
@@ -474,6 +729,24 @@ int hip_status(hipError_t e, const char *where = "launch") {
   return GLQ_ERR_HIP;
 }
 
+// Allow dynamic LDS above the 64 KiB default (gfx950 has 160 KiB per CU).
+// The attribute is raised once per kernel to the largest size asked so far.
+template <class K>
+int allow_lds(K kernel, size_t bytes) {
+  if (bytes <= 60 * 1024) return GLQ_OK;
+  static std::atomic<size_t> granted{0};
+  if (granted.load(std::memory_order_acquire) >= bytes) return GLQ_OK;
+  const int rc = hip_status(hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes),
+                            "hipFuncSetAttribute");
+  if (rc == GLQ_OK) {
+    size_t cur = granted.load();
+    while (cur < bytes && !granted.compare_exchange_weak(cur, bytes)) {
+    }
+  }
+  return rc;
+}
+
 constexpr int kMaxLogBlock = 14;   // Hadamard block <= 16384 (64 KiB of float32 in LDS)
 
 int log2_block(int64_t len) {
@@ -495,13 +768,38 @@ int cu_count() {
   return cus;
 }
 
-template <class K>
-int allow_lds(K kernel, size_t bytes);
+template <bool IB, bool OB, bool TR>
+int launch_rht_vec(const void *in, void *out, int64_t rows, int64_t n, int lb, const int8_t *signs,
+                   float *rowsum, hipStream_t st) {
+  const int64_t grid = rows < 8192 ? rows : 8192;
+  const size_t shm = sizeof(float) * (size_t)n;
+  const int rc = allow_lds(rht_rows_vec<IB, OB, TR>, shm + 1024);
+  if (rc) return rc;
+  hipLaunchKernelGGL((rht_rows_vec<IB, OB, TR>), dim3((unsigned)grid), dim3(256), shm, st, in, out, rows, n, lb,
+                     signs, rowsum);
+  return hip_status(hipGetLastError());
+}
 
 int launch_rht(const void *in, glq_dtype in_dt, void *out, glq_dtype out_dt, int64_t rows,
                int64_t n, const int8_t *signs, int transpose, float *rowsum, hipStream_t st) {
   const int lb = log2_block(n);
   if (lb > kMaxLogBlock) return GLQ_ERR_UNSUPPORTED;
+  const bool aligned = ((reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out) |
+                         reinterpret_cast<uintptr_t>(signs)) & 15) == 0;
+  if (n % 8 == 0 && n <= RV_MAX && aligned && in != out) {
+    const bool ib = in_dt == GLQ_BF16, ob = out_dt == GLQ_BF16;
+    if (transpose) {
+      if (ib) return ob ? launch_rht_vec<true, true, true>(in, out, rows, n, lb, signs, rowsum, st)
+                        : launch_rht_vec<true, false, true>(in, out, rows, n, lb, signs, rowsum, st);
+      return ob ? launch_rht_vec<false, true, true>(in, out, rows, n, lb, signs, rowsum, st)
+                : launch_rht_vec<false, false, true>(in, out, rows, n, lb, signs, rowsum, st);
+    }
+    if (ib) return ob ? launch_rht_vec<true, true, false>(in, out, rows, n, lb, signs, rowsum, st)
+                      : launch_rht_vec<true, false, false>(in, out, rows, n, lb, signs, rowsum, st);
+    return ob ? launch_rht_vec<false, true, false>(in, out, rows, n, lb, signs, rowsum, st)
+              : launch_rht_vec<false, false, false>(in, out, rows, n, lb, signs, rowsum, st);
+  }
+  // generic path: any n, in-place, unaligned pointers
   const int64_t grid = rows < 4096 ? rows : 4096;
   const size_t shm = sizeof(float) << lb;
   const int rc = allow_lds(rht_rows, shm + 1024);
@@ -509,15 +807,6 @@ int launch_rht(const void *in, glq_dtype in_dt, void *out, glq_dtype out_dt, int
   hipLaunchKernelGGL(rht_rows, dim3((unsigned)grid), dim3(256), shm, st, in, in_dt, out, out_dt,
                      rows, n, lb, signs, transpose, rowsum);
   return hip_status(hipGetLastError());
-}
-
-// Allow dynamic LDS above the 64 KiB default (gfx950 has 160 KiB per CU).
-template <class K>
-int allow_lds(K kernel, size_t bytes) {
-  if (bytes <= 60 * 1024) return GLQ_OK;
-  return hip_status(hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes),
-                    "hipFuncSetAttribute");
 }
 
 bool valid_dtype(int dt) { return dt == GLQ_F32 || dt == GLQ_BF16; }
@@ -594,19 +883,30 @@ int launch_matmul(const glq_layer *L, const void *xt, glq_dtype x_dt, const floa
   const uint16_t *xb = reinterpret_cast<const uint16_t *>(xt);
   if (m <= 16) {
     const int64_t grid = (L->n + 15) / 16;
-    const size_t shm = tab + 4 * 16 * 16 * 4;
-    int rc = allow_lds(gemv_bf16<BPW>, shm);
+    const size_t shm = tab + GV_WAVES * 16 * 16 * 4;
+    const bool g8 = ((L->k / 8) % 8) == 0;
+    int rc = g8 ? allow_lds(gemv_bf16<BPW, true>, shm) : allow_lds(gemv_bf16<BPW, false>, shm);
     if (rc) return rc;
-    hipLaunchKernelGGL(gemv_bf16<BPW>, dim3((unsigned)grid), dim3(256), shm, st,
-                       L->idx1, L->idx2, blob, xb, rowsum, m, L->n, L->k, post, out, out_dt);
+    if (g8)
+      hipLaunchKernelGGL((gemv_bf16<BPW, true>), dim3((unsigned)grid), dim3(64 * GV_WAVES), shm, st,
+                         L->idx1, L->idx2, blob, xb, rowsum, m, L->n, L->k, post, out, out_dt);
+    else
+      hipLaunchKernelGGL((gemv_bf16<BPW, false>), dim3((unsigned)grid), dim3(64 * GV_WAVES), shm, st,
+                         L->idx1, L->idx2, blob, xb, rowsum, m, L->n, L->k, post, out, out_dt);
   } else {
-    const int64_t gx = (L->n + GM_BN - 1) / GM_BN, gy = (m + GM_BM - 1) / GM_BM;
-    if (gy > 65535) return GLQ_ERR_UNSUPPORTED;
-    const size_t shm = tab + GM_BM * GM_LDA * 2;
-    int rc = allow_lds(gemm_bf16<BPW>, shm);
+    const int64_t mb = (m + GM_BM - 1) / GM_BM, nb = (L->n + GM_BN - 1) / GM_BN;
+    const int64_t tiles = mb * nb;
+    if (tiles > 0x7FFFFFFF) return GLQ_ERR_UNSUPPORTED;
+    const size_t shm = tab + 2 * GM_A_BYTES;
+    const bool even_g = ((L->k / 8) % 4) == 0;
+    int rc = even_g ? allow_lds(gemm_bf16<BPW, true>, shm) : allow_lds(gemm_bf16<BPW, false>, shm);
     if (rc) return rc;
-    hipLaunchKernelGGL(gemm_bf16<BPW>, dim3((unsigned)gx, (unsigned)gy), dim3(256), shm, st, L->idx1, L->idx2, blob, xb, rowsum, m, L->n, L->k,
-                       post, out, out_dt);
+    if (even_g)
+      hipLaunchKernelGGL((gemm_bf16<BPW, true>), dim3((unsigned)tiles), dim3(256), shm, st, L->idx1, L->idx2,
+                         blob, xb, rowsum, m, L->n, L->k, post, out, out_dt, mb, tiles);
+    else
+      hipLaunchKernelGGL((gemm_bf16<BPW, false>), dim3((unsigned)tiles), dim3(256), shm, st, L->idx1, L->idx2,
+                         blob, xb, rowsum, m, L->n, L->k, post, out, out_dt, mb, tiles);
   }
   return hip_status(hipGetLastError());
 }

@@ -163,6 +163,13 @@ class Layer:
     cb: object                  # torch uint8 device tables
 
     def struct(self) -> GlqLayerStruct:
+        st = self.__dict__.get("_st")
+        if st is None:
+            st = self._make_struct()
+            self.__dict__["_st"] = st
+        return st
+
+    def _make_struct(self) -> GlqLayerStruct:
         return GlqLayerStruct(
             self.n, self.k, self.bpw, {2: 0, 3: 1, 4: 2}[self.bpw], float(self.scale),
             self.idx1.data_ptr(), 0 if self.idx2 is None else self.idx2.data_ptr(),
