@@ -7,10 +7,13 @@ RHT, all in libglq.so. Steps rotate through --layers distinct copies of the
 layer's index planes (128 x 4 MiB = 512 MiB, twice the 256 MB Infinity
 Cache), so each step streams its compressed weights from HBM.
 
-value = compressed-weight bytes moved per second (GB/s) over the timed steps.
-roofline = the dominant kernel (the fused decode-GEMV) timed alone with HIP
-events around each launch on the launch stream: compressed bytes per launch /
-mean launch duration, against 8 TB/s HBM. traffic = HBM bytes per launch from
+value = compressed-weight bytes moved per second (GB/s) over the timed steps,
+which replay a HIP graph of one step per layer copy (no host launch cost).
+roofline = the dominant kernel of the step, timed with HIP events on its
+launch stream (graph replays): compressed bytes per launch / mean launch
+duration against 8 TB/s HBM (small batch), or 2 M N K per launch / duration
+against 2.5 PFLOP/s bf16 MFMA (prefill). At batch 1 the whole layer is one
+kernel, so its launches are the timed steps. traffic = HBM bytes per launch from
 rocprofv3 FETCH_SIZE + WRITE_SIZE counters (profiles/), scaled by what the
 counters read for a plain copy of known size; null if the kernel source has
 changed since those counters were taken.
@@ -97,14 +100,24 @@ def build_layers(workload, n_layers, device):
         ydt = torch.float32 if spec.y_dtype == "f32" else torch.bfloat16
         xt = torch.from_numpy(x).to(device=device, dtype=xdt)
         y = torch.empty((spec.m, spec.n), device=device, dtype=ydt)
-        ws = torch.empty(glq.workspace_bytes(base, spec.m), device=device, dtype=torch.uint8)
+        ws = torch.zeros(glq.workspace_bytes(base, spec.m), device=device, dtype=torch.uint8)
         built.append(dict(spec=spec, layers=copies, x=xt, y=y, ws=ws, idx=(i1, i2, s, sn, sk), xnp=x))
     return built
+
+
+def single_launch(spec):
+    """True when a full layer forward of this shape is one kernel (the
+    small-batch whole-layer kernel): bf16 x, m <= 4, m*k and m*n <= 16384,
+    k/8 a multiple of 8."""
+    return (spec.x_dtype == "bf16" and spec.m <= 4 and spec.m * spec.k <= 16384
+            and spec.m * spec.n <= 16384 and (spec.k // 8) % 8 == 0)
 
 
 def dominant_kernel(spec):
     if spec.x_dtype == "f32":
         return f"gemv_f32<{spec.bpw}>"
+    if single_launch(spec):
+        return f"layer_small<{spec.bpw}>"
     return f"gemv_bf16<{spec.bpw}>" if spec.m <= 16 else f"gemm_bf16<{spec.bpw}>"
 
 
@@ -196,7 +209,9 @@ def run_bench(args):
         kgraph.replay()
     k1.record()
     torch.cuda.synchronize()
-    k_mean = k0.elapsed_time(k1) * 1e-3 / (krep * len(b0["layers"]))
+    core_mean = k0.elapsed_time(k1) * 1e-3 / (krep * len(b0["layers"]))
+    # the whole-layer kernel is the step itself: its mean launch is the step time
+    k_mean = ms_step * 1e-3 if single_launch(spec0) and len(built) == 1 else core_mean
     # rotated-basis launches of 3/4 bpw also run a small row-sum kernel
     L0 = b0["layers"][0]
     k_bytes = L0.idx1.numel() * 2 + (0 if L0.idx2 is None else L0.idx2.numel() * L0.idx2.element_size())
@@ -215,7 +230,14 @@ def run_bench(args):
     roof["traffic"] = traffic
     roof["kernel"] = dom
     roof["kernel_mean_us"] = round(k_mean * 1e6, 3)
-    roof["timing"] = f"HIP events around {krep} replays of a graph of {len(b0['layers'])} launches"
+    if single_launch(spec0) and len(built) == 1:
+        roof["timing"] = (f"HIP events around {replays} replays of a graph of {per_graph} whole-layer launches "
+                          "(the timed steps)")
+        roof["matmul_core"] = {"kernel": f"gemv_bf16<{spec0.bpw}>", "mean_us": round(core_mean * 1e6, 3),
+                               "achieved_gbs": round(k_bytes / core_mean / 1e9, 2),
+                               "note": "decode-GEMV alone (x already rotated, z left rotated), as in the multi-kernel path"}
+    else:
+        roof["timing"] = f"HIP events around {krep} replays of a graph of {len(b0['layers'])} launches"
     roof["algorithmic_bytes_per_launch"] = k_bytes
     roof["algorithmic_flops_per_launch"] = k_flops
 

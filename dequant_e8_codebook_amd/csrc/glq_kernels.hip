@@ -172,6 +172,11 @@ __device__ __forceinline__ void fwht_regs(float *v) {
       }
 }
 
+// LDS layout of every FWHT buffer: one pad float after each 16, so that the
+// radix-16 passes (element strides 1, 16, 256, ...) hit distinct banks.
+__device__ __forceinline__ int pidx(int i) { return i + (i >> 4); }
+__host__ __device__ constexpr size_t padded_floats(size_t n) { return n + n / 16 + 1; }
+
 template <int R>
 __device__ __forceinline__ void fwht_pass(float *buf, int b, int lo) {
   const int h = 1 << lo;
@@ -180,10 +185,10 @@ __device__ __forceinline__ void fwht_pass(float *buf, int b, int lo) {
     const int base = (q >> lo) * (h * R) + (q & (h - 1));
     float v[R];
 #pragma unroll
-    for (int m = 0; m < R; ++m) v[m] = buf[base + m * h];
+    for (int m = 0; m < R; ++m) v[m] = buf[pidx(base + m * h)];
     fwht_regs<R>(v);
 #pragma unroll
-    for (int m = 0; m < R; ++m) buf[base + m * h] = v[m];
+    for (int m = 0; m < R; ++m) buf[pidx(base + m * h)] = v[m];
   }
 }
 
@@ -207,7 +212,7 @@ rht_rows(const void *in, glq_dtype in_dt, void *out, glq_dtype out_dt, int64_t r
       for (int i = threadIdx.x; i < b; i += blockDim.x) {
         float v = load_elem(in, in_dt, base + i);
         if (!transpose) v *= (float)signs[blk + i];
-        buf[i] = v;
+        buf[pidx(i)] = v;
       }
       __syncthreads();
       int lo = 0;
@@ -220,7 +225,7 @@ rht_rows(const void *in, glq_dtype in_dt, void *out, glq_dtype out_dt, int64_t r
       }
       __syncthreads();
       for (int i = threadIdx.x; i < b; i += blockDim.x) {
-        float v = buf[i] * inv;
+        float v = buf[pidx(i)] * inv;
         if (transpose) v *= (float)signs[blk + i];
         if (out_dt == GLQ_F32) {
           reinterpret_cast<float *>(out)[base + i] = v;
@@ -288,25 +293,23 @@ rht_rows_vec(const void *in, void *out, int64_t rows, int64_t n, int logb, const
     const size_t base = (size_t)row * n;
     __syncthreads();                           // previous row's readers are done with buf
     for (int p0 = threadIdx.x; p0 < pieces; p0 += 4 * 256) {
-      float v[4][8];
+      float v[4][8], sg[4][8];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int pc = min(p0 + 256 * u, pieces - 1);
         rv_load_piece<IN_BF16>(in, base + 8 * (size_t)pc, v[u]);
+        if (!TRANSPOSE) rv_signs(signs, 8 * (int64_t)pc, sg[u]);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int pc = p0 + 256 * u;
         if (pc < pieces) {
           if (!TRANSPOSE) {
-            float sg[8];
-            rv_signs(signs, 8 * (int64_t)pc, sg);
 #pragma unroll
-            for (int t = 0; t < 8; ++t) v[u][t] *= sg[t];
+            for (int t = 0; t < 8; ++t) v[u][t] *= sg[u][t];
           }
-          float4 *d = reinterpret_cast<float4 *>(buf + 8 * pc);
-          d[0] = make_float4(v[u][0], v[u][1], v[u][2], v[u][3]);
-          d[1] = make_float4(v[u][4], v[u][5], v[u][6], v[u][7]);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) buf[pidx(8 * pc + t)] = v[u][t];
         }
       }
     }
@@ -322,11 +325,11 @@ rht_rows_vec(const void *in, void *out, int64_t rows, int64_t n, int logb, const
     __syncthreads();
     float rs = 0.0f;
     for (int pc = threadIdx.x; pc < pieces; pc += 256) {
-      const float4 a = reinterpret_cast<const float4 *>(buf + 8 * pc)[0];
-      const float4 c = reinterpret_cast<const float4 *>(buf + 8 * pc)[1];
-      float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
       float sg[8];
-      if (TRANSPOSE) rv_signs(signs, 8 * (int64_t)pc, sg);
+      if (TRANSPOSE) rv_signs(signs, 8 * (int64_t)pc, sg);      // issued before the LDS reads
+      float v[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) v[t] = buf[pidx(8 * pc + t)];
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         v[t] *= inv;
@@ -514,6 +517,174 @@ gemv_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
       store_out(out, out_dt, (size_t)r * n + nrow, post * v);
     }
   }
+}
+
+// ---------------------------------------------------------------- whole layer (m <= 4)
+// One launch for y = U^T (s W^) (V x) at a few activation rows (decode-time
+// batch sizes), where separate RHT launches would cost more than the
+// decode-GEMV itself. Every workgroup: issues its first index loads, copies
+// the decode tables, rotates x in LDS (signs, block FWHT along k, 1/sqrt(b),
+// bf16 rounding, row sums), then runs the 16-wave decode-GEMV of gemv_bf16
+// over its 16-row weight tiles with the x~ operands read from LDS, and writes
+// z (float32) to the workspace. The last workgroup to finish (threadfence +
+// atomic ticket, the counter reset to zero by that workgroup) loads all of z,
+// applies U^T (block FWHT along n, then signs) and writes y.
+constexpr int LY_MAXE = 16384;                       // m*k and m*n limit (64 KiB of float32)
+constexpr size_t LY_BUF_BYTES = padded_floats(LY_MAXE) * 4 + 12;   // 16-byte multiple
+
+template <int BPW>
+constexpr size_t ly_lds_bytes() { return lds_table_bytes<BPW>() + LY_BUF_BYTES + GV_WAVES * 256 * 4 + 64; }
+
+__device__ __forceinline__ void ly_fwht(float *buf, int total, int logb) {
+  int lo = 0;
+  for (; lo + 4 <= logb; lo += 4) { fwht_pass<16>(buf, total, lo); __syncthreads(); }
+  switch (logb - lo) {
+    case 1: fwht_pass<2>(buf, total, lo); break;
+    case 2: fwht_pass<4>(buf, total, lo); break;
+    case 3: fwht_pass<8>(buf, total, lo); break;
+    default: break;
+  }
+  __syncthreads();
+}
+
+template <int BPW>
+__global__ void __launch_bounds__(64 * GV_WAVES, 1)
+layer_small(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uint16_t *x,
+            const int8_t *sign_k, const int8_t *sign_n, int64_t m, int64_t n, int64_t k, int logbk,
+            int logbn, float post, void *y, glq_dtype y_dt, float *z, unsigned int *counter) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  float *xs = reinterpret_cast<float *>(lds + lds_table_bytes<BPW>());
+  float *red = reinterpret_cast<float *>(lds + lds_table_bytes<BPW>() + LY_BUF_BYTES);
+  float *misc = red + GV_WAVES * 256;                 // [0..3] row sums, [8] last-workgroup flag
+  const uint16_t *xb = reinterpret_cast<const uint16_t *>(xs);   // x~ as bf16 [m][k] after rotation
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j = lane & 15, q = lane >> 4;
+  const int64_t G = k / 8, chunks = (G + 31) / 32;
+  const int64_t tiles = (n + 15) / 16;
+  const bool a_row = j < m;
+
+  // 1. first index loads in flight before anything else
+  int64_t tile = blockIdx.x, c = wave;
+  uint32_t i1[8], i2[8];
+  if (tile < tiles && c < chunks)
+    gv_load_idx<BPW, true>(idx1, idx2, min(tile * 16 + j, n - 1), G, 32 * c + 8 * q, i1, i2);
+  // 2. decode tables, 3. x -> LDS with the input signs
+  load_tables<BPW, 64 * GV_WAVES>(lds, blob);
+  const int64_t mk = m * k;
+  for (int64_t e = 8 * (int64_t)tid; e < mk; e += 8 * 64 * GV_WAVES) {
+    float v[8], sg[8];
+    rv_signs(sign_k, e - k * ((e >= k) + (e >= 2 * k) + (e >= 3 * k)), sg);
+    rv_load_piece<true>(x, (size_t)e, v);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) xs[pidx((int)e + t)] = v[t] * sg[t];
+  }
+  __syncthreads();
+  ly_fwht(xs, (int)mk, logbk);
+  {  // 4. scale, round to bf16 in place (read all, barrier, write), row sums
+    const float inv = 1.0f / sqrtf((float)(1 << logbk));
+    float v[LY_MAXE / (64 * GV_WAVES)];
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < LY_MAXE / (64 * GV_WAVES); ++u) {
+      const int64_t e = tid + (int64_t)u * 64 * GV_WAVES;
+      v[u] = e < mk ? xs[pidx((int)e)] * inv : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < LY_MAXE / (64 * GV_WAVES); ++u) {
+      const int64_t e = tid + (int64_t)u * 64 * GV_WAVES;
+      if (e < mk) {
+        const uint16_t h = f32_to_bf16_rne(v[u]);
+        reinterpret_cast<uint16_t *>(xs)[e] = h;
+        const float hv = __uint_as_float((uint32_t)h << 16);
+        const int r = (e >= k) + (e >= 2 * k) + (e >= 3 * k);   // m <= 4
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) rs[rr] += rr == r ? hv : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      float t = rs[rr];
+      for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off);
+      if (lane == 0) red[wave * 4 + rr] = t;
+    }
+    __syncthreads();
+    if (tid < 4) {
+      float t = 0.0f;
+      for (int w = 0; w < GV_WAVES; ++w) t += red[w * 4 + tid];
+      misc[tid] = t;
+    }
+    __syncthreads();
+  }
+  // 5. decode-GEMV over this workgroup's tiles
+  const uint16_t *xrow = xb + (size_t)min((int64_t)j, m - 1) * k;
+  for (; tile < tiles; tile += gridDim.x) {
+    const int64_t row = min(tile * 16 + j, n - 1);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (c = wave; c < chunks; c += GV_WAVES) {
+      if (!(tile == (int64_t)blockIdx.x && c == wave))
+        gv_load_idx<BPW, true>(idx1, idx2, row, G, 32 * c + 8 * q, i1, i2);
+      const int64_t g0 = 32 * c + 8 * q;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int64_t g = g0 + s;
+        const uint4 v = *reinterpret_cast<const uint4 *>(xrow + 8 * min(g, G - 1));
+        const uint4 av = (a_row && g < G) ? v : make_uint4(0, 0, 0, 0);
+        const uint4 bv = decode_group<BPW>(i1[s], i2[s], lds);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                      __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) red[(wave * 16 + 4 * q + t) * 16 + j] = acc[t];
+    __syncthreads();
+    if (tid < 256) {
+      const int r = tid >> 4, col = tid & 15;
+      float v = 0.0f;
+#pragma unroll
+      for (int w = 0; w < GV_WAVES; ++w) v += red[(w * 16 + r) * 16 + col];
+      const int64_t nrow = tile * 16 + col;
+      if (r < m && nrow < n) {
+        if (Epi<BPW>::bias != 0.0f) v -= Epi<BPW>::bias * misc[r];
+        // coherent (write-through) store: visible to every XCD without an L2 writeback
+        __hip_atomic_store(z + (size_t)r * n + nrow, post * v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __syncthreads();
+  }
+  // 6. the last workgroup applies U^T. z went out with coherent stores; once
+  // they have completed (s_waitcnt) the workgroup takes a ticket. The
+  // workgroup holding the last ticket reads z with coherent loads. (A
+  // threadfence here would write back the whole L2 of the XCD, once per
+  // workgroup.)
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned int ticket = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    misc[8] = ticket == gridDim.x - 1 ? 1.0f : 0.0f;
+  }
+  __syncthreads();
+  if (misc[8] == 0.0f) return;
+  const int mn = (int)(m * n);
+  {
+    constexpr int U = LY_MAXE / (64 * GV_WAVES);
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)        // all loads in flight before the first LDS write
+      v[u] = __hip_atomic_load(z + min(tid + u * 64 * GV_WAVES, mn - 1), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (tid + u * 64 * GV_WAVES < mn) xs[pidx(tid + u * 64 * GV_WAVES)] = v[u];
+  }
+  __syncthreads();
+  ly_fwht(xs, mn, logbn);
+  const float invn = 1.0f / sqrtf((float)(1 << logbn));
+  for (int e = tid; e < mn; e += 64 * GV_WAVES) {
+    const int col = e - (int)n * ((e >= n) + (e >= 2 * n) + (e >= 3 * n));
+    store_out(y, y_dt, (size_t)e, xs[pidx(e)] * invn * (float)sign_n[col]);
+  }
+  if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------- GEMM (m > 16)
@@ -772,7 +943,7 @@ template <bool IB, bool OB, bool TR>
 int launch_rht_vec(const void *in, void *out, int64_t rows, int64_t n, int lb, const int8_t *signs,
                    float *rowsum, hipStream_t st) {
   const int64_t grid = rows < 8192 ? rows : 8192;
-  const size_t shm = sizeof(float) * (size_t)n;
+  const size_t shm = sizeof(float) * padded_floats((size_t)n);
   const int rc = allow_lds(rht_rows_vec<IB, OB, TR>, shm + 1024);
   if (rc) return rc;
   hipLaunchKernelGGL((rht_rows_vec<IB, OB, TR>), dim3((unsigned)grid), dim3(256), shm, st, in, out, rows, n, lb,
@@ -801,7 +972,7 @@ int launch_rht(const void *in, glq_dtype in_dt, void *out, glq_dtype out_dt, int
   }
   // generic path: any n, in-place, unaligned pointers
   const int64_t grid = rows < 4096 ? rows : 4096;
-  const size_t shm = sizeof(float) << lb;
+  const size_t shm = sizeof(float) * padded_floats((size_t)1 << lb);
   const int rc = allow_lds(rht_rows, shm + 1024);
   if (rc) return rc;
   hipLaunchKernelGGL(rht_rows, dim3((unsigned)grid), dim3(256), shm, st, in, in_dt, out, out_dt,
@@ -827,12 +998,16 @@ int check_layer(const glq_layer *L, bool need_signs) {
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-struct WsLayout { size_t xt, rowsum, z, total; };
+// Workspace: [0, 256) control words (the whole-layer kernel's completion
+// counter: zero before first use, left zero by every call), then x~, row sums
+// of x~ and z = s W^ x~.
+struct WsLayout { size_t ctrl, xt, rowsum, z, total; };
 
 WsLayout ws_layout(int64_t n, int64_t k, int64_t m) {
   WsLayout w;
-  w.xt = 0;
-  w.rowsum = align256((size_t)m * (size_t)k * 4);
+  w.ctrl = 0;
+  w.xt = 256;
+  w.rowsum = w.xt + align256((size_t)m * (size_t)k * 4);
   w.z = w.rowsum + align256((size_t)m * 4);
   w.total = w.z + align256((size_t)m * (size_t)n * 4);
   return w;
@@ -969,6 +1144,33 @@ extern "C" int glq_fused_linear(const glq_layer *L, const void *x, glq_dtype x_d
   float *rowsum = reinterpret_cast<float *>(wsb + ws.rowsum);
   float *z = reinterpret_cast<float *>(wsb + ws.z);
 
+  // whole layer in one launch at decode-time batch sizes
+  if (x_dt == GLQ_BF16 && in_rht && out_rht && m <= 4 && m * L->k <= LY_MAXE && m * L->n <= LY_MAXE &&
+      (L->k / 8) % 8 == 0 && ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(L->idx1)) & 15) == 0 &&
+      (reinterpret_cast<uintptr_t>(L->sign_k) & 7) == 0 &&
+      (L->bpw != 4 || (reinterpret_cast<uintptr_t>(L->idx2) & 15) == 0) &&
+      (L->bpw != 3 || (reinterpret_cast<uintptr_t>(L->idx2) & 7) == 0)) {
+    const int64_t tiles = (L->n + 15) / 16;
+    const int64_t grid = tiles < cu_count() ? tiles : cu_count();
+    const float post = L->scale * (L->bpw == 2 ? 1.0f : L->bpw == 3 ? 0.25f : 0.125f);
+    unsigned int *counter = reinterpret_cast<unsigned int *>(wsb + ws.ctrl);
+    const uint8_t *blob = reinterpret_cast<const uint8_t *>(L->cb);
+    const uint16_t *xb = reinterpret_cast<const uint16_t *>(x);
+    const int lbk = log2_block(L->k), lbn = log2_block(L->n);
+#define GLQ_LAYER_SMALL(B)                                                                              \
+  do {                                                                                                  \
+    rc = allow_lds(layer_small<B>, ly_lds_bytes<B>());                                                  \
+    if (rc) return rc;                                                                                  \
+    hipLaunchKernelGGL(layer_small<B>, dim3((unsigned)grid), dim3(64 * GV_WAVES), ly_lds_bytes<B>(), st, \
+                       L->idx1, L->idx2, blob, xb, L->sign_k, L->sign_n, m, L->n, L->k, lbk, lbn, post, y, \
+                       y_dt, z, counter);                                                               \
+  } while (0)
+    if (L->bpw == 2) GLQ_LAYER_SMALL(2);
+    else if (L->bpw == 3) GLQ_LAYER_SMALL(3);
+    else GLQ_LAYER_SMALL(4);
+#undef GLQ_LAYER_SMALL
+    return hip_status(hipGetLastError());
+  }
   const void *xt_use = x;
   if (x_dt == GLQ_F32) {
     if (in_rht) {

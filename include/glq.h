@@ -140,7 +140,8 @@ int glq_rht_apply(const void *in, glq_dtype in_dt, void *out, glq_dtype out_dt,
  */
 int glq_decode_weights(const glq_layer *L, void *w_out, glq_dtype out_dt, void *hip_stream);
 
-/* Bytes of device workspace glq_fused_linear needs for m rows (any dtype, any flags). */
+/* Bytes of device workspace glq_fused_linear needs for m rows (any dtype, any
+ * flags), including the 256 bytes of control words at its start. */
 size_t glq_fused_linear_workspace(const glq_layer *L, int64_t m);
 
 /*
@@ -151,7 +152,12 @@ size_t glq_fused_linear_workspace(const glq_layer *L, int64_t m);
  *   x_dt = GLQ_BF16: bf16 matrix-core path (x~ rounded to bf16, weights exact
  *                    in bf16, float32 accumulation, scale in the epilogue)
  *   y_dt             GLQ_F32 or GLQ_BF16 (round-to-nearest-even)
- *   workspace        device, >= glq_fused_linear_workspace(L, m) bytes, 256-byte aligned
+ *   workspace        device, >= glq_fused_linear_workspace(L, m) bytes, 256-byte aligned.
+ *                    Its first 256 bytes are control words (a completion counter
+ *                    of the single-launch layer used at small m): they must be
+ *                    zero before the first call with a workspace, every call
+ *                    leaves them zero, and calls that run concurrently need
+ *                    separate workspaces. The rest is scratch.
  *   flags            GLQ_FLAG_* (0 = the full layer)
  * m == 0 is a successful no-op. x and y must not overlap the workspace.
  */

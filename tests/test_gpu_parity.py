@@ -64,7 +64,7 @@ def _run_linear(G, cb, i1, i2, s, sn, sk, x, x_dt, y_dt, flags=0):
     m = x.shape[0]
     xt = _t(x.astype(np.float32), torch.float32 if x_dt == "f32" else torch.bfloat16)
     y = torch.empty((m, L.n), device="cuda", dtype=torch.float32 if y_dt == "f32" else torch.bfloat16)
-    ws = torch.empty(max(G.workspace_bytes(L, max(m, 1)), 256), device="cuda", dtype=torch.uint8)
+    ws = torch.zeros(max(G.workspace_bytes(L, max(m, 1)), 256), device="cuda", dtype=torch.uint8)
     G.fused_linear(L, xt, y, ws, flags)
     torch.cuda.synchronize()
     return y.float().cpu().numpy()
@@ -228,7 +228,7 @@ def test_m_zero_is_noop(G, cb):
     L = G.Layer.from_numpy(i1, i2, 1.0, workloads.signs(16, 1), workloads.signs(64, 2), cb)
     x = torch.empty((0, 64), device="cuda", dtype=torch.bfloat16)
     y = torch.empty((0, 16), device="cuda", dtype=torch.bfloat16)
-    ws = torch.empty(256, device="cuda", dtype=torch.uint8)
+    ws = torch.zeros(256, device="cuda", dtype=torch.uint8)
     G.fused_linear(L, x, y, ws)
 
 
@@ -256,3 +256,28 @@ def test_full_size_workload(G, cb, name):
 def test_full_size_dit_block(G, cb, which):
     spec = workloads.layer_specs("dit_block")[which]
     _full_check(G, cb, spec, [0, 2047, 4095])
+
+
+# ------------------------------------- single-launch layer at small batch ----
+
+@pytest.mark.parametrize("bpw", [2, 3, 4])
+@pytest.mark.parametrize("n,k,m", [(150, 512, 1), (4100, 1024, 2), (64, 4096, 4), (4096, 4096, 1),
+                                   (3072, 3072, 3)])
+def test_small_batch_single_launch(G, cb, bpw, n, k, m):
+    # eligible for the one-kernel layer: bf16 x, m <= 4, m*k and m*n <= 16384,
+    # k/8 a multiple of 8; n = 4100 has more 16-row tiles than workgroups
+    i1, i2 = _random_layer(n, k, bpw, 3000 + n + m)
+    s = np.float32(0.017)
+    sn, sk = workloads.signs(n, 41), workloads.signs(k, 42)
+    L = G.Layer.from_numpy(i1, i2, s, sn, sk, cb)
+    ws = torch.zeros(G.workspace_bytes(L, m), device="cuda", dtype=torch.uint8)
+    ref = None
+    for call in range(3):                      # the same workspace, three calls in a row
+        x = workloads.bf16_round_trip(np.random.default_rng(call + m).standard_normal((m, k)).astype(np.float32))
+        for y_dt in (torch.bfloat16, torch.float32):
+            y = torch.empty((m, n), device="cuda", dtype=y_dt)
+            G.fused_linear(L, _t(x, torch.bfloat16), y, ws)
+            torch.cuda.synchronize()
+            ref = og.layer_reference(x, i1, i2, bpw, s, sn, sk)
+            assert og.relative_error(y.float().cpu().numpy(), ref) <= TOL_BF16
+            assert int(ws[:4].view(torch.int32).item()) == 0     # completion counter left at zero
