@@ -83,13 +83,39 @@ __device__ __forceinline__ void load_tables(uint8_t *lds, const uint8_t *blob) {
   }
 }
 
-// Table walk for one 16-bit index (see glq_tables.h): byte offsets of the
-// low and high signed half-vectors within a half table.
-__device__ __forceinline__ void walk(uint32_t i, const uint8_t *lds, uint32_t &lo, uint32_t &hi) {
-  const uint32_t ip = (i - 1u) & 0xFFFFu;
-  const uint32_t e = *reinterpret_cast<const uint16_t *>(lds + kLdsCt + ((ip >> 4) << 1));
+// LDS pointers built from absolute addresses. Every kernel that decodes uses
+// dynamic LDS only (no static __shared__), so its dynamic region starts at
+// offset 0 and the table offsets are compile-time constants that fold into
+// the DS instructions' offset field (a pointer to the extern array would add
+// its link-time base with a VALU add on every lookup).
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const uint16_t lds_u16;
+typedef __attribute__((address_space(3))) const u32x2_t lds_u64;
+typedef __attribute__((address_space(3))) const u32x4_t lds_u128;
+__device__ __forceinline__ uint32_t lds16(uint32_t addr) {
+  return *reinterpret_cast<lds_u16 *>(static_cast<uintptr_t>(addr));
+}
+__device__ __forceinline__ uint2 lds64(uint32_t addr) {
+  const u32x2_t v = *reinterpret_cast<lds_u64 *>(static_cast<uintptr_t>(addr));
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint4 lds128(uint32_t addr) {
+  const u32x4_t v = *reinterpret_cast<lds_u128 *>(static_cast<uintptr_t>(addr));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// i' = i - 1 (mod 2^16) for the two 16-bit indices packed in a word.
+__device__ __forceinline__ uint32_t pk_dec16(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, w) - (u16x2)(1));
+}
+
+// Table walk for one index, given as i' = i - 1 mod 2^16 (see glq_tables.h):
+// byte offsets of the low and high signed half-vectors within a half table.
+__device__ __forceinline__ void walk(uint32_t ip, uint32_t &lo, uint32_t &hi) {
+  const uint32_t e = lds16(kLdsCt + ((ip >> 4) << 1));
   const uint32_t rec = (e >> 5) + ((ip & 15u) >> (e & 31u));
-  const uint4 R = *reinterpret_cast<const uint4 *>(lds + kLdsOt + (rec << 4));
+  const uint4 R = lds128(kLdsOt + (rec << 4));
   lo = R.y + (__builtin_amdgcn_ubfe(ip, 0, R.x) << 3);
   const uint32_t q = __builtin_popcount(__builtin_amdgcn_ubfe(ip, 0, R.w)) & 1u;
   hi = R.z + ((ip >> R.x) << 3) + (q << 6);
@@ -101,26 +127,33 @@ __device__ __forceinline__ uint32_t pk_add16(uint32_t a, uint32_t b) {
 
 // Decode one group into 8 x 16-bit operand values, coordinate t in half t of
 // the result (uint4 = 8 halves). 2 bpw: bf16 of v. 3/4 bpw: bf16 of 192 + u
-// with u = 4 v (3 bpw) or 8 v (4 bpw).
+// with u = 4 v (3 bpw) or 8 v (4 bpw). ip1 = i1 - 1 mod 2^16; at 4 bpw
+// a2 = i2 - 1 mod 2^16 too, at 3 bpw a2 = i2 (a direct table row).
 template <int BPW>
-__device__ __forceinline__ uint4 decode_group(uint32_t i1, uint32_t i2, const uint8_t *lds) {
+__device__ __forceinline__ uint4 decode_ip(uint32_t ip1, uint32_t a2) {
   uint32_t lo, hi;
-  walk(i1, lds, lo, hi);
-  const uint2 a = *reinterpret_cast<const uint2 *>(lds + kLdsHt1 + lo);
-  const uint2 b = *reinterpret_cast<const uint2 *>(lds + kLdsHt1 + hi);
+  walk(ip1, lo, hi);
+  const uint2 a = lds64(kLdsHt1 + lo);
+  const uint2 b = lds64(kLdsHt1 + hi);
   if constexpr (BPW == 2) {
-    (void)i2;
+    (void)a2;
     return make_uint4(a.x, a.y, b.x, b.y);
   } else if constexpr (BPW == 3) {
-    const uint4 r = *reinterpret_cast<const uint4 *>(lds + kLdsHt2 + (i2 << 4));
+    const uint4 r = lds128(kLdsHt2 + (a2 << 4));
     return make_uint4(pk_add16(a.x, r.x), pk_add16(a.y, r.y), pk_add16(b.x, r.z), pk_add16(b.y, r.w));
   } else {
     uint32_t lo2, hi2;
-    walk(i2, lds, lo2, hi2);
-    const uint2 c = *reinterpret_cast<const uint2 *>(lds + kLdsHt2 + lo2);
-    const uint2 d = *reinterpret_cast<const uint2 *>(lds + kLdsHt2 + hi2);
+    walk(a2, lo2, hi2);
+    const uint2 c = lds64(kLdsHt2 + lo2);
+    const uint2 d = lds64(kLdsHt2 + hi2);
     return make_uint4(pk_add16(a.x, c.x), pk_add16(a.y, c.y), pk_add16(b.x, d.x), pk_add16(b.y, d.y));
   }
+}
+
+// Same, from plain indices (i1, and i2 of its plane).
+template <int BPW>
+__device__ __forceinline__ uint4 decode_group(uint32_t i1, uint32_t i2, const uint8_t *) {
+  return decode_ip<BPW>((i1 - 1u) & 0xFFFFu, BPW == 4 ? ((i2 - 1u) & 0xFFFFu) : i2);
 }
 
 // value of one decoded 16-bit operand as the exact float32 v
@@ -424,6 +457,7 @@ decode_weights_k(const uint16_t *idx1, const void *idx2, const uint8_t *blob, fl
 // decode. Partial sums of the 16 waves meet in LDS.
 constexpr int GV_WAVES = 16;
 
+// Indices come back as i' = i - 1 mod 2^16 (stage 1, and stage 2 at 4 bpw).
 template <int BPW, bool G8>
 __device__ __forceinline__ void gv_load_idx(const uint16_t *idx1, const void *idx2, int64_t row, int64_t G,
                                             int64_t g0, uint32_t (&i1)[8], uint32_t (&i2)[8]) {
@@ -431,7 +465,7 @@ __device__ __forceinline__ void gv_load_idx(const uint16_t *idx1, const void *id
   if constexpr (G8) {
     const int64_t off = row * G + min(g0, G - 8);
     const uint4 a = *reinterpret_cast<const uint4 *>(idx1 + off);
-    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+    const uint32_t w[4] = {pk_dec16(a.x), pk_dec16(a.y), pk_dec16(a.z), pk_dec16(a.w)};
 #pragma unroll
     for (int u = 0; u < 4; ++u) { i1[2 * u] = w[u] & 0xFFFFu; i1[2 * u + 1] = w[u] >> 16; }
     if constexpr (BPW == 3) {
@@ -440,7 +474,7 @@ __device__ __forceinline__ void gv_load_idx(const uint16_t *idx1, const void *id
       for (int u = 0; u < 4; ++u) { i2[u] = (b.x >> (8 * u)) & 0xFFu; i2[4 + u] = (b.y >> (8 * u)) & 0xFFu; }
     } else if constexpr (BPW == 4) {
       const uint4 b = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(idx2) + off);
-      const uint32_t x[4] = {b.x, b.y, b.z, b.w};
+      const uint32_t x[4] = {pk_dec16(b.x), pk_dec16(b.y), pk_dec16(b.z), pk_dec16(b.w)};
 #pragma unroll
       for (int u = 0; u < 4; ++u) { i2[2 * u] = x[u] & 0xFFFFu; i2[2 * u + 1] = x[u] >> 16; }
     } else {
@@ -451,8 +485,8 @@ __device__ __forceinline__ void gv_load_idx(const uint16_t *idx1, const void *id
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int64_t o = row * G + min(g0 + u, G - 1);
-      i1[u] = idx1[o];
-      i2[u] = BPW > 2 ? load_idx2(idx2, o, BPW) : 0u;
+      i1[u] = ((uint32_t)idx1[o] - 1u) & 0xFFFFu;
+      i2[u] = BPW == 4 ? ((load_idx2(idx2, o, 4) - 1u) & 0xFFFFu) : BPW == 3 ? load_idx2(idx2, o, 3) : 0u;
     }
   }
 }
@@ -495,7 +529,7 @@ gemv_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
   while (c < chunks) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const uint4 bv = decode_group<BPW>(i1[s], i2[s], lds);
+      const uint4 bv = decode_ip<BPW>(i1[s], i2[s]);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[s]),
                                                     __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
     }
@@ -630,7 +664,7 @@ layer_small(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const u
         const int64_t g = g0 + s;
         const uint4 v = *reinterpret_cast<const uint4 *>(xrow + 8 * min(g, G - 1));
         const uint4 av = (a_row && g < G) ? v : make_uint4(0, 0, 0, 0);
-        const uint4 bv = decode_group<BPW>(i1[s], i2[s], lds);
+        const uint4 bv = decode_ip<BPW>(i1[s], i2[s]);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
                                                       __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
       }
@@ -706,7 +740,7 @@ constexpr size_t GM_A_BYTES = (size_t)GM_BM * GM_LDA * 2;   // one buffer
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // Index planes for k-step s: rows nrow0 + 32 t + c (t = 0, 1), groups
-// 8 s + 4 p .. +3. Addresses are clamped into the planes instead of
+// 8 s + 4 p .. +3, returned as i' = i - 1 mod 2^16 (stage 1, stage 2 at 4 bpw). Addresses are clamped into the planes instead of
 // branching: out-of-range rows are never stored, out-of-range groups meet
 // zero activations, and any index decodes to finite values. G4: k/8 is a
 // multiple of 4, so the 4 indices are one aligned 8-byte load.
@@ -719,9 +753,13 @@ __device__ __forceinline__ void gm_load_idx(const uint16_t *idx1, const void *id
     const int64_t row = min(nrow0 + 32 * t + c, n - 1);
     if constexpr (G4) {
       const int64_t off = row * G + min(8 * s + 4 * p, G - 4);
-      i1[t] = *reinterpret_cast<const uint2 *>(idx1 + off);
+      const uint2 a = *reinterpret_cast<const uint2 *>(idx1 + off);
+      i1[t] = make_uint2(pk_dec16(a.x), pk_dec16(a.y));
       if constexpr (BPW == 3) i2[t] = make_uint2(*reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint8_t *>(idx2) + off), 0u);
-      if constexpr (BPW == 4) i2[t] = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(idx2) + off);
+      if constexpr (BPW == 4) {
+        const uint2 b = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(idx2) + off);
+        i2[t] = make_uint2(pk_dec16(b.x), pk_dec16(b.y));
+      }
       if constexpr (BPW == 2) i2[t] = make_uint2(0u, 0u);
     } else {
       uint32_t w1[4], w2[4];
@@ -731,9 +769,9 @@ __device__ __forceinline__ void gm_load_idx(const uint16_t *idx1, const void *id
         w1[u] = idx1[o];
         w2[u] = BPW > 2 ? load_idx2(idx2, o, BPW) : 0u;
       }
-      i1[t] = make_uint2(w1[0] | (w1[1] << 16), w1[2] | (w1[3] << 16));
+      i1[t] = make_uint2(pk_dec16(w1[0] | (w1[1] << 16)), pk_dec16(w1[2] | (w1[3] << 16)));
       if constexpr (BPW == 3) i2[t] = make_uint2(w2[0] | (w2[1] << 8) | (w2[2] << 16) | (w2[3] << 24), 0u);
-      else i2[t] = make_uint2(w2[0] | (w2[1] << 16), w2[2] | (w2[3] << 16));
+      else i2[t] = make_uint2(pk_dec16(w2[0] | (w2[1] << 16)), pk_dec16(w2[2] | (w2[3] << 16)));
     }
   }
 }
@@ -770,7 +808,8 @@ __device__ __forceinline__ uint4 gm_decode_one(const uint2 (&i1)[2], const uint2
   uint32_t a2 = 0;
   if constexpr (BPW == 3) a2 = (i2[t].x >> (8 * u)) & 0xFFu;
   if constexpr (BPW == 4) a2 = ((u < 2 ? i2[t].x : i2[t].y) >> (16 * (u & 1))) & 0xFFFFu;
-  return decode_group<BPW>(a1, a2, lds);
+  (void)lds;
+  return decode_ip<BPW>(a1, a2);
 }
 
 template <int BPW, bool G4>
