@@ -849,26 +849,51 @@ gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][t][e] = 0.f;
 
+  // software pipeline: the weights of step s + 1 are decoded while the MFMAs
+  // of step s run; the scheduler is told to interleave them (one MFMA, then
+  // a few VALU and LDS instructions), since a wave issues in order and each
+  // SIMD holds one wave
+  uint4 bv[2][4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    bv[0][u] = gm_decode_one<BPW>(i1, i2, 0, u, lds);
+    bv[1][u] = gm_decode_one<BPW>(i1, i2, 1, u, lds);
+  }
+  gm_load_idx<BPW, G4>(idx1, idx2, n, G, n0, c, p, min((int64_t)1, S - 1), i1, i2);
+
   for (int64_t s = 0; s < S; ++s) {
     const uint16_t *Acur = (s & 1) ? As1 : As0;
     const uint2 c1[2] = {i1[0], i1[1]}, c2[2] = {i2[0], i2[1]};
-    gm_load_idx<BPW, G4>(idx1, idx2, n, G, n0, c, p, min(s + 1, S - 1), i1, i2);
-    // decode and MFMAs in one basic block so the scheduler overlaps them
+    gm_load_idx<BPW, G4>(idx1, idx2, n, G, n0, c, p, min(s + 2, S - 1), i1, i2);
+    uint4 bn[2][4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const uint4 b0 = gm_decode_one<BPW>(c1, c2, 0, u, lds);
-      const uint4 b1 = gm_decode_one<BPW>(c1, c2, 1, u, lds);
+      bn[0][u] = gm_decode_one<BPW>(c1, c2, 0, u, lds);
+      bn[1][u] = gm_decode_one<BPW>(c1, c2, 1, u, lds);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
 #pragma unroll
       for (int a = 0; a < 8; ++a) {
         const uint4 av = *reinterpret_cast<const uint4 *>(Acur + (32 * a + c) * GM_LDA + 32 * p + 8 * u);
         acc[a][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
-                                                            __builtin_bit_cast(bf16x8, b0), acc[a][0], 0, 0, 0);
+                                                            __builtin_bit_cast(bf16x8, bv[0][u]), acc[a][0], 0, 0, 0);
         acc[a][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
-                                                            __builtin_bit_cast(bf16x8, b1), acc[a][1], 0, 0, 0);
+                                                            __builtin_bit_cast(bf16x8, bv[1][u]), acc[a][1], 0, 0, 0);
       }
     }
     gm_store_a((s & 1) ? As0 : As1, ra);             // tile s + 1 (harmless past the end)
     gm_load_a(xt, m, k, m0, min(s + 2, S - 1), ra);
+#pragma unroll
+    for (int g = 0; g < 64; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // 4 VALU
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) bv[t][u] = bn[t][u];
     __syncthreads();
   }
 #pragma unroll
