@@ -777,26 +777,37 @@ __device__ __forceinline__ void gm_load_idx(const uint16_t *idx1, const void *id
 }
 
 // x~ tile of k-step s: 256 rows x 64 inputs (128 B per row); piece
-// pc = tid + 256 u is row pc >> 3, 16-byte column pc & 7. Clamped loads,
-// zeroed outside [0, m) x [0, k).
+// pc = tid + 256 u is row pc >> 3, 16-byte column pc & 7. The loads are
+// unconditional with clamped addresses: rows past m only feed accumulator rows
+// that are never stored, and columns past k are zeroed when the tile is
+// written to LDS (a select on the loaded value here would turn the loads into
+// branches and make the wave wait for them at once).
 __device__ __forceinline__ void gm_load_a(const uint16_t *xt, int64_t m, int64_t k, int64_t m0, int64_t s,
                                           uint4 (&ra)[8]) {
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int pc = threadIdx.x + 256 * u;
-    const int64_t r = m0 + (pc >> 3);
-    const int64_t kk = GM_BK * s + 8 * (pc & 7);
-    const bool ok = r < m && kk < k;
-    const uint4 v = *reinterpret_cast<const uint4 *>(xt + (size_t)min(r, m - 1) * k + min(kk, k - 8));
-    ra[u] = ok ? v : make_uint4(0, 0, 0, 0);
+    const int64_t r = min(m0 + (pc >> 3), m - 1);
+    const int64_t kk = min(GM_BK * s + 8 * (pc & 7), k - 8);
+    ra[u] = *reinterpret_cast<const uint4 *>(xt + (size_t)r * k + kk);
   }
 }
 
-__device__ __forceinline__ void gm_store_a(uint16_t *As, const uint4 (&ra)[8]) {
+// kvalid = inputs of this tile that lie inside [0, k) (uniform)
+__device__ __forceinline__ void gm_store_a(uint16_t *As, const uint4 (&ra)[8], int64_t kvalid) {
+  if (kvalid >= GM_BK) {
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int pc = threadIdx.x + 256 * u;
-    *reinterpret_cast<uint4 *>(As + (pc >> 3) * GM_LDA + 8 * (pc & 7)) = ra[u];
+    for (int u = 0; u < 8; ++u) {
+      const int pc = threadIdx.x + 256 * u;
+      *reinterpret_cast<uint4 *>(As + (pc >> 3) * GM_LDA + 8 * (pc & 7)) = ra[u];
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int pc = threadIdx.x + 256 * u;
+      const bool ok = 8 * (pc & 7) < kvalid;
+      *reinterpret_cast<uint4 *>(As + (pc >> 3) * GM_LDA + 8 * (pc & 7)) = ok ? ra[u] : make_uint4(0, 0, 0, 0);
+    }
   }
 }
 
@@ -835,9 +846,12 @@ gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
   load_tables<BPW>(lds, blob);
   uint4 ra[8];
   gm_load_a(xt, m, k, m0, 0, ra);
-  uint2 i1[2], i2[2];
+  uint2 i1[2], i2[2], j1[2], j2[2];
   gm_load_idx<BPW, G4>(idx1, idx2, n, G, n0, c, p, 0, i1, i2);
-  gm_store_a(As0, ra);
+  gm_store_a(As0, ra, k);
+  // indices of step 1, then x~ tile 1: the same issue order as in the loop,
+  // so that the loop-entry wait for the indices does not cover the tile
+  gm_load_idx<BPW, G4>(idx1, idx2, n, G, n0, c, p, min((int64_t)1, S - 1), j1, j2);
   gm_load_a(xt, m, k, m0, min((int64_t)1, S - 1), ra);
   __syncthreads();                                   // tables and x~ tile 0 in LDS
 
@@ -849,30 +863,35 @@ gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][t][e] = 0.f;
 
-  // software pipeline: the weights of step s + 1 are decoded while the MFMAs
-  // of step s run; the scheduler is told to interleave them (one MFMA, then
-  // a few VALU and LDS instructions), since a wave issues in order and each
-  // SIMD holds one wave
+  // Software pipeline: the weights of step s + 1 are decoded while the MFMAs
+  // of step s run. A wave issues in order and each SIMD holds one wave, so the
+  // table walk of all 8 groups is split into phases, one per MFMA block (chunk
+  // entries, orbit records, half-vectors, combine), and each phase's LDS reads
+  // have a whole block of MFMAs to return instead of stalling the wave.
   uint4 bv[2][4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     bv[0][u] = gm_decode_one<BPW>(i1, i2, 0, u, lds);
     bv[1][u] = gm_decode_one<BPW>(i1, i2, 1, u, lds);
   }
-  gm_load_idx<BPW, G4>(idx1, idx2, n, G, n0, c, p, min((int64_t)1, S - 1), i1, i2);
+#pragma unroll
+  for (int t = 0; t < 2; ++t) { i1[t] = j1[t]; i2[t] = j2[t]; }
 
   for (int64_t s = 0; s < S; ++s) {
     const uint16_t *Acur = (s & 1) ? As1 : As0;
-    const uint2 c1[2] = {i1[0], i1[1]}, c2[2] = {i2[0], i2[1]};
-    gm_load_idx<BPW, G4>(idx1, idx2, n, G, n0, c, p, min(s + 2, S - 1), i1, i2);
-    uint4 bn[2][4];
+    // indices of step s + 1 (group g = 4 t + u), as i' = i - 1 mod 2^16
+    uint32_t q1[8], q2[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      bn[0][u] = gm_decode_one<BPW>(c1, c2, 0, u, lds);
-      bn[1][u] = gm_decode_one<BPW>(c1, c2, 1, u, lds);
+    for (int g = 0; g < 8; ++g) {
+      const int t = g >> 2, u = g & 3;
+      q1[g] = ((u < 2 ? i1[t].x : i1[t].y) >> (16 * (u & 1))) & 0xFFFFu;
+      if constexpr (BPW == 3) q2[g] = (i2[t].x >> (8 * u)) & 0xFFu;
+      else if constexpr (BPW == 4) q2[g] = ((u < 2 ? i2[t].x : i2[t].y) >> (16 * (u & 1))) & 0xFFFFu;
+      else q2[g] = 0u;
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    gm_load_idx<BPW, G4>(idx1, idx2, n, G, n0, c, p, min(s + 2, S - 1), i1, i2);
+
+    auto mfma_block = [&](int u) {
 #pragma unroll
       for (int a = 0; a < 8; ++a) {
         const uint4 av = *reinterpret_cast<const uint4 *>(Acur + (32 * a + c) * GM_LDA + 32 * p + 8 * u);
@@ -881,19 +900,67 @@ gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
         acc[a][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
                                                             __builtin_bit_cast(bf16x8, bv[1][u]), acc[a][1], 0, 0, 0);
       }
+    };
+
+    // phase 1: chunk-table entries (and the direct residual rows at 3 bpw)
+    uint32_t e1[8], e2[8];
+    uint4 r3[8];
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      e1[g] = lds16(kLdsCt + ((q1[g] >> 4) << 1));
+      if constexpr (BPW == 4) e2[g] = lds16(kLdsCt + ((q2[g] >> 4) << 1));
+      if constexpr (BPW == 3) r3[g] = lds128(kLdsHt2 + (q2[g] << 4));
     }
-    gm_store_a((s & 1) ? As0 : As1, ra);             // tile s + 1 (harmless past the end)
+    mfma_block(0);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // phase 2: orbit records
+    uint4 R1[8], R2[8];
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      R1[g] = lds128(kLdsOt + (((e1[g] >> 5) + ((q1[g] & 15u) >> (e1[g] & 31u))) << 4));
+      if constexpr (BPW == 4) R2[g] = lds128(kLdsOt + (((e2[g] >> 5) + ((q2[g] & 15u) >> (e2[g] & 31u))) << 4));
+    }
+    mfma_block(1);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // phase 3: the signed half-vectors
+    uint2 va[8], vb[8], vc[8], vd[8];
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const uint4 R = R1[g];
+      const uint32_t lo = R.y + (__builtin_amdgcn_ubfe(q1[g], 0, R.x) << 3);
+      const uint32_t hi = R.z + ((q1[g] >> R.x) << 3) + ((__builtin_popcount(__builtin_amdgcn_ubfe(q1[g], 0, R.w)) & 1u) << 6);
+      va[g] = lds64(kLdsHt1 + lo);
+      vb[g] = lds64(kLdsHt1 + hi);
+      if constexpr (BPW == 4) {
+        const uint4 Q = R2[g];
+        const uint32_t lo2 = Q.y + (__builtin_amdgcn_ubfe(q2[g], 0, Q.x) << 3);
+        const uint32_t hi2 = Q.z + ((q2[g] >> Q.x) << 3) + ((__builtin_popcount(__builtin_amdgcn_ubfe(q2[g], 0, Q.w)) & 1u) << 6);
+        vc[g] = lds64(kLdsHt2 + lo2);
+        vd[g] = lds64(kLdsHt2 + hi2);
+      }
+    }
+    mfma_block(2);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // phase 4: combine into operand form; stage the next x~ tile
+    uint4 bn[8];
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      if constexpr (BPW == 2) bn[g] = make_uint4(va[g].x, va[g].y, vb[g].x, vb[g].y);
+      else if constexpr (BPW == 3)
+        bn[g] = make_uint4(pk_add16(va[g].x, r3[g].x), pk_add16(va[g].y, r3[g].y),
+                           pk_add16(vb[g].x, r3[g].z), pk_add16(vb[g].y, r3[g].w));
+      else
+        bn[g] = make_uint4(pk_add16(va[g].x, vc[g].x), pk_add16(va[g].y, vc[g].y),
+                           pk_add16(vb[g].x, vd[g].x), pk_add16(vb[g].y, vd[g].y));
+    }
+    mfma_block(3);
+    gm_store_a((s & 1) ? As0 : As1, ra, k - GM_BK * (s + 1));   // tile s + 1 (unused past the end)
     gm_load_a(xt, m, k, m0, min(s + 2, S - 1), ra);
 #pragma unroll
-    for (int g = 0; g < 64; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // 4 VALU
-    }
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) bv[t][u] = bn[t][u];
+    for (int g = 0; g < 8; ++g) bv[g >> 2][g & 3] = bn[g];
     __syncthreads();
   }
 #pragma unroll
