@@ -26,6 +26,9 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
+#include <utility>
+#include <vector>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -103,6 +106,15 @@ __device__ __forceinline__ uint2 lds64(uint32_t addr) {
 __device__ __forceinline__ uint4 lds128(uint32_t addr) {
   const u32x4_t v = *reinterpret_cast<lds_u128 *>(static_cast<uintptr_t>(addr));
   return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+typedef __attribute__((address_space(3))) uint16_t lds_u16_w;
+typedef __attribute__((address_space(3))) float lds_f32_w;
+__device__ __forceinline__ void lds_st16(uint32_t addr, uint32_t v) {
+  *reinterpret_cast<lds_u16_w *>(static_cast<uintptr_t>(addr)) = static_cast<uint16_t>(v);
+}
+__device__ __forceinline__ void lds_stf(uint32_t addr, float v) {
+  *reinterpret_cast<lds_f32_w *>(static_cast<uintptr_t>(addr)) = v;
 }
 
 // i' = i - 1 (mod 2^16) for the two 16-bit indices packed in a word.
@@ -823,11 +835,96 @@ __device__ __forceinline__ uint4 gm_decode_one(const uint2 (&i1)[2], const uint2
   return decode_ip<BPW>(a1, a2);
 }
 
-template <int BPW, bool G4>
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// GEMM epilogue: z = post * acc + cz(row) with cz = -post * bias * rowsum(x~),
+// staged through LDS (free once the k-loop has ended) so that every lane
+// stores 16 contiguous bytes of an output row. Each wave stages its own
+// 256 x 64 tile in chunks of CH 32-row blocks. vec: 16-byte stores are
+// aligned (n * element size % 16 == 0 and an aligned output pointer).
+template <int BPW, bool OUT_BF16>
+__device__ __forceinline__ void gm_epilogue(const f32x16 (&acc)[8][2], const float *rowsum, float post,
+                                            void *out, int64_t m, int64_t n, int64_t m0, int64_t n0,
+                                            int lane, int wave, bool vec) {
+  constexpr int ES = OUT_BF16 ? 2 : 4;              // bytes per output value
+  constexpr int CH = OUT_BF16 ? 4 : 2;              // 32-row blocks per chunk
+  constexpr uint32_t SB = 64 * ES + 16;             // padded LDS row stride (bytes)
+  constexpr uint32_t WAVE_BYTES = 32 * CH * SB;
+  constexpr int CPR = 64 * ES / 16;                 // 16-byte pieces per row
+  constexpr int RPI = 64 / CPR;                     // rows per pass of the wave
+  constexpr int EPP = 16 / ES;                      // values per piece
+  const int c = lane & 31, p = lane >> 5;
+  const uint32_t wbase = wave * WAVE_BYTES;
+  const int64_t rlast4 = ((m - 1) >> 2) << 2;
+#pragma unroll
+  for (int a0 = 0; a0 < 8; a0 += CH) {
+#pragma unroll
+    for (int a = a0; a < a0 + CH; ++a) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float cz[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (Epi<BPW>::bias != 0.0f) {
+          // rows r0 .. r0 + 3 (r0 % 4 == 0); the clamped 16-byte load stays
+          // inside the 256-byte-aligned row-sum buffer
+          const int64_t r0 = min(m0 + 32 * a + 8 * q + 4 * p, rlast4);
+          const float4 rs = *reinterpret_cast<const float4 *>(rowsum + r0);
+          const float f = -post * Epi<BPW>::bias;
+          cz[0] = f * rs.x; cz[1] = f * rs.y; cz[2] = f * rs.z; cz[3] = f * rs.w;
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const uint32_t base = wbase + (32 * (a - a0) + 8 * q + 4 * p) * SB + (32 * t + c) * ES;
+          float v[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[j] = fmaf(acc[a][t][4 * q + j], post, cz[j]);
+          if constexpr (OUT_BF16) {
+#pragma unroll
+            for (int j = 0; j < 4; j += 2) {
+              const f32x2_t f2 = {v[j], v[j + 1]};
+              const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2, bf16x2_t));
+              lds_st16(base + j * SB, h);
+              lds_st16(base + (j + 1) * SB, h >> 16);
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) lds_stf(base + j * SB, v[j]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 32 * CH / RPI; ++it) {
+      const int rl = it * RPI + lane / CPR, pc = lane % CPR;
+      const uint4 v = lds128(wbase + rl * SB + pc * 16);
+      const int64_t r = m0 + 32 * a0 + rl;
+      const int64_t col = n0 + pc * EPP;
+      if (r < m) {
+        uint8_t *dst = reinterpret_cast<uint8_t *>(out) + ((size_t)r * n + col) * ES;
+        if (vec && col + EPP <= n) {
+          *reinterpret_cast<uint4 *>(dst) = v;
+        } else {
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < EPP; ++e) {
+            if (col + e < n) {
+              if constexpr (OUT_BF16) reinterpret_cast<uint16_t *>(dst)[e] = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+              else reinterpret_cast<uint32_t *>(dst)[e] = w[e];
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int BPW, bool G4, bool OUT_BF16>
 __global__ void __launch_bounds__(256, 1)
 gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uint16_t *xt,
           const float *rowsum, int64_t m, int64_t n, int64_t k, float post, void *out,
-          glq_dtype out_dt, int64_t mblocks, int64_t tiles) {
+          int vec, int64_t mblocks, int64_t tiles) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   uint16_t *As0 = reinterpret_cast<uint16_t *>(lds + lds_table_bytes<BPW>());
   uint16_t *As1 = As0 + GM_BM * GM_LDA;
@@ -963,20 +1060,7 @@ gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
     for (int g = 0; g < 8; ++g) bv[g >> 2][g & 3] = bn[g];
     __syncthreads();
   }
-#pragma unroll
-  for (int a = 0; a < 8; ++a) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int64_t r = m0 + 32 * a + 8 * (i >> 2) + 4 * p + (i & 3);
-      if (r >= m) continue;
-      const float bias = Epi<BPW>::bias != 0.0f ? Epi<BPW>::bias * rowsum[r] : 0.0f;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int64_t col = n0 + 32 * t + c;
-        if (col < n) store_out(out, out_dt, (size_t)r * n + col, post * (acc[a][t][i] - bias));
-      }
-    }
-  }
+  gm_epilogue<BPW, OUT_BF16>(acc, rowsum, post, out, m, n, m0, n0, lane, wave, vec != 0);
 }
 
 // ---------------------------------------------------------------- float32 path
@@ -1032,20 +1116,26 @@ int hip_status(hipError_t e, const char *where = "launch") {
 }
 
 // Allow dynamic LDS above the 64 KiB default (gfx950 has 160 KiB per CU).
-// The attribute is raised once per kernel to the largest size asked so far.
+// The attribute is raised once per kernel (keyed by its address: kernels of
+// one signature share a function-pointer type) to the largest size asked.
 template <class K>
 int allow_lds(K kernel, size_t bytes) {
   if (bytes <= 60 * 1024) return GLQ_OK;
-  static std::atomic<size_t> granted{0};
-  if (granted.load(std::memory_order_acquire) >= bytes) return GLQ_OK;
-  const int rc = hip_status(hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
-                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes),
-                            "hipFuncSetAttribute");
-  if (rc == GLQ_OK) {
-    size_t cur = granted.load();
-    while (cur < bytes && !granted.compare_exchange_weak(cur, bytes)) {
+  static std::mutex mu;
+  static std::vector<std::pair<const void *, size_t>> granted;
+  const void *key = reinterpret_cast<const void *>(kernel);
+  std::lock_guard<std::mutex> lock(mu);
+  for (auto &g : granted)
+    if (g.first == key) {
+      if (g.second >= bytes) return GLQ_OK;
+      const int rc = hip_status(hipFuncSetAttribute(key, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes),
+                                "hipFuncSetAttribute");
+      if (rc == GLQ_OK) g.second = bytes;
+      return rc;
     }
-  }
+  const int rc = hip_status(hipFuncSetAttribute(key, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes),
+                            "hipFuncSetAttribute");
+  if (rc == GLQ_OK) granted.emplace_back(key, bytes);
   return rc;
 }
 
@@ -1205,14 +1295,14 @@ int launch_matmul(const glq_layer *L, const void *xt, glq_dtype x_dt, const floa
     if (tiles > 0x7FFFFFFF) return GLQ_ERR_UNSUPPORTED;
     const size_t shm = tab + 2 * GM_A_BYTES;
     const bool even_g = ((L->k / 8) % 4) == 0;
-    int rc = even_g ? allow_lds(gemm_bf16<BPW, true>, shm) : allow_lds(gemm_bf16<BPW, false>, shm);
+    const bool ob = out_dt == GLQ_BF16;
+    const int vec = ((L->n * (ob ? 2 : 4)) % 16 == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0) ? 1 : 0;
+    auto kern = even_g ? (ob ? gemm_bf16<BPW, true, true> : gemm_bf16<BPW, true, false>)
+                       : (ob ? gemm_bf16<BPW, false, true> : gemm_bf16<BPW, false, false>);
+    int rc = allow_lds(kern, shm);
     if (rc) return rc;
-    if (even_g)
-      hipLaunchKernelGGL((gemm_bf16<BPW, true>), dim3((unsigned)tiles), dim3(256), shm, st, L->idx1, L->idx2,
-                         blob, xb, rowsum, m, L->n, L->k, post, out, out_dt, mb, tiles);
-    else
-      hipLaunchKernelGGL((gemm_bf16<BPW, false>), dim3((unsigned)tiles), dim3(256), shm, st, L->idx1, L->idx2,
-                         blob, xb, rowsum, m, L->n, L->k, post, out, out_dt, mb, tiles);
+    hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(256), shm, st, L->idx1, L->idx2, blob, xb, rowsum, m,
+                       L->n, L->k, post, out, vec, mb, tiles);
   }
   return hip_status(hipGetLastError());
 }

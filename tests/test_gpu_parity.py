@@ -197,6 +197,53 @@ def test_fused_shapes_bf16(G, cb, bpw, m):
 
 
 @pytest.mark.parametrize("bpw", [2, 3, 4])
+@pytest.mark.parametrize("m,n,k", [(300, 320, 512), (257, 264, 160), (64, 512, 4160), (40, 136, 72)])
+def test_prefill_tiles(G, cb, bpw, m, n, k):
+    # several 256 x 256 output tiles with ragged row and column tails, the
+    # 16-byte-store epilogue (n * element size % 16 == 0) and its per-element
+    # fallback, and a k that is not a multiple of the 64-input k-step
+    i1, i2 = _random_layer(n, k, bpw, 3000 + m + n + k)
+    s = np.float32(0.017)
+    sn, sk = workloads.signs(n, 41), workloads.signs(k, 42)
+    x = workloads.bf16_round_trip(np.random.default_rng(m + k).standard_normal((m, k)).astype(np.float32))
+    ref = og.layer_reference(x, i1, i2, bpw, s, sn, sk)
+    for y_dt in ("bf16", "f32"):
+        y = _run_linear(G, cb, i1, i2, s, sn, sk, x, "bf16", y_dt)
+        assert og.relative_error(y, ref) <= TOL_BF16
+
+
+_LDS_ORDER_SCRIPT = r"""
+import numpy as np, torch
+from dequant_e8_codebook_amd import glq
+import workloads
+cb = glq.device_codebook("cuda")
+for bpw in (4, 3, 2):
+    n, k, m = 256, 256, 64
+    i1 = workloads.random_indices((n, k // 8), 5)
+    i2 = None if bpw == 2 else workloads.random_indices((n, k // 8), 6, 256 if bpw == 3 else 65536,
+                                                         np.uint8 if bpw == 3 else np.uint16)
+    L = glq.Layer.from_numpy(i1, i2, 0.01, workloads.signs(n, 1), workloads.signs(k, 2), cb)
+    x = torch.randn(m, k, device="cuda").to(torch.bfloat16)
+    for y_dt in (torch.float32, torch.bfloat16):
+        y = torch.empty(m, n, device="cuda", dtype=y_dt)
+        ws = torch.zeros(glq.workspace_bytes(L, m), device="cuda", dtype=torch.uint8)
+        glq.fused_linear(L, x, y, ws)
+torch.cuda.synchronize()
+print("ok", flush=True)
+"""
+
+
+def test_lds_limit_any_call_order(G):
+    # a fresh process whose first prefill call needs the most LDS (4 bpw) and
+    # whose later calls need less: each kernel gets its own LDS limit
+    import os, subprocess, sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", _LDS_ORDER_SCRIPT], cwd=root, capture_output=True, text=True,
+                       timeout=110)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout + r.stderr
+
+
+@pytest.mark.parametrize("bpw", [2, 3, 4])
 @pytest.mark.parametrize("m,n,k", [(1, 1, 8), (4, 17, 24), (6, 64, 520), (2, 300, 256)])
 def test_fused_shapes_f32(G, cb, bpw, m, n, k):
     i1, i2 = _random_layer(n, k, bpw, 2000 + n + k + m)
