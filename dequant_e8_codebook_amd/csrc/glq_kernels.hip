@@ -988,14 +988,26 @@ gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
     }
     gm_load_idx<BPW, G4>(idx1, idx2, n, G, n0, c, p, min(s + 2, S - 1), i1, i2);
 
+    // A operands: those of block u + 1 are read while block u runs
+    uint4 av[8], an[8];
+#pragma unroll
+    for (int a = 0; a < 8; ++a) av[a] = *reinterpret_cast<const uint4 *>(Acur + (32 * a + c) * GM_LDA + 32 * p);
     auto mfma_block = [&](int u) {
+      if (u < 3) {
+#pragma unroll
+        for (int a = 0; a < 8; ++a)
+          an[a] = *reinterpret_cast<const uint4 *>(Acur + (32 * a + c) * GM_LDA + 32 * p + 8 * (u + 1));
+      }
 #pragma unroll
       for (int a = 0; a < 8; ++a) {
-        const uint4 av = *reinterpret_cast<const uint4 *>(Acur + (32 * a + c) * GM_LDA + 32 * p + 8 * u);
-        acc[a][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+        acc[a][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[a]),
                                                             __builtin_bit_cast(bf16x8, bv[0][u]), acc[a][0], 0, 0, 0);
-        acc[a][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+        acc[a][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[a]),
                                                             __builtin_bit_cast(bf16x8, bv[1][u]), acc[a][1], 0, 0, 0);
+      }
+      if (u < 3) {
+#pragma unroll
+        for (int a = 0; a < 8; ++a) av[a] = an[a];
       }
     };
 
