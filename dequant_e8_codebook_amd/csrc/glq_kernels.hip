@@ -58,33 +58,34 @@ template <> struct TabCfg<4> { static constexpr uint32_t ht1 = kHtA4Off, ht2 = k
 template <int BPW>
 constexpr uint32_t lds_table_bytes() { return kLdsHt2 + TabCfg<BPW>::ht2_bytes; }
 
-// Copy CT + OT + the two value tables of this bit width into LDS. Each
-// thread first issues all of its 16-byte loads (clamped addresses, no
-// branches) and only then writes LDS, so the global-memory latency is paid
-// once per workgroup instead of once per chunk.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// Copy CT + OT + the two value tables of this bit width into LDS (bytes
+// 0 .. lds_table_bytes) with global-to-LDS loads: no registers held, nothing
+// waited for here. Run r (1 KiB of the LDS image) is copied by wave r mod the
+// wave count, lane i writing its bytes 16 i .. 16 i + 15. The caller waits
+// with tables_landed() before the barrier that publishes the tables.
 template <int BPW, int NT = 256>
-__device__ __forceinline__ void load_tables(uint8_t *lds, const uint8_t *blob) {
-  constexpr uint32_t c01 = (kCtBytes + kOtBytes) / 16;          // CT + OT (contiguous in both)
-  constexpr uint32_t c2 = c01 + kHtBytes / 16;                   // + stage-1 half table
-  constexpr uint32_t total = lds_table_bytes<BPW>() / 16;
-  constexpr uint32_t per = (total + NT - 1) / NT;
-  static_assert(kLdsCt == 0 && kLdsOt == kCtBytes && kLdsHt1 == kCtBytes + kOtBytes, "LDS table order");
-  const uint32_t tid = threadIdx.x;       // blockDim.x == NT
-  uint4 v[per];
-#pragma unroll
-  for (uint32_t r = 0; r < per; ++r) {
-    const uint32_t i = min(tid + NT * r, total - 1);
-    const uint32_t src = i < c01 ? kCtOff + 16 * i
-                       : i < c2  ? TabCfg<BPW>::ht1 + 16 * (i - c01)
-                                 : TabCfg<BPW>::ht2 + 16 * (i - c2);
-    v[r] = *reinterpret_cast<const uint4 *>(blob + src);
-  }
-#pragma unroll
-  for (uint32_t r = 0; r < per; ++r) {
-    const uint32_t i = tid + NT * r;
-    if (i < total) reinterpret_cast<uint4 *>(lds)[i] = v[r];
+__device__ __forceinline__ void load_tables(uint8_t *, const uint8_t *blob) {
+  constexpr uint32_t b01 = kCtBytes + kOtBytes;                 // CT + OT (contiguous in both)
+  constexpr uint32_t b2 = b01 + kHtBytes;                       // + stage-1 half table
+  constexpr uint32_t total = lds_table_bytes<BPW>();
+  constexpr uint32_t runs = (total + 1023) / 1024;
+  static_assert(kLdsCt == 0 && kLdsOt == kCtBytes && kLdsHt1 == b01 && total % 16 == 0, "LDS table order");
+  const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (uint32_t r = wave; r < runs; r += NT / 64) {
+    const uint32_t pos = 1024 * r + 16 * lane;
+    if (pos < total) {
+      const uint32_t src = pos < b01 ? kCtOff + pos : pos < b2 ? TabCfg<BPW>::ht1 + (pos - b01)
+                                                               : TabCfg<BPW>::ht2 + (pos - b2);
+      __builtin_amdgcn_global_load_lds((glb_void_t *)(blob + src), (lds_void_t *)(uintptr_t)(1024 * r), 16, 0, 0);
+    }
   }
 }
+
+// wait for this wave's vector-memory loads, the table copies included
+__device__ __forceinline__ void tables_landed() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 
 // LDS pointers built from absolute addresses. Every kernel that decodes uses
 // dynamic LDS only (no static __shared__), so its dynamic region starts at
@@ -167,6 +168,63 @@ template <int BPW>
 __device__ __forceinline__ uint4 decode_group(uint32_t i1, uint32_t i2, const uint8_t *) {
   return decode_ip<BPW>((i1 - 1u) & 0xFFFFu, BPW == 4 ? ((i2 - 1u) & 0xFFFFu) : i2);
 }
+
+// Table walk of 8 groups split into phases, so that the LDS reads of one
+// phase for all 8 groups are in flight together: p1 chunk-table entries (and
+// the direct residual rows at 3 bpw), p2 orbit records, p3 the signed
+// half-vectors, p4 the combine into operand form (as decode_ip). q1 / q2 hold
+// the indices as decode_ip takes them.
+template <int BPW>
+struct Dec8 {
+  uint32_t e1[8], e2[8];
+  uint4 r3[8], R1[8], R2[8];
+  uint2 va[8], vb[8], vc[8], vd[8];
+
+  __device__ __forceinline__ void p1(const uint32_t (&q1)[8], const uint32_t (&q2)[8]) {
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      e1[g] = lds16(kLdsCt + ((q1[g] >> 4) << 1));
+      if constexpr (BPW == 4) e2[g] = lds16(kLdsCt + ((q2[g] >> 4) << 1));
+      if constexpr (BPW == 3) r3[g] = lds128(kLdsHt2 + (q2[g] << 4));
+    }
+  }
+  __device__ __forceinline__ void p2(const uint32_t (&q1)[8], const uint32_t (&q2)[8]) {
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      R1[g] = lds128(kLdsOt + (((e1[g] >> 5) + ((q1[g] & 15u) >> (e1[g] & 31u))) << 4));
+      if constexpr (BPW == 4) R2[g] = lds128(kLdsOt + (((e2[g] >> 5) + ((q2[g] & 15u) >> (e2[g] & 31u))) << 4));
+    }
+  }
+  __device__ __forceinline__ void p3(const uint32_t (&q1)[8], const uint32_t (&q2)[8]) {
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const uint4 R = R1[g];
+      const uint32_t lo = R.y + (__builtin_amdgcn_ubfe(q1[g], 0, R.x) << 3);
+      const uint32_t hi = R.z + ((q1[g] >> R.x) << 3) + ((__builtin_popcount(__builtin_amdgcn_ubfe(q1[g], 0, R.w)) & 1u) << 6);
+      va[g] = lds64(kLdsHt1 + lo);
+      vb[g] = lds64(kLdsHt1 + hi);
+      if constexpr (BPW == 4) {
+        const uint4 Q = R2[g];
+        const uint32_t lo2 = Q.y + (__builtin_amdgcn_ubfe(q2[g], 0, Q.x) << 3);
+        const uint32_t hi2 = Q.z + ((q2[g] >> Q.x) << 3) + ((__builtin_popcount(__builtin_amdgcn_ubfe(q2[g], 0, Q.w)) & 1u) << 6);
+        vc[g] = lds64(kLdsHt2 + lo2);
+        vd[g] = lds64(kLdsHt2 + hi2);
+      }
+    }
+  }
+  __device__ __forceinline__ void p4(uint4 (&out)[8]) {
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      if constexpr (BPW == 2) out[g] = make_uint4(va[g].x, va[g].y, vb[g].x, vb[g].y);
+      else if constexpr (BPW == 3)
+        out[g] = make_uint4(pk_add16(va[g].x, r3[g].x), pk_add16(va[g].y, r3[g].y),
+                            pk_add16(vb[g].x, r3[g].z), pk_add16(vb[g].y, r3[g].w));
+      else
+        out[g] = make_uint4(pk_add16(va[g].x, vc[g].x), pk_add16(va[g].y, vc[g].y),
+                            pk_add16(vb[g].x, vd[g].x), pk_add16(vb[g].y, vd[g].y));
+    }
+  }
+};
 
 // value of one decoded 16-bit operand as the exact float32 v
 template <int BPW>
@@ -430,6 +488,7 @@ decode_weights_k(const uint16_t *idx1, const void *idx2, const uint8_t *blob, fl
                  int64_t groups, void *out) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   load_tables<BPW>(lds, blob);
+  tables_landed();
   __syncthreads();
   for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < groups;
        g += (int64_t)gridDim.x * blockDim.x) {
@@ -469,37 +528,62 @@ decode_weights_k(const uint16_t *idx1, const void *idx2, const uint8_t *blob, fl
 // decode. Partial sums of the 16 waves meet in LDS.
 constexpr int GV_WAVES = 16;
 
-// Indices come back as i' = i - 1 mod 2^16 (stage 1, and stage 2 at 4 bpw).
+// Index loads of 8 consecutive groups of one weight row, kept as loaded so
+// that nothing waits for them until gv_unpack (a computation on a loaded
+// value placed right after its load would stall the wave there).
+struct GvRaw { uint4 a, b; };
+
 template <int BPW, bool G8>
-__device__ __forceinline__ void gv_load_idx(const uint16_t *idx1, const void *idx2, int64_t row, int64_t G,
-                                            int64_t g0, uint32_t (&i1)[8], uint32_t (&i2)[8]) {
-  // row is clamped to the layer; groups past G are clamped (they meet zero x~)
+__device__ __forceinline__ GvRaw gv_load_raw(const uint16_t *idx1, const void *idx2, int64_t row, int64_t G,
+                                             int64_t g0) {
+  // row is clamped to the layer; groups past G are clamped (they meet zero weight operands)
+  GvRaw r;
   if constexpr (G8) {
     const int64_t off = row * G + min(g0, G - 8);
-    const uint4 a = *reinterpret_cast<const uint4 *>(idx1 + off);
-    const uint32_t w[4] = {pk_dec16(a.x), pk_dec16(a.y), pk_dec16(a.z), pk_dec16(a.w)};
-#pragma unroll
-    for (int u = 0; u < 4; ++u) { i1[2 * u] = w[u] & 0xFFFFu; i1[2 * u + 1] = w[u] >> 16; }
+    r.a = *reinterpret_cast<const uint4 *>(idx1 + off);
     if constexpr (BPW == 3) {
       const uint2 b = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint8_t *>(idx2) + off);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) { i2[u] = (b.x >> (8 * u)) & 0xFFu; i2[4 + u] = (b.y >> (8 * u)) & 0xFFu; }
+      r.b = make_uint4(b.x, b.y, 0u, 0u);
     } else if constexpr (BPW == 4) {
-      const uint4 b = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(idx2) + off);
-      const uint32_t x[4] = {pk_dec16(b.x), pk_dec16(b.y), pk_dec16(b.z), pk_dec16(b.w)};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) { i2[2 * u] = x[u] & 0xFFFFu; i2[2 * u + 1] = x[u] >> 16; }
+      r.b = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(idx2) + off);
     } else {
-#pragma unroll
-      for (int u = 0; u < 8; ++u) i2[u] = 0;
+      r.b = make_uint4(0u, 0u, 0u, 0u);
     }
   } else {
+    uint32_t w1[8], w2[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int64_t o = row * G + min(g0 + u, G - 1);
-      i1[u] = ((uint32_t)idx1[o] - 1u) & 0xFFFFu;
-      i2[u] = BPW == 4 ? ((load_idx2(idx2, o, 4) - 1u) & 0xFFFFu) : BPW == 3 ? load_idx2(idx2, o, 3) : 0u;
+      w1[u] = idx1[o];
+      w2[u] = BPW == 2 ? 0u : load_idx2(idx2, o, BPW);
     }
+    r.a = make_uint4(w1[0] | (w1[1] << 16), w1[2] | (w1[3] << 16), w1[4] | (w1[5] << 16), w1[6] | (w1[7] << 16));
+    if constexpr (BPW == 3)
+      r.b = make_uint4(w2[0] | (w2[1] << 8) | (w2[2] << 16) | (w2[3] << 24),
+                       w2[4] | (w2[5] << 8) | (w2[6] << 16) | (w2[7] << 24), 0u, 0u);
+    else
+      r.b = make_uint4(w2[0] | (w2[1] << 16), w2[2] | (w2[3] << 16), w2[4] | (w2[5] << 16), w2[6] | (w2[7] << 16));
+  }
+  return r;
+}
+
+// i1 = i' = i - 1 mod 2^16 of stage 1; i2 = i' of stage 2 at 4 bpw, the plain
+// residual row at 3 bpw
+template <int BPW>
+__device__ __forceinline__ void gv_unpack(const GvRaw &r, uint32_t (&i1)[8], uint32_t (&i2)[8]) {
+  const uint32_t w[4] = {pk_dec16(r.a.x), pk_dec16(r.a.y), pk_dec16(r.a.z), pk_dec16(r.a.w)};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) { i1[2 * u] = w[u] & 0xFFFFu; i1[2 * u + 1] = w[u] >> 16; }
+  if constexpr (BPW == 3) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) { i2[u] = (r.b.x >> (8 * u)) & 0xFFu; i2[4 + u] = (r.b.y >> (8 * u)) & 0xFFu; }
+  } else if constexpr (BPW == 4) {
+    const uint32_t x[4] = {pk_dec16(r.b.x), pk_dec16(r.b.y), pk_dec16(r.b.z), pk_dec16(r.b.w)};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) { i2[2 * u] = x[u] & 0xFFFFu; i2[2 * u + 1] = x[u] >> 16; }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) i2[u] = 0u;
   }
 }
 
@@ -516,34 +600,43 @@ gemv_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
   const int64_t row = min(n0 + j, n - 1);
   const int64_t G = k / 8;
   const int64_t chunks = (G + 31) / 32;
-  const bool a_row = j < m;
   const uint16_t *xrow = xt + (size_t)min((int64_t)j, m - 1) * k;
 
-  // the first chunk's loads go out before the table copy; later chunks (k >
-  // 4096) are loaded one at a time: the other waves of the SIMD hide the wait
+  // The first chunk's loads go out before the table copy; later chunks (k >
+  // 4096) are loaded one at a time: the other waves of the SIMD hide the wait.
+  // All loads are unconditional with clamped addresses (a select on a loaded
+  // value would make each load a branch that waits for it): x~ rows past m
+  // only feed output rows that are not stored, and groups past k meet zero
+  // weight operands.
   int64_t c = wave;
-  uint32_t i1[8], i2[8];
+  GvRaw raw;
   uint4 av[8];
   auto load_chunk = [&](int64_t cc) {
     const int64_t g0 = 32 * cc + 8 * q;
-    gv_load_idx<BPW, G8>(idx1, idx2, row, G, g0, i1, i2);
+    raw = gv_load_raw<BPW, G8>(idx1, idx2, row, G, g0);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int64_t g = g0 + s;
-      const uint4 v = *reinterpret_cast<const uint4 *>(xrow + 8 * min(g, G - 1));
-      av[s] = (a_row && g < G) ? v : make_uint4(0, 0, 0, 0);
-    }
+    for (int s = 0; s < 8; ++s) av[s] = *reinterpret_cast<const uint4 *>(xrow + 8 * min(g0 + s, G - 1));
   };
   if (c < chunks) load_chunk(c);
   load_tables<BPW, 64 * GV_WAVES>(lds, blob);
+  tables_landed();
   __syncthreads();
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   while (c < chunks) {
+    const int64_t g0 = 32 * c + 8 * q;
+    uint32_t i1[8], i2[8];
+    gv_unpack<BPW>(raw, i1, i2);
+    Dec8<BPW> D;
+    uint4 bv[8];
+    D.p1(i1, i2);
+    D.p2(i1, i2);
+    D.p3(i1, i2);
+    D.p4(bv);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const uint4 bv = decode_ip<BPW>(i1[s], i2[s]);
+      const uint4 b = g0 + s < G ? bv[s] : make_uint4(0, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[s]),
-                                                    __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
+                                                    __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
     }
     c += GV_WAVES;
     if (c < chunks) load_chunk(c);
@@ -607,13 +700,11 @@ layer_small(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const u
   const int j = lane & 15, q = lane >> 4;
   const int64_t G = k / 8, chunks = (G + 31) / 32;
   const int64_t tiles = (n + 15) / 16;
-  const bool a_row = j < m;
 
   // 1. first index loads in flight before anything else
   int64_t tile = blockIdx.x, c = wave;
-  uint32_t i1[8], i2[8];
-  if (tile < tiles && c < chunks)
-    gv_load_idx<BPW, true>(idx1, idx2, min(tile * 16 + j, n - 1), G, 32 * c + 8 * q, i1, i2);
+  GvRaw raw;
+  if (tile < tiles && c < chunks) raw = gv_load_raw<BPW, true>(idx1, idx2, min(tile * 16 + j, n - 1), G, 32 * c + 8 * q);
   // 2. decode tables, 3. x -> LDS with the input signs
   load_tables<BPW, 64 * GV_WAVES>(lds, blob);
   const int64_t mk = m * k;
@@ -624,6 +715,7 @@ layer_small(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const u
 #pragma unroll
     for (int t = 0; t < 8; ++t) xs[pidx((int)e + t)] = v[t] * sg[t];
   }
+  tables_landed();
   __syncthreads();
   ly_fwht(xs, (int)mk, logbk);
   {  // 4. scale, round to bf16 in place (read all, barrier, write), row sums
@@ -668,17 +760,24 @@ layer_small(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const u
     const int64_t row = min(tile * 16 + j, n - 1);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (c = wave; c < chunks; c += GV_WAVES) {
-      if (!(tile == (int64_t)blockIdx.x && c == wave))
-        gv_load_idx<BPW, true>(idx1, idx2, row, G, 32 * c + 8 * q, i1, i2);
+      if (!(tile == (int64_t)blockIdx.x && c == wave)) raw = gv_load_raw<BPW, true>(idx1, idx2, row, G, 32 * c + 8 * q);
       const int64_t g0 = 32 * c + 8 * q;
+      uint32_t i1[8], i2[8];
+      gv_unpack<BPW>(raw, i1, i2);
+      Dec8<BPW> D;
+      uint4 bv[8];
+      D.p1(i1, i2);
+      D.p2(i1, i2);
+      D.p3(i1, i2);
+      D.p4(bv);
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const int64_t g = g0 + s;
-        const uint4 v = *reinterpret_cast<const uint4 *>(xrow + 8 * min(g, G - 1));
-        const uint4 av = (a_row && g < G) ? v : make_uint4(0, 0, 0, 0);
-        const uint4 bv = decode_ip<BPW>(i1[s], i2[s]);
+        // x~ rows past m feed output rows that are not stored; groups past k
+        // meet zero weight operands
+        const uint4 av = *reinterpret_cast<const uint4 *>(xrow + 8 * min(g0 + s, G - 1));
+        const uint4 b = g0 + s < G ? bv[s] : make_uint4(0, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
-                                                      __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
+                                                      __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
       }
     }
 #pragma unroll
@@ -945,6 +1044,7 @@ gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
   gm_load_a(xt, m, k, m0, 0, ra);
   uint2 i1[2], i2[2], j1[2], j2[2];
   gm_load_idx<BPW, G4>(idx1, idx2, n, G, n0, c, p, 0, i1, i2);
+  tables_landed();                                   // tables, x~ tile 0, step-0 indices
   gm_store_a(As0, ra, k);
   // indices of step 1, then x~ tile 1: the same issue order as in the loop,
   // so that the loop-entry wait for the indices does not cover the tile
@@ -1011,60 +1111,18 @@ gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
       }
     };
 
-    // phase 1: chunk-table entries (and the direct residual rows at 3 bpw)
-    uint32_t e1[8], e2[8];
-    uint4 r3[8];
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      e1[g] = lds16(kLdsCt + ((q1[g] >> 4) << 1));
-      if constexpr (BPW == 4) e2[g] = lds16(kLdsCt + ((q2[g] >> 4) << 1));
-      if constexpr (BPW == 3) r3[g] = lds128(kLdsHt2 + (q2[g] << 4));
-    }
+    Dec8<BPW> D;
+    D.p1(q1, q2);
     mfma_block(0);
     __builtin_amdgcn_sched_barrier(0);
-
-    // phase 2: orbit records
-    uint4 R1[8], R2[8];
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      R1[g] = lds128(kLdsOt + (((e1[g] >> 5) + ((q1[g] & 15u) >> (e1[g] & 31u))) << 4));
-      if constexpr (BPW == 4) R2[g] = lds128(kLdsOt + (((e2[g] >> 5) + ((q2[g] & 15u) >> (e2[g] & 31u))) << 4));
-    }
+    D.p2(q1, q2);
     mfma_block(1);
     __builtin_amdgcn_sched_barrier(0);
-
-    // phase 3: the signed half-vectors
-    uint2 va[8], vb[8], vc[8], vd[8];
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      const uint4 R = R1[g];
-      const uint32_t lo = R.y + (__builtin_amdgcn_ubfe(q1[g], 0, R.x) << 3);
-      const uint32_t hi = R.z + ((q1[g] >> R.x) << 3) + ((__builtin_popcount(__builtin_amdgcn_ubfe(q1[g], 0, R.w)) & 1u) << 6);
-      va[g] = lds64(kLdsHt1 + lo);
-      vb[g] = lds64(kLdsHt1 + hi);
-      if constexpr (BPW == 4) {
-        const uint4 Q = R2[g];
-        const uint32_t lo2 = Q.y + (__builtin_amdgcn_ubfe(q2[g], 0, Q.x) << 3);
-        const uint32_t hi2 = Q.z + ((q2[g] >> Q.x) << 3) + ((__builtin_popcount(__builtin_amdgcn_ubfe(q2[g], 0, Q.w)) & 1u) << 6);
-        vc[g] = lds64(kLdsHt2 + lo2);
-        vd[g] = lds64(kLdsHt2 + hi2);
-      }
-    }
+    D.p3(q1, q2);
     mfma_block(2);
     __builtin_amdgcn_sched_barrier(0);
-
-    // phase 4: combine into operand form; stage the next x~ tile
     uint4 bn[8];
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      if constexpr (BPW == 2) bn[g] = make_uint4(va[g].x, va[g].y, vb[g].x, vb[g].y);
-      else if constexpr (BPW == 3)
-        bn[g] = make_uint4(pk_add16(va[g].x, r3[g].x), pk_add16(va[g].y, r3[g].y),
-                           pk_add16(vb[g].x, r3[g].z), pk_add16(vb[g].y, r3[g].w));
-      else
-        bn[g] = make_uint4(pk_add16(va[g].x, vc[g].x), pk_add16(va[g].y, vc[g].y),
-                           pk_add16(vb[g].x, vd[g].x), pk_add16(vb[g].y, vd[g].y));
-    }
+    D.p4(bn);
     mfma_block(3);
     gm_store_a((s & 1) ? As0 : As1, ra, k - GM_BK * (s + 1));   // tile s + 1 (unused past the end)
     gm_load_a(xt, m, k, m0, min(s + 2, S - 1), ra);
@@ -1084,6 +1142,7 @@ gemv_f32(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const floa
          int64_t m0, int64_t mc, int64_t n, int64_t k, float scale, void *out, glq_dtype out_dt) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   load_tables<BPW>(lds, blob);
+  tables_landed();
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int64_t waves = (int64_t)gridDim.x * (blockDim.x >> 6);
