@@ -661,100 +661,291 @@ gemv_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
 // ---------------------------------------------------------------- whole layer (m <= 4)
 // One launch for y = U^T (s W^) (V x) at a few activation rows (decode-time
 // batch sizes), where separate RHT launches would cost more than the
-// decode-GEMV itself. Every workgroup: issues its first index loads, copies
-// the decode tables, rotates x in LDS (signs, block FWHT along k, 1/sqrt(b),
-// bf16 rounding, row sums), then runs the 16-wave decode-GEMV of gemv_bf16
-// over its 16-row weight tiles with the x~ operands read from LDS, and writes
-// z (float32) to the workspace. The last workgroup to finish (threadfence +
-// atomic ticket, the counter reset to zero by that workgroup) loads all of z,
-// applies U^T (block FWHT along n, then signs) and writes y.
+// decode-GEMV itself. Every workgroup: issues its first index loads and the
+// table copy, loads x (with the input signs) into registers and rotates it
+// (block FWHT along k in registers and lane shuffles, one LDS transpose,
+// 1/sqrt(b), bf16 rounding, row sums), runs the 16-wave decode-GEMV of
+// gemv_bf16 over its 16-row weight tiles with the x~ operands read from LDS,
+// and writes z (float32) to the workspace with write-through stores. Tickets
+// on 16 group counters and one top counter (each reset by its last taker)
+// pick the last workgroup, which loads all of z, applies U^T (block FWHT
+// along n, then signs) and writes y.
 constexpr int LY_MAXE = 16384;                       // m*k and m*n limit (64 KiB of float32)
-constexpr size_t LY_BUF_BYTES = padded_floats(LY_MAXE) * 4 + 12;   // 16-byte multiple
+constexpr int LY_THREADS = 64 * GV_WAVES;            // 1024
+constexpr size_t LY_BUF_BYTES = (LY_MAXE + 4 * 16) * 4;   // float32 transpose buffer (padded)
 
 template <int BPW>
 constexpr size_t ly_lds_bytes() { return lds_table_bytes<BPW>() + LY_BUF_BYTES + GV_WAVES * 256 * 4 + 64; }
 
-__device__ __forceinline__ void ly_fwht(float *buf, int total, int logb) {
-  int lo = 0;
-  for (; lo + 4 <= logb; lo += 4) { fwht_pass<16>(buf, total, lo); __syncthreads(); }
-  switch (logb - lo) {
-    case 1: fwht_pass<2>(buf, total, lo); break;
-    case 2: fwht_pass<4>(buf, total, lo); break;
-    case 3: fwht_pass<8>(buf, total, lo); break;
-    default: break;
+// Control words of the single-launch layer at the start of the workspace:
+// group counters g = 0 .. 15 at byte 256 g, the top counter at byte 4096 (each
+// on its own cache line, so the tickets of different groups do not contend).
+constexpr int LY_GROUPS = 16;
+constexpr size_t kCtrlBytes = GLQ_WS_CTRL_BYTES;
+static_assert(kCtrlBytes % 256 == 0 && kCtrlBytes >= 4096 + 4, "ticket counters fit");
+
+// v of lane (lane ^ mask) within the wave, mask a power of two <= 32 known at
+// compile time: DPP moves for masks below 16 (quad_perm for 1 and 2; a half-row
+// mirror (lane ^ 7) then quad_perm [3,2,1,0] (lane ^ 3) for 4; a row mirror
+// (lane ^ 15) then a half-row mirror for 8), a swizzle for 16, a permute for 32.
+#define GLQ_DPP(v, ctrl) __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xF, 0xF, false))
+__device__ __forceinline__ float lane_xor(float v, int mask) {
+  switch (mask) {
+    case 1: return GLQ_DPP(v, 0xB1);
+    case 2: return GLQ_DPP(v, 0x4E);
+    case 4: return GLQ_DPP(GLQ_DPP(v, 0x141), 0x1B);
+    case 8: return GLQ_DPP(GLQ_DPP(v, 0x140), 0x141);
+    case 16: return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+    default: return __shfl_xor(v, 32);
+  }
+}
+#undef GLQ_DPP
+
+// Block FWHT over bits 0 .. logb - 1 of the flat index of 1024 E elements
+// (E = 1, 2, 4, 8, 16; 2^logb <= 1024 E), held E per thread. On entry thread t
+// holds elements E t + i in v[i]. The low L = log2 E + 6 bits are transformed
+// in registers and across the lanes of the wave; when logb > L the values pass
+// once through LDS (buf; row pad 4 floats per 2^L elements keeps the reads
+// conflict-free) and the remaining bits (at most 4) are transformed the same
+// way. Afterwards thread t holds element ly_elem<E>(t, i, transposed) in v[i].
+// Unscaled: (a, b) -> (a + b, a - b) at every stage.
+template <int E> struct LyF {
+  static constexpr int LE = E == 1 ? 0 : E == 2 ? 1 : E == 4 ? 2 : E == 8 ? 3 : 4;
+  static constexpr int L = LE + 6;
+  static constexpr int LPC = 16 / E;                // lanes per column after the transpose
+};
+
+template <int E>
+__device__ __forceinline__ int ly_elem(int tid, int i, bool transposed) {
+  if (!transposed) return E * tid + i;
+  const int lo = tid / LyF<E>::LPC, sub = tid % LyF<E>::LPC;
+  return lo + ((sub * E + i) << LyF<E>::L);
+}
+
+template <int E>
+__device__ __forceinline__ void ly_stage_regs(float (&v)[E], int s) {
+#pragma unroll
+  for (int i = 0; i < E; ++i)
+    if (!(i & (1 << s))) {
+      const float a = v[i], b = v[i + (1 << s)];
+      v[i] = a + b;
+      v[i + (1 << s)] = a - b;
+    }
+}
+
+template <int E>
+__device__ __forceinline__ void ly_stage_lanes(float (&v)[E], int mask, bool upper) {
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const float o = lane_xor(v[i], mask);
+    v[i] = upper ? o - v[i] : v[i] + o;
+  }
+}
+
+template <int E>
+__device__ __forceinline__ bool ly_fwht(float (&v)[E], float *buf, int logb, int tid) {
+  constexpr int LE = LyF<E>::LE, L = LyF<E>::L;
+  const int lane = tid & 63;
+#pragma unroll
+  for (int s = 0; s < LE; ++s)
+    if (s < logb) ly_stage_regs<E>(v, s);
+#pragma unroll
+  for (int s = 0; s < 6; ++s)
+    if (LE + s < logb) ly_stage_lanes<E>(v, 1 << s, (lane >> s) & 1);
+  if (logb <= L) return false;
+  {
+    float *w = buf + E * tid + 4 * (tid >> 6);         // element E tid + i at e + 4 (e >> L)
+    if constexpr (E >= 4) {
+#pragma unroll
+      for (int i = 0; i < E; i += 4) *reinterpret_cast<float4 *>(w + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < E; ++i) w[i] = v[i];
+    }
+  }
+  __syncthreads();
+  const int lo = tid / LyF<E>::LPC, sub = tid % LyF<E>::LPC;
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const int hi = sub * E + i;
+    v[i] = buf[lo + (hi << L) + 4 * hi];
+  }
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    if (L + h >= logb) break;
+    if (h < LE) ly_stage_regs<E>(v, h);
+    else ly_stage_lanes<E>(v, 1 << (h - LE), (sub >> (h - LE)) & 1);
+  }
+  return true;
+}
+
+// E consecutive bf16 values of x from element e (16-byte aligned x; e % E == 0)
+template <int E>
+__device__ __forceinline__ void ly_load_x(const uint16_t *x, int e, float (&v)[E]) {
+  uint32_t w[(E + 1) / 2];
+  if constexpr (E == 1) w[0] = x[e];
+  else if constexpr (E == 2) w[0] = *reinterpret_cast<const uint32_t *>(x + e);
+  else if constexpr (E == 4) { const uint2 u = *reinterpret_cast<const uint2 *>(x + e); w[0] = u.x; w[1] = u.y; }
+  else {
+#pragma unroll
+    for (int c = 0; c < E / 8; ++c) {
+      const uint4 u = *reinterpret_cast<const uint4 *>(x + e + 8 * c);
+      w[4 * c] = u.x; w[4 * c + 1] = u.y; w[4 * c + 2] = u.z; w[4 * c + 3] = u.w;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < E; ++i) v[i] = __uint_as_float(((w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) << 16);
+}
+
+// E consecutive signs from index c (8-byte aligned signs; c % E == 0)
+template <int E>
+__device__ __forceinline__ void ly_load_signs(const int8_t *sg, int c, float (&v)[E]) {
+  uint32_t w[(E + 3) / 4];
+  if constexpr (E == 1) w[0] = (uint8_t)sg[c];
+  else if constexpr (E == 2) w[0] = *reinterpret_cast<const uint16_t *>(sg + c);
+  else if constexpr (E == 4) w[0] = *reinterpret_cast<const uint32_t *>(sg + c);
+  else {
+#pragma unroll
+    for (int q = 0; q < E / 8; ++q) {
+      const uint2 u = *reinterpret_cast<const uint2 *>(sg + c + 8 * q);
+      w[2 * q] = u.x; w[2 * q + 1] = u.y;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < E; ++i) v[i] = (float)(int8_t)((w[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+}
+
+// Input side: x~ = bf16( H (sign_k . x) / sqrt(b) ) into xb (LDS, [m][k] bf16),
+// per-wave row-sum partials into red[wave * 4 + r]. Ends with a barrier.
+template <int E>
+__device__ __forceinline__ void ly_input(const uint16_t *x, const int8_t *sign_k, int mk, int k, int logbk,
+                                         float *buf, uint16_t *xb, float *red, int tid) {
+  float v[E];
+  const int e0 = E * tid;
+  if (e0 < mk) {
+    float sg[E];
+    ly_load_x<E>(x, e0, v);
+    ly_load_signs<E>(sign_k, e0 % k, sg);
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] *= sg[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = 0.0f;
+  }
+  tables_landed();                                   // this wave's table copies: published by the next barrier
+  const bool tr = ly_fwht<E>(v, buf, logbk, tid);
+  if (!tr) __syncthreads();                          // tables visible
+  const float inv = 1.0f / sqrtf((float)(1 << logbk));
+  float rs[4] = {0.f, 0.f, 0.f, 0.f};
+  uint16_t h[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const int e = ly_elem<E>(tid, i, tr);
+    h[i] = f32_to_bf16_rne(v[i] * inv);
+    if (e < mk) {
+      const float hv = __uint_as_float((uint32_t)h[i] << 16);
+      const int r = (e >= k) + (e >= 2 * k) + (e >= 3 * k);   // m <= 4
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) rs[rr] += rr == r ? hv : 0.0f;
+    }
+  }
+  if (tr) __syncthreads();                           // every thread has read buf (xb aliases it)
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const int e = ly_elem<E>(tid, i, tr);
+    if (e < mk) xb[e] = h[i];
+  }
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    if (rr * k >= mk) break;                          // rows past m
+    float t = rs[rr];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) t += lane_xor(t, off);
+    if ((tid & 63) == 0) red[(tid >> 6) * 4 + rr] = t;
   }
   __syncthreads();
 }
 
+// Output side (last workgroup): y = sign_n . H z / sqrt(b); sn = this thread's
+// signs (raw bytes) for ly_elem(tid, i, logbn > L), loaded at the start.
+template <int E>
+__device__ __forceinline__ void ly_output(const float *z, const int (&sn)[16], int mn, int logbn, float *buf,
+                                          void *y, glq_dtype y_dt, int tid) {
+  float v[E];
+  const int e0 = E * tid;
+#pragma unroll
+  for (int i = 0; i < E; ++i)   // padding elements form whole blocks of their own
+    v[i] = e0 + i < mn ? __hip_atomic_load(z + e0 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0f;
+  const bool tr = ly_fwht<E>(v, buf, logbn, tid);
+  const float inv = 1.0f / sqrtf((float)(1 << logbn));
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const int e = ly_elem<E>(tid, i, tr);
+    if (e < mn) store_out(y, y_dt, (size_t)e, v[i] * inv * (float)(int8_t)sn[i]);
+  }
+}
+
+template <int E>
+__device__ __forceinline__ void ly_out_signs(const int8_t *sign_n, int n, int mn, int logbn, int tid, int (&sn)[16]) {
+  const bool tr = logbn > LyF<E>::L;
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const int e = ly_elem<E>(tid, i, tr);
+    sn[i] = sign_n[min(e, mn - 1) % n];
+  }
+}
+
+__device__ __forceinline__ int ly_e(int count) {    // elements per thread for count <= 16384 elements
+  int e = 1;
+  while (e * LY_THREADS < count) e <<= 1;
+  return e;
+}
+
 template <int BPW>
-__global__ void __launch_bounds__(64 * GV_WAVES, 1)
+__global__ void __launch_bounds__(LY_THREADS, 1)
 layer_small(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uint16_t *x,
             const int8_t *sign_k, const int8_t *sign_n, int64_t m, int64_t n, int64_t k, int logbk,
-            int logbn, float post, void *y, glq_dtype y_dt, float *z, unsigned int *counter) {
+            int logbn, float post, void *y, glq_dtype y_dt, float *z, unsigned int *ctrl) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   float *xs = reinterpret_cast<float *>(lds + lds_table_bytes<BPW>());
   float *red = reinterpret_cast<float *>(lds + lds_table_bytes<BPW>() + LY_BUF_BYTES);
   float *misc = red + GV_WAVES * 256;                 // [0..3] row sums, [8] last-workgroup flag
-  const uint16_t *xb = reinterpret_cast<const uint16_t *>(xs);   // x~ as bf16 [m][k] after rotation
+  uint16_t *xb = reinterpret_cast<uint16_t *>(xs);   // x~ as bf16 [m][k] after rotation
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 15, q = lane >> 4;
   const int64_t G = k / 8, chunks = (G + 31) / 32;
   const int64_t tiles = (n + 15) / 16;
+  const int mk = (int)(m * k), mn = (int)(m * n);
 
-  // 1. first index loads in flight before anything else
+  // 1. first index loads and the table copy in flight before anything else
   int64_t tile = blockIdx.x, c = wave;
   GvRaw raw;
   if (tile < tiles && c < chunks) raw = gv_load_raw<BPW, true>(idx1, idx2, min(tile * 16 + j, n - 1), G, 32 * c + 8 * q);
-  // 2. decode tables, 3. x -> LDS with the input signs
-  load_tables<BPW, 64 * GV_WAVES>(lds, blob);
-  const int64_t mk = m * k;
-  for (int64_t e = 8 * (int64_t)tid; e < mk; e += 8 * 64 * GV_WAVES) {
-    float v[8], sg[8];
-    rv_signs(sign_k, e - k * ((e >= k) + (e >= 2 * k) + (e >= 3 * k)), sg);
-    rv_load_piece<true>(x, (size_t)e, v);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) xs[pidx((int)e + t)] = v[t] * sg[t];
+  load_tables<BPW, LY_THREADS>(lds, blob);
+  // the output signs this thread will apply if its workgroup finishes last
+  const int eo = ly_e(mn);
+  int sn[16];
+  switch (eo) {
+    case 1: ly_out_signs<1>(sign_n, (int)n, mn, logbn, tid, sn); break;
+    case 2: ly_out_signs<2>(sign_n, (int)n, mn, logbn, tid, sn); break;
+    case 4: ly_out_signs<4>(sign_n, (int)n, mn, logbn, tid, sn); break;
+    case 8: ly_out_signs<8>(sign_n, (int)n, mn, logbn, tid, sn); break;
+    default: ly_out_signs<16>(sign_n, (int)n, mn, logbn, tid, sn); break;
   }
-  tables_landed();
-  __syncthreads();
-  ly_fwht(xs, (int)mk, logbk);
-  {  // 4. scale, round to bf16 in place (read all, barrier, write), row sums
-    const float inv = 1.0f / sqrtf((float)(1 << logbk));
-    float v[LY_MAXE / (64 * GV_WAVES)];
-    float rs[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < LY_MAXE / (64 * GV_WAVES); ++u) {
-      const int64_t e = tid + (int64_t)u * 64 * GV_WAVES;
-      v[u] = e < mk ? xs[pidx((int)e)] * inv : 0.0f;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < LY_MAXE / (64 * GV_WAVES); ++u) {
-      const int64_t e = tid + (int64_t)u * 64 * GV_WAVES;
-      if (e < mk) {
-        const uint16_t h = f32_to_bf16_rne(v[u]);
-        reinterpret_cast<uint16_t *>(xs)[e] = h;
-        const float hv = __uint_as_float((uint32_t)h << 16);
-        const int r = (e >= k) + (e >= 2 * k) + (e >= 3 * k);   // m <= 4
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) rs[rr] += rr == r ? hv : 0.0f;
-      }
-    }
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      float t = rs[rr];
-      for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off);
-      if (lane == 0) red[wave * 4 + rr] = t;
-    }
-    __syncthreads();
-    if (tid < 4) {
-      float t = 0.0f;
-      for (int w = 0; w < GV_WAVES; ++w) t += red[w * 4 + tid];
-      misc[tid] = t;
-    }
-    __syncthreads();
+  // 2. x~ into LDS (the barriers inside also publish the tables)
+  switch (ly_e(mk)) {
+    case 1: ly_input<1>(x, sign_k, mk, (int)k, logbk, xs, xb, red, tid); break;
+    case 2: ly_input<2>(x, sign_k, mk, (int)k, logbk, xs, xb, red, tid); break;
+    case 4: ly_input<4>(x, sign_k, mk, (int)k, logbk, xs, xb, red, tid); break;
+    case 8: ly_input<8>(x, sign_k, mk, (int)k, logbk, xs, xb, red, tid); break;
+    default: ly_input<16>(x, sign_k, mk, (int)k, logbk, xs, xb, red, tid); break;
   }
-  // 5. decode-GEMV over this workgroup's tiles
+  if (tid < m) {
+    float t = 0.0f;
+    for (int w = 0; w < GV_WAVES; ++w) t += red[w * 4 + tid];
+    misc[tid] = t;                                   // read after the next barrier
+  }
+  // 3. decode-GEMV over this workgroup's tiles
   const uint16_t *xrow = xb + (size_t)min((int64_t)j, m - 1) * k;
   for (; tile < tiles; tile += gridDim.x) {
     const int64_t row = min(tile * 16 + j, n - 1);
@@ -797,39 +988,38 @@ layer_small(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const u
     }
     __syncthreads();
   }
-  // 6. the last workgroup applies U^T. z went out with coherent stores; once
-  // they have completed (s_waitcnt) the workgroup takes a ticket. The
-  // workgroup holding the last ticket reads z with coherent loads. (A
-  // threadfence here would write back the whole L2 of the XCD, once per
-  // workgroup.)
+  // 4. tickets. z went out with coherent stores; once they have completed
+  // (s_waitcnt) the workgroup takes a ticket of its group counter; the last
+  // taker of each group takes one of the top counter, and the last taker of
+  // that one applies U^T. (A threadfence here would write back the whole L2
+  // of the XCD, once per workgroup.)
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
-    const unsigned int ticket = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    misc[8] = ticket == gridDim.x - 1 ? 1.0f : 0.0f;
+    const unsigned int g = blockIdx.x % LY_GROUPS;
+    const unsigned int ngroups = min(gridDim.x, (unsigned)LY_GROUPS);
+    const unsigned int in_group = (gridDim.x - g + LY_GROUPS - 1) / LY_GROUPS;   // workgroups b with b % 16 == g
+    unsigned int *gc = ctrl + 64 * g, *top = ctrl + 1024;
+    float last = 0.0f;
+    if (__hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == in_group - 1) {
+      __hip_atomic_store(gc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ngroups - 1) {
+        __hip_atomic_store(top, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = 1.0f;
+      }
+    }
+    misc[8] = last;
   }
   __syncthreads();
   if (misc[8] == 0.0f) return;
-  const int mn = (int)(m * n);
-  {
-    constexpr int U = LY_MAXE / (64 * GV_WAVES);
-    float v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u)        // all loads in flight before the first LDS write
-      v[u] = __hip_atomic_load(z + min(tid + u * 64 * GV_WAVES, mn - 1), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (tid + u * 64 * GV_WAVES < mn) xs[pidx(tid + u * 64 * GV_WAVES)] = v[u];
+  // 5. the last workgroup: y = U^T z
+  switch (eo) {
+    case 1: ly_output<1>(z, sn, mn, logbn, xs, y, y_dt, tid); break;
+    case 2: ly_output<2>(z, sn, mn, logbn, xs, y, y_dt, tid); break;
+    case 4: ly_output<4>(z, sn, mn, logbn, xs, y, y_dt, tid); break;
+    case 8: ly_output<8>(z, sn, mn, logbn, xs, y, y_dt, tid); break;
+    default: ly_output<16>(z, sn, mn, logbn, xs, y, y_dt, tid); break;
   }
-  __syncthreads();
-  ly_fwht(xs, mn, logbn);
-  const float invn = 1.0f / sqrtf((float)(1 << logbn));
-  for (int e = tid; e < mn; e += 64 * GV_WAVES) {
-    const int col = e - (int)n * ((e >= n) + (e >= 2 * n) + (e >= 3 * n));
-    store_out(y, y_dt, (size_t)e, xs[pidx(e)] * invn * (float)sign_n[col]);
-  }
-  if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------- GEMM (m > 16)
@@ -1298,7 +1488,7 @@ struct WsLayout { size_t ctrl, xt, rowsum, z, total; };
 WsLayout ws_layout(int64_t n, int64_t k, int64_t m) {
   WsLayout w;
   w.ctrl = 0;
-  w.xt = 256;
+  w.xt = kCtrlBytes;
   w.rowsum = w.xt + align256((size_t)m * (size_t)k * 4);
   w.z = w.rowsum + align256((size_t)m * 4);
   w.total = w.z + align256((size_t)m * (size_t)n * 4);

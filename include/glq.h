@@ -50,7 +50,7 @@ extern "C" {
 typedef enum {
     GLQ_OK = 0,
     GLQ_ERR_ARG = -1,          /* invalid argument (null pointer, bad size, bad enum) */
-    GLQ_ERR_UNSUPPORTED = -2,  /* valid but unsupported shape (e.g. Hadamard block > 32768) */
+    GLQ_ERR_UNSUPPORTED = -2,  /* valid but unsupported shape (e.g. Hadamard block > 16384) */
     GLQ_ERR_HIP = -3,          /* a HIP launch or runtime call failed */
     GLQ_ERR_WORKSPACE = -4     /* workspace missing or smaller than required */
 } glq_status;
@@ -119,7 +119,7 @@ int glq_encode_ref(const float *w, int64_t n, int64_t k, int32_t bpw,
 /*
  * glq_rht_apply -- randomized Hadamard transform along the last axis of a
  * [rows][n] array ("glq 0.1.1", "How it works", item 2), b = largest power of
- * two dividing n (<= 32768), computed in float32:
+ * two dividing n (<= 16384), computed in float32:
  *   transpose = 0:  out = (I (x) H_b) diag(signs) in / sqrt(b)   (signs, then FWHT)
  *   transpose = 1:  out = diag(signs) (I (x) H_b) in / sqrt(b)   (FWHT, then signs)
  *   in, out    device, dtype in_dt / out_dt; may be the same buffer when
@@ -141,7 +141,8 @@ int glq_rht_apply(const void *in, glq_dtype in_dt, void *out, glq_dtype out_dt,
 int glq_decode_weights(const glq_layer *L, void *w_out, glq_dtype out_dt, void *hip_stream);
 
 /* Bytes of device workspace glq_fused_linear needs for m rows (any dtype, any
- * flags), including the 256 bytes of control words at its start. */
+ * flags), including the control words at its start (GLQ_WS_CTRL_BYTES). */
+#define GLQ_WS_CTRL_BYTES 4352
 size_t glq_fused_linear_workspace(const glq_layer *L, int64_t m);
 
 /*
@@ -153,11 +154,11 @@ size_t glq_fused_linear_workspace(const glq_layer *L, int64_t m);
  *                    in bf16, float32 accumulation, scale in the epilogue)
  *   y_dt             GLQ_F32 or GLQ_BF16 (round-to-nearest-even)
  *   workspace        device, >= glq_fused_linear_workspace(L, m) bytes, 256-byte aligned.
- *                    Its first 256 bytes are control words (a completion counter
- *                    of the single-launch layer used at small m): they must be
- *                    zero before the first call with a workspace, every call
- *                    leaves them zero, and calls that run concurrently need
- *                    separate workspaces. The rest is scratch.
+ *                    Its first GLQ_WS_CTRL_BYTES bytes are control words
+ *                    (completion counters of the single-launch layer used at
+ *                    small m): they must be zero before the first call with a
+ *                    workspace, every call leaves them zero, and calls that run
+ *                    concurrently need separate workspaces. The rest is scratch.
  *   flags            GLQ_FLAG_* (0 = the full layer)
  * m == 0 is a successful no-op. x and y must not overlap the workspace.
  */

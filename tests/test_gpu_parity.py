@@ -327,4 +327,4 @@ def test_small_batch_single_launch(G, cb, bpw, n, k, m):
             torch.cuda.synchronize()
             ref = og.layer_reference(x, i1, i2, bpw, s, sn, sk)
             assert og.relative_error(y.float().cpu().numpy(), ref) <= TOL_BF16
-            assert int(ws[:4].view(torch.int32).item()) == 0     # completion counter left at zero
+            assert int(ws[:4352].count_nonzero().item()) == 0     # completion counters left at zero
