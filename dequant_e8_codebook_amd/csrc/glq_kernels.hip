@@ -481,6 +481,297 @@ row_sums_bf16(const uint16_t *x, int64_t rows, int64_t n, float *rowsum) {
   }
 }
 
+// v of lane (lane ^ mask) within the wave, mask a power of two <= 32 known at
+// compile time: DPP moves for masks below 16 (quad_perm for 1 and 2; a half-row
+// mirror (lane ^ 7) then quad_perm [3,2,1,0] (lane ^ 3) for 4; a row mirror
+// (lane ^ 15) then a half-row mirror for 8), a swizzle for 16, a permute for 32.
+#define GLQ_DPP(v, ctrl) __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xF, 0xF, false))
+__device__ __forceinline__ float lane_xor(float v, int mask) {
+  switch (mask) {
+    case 1: return GLQ_DPP(v, 0xB1);
+    case 2: return GLQ_DPP(v, 0x4E);
+    case 4: return GLQ_DPP(GLQ_DPP(v, 0x141), 0x1B);
+    case 8: return GLQ_DPP(GLQ_DPP(v, 0x140), 0x141);
+    case 16: return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+    default: return __shfl_xor(v, 32);
+  }
+}
+#undef GLQ_DPP
+
+// Block FWHT over bits 0 .. logb - 1 of the flat index of 64 NW E elements
+// (E = 1, 2, 4, 8, 16 per thread, NW = 4, 8 or 16 waves; 2^logb <= 64 NW E)
+// held E per thread. On entry thread t holds elements E t + i in v[i]. The low
+// L = log2 E + 6 bits are transformed in registers and across the lanes of the
+// wave; when logb > L the values pass once through LDS (buf, 64 NW E + 64
+// floats; a pad of 4 floats per 2^L elements keeps the reads conflict-free)
+// and the remaining log2 NW bits are transformed the same way. Afterwards
+// thread t holds element ly_elem<E, NW>(t, i, transposed) in v[i]: with
+// e = lo + 2^L hi, either (E < NW) LPC = NW / E lanes share a column lo, lane
+// sub of them holding hi = sub E + i, or (E >= NW) a thread holds the NW
+// elements of each of its E / NW columns lo = t + 64 NW c, i = NW c + hi.
+// Unscaled: (a, b) -> (a + b, a - b) at every stage.
+template <int E, int NW = 16> struct LyF {
+  static constexpr int LE = E == 1 ? 0 : E == 2 ? 1 : E == 4 ? 2 : E == 8 ? 3 : 4;
+  static constexpr int L = LE + 6;
+  static constexpr int WB = NW == 4 ? 2 : NW == 8 ? 3 : 4;
+  static constexpr int LPC = E < NW ? NW / E : 1;  // lanes per column after the transpose
+  static constexpr int CPT = E < NW ? 1 : E / NW;  // columns per thread after the transpose
+};
+
+template <int E, int NW = 16>
+__device__ __forceinline__ int ly_elem(int tid, int i, bool transposed) {
+  using F = LyF<E, NW>;
+  if (!transposed) return E * tid + i;
+  if constexpr (E < NW) {
+    const int lo = tid / F::LPC, sub = tid % F::LPC;
+    return lo + ((sub * E + i) << F::L);
+  } else {
+    return tid + 64 * NW * (i / NW) + ((i % NW) << F::L);
+  }
+}
+
+template <int E>
+__device__ __forceinline__ void ly_stage_regs(float (&v)[E], int s) {
+#pragma unroll
+  for (int i = 0; i < E; ++i)
+    if (!(i & (1 << s))) {
+      const float a = v[i], b = v[i + (1 << s)];
+      v[i] = a + b;
+      v[i + (1 << s)] = a - b;
+    }
+}
+
+// one butterfly stage across lane pairs (lane, lane ^ mask): the lower lane
+// keeps a + b, the upper one a - b, as o + (+-1) v in one exact fma
+template <int E>
+__device__ __forceinline__ void ly_stage_lanes(float (&v)[E], int mask, bool upper) {
+  const float sg = upper ? -1.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < E; ++i) v[i] = fmaf(v[i], sg, lane_xor(v[i], mask));
+}
+
+template <int E, int NW = 16>
+__device__ __forceinline__ bool ly_fwht(float (&v)[E], float *buf, int logb, int tid) {
+  using F = LyF<E, NW>;
+  constexpr int LE = F::LE, L = F::L;
+  const int lane = tid & 63;
+#pragma unroll
+  for (int s = 0; s < LE; ++s)
+    if (s < logb) ly_stage_regs<E>(v, s);
+#pragma unroll
+  for (int s = 0; s < 6; ++s)
+    if (LE + s < logb) ly_stage_lanes<E>(v, 1 << s, (lane >> s) & 1);
+  if (logb <= L) return false;
+  {
+    float *w = buf + E * tid + 4 * (tid >> 6);         // element E tid + i at e + 4 (e >> L)
+    if constexpr (E >= 4) {
+#pragma unroll
+      for (int i = 0; i < E; i += 4) *reinterpret_cast<float4 *>(w + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < E; ++i) w[i] = v[i];
+    }
+  }
+  __syncthreads();
+  if constexpr (E < NW) {
+    const int lo = tid / F::LPC, sub = tid % F::LPC;
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const int hi = sub * E + i;
+      v[i] = buf[lo + (hi << L) + 4 * hi];
+    }
+#pragma unroll
+    for (int h = 0; h < F::WB; ++h) {
+      if (L + h >= logb) break;
+      if (h < LE) ly_stage_regs<E>(v, h);
+      else ly_stage_lanes<E>(v, 1 << (h - LE), (sub >> (h - LE)) & 1);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const int hi = i % NW;
+      v[i] = buf[tid + 64 * NW * (i / NW) + (hi << L) + 4 * hi];
+    }
+#pragma unroll
+    for (int h = 0; h < F::WB; ++h) {
+      if (L + h >= logb) break;
+      ly_stage_regs<E>(v, h);
+    }
+  }
+  return true;
+}
+
+__device__ __forceinline__ int ly_e(int count) {    // elements per thread for count <= 16384 elements
+  int e = 1;
+  while (e * 1024 < count) e <<= 1;
+  return e;
+}
+
+// RHT of rows of length n <= 16384 (n % 8 == 0, 16-byte aligned rows and
+// pointers, in != out): one row per workgroup of 64 NW threads (grid-stride),
+// the block FWHT in registers and lane exchanges (ly_fwht).
+// Raw loads of the thread's E consecutive inputs from element e0 of a row
+// (zeros past n), unpacked by rr_unpack: split so that the loads of the next
+// row can be in flight while the current one is transformed.
+template <int E, bool IN_BF16> struct RrRaw {
+  static constexpr int W = IN_BF16 ? (E + 1) / 2 : E;
+  uint32_t w[W];
+};
+
+template <int E, bool IN_BF16>
+__device__ __forceinline__ void rr_fetch(const void *in, size_t base, int e0, int n, RrRaw<E, IN_BF16> &r) {
+  bool whole = e0 + E <= n;
+  if constexpr (E == 1) whole = false;
+  if (whole) {
+    if constexpr (IN_BF16) {
+      const uint16_t *p = reinterpret_cast<const uint16_t *>(in) + base + e0;
+      if constexpr (E == 2) r.w[0] = *reinterpret_cast<const uint32_t *>(p);
+      else if constexpr (E == 4) { const uint2 u = *reinterpret_cast<const uint2 *>(p); r.w[0] = u.x; r.w[1] = u.y; }
+      else {
+#pragma unroll
+        for (int c = 0; c < E / 8; ++c) {
+          const uint4 u = *reinterpret_cast<const uint4 *>(p + 8 * c);
+          r.w[4 * c] = u.x; r.w[4 * c + 1] = u.y; r.w[4 * c + 2] = u.z; r.w[4 * c + 3] = u.w;
+        }
+      }
+    } else {
+      const uint32_t *p = reinterpret_cast<const uint32_t *>(in) + base + e0;
+      if constexpr (E == 2) { const uint2 u = *reinterpret_cast<const uint2 *>(p); r.w[0] = u.x; r.w[1] = u.y; }
+      else if constexpr (E >= 4) {
+#pragma unroll
+        for (int c = 0; c < E / 4; ++c) {
+          const uint4 u = *reinterpret_cast<const uint4 *>(p + 4 * c);
+          r.w[4 * c] = u.x; r.w[4 * c + 1] = u.y; r.w[4 * c + 2] = u.z; r.w[4 * c + 3] = u.w;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < RrRaw<E, IN_BF16>::W; ++i) r.w[i] = 0u;
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const int e = e0 + i;
+      if (e < n) {
+        if constexpr (IN_BF16) r.w[i >> 1] |= (uint32_t)reinterpret_cast<const uint16_t *>(in)[base + e] << (16 * (i & 1));
+        else r.w[i] = reinterpret_cast<const uint32_t *>(in)[base + e];
+      }
+    }
+  }
+}
+
+template <int E, bool IN_BF16>
+__device__ __forceinline__ void rr_unpack(const RrRaw<E, IN_BF16> &r, float (&v)[E]) {
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    if constexpr (IN_BF16) v[i] = __uint_as_float(((r.w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) << 16);
+    else v[i] = __uint_as_float(r.w[i]);
+  }
+}
+
+
+
+template <int E, int NW, bool IN_BF16, bool OUT_BF16, bool TRANSPOSE>
+__device__ __forceinline__ void rr_rows(const void *in, void *out, int64_t rows, int n, int logb,
+                                        const int8_t *signs, float *rowsum, float *buf, float *red) {
+  const int tid = threadIdx.x;
+  const int e0 = E * tid;
+  const float inv = 1.0f / sqrtf((float)(1 << logb));
+  // signs of this thread's elements before (sign then FWHT) or after the
+  // transform (FWHT then sign); the element map is the same for every row
+  const bool trx = logb > LyF<E, NW>::L;
+  float sg[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const int e = TRANSPOSE ? ly_elem<E, NW>(tid, i, trx) : e0 + i;
+    sg[i] = e < n ? (float)signs[e] : 0.0f;
+  }
+  RrRaw<E, IN_BF16> raw;
+  if ((int64_t)blockIdx.x < rows) rr_fetch<E, IN_BF16>(in, (size_t)blockIdx.x * n, e0, n, raw);
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    const size_t base = (size_t)row * n;
+    float v[E];
+    rr_unpack<E, IN_BF16>(raw, v);
+    if (row + gridDim.x < rows) rr_fetch<E, IN_BF16>(in, base + (size_t)gridDim.x * n, e0, n, raw);   // next row
+    if (!TRANSPOSE) {
+#pragma unroll
+      for (int i = 0; i < E; ++i) v[i] *= sg[i];
+    }
+    __syncthreads();                                 // the previous row is out of buf and red
+    const bool tr = ly_fwht<E, NW>(v, buf, logb, tid);
+    float rs = 0.0f;
+    float x[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      x[i] = v[i] * inv;
+      if (TRANSPOSE) x[i] *= sg[i];
+      if constexpr (OUT_BF16) x[i] = __uint_as_float((uint32_t)f32_to_bf16_rne(x[i]) << 16);
+    }
+    if (!tr && E >= 2 && e0 + E <= n) {
+      // untransposed: the thread's E consecutive outputs in vector stores
+      if constexpr (OUT_BF16) {
+        uint32_t w[E / 2 > 0 ? E / 2 : 1];
+#pragma unroll
+        for (int i = 0; i + 1 < E; i += 2) w[i / 2] = (__float_as_uint(x[i]) >> 16) | (__float_as_uint(x[i + 1]) & 0xFFFF0000u);
+        uint16_t *o = reinterpret_cast<uint16_t *>(out) + base + e0;
+        if constexpr (E == 2) *reinterpret_cast<uint32_t *>(o) = w[0];
+        else if constexpr (E == 4) *reinterpret_cast<uint2 *>(o) = make_uint2(w[0], w[1]);
+        else {
+#pragma unroll
+          for (int c = 0; c < E / 8; ++c)
+            *reinterpret_cast<uint4 *>(o + 8 * c) = make_uint4(w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]);
+        }
+      } else {
+        float *o = reinterpret_cast<float *>(out) + base + e0;
+        if constexpr (E == 2) *reinterpret_cast<float2 *>(o) = make_float2(x[0], x[1]);
+        else if constexpr (E >= 4) {
+#pragma unroll
+          for (int c = 0; c < E / 4; ++c)
+            *reinterpret_cast<float4 *>(o + 4 * c) = make_float4(x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < E; ++i) rs += x[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        const int e = ly_elem<E, NW>(tid, i, tr);
+        if (e < n) {
+          if constexpr (OUT_BF16) reinterpret_cast<uint16_t *>(out)[base + e] = (uint16_t)(__float_as_uint(x[i]) >> 16);
+          else reinterpret_cast<float *>(out)[base + e] = x[i];
+          rs += x[i];
+        }
+      }
+    }
+    if (rowsum) {
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) rs += lane_xor(rs, off);
+      if ((tid & 63) == 0) red[tid >> 6] = rs;
+      __syncthreads();
+      if (tid == 0) {
+        float t = 0.0f;
+        for (int w = 0; w < NW; ++w) t += red[w];
+        rowsum[row] = t;
+      }
+    }
+  }
+}
+
+template <bool IN_BF16, bool OUT_BF16, bool TRANSPOSE, int NW>
+__global__ void __launch_bounds__(64 * NW)
+rht_rows_reg(const void *in, void *out, int64_t rows, int n, int logb, const int8_t *signs, float *rowsum) {
+  extern __shared__ __attribute__((aligned(16))) float rr_buf[];   // 64 NW E + 64 floats
+  __shared__ float red[NW];
+  int e = 1;
+  while (e * 64 * NW < n) e <<= 1;
+  switch (e) {
+    case 1: rr_rows<1, NW, IN_BF16, OUT_BF16, TRANSPOSE>(in, out, rows, n, logb, signs, rowsum, rr_buf, red); break;
+    case 2: rr_rows<2, NW, IN_BF16, OUT_BF16, TRANSPOSE>(in, out, rows, n, logb, signs, rowsum, rr_buf, red); break;
+    case 4: rr_rows<4, NW, IN_BF16, OUT_BF16, TRANSPOSE>(in, out, rows, n, logb, signs, rowsum, rr_buf, red); break;
+    case 8: rr_rows<8, NW, IN_BF16, OUT_BF16, TRANSPOSE>(in, out, rows, n, logb, signs, rowsum, rr_buf, red); break;
+    default: rr_rows<16, NW, IN_BF16, OUT_BF16, TRANSPOSE>(in, out, rows, n, logb, signs, rowsum, rr_buf, red); break;
+  }
+}
+
 // ---------------------------------------------------------------- decode only
 template <int BPW, bool OUT_F32>
 __global__ void __launch_bounds__(256)
@@ -618,6 +909,10 @@ gemv_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
     for (int s = 0; s < 8; ++s) av[s] = *reinterpret_cast<const uint4 *>(xrow + 8 * min(g0 + s, G - 1));
   };
   if (c < chunks) load_chunk(c);
+  // row sum of the activation row this thread reduces at the end (loaded
+  // unconditionally, clamped, used only after the reduction)
+  float rs_raw = 0.0f;
+  if constexpr (Epi<BPW>::bias != 0.0f) rs_raw = rowsum[min((int64_t)(threadIdx.x >> 4), m - 1)];
   load_tables<BPW, 64 * GV_WAVES>(lds, blob);
   tables_landed();
   __syncthreads();
@@ -652,8 +947,7 @@ gemv_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
     for (int w = 0; w < GV_WAVES; ++w) v += red[(w * 16 + r) * 16 + col];
     const int64_t nrow = n0 + col;
     if (r < m && nrow < n) {
-      if (Epi<BPW>::bias != 0.0f) v -= Epi<BPW>::bias * rowsum[r];
-      store_out(out, out_dt, (size_t)r * n + nrow, post * v);
+      store_out(out, out_dt, (size_t)r * n + nrow, post * (v - Epi<BPW>::bias * rs_raw));
     }
   }
 }
@@ -683,101 +977,6 @@ constexpr size_t ly_lds_bytes() { return lds_table_bytes<BPW>() + LY_BUF_BYTES +
 constexpr int LY_GROUPS = 16;
 constexpr size_t kCtrlBytes = GLQ_WS_CTRL_BYTES;
 static_assert(kCtrlBytes % 256 == 0 && kCtrlBytes >= 4096 + 4, "ticket counters fit");
-
-// v of lane (lane ^ mask) within the wave, mask a power of two <= 32 known at
-// compile time: DPP moves for masks below 16 (quad_perm for 1 and 2; a half-row
-// mirror (lane ^ 7) then quad_perm [3,2,1,0] (lane ^ 3) for 4; a row mirror
-// (lane ^ 15) then a half-row mirror for 8), a swizzle for 16, a permute for 32.
-#define GLQ_DPP(v, ctrl) __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xF, 0xF, false))
-__device__ __forceinline__ float lane_xor(float v, int mask) {
-  switch (mask) {
-    case 1: return GLQ_DPP(v, 0xB1);
-    case 2: return GLQ_DPP(v, 0x4E);
-    case 4: return GLQ_DPP(GLQ_DPP(v, 0x141), 0x1B);
-    case 8: return GLQ_DPP(GLQ_DPP(v, 0x140), 0x141);
-    case 16: return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
-    default: return __shfl_xor(v, 32);
-  }
-}
-#undef GLQ_DPP
-
-// Block FWHT over bits 0 .. logb - 1 of the flat index of 1024 E elements
-// (E = 1, 2, 4, 8, 16; 2^logb <= 1024 E), held E per thread. On entry thread t
-// holds elements E t + i in v[i]. The low L = log2 E + 6 bits are transformed
-// in registers and across the lanes of the wave; when logb > L the values pass
-// once through LDS (buf; row pad 4 floats per 2^L elements keeps the reads
-// conflict-free) and the remaining bits (at most 4) are transformed the same
-// way. Afterwards thread t holds element ly_elem<E>(t, i, transposed) in v[i].
-// Unscaled: (a, b) -> (a + b, a - b) at every stage.
-template <int E> struct LyF {
-  static constexpr int LE = E == 1 ? 0 : E == 2 ? 1 : E == 4 ? 2 : E == 8 ? 3 : 4;
-  static constexpr int L = LE + 6;
-  static constexpr int LPC = 16 / E;                // lanes per column after the transpose
-};
-
-template <int E>
-__device__ __forceinline__ int ly_elem(int tid, int i, bool transposed) {
-  if (!transposed) return E * tid + i;
-  const int lo = tid / LyF<E>::LPC, sub = tid % LyF<E>::LPC;
-  return lo + ((sub * E + i) << LyF<E>::L);
-}
-
-template <int E>
-__device__ __forceinline__ void ly_stage_regs(float (&v)[E], int s) {
-#pragma unroll
-  for (int i = 0; i < E; ++i)
-    if (!(i & (1 << s))) {
-      const float a = v[i], b = v[i + (1 << s)];
-      v[i] = a + b;
-      v[i + (1 << s)] = a - b;
-    }
-}
-
-template <int E>
-__device__ __forceinline__ void ly_stage_lanes(float (&v)[E], int mask, bool upper) {
-#pragma unroll
-  for (int i = 0; i < E; ++i) {
-    const float o = lane_xor(v[i], mask);
-    v[i] = upper ? o - v[i] : v[i] + o;
-  }
-}
-
-template <int E>
-__device__ __forceinline__ bool ly_fwht(float (&v)[E], float *buf, int logb, int tid) {
-  constexpr int LE = LyF<E>::LE, L = LyF<E>::L;
-  const int lane = tid & 63;
-#pragma unroll
-  for (int s = 0; s < LE; ++s)
-    if (s < logb) ly_stage_regs<E>(v, s);
-#pragma unroll
-  for (int s = 0; s < 6; ++s)
-    if (LE + s < logb) ly_stage_lanes<E>(v, 1 << s, (lane >> s) & 1);
-  if (logb <= L) return false;
-  {
-    float *w = buf + E * tid + 4 * (tid >> 6);         // element E tid + i at e + 4 (e >> L)
-    if constexpr (E >= 4) {
-#pragma unroll
-      for (int i = 0; i < E; i += 4) *reinterpret_cast<float4 *>(w + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < E; ++i) w[i] = v[i];
-    }
-  }
-  __syncthreads();
-  const int lo = tid / LyF<E>::LPC, sub = tid % LyF<E>::LPC;
-#pragma unroll
-  for (int i = 0; i < E; ++i) {
-    const int hi = sub * E + i;
-    v[i] = buf[lo + (hi << L) + 4 * hi];
-  }
-#pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    if (L + h >= logb) break;
-    if (h < LE) ly_stage_regs<E>(v, h);
-    else ly_stage_lanes<E>(v, 1 << (h - LE), (sub >> (h - LE)) & 1);
-  }
-  return true;
-}
 
 // E consecutive bf16 values of x from element e (16-byte aligned x; e % E == 0)
 template <int E>
@@ -895,11 +1094,6 @@ __device__ __forceinline__ void ly_out_signs(const int8_t *sign_n, int n, int mn
   }
 }
 
-__device__ __forceinline__ int ly_e(int count) {    // elements per thread for count <= 16384 elements
-  int e = 1;
-  while (e * LY_THREADS < count) e <<= 1;
-  return e;
-}
 
 template <int BPW>
 __global__ void __launch_bounds__(LY_THREADS, 1)
@@ -1433,12 +1627,55 @@ int launch_rht_vec(const void *in, void *out, int64_t rows, int64_t n, int lb, c
   return hip_status(hipGetLastError());
 }
 
+// rows of n <= 4096 on 256-thread workgroups, longer rows on 512 or 1024
+// threads (16 elements per thread)
+template <bool IB, bool OB, bool TR, int NW>
+int launch_rht_reg_nw(const void *in, void *out, int64_t rows, int64_t n, int lb, const int8_t *signs,
+                      float *rowsum, hipStream_t st) {
+  int64_t e = 1;
+  while (e * 64 * NW < n) e <<= 1;
+  const size_t shm = sizeof(float) * (size_t)(64 * NW * e + 64);
+  const int64_t cap = (int64_t)cu_count() * (32 / NW);
+  const int64_t grid = rows < cap ? rows : cap;
+  const int rc = allow_lds(rht_rows_reg<IB, OB, TR, NW>, shm + 64);
+  if (rc) return rc;
+  hipLaunchKernelGGL((rht_rows_reg<IB, OB, TR, NW>), dim3((unsigned)grid), dim3(64 * NW), shm, st, in, out,
+                     rows, (int)n, lb, signs, rowsum);
+  return hip_status(hipGetLastError());
+}
+
+template <bool IB, bool OB, bool TR>
+int launch_rht_reg(const void *in, void *out, int64_t rows, int64_t n, int lb, const int8_t *signs,
+                   float *rowsum, hipStream_t st) {
+  if (rows <= 64) return launch_rht_reg_nw<IB, OB, TR, 16>(in, out, rows, n, lb, signs, rowsum, st);
+  if (n <= 4096) return launch_rht_reg_nw<IB, OB, TR, 4>(in, out, rows, n, lb, signs, rowsum, st);
+  if (n <= 8192) return launch_rht_reg_nw<IB, OB, TR, 8>(in, out, rows, n, lb, signs, rowsum, st);
+  return launch_rht_reg_nw<IB, OB, TR, 16>(in, out, rows, n, lb, signs, rowsum, st);
+}
+
 int launch_rht(const void *in, glq_dtype in_dt, void *out, glq_dtype out_dt, int64_t rows,
                int64_t n, const int8_t *signs, int transpose, float *rowsum, hipStream_t st) {
   const int lb = log2_block(n);
   if (lb > kMaxLogBlock) return GLQ_ERR_UNSUPPORTED;
   const bool aligned = ((reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out) |
                          reinterpret_cast<uintptr_t>(signs)) & 15) == 0;
+  // the register kernel where it measured faster: rows of 16384, and a few
+  // rows (decode-time batches, latency-bound: 1024 threads per row); the LDS
+  // radix-16 kernel below for thousands of rows of 3072 .. 12288
+  const bool few = rows <= 64 && n % 8 == 0 && n <= 16384;
+  if ((n == 16384 || few) && aligned && in != out) {
+    const bool ib = in_dt == GLQ_BF16, ob = out_dt == GLQ_BF16;
+    if (transpose) {
+      if (ib) return ob ? launch_rht_reg<true, true, true>(in, out, rows, n, lb, signs, rowsum, st)
+                        : launch_rht_reg<true, false, true>(in, out, rows, n, lb, signs, rowsum, st);
+      return ob ? launch_rht_reg<false, true, true>(in, out, rows, n, lb, signs, rowsum, st)
+                : launch_rht_reg<false, false, true>(in, out, rows, n, lb, signs, rowsum, st);
+    }
+    if (ib) return ob ? launch_rht_reg<true, true, false>(in, out, rows, n, lb, signs, rowsum, st)
+                      : launch_rht_reg<true, false, false>(in, out, rows, n, lb, signs, rowsum, st);
+    return ob ? launch_rht_reg<false, true, false>(in, out, rows, n, lb, signs, rowsum, st)
+              : launch_rht_reg<false, false, false>(in, out, rows, n, lb, signs, rowsum, st);
+  }
   if (n % 8 == 0 && n <= RV_MAX && aligned && in != out) {
     const bool ib = in_dt == GLQ_BF16, ob = out_dt == GLQ_BF16;
     if (transpose) {
@@ -1542,14 +1779,11 @@ int launch_matmul(const glq_layer *L, const void *xt, glq_dtype x_dt, const floa
     const int64_t grid = (L->n + 15) / 16;
     const size_t shm = tab + GV_WAVES * 16 * 16 * 4;
     const bool g8 = ((L->k / 8) % 8) == 0;
-    int rc = g8 ? allow_lds(gemv_bf16<BPW, true>, shm) : allow_lds(gemv_bf16<BPW, false>, shm);
+    auto kern = g8 ? gemv_bf16<BPW, true> : gemv_bf16<BPW, false>;
+    int rc = allow_lds(kern, shm);
     if (rc) return rc;
-    if (g8)
-      hipLaunchKernelGGL((gemv_bf16<BPW, true>), dim3((unsigned)grid), dim3(64 * GV_WAVES), shm, st,
-                         L->idx1, L->idx2, blob, xb, rowsum, m, L->n, L->k, post, out, out_dt);
-    else
-      hipLaunchKernelGGL((gemv_bf16<BPW, false>), dim3((unsigned)grid), dim3(64 * GV_WAVES), shm, st,
-                         L->idx1, L->idx2, blob, xb, rowsum, m, L->n, L->k, post, out, out_dt);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * GV_WAVES), shm, st, L->idx1, L->idx2, blob, xb,
+                       rowsum, m, L->n, L->k, post, out, out_dt);
   } else {
     const int64_t mb = (m + GM_BM - 1) / GM_BM, nb = (L->n + GM_BN - 1) / GM_BN;
     const int64_t tiles = mb * nb;
@@ -1673,14 +1907,18 @@ extern "C" int glq_fused_linear(const glq_layer *L, const void *x, glq_dtype x_d
       if (rc) return rc;
     }
   }
+  // z between the matrix product and the output rotation: float32, except on
+  // the prefill path with a bf16 y, where it is rounded to bf16 (half the
+  // bytes of the largest intermediate; the extra rounding is a relative
+  // 2^-9 per element of z, spread over the Hadamard sums)
   void *mm_out = out_rht ? (void *)z : y;
-  const glq_dtype mm_dt = out_rht ? GLQ_F32 : y_dt;
+  const glq_dtype mm_dt = !out_rht ? y_dt : (x_dt == GLQ_BF16 && y_dt == GLQ_BF16 && m > 16) ? GLQ_BF16 : GLQ_F32;
   switch (L->bpw) {
     case 2: rc = launch_matmul<2>(L, xt_use, x_dt, rowsum, m, mm_out, mm_dt, st); break;
     case 3: rc = launch_matmul<3>(L, xt_use, x_dt, rowsum, m, mm_out, mm_dt, st); break;
     default: rc = launch_matmul<4>(L, xt_use, x_dt, rowsum, m, mm_out, mm_dt, st); break;
   }
   if (rc) return rc;
-  if (out_rht) return launch_rht(z, GLQ_F32, y, y_dt, m, L->n, L->sign_n, 1, nullptr, st);
+  if (out_rht) return launch_rht(z, mm_dt, y, y_dt, m, L->n, L->sign_n, 1, nullptr, st);
   return GLQ_OK;
 }

@@ -131,6 +131,22 @@ def test_rht_f32(G, n, rows, transpose):
     assert np.max(np.abs(got - ref)) <= 1e-6 * np.max(np.abs(ref)) * np.log2(max(rht.block_size(n), 2))
 
 
+@pytest.mark.parametrize("n", [3072, 4096, 16384, 8200])
+@pytest.mark.parametrize("transpose", [0, 1])
+def test_rht_many_rows(G, n, transpose):
+    # more rows than the few-row path takes: the LDS radix-16 kernel (3072,
+    # 4096, 8200) and the register kernel on 256 .. 1024 threads (16384)
+    rows = 96
+    rng = np.random.default_rng(n + transpose)
+    x = rng.standard_normal((rows, n)).astype(np.float32)
+    sig = workloads.signs(n, n + 3)
+    out = torch.empty((rows, n), device="cuda", dtype=torch.float32)
+    G.rht_apply(_t(x), out, _t(sig), bool(transpose))
+    torch.cuda.synchronize()
+    ref = (rht.rht_transpose if transpose else rht.rht_forward)(x.astype(np.float64), sig)
+    assert np.max(np.abs(out.cpu().numpy() - ref)) <= 1e-6 * np.max(np.abs(ref)) * np.log2(rht.block_size(n))
+
+
 def test_rht_bf16_in_out(G):
     n, rows = 4096, 3
     x = workloads.bf16_round_trip(np.random.default_rng(1).standard_normal((rows, n)).astype(np.float32))
