@@ -32,6 +32,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 
 #include "glq.h"
 #include "glq_tables.h"
@@ -878,17 +879,17 @@ __device__ __forceinline__ void gv_unpack(const GvRaw &r, uint32_t (&i1)[8], uin
   }
 }
 
-template <int BPW, bool G8>
+template <int BPW, bool G8, int RT>
 __global__ void __launch_bounds__(64 * GV_WAVES, 1)
 gemv_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uint16_t *xt,
           const float *rowsum, int64_t m, int64_t n, int64_t k, float post, void *out,
           glq_dtype out_dt) {
+  // RT tiles of 16 weight rows per workgroup share every x~ operand load
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  float *red = reinterpret_cast<float *>(lds + lds_table_bytes<BPW>());
+  float *red = reinterpret_cast<float *>(lds + lds_table_bytes<BPW>());   // [RT][waves][16][16]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 15, q = lane >> 4;
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
-  const int64_t row = min(n0 + j, n - 1);
+  const int64_t n0 = (int64_t)blockIdx.x * 16 * RT;
   const int64_t G = k / 8;
   const int64_t chunks = (G + 31) / 32;
   const uint16_t *xrow = xt + (size_t)min((int64_t)j, m - 1) * k;
@@ -900,11 +901,12 @@ gemv_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
   // only feed output rows that are not stored, and groups past k meet zero
   // weight operands.
   int64_t c = wave;
-  GvRaw raw;
+  GvRaw raw[RT];
   uint4 av[8];
   auto load_chunk = [&](int64_t cc) {
     const int64_t g0 = 32 * cc + 8 * q;
-    raw = gv_load_raw<BPW, G8>(idx1, idx2, row, G, g0);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) raw[rt] = gv_load_raw<BPW, G8>(idx1, idx2, min(n0 + 16 * rt + j, n - 1), G, g0);
 #pragma unroll
     for (int s = 0; s < 8; ++s) av[s] = *reinterpret_cast<const uint4 *>(xrow + 8 * min(g0 + s, G - 1));
   };
@@ -912,43 +914,48 @@ gemv_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
   // row sum of the activation row this thread reduces at the end (loaded
   // unconditionally, clamped, used only after the reduction)
   float rs_raw = 0.0f;
-  if constexpr (Epi<BPW>::bias != 0.0f) rs_raw = rowsum[min((int64_t)(threadIdx.x >> 4), m - 1)];
+  if constexpr (Epi<BPW>::bias != 0.0f) rs_raw = rowsum[min((int64_t)((threadIdx.x >> 4) & 15), m - 1)];
   load_tables<BPW, 64 * GV_WAVES>(lds, blob);
   tables_landed();
   __syncthreads();
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   while (c < chunks) {
     const int64_t g0 = 32 * c + 8 * q;
-    uint32_t i1[8], i2[8];
-    gv_unpack<BPW>(raw, i1, i2);
-    Dec8<BPW> D;
-    uint4 bv[8];
-    D.p1(i1, i2);
-    D.p2(i1, i2);
-    D.p3(i1, i2);
-    D.p4(bv);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const uint4 b = g0 + s < G ? bv[s] : make_uint4(0, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[s]),
-                                                    __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+    for (int rt = 0; rt < RT; ++rt) {
+      uint32_t i1[8], i2[8];
+      gv_unpack<BPW>(raw[rt], i1, i2);
+      Dec8<BPW> D;
+      uint4 bv[8];
+      D.p1(i1, i2);
+      D.p2(i1, i2);
+      D.p3(i1, i2);
+      D.p4(bv);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const uint4 b = g0 + s < G ? bv[s] : make_uint4(0, 0, 0, 0);
+        acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[s]),
+                                                          __builtin_bit_cast(bf16x8, b), acc[rt], 0, 0, 0);
+      }
     }
     c += GV_WAVES;
     if (c < chunks) load_chunk(c);
   }
   // D[r][col]: lane holds rows 4 (lane >> 4) + t (activation row), column lane & 15 (weight row)
 #pragma unroll
-  for (int t = 0; t < 4; ++t) red[(wave * 16 + 4 * q + t) * 16 + j] = acc[t];
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) red[((rt * GV_WAVES + wave) * 16 + 4 * q + t) * 16 + j] = acc[rt][t];
   __syncthreads();
-  if (threadIdx.x < 256) {
-    const int r = threadIdx.x >> 4, col = threadIdx.x & 15;
+  if (threadIdx.x < 256 * RT) {
+    const int rt = threadIdx.x >> 8, r = (threadIdx.x >> 4) & 15, col = threadIdx.x & 15;
     float v = 0.0f;
 #pragma unroll
-    for (int w = 0; w < GV_WAVES; ++w) v += red[(w * 16 + r) * 16 + col];
-    const int64_t nrow = n0 + col;
-    if (r < m && nrow < n) {
-      store_out(out, out_dt, (size_t)r * n + nrow, post * (v - Epi<BPW>::bias * rs_raw));
-    }
+    for (int w = 0; w < GV_WAVES; ++w) v += red[((rt * GV_WAVES + w) * 16 + r) * 16 + col];
+    const int64_t nrow = n0 + 16 * rt + col;
+    if (r < m && nrow < n) store_out(out, out_dt, (size_t)r * n + nrow, post * (v - Epi<BPW>::bias * rs_raw));
   }
 }
 
@@ -1752,6 +1759,11 @@ int launch_decode(const glq_layer *L, void *w_out, glq_dtype out_dt, hipStream_t
   return hip_status(hipGetLastError());
 }
 
+// Row tiles per GEMV workgroup: more than one only where it measured faster
+// (2 bpw layers of at least 1024 tiles, e.g. 16384 x 16384: 60 -> 41 us at
+// m = 8); at 3/4 bpw the extra accumulators spill.
+int gv_row_tiles(int bpw, int64_t tiles) { return bpw == 2 && tiles >= 1024 ? 4 : 1; }
+
 template <int BPW>
 int launch_matmul(const glq_layer *L, const void *xt, glq_dtype x_dt, const float *rowsum, int64_t m,
                   void *out, glq_dtype out_dt, hipStream_t st) {
@@ -1776,10 +1788,16 @@ int launch_matmul(const glq_layer *L, const void *xt, glq_dtype x_dt, const floa
   const float post = L->scale * Epi<BPW>::mul;
   const uint16_t *xb = reinterpret_cast<const uint16_t *>(xt);
   if (m <= 16) {
-    const int64_t grid = (L->n + 15) / 16;
-    const size_t shm = tab + GV_WAVES * 16 * 16 * 4;
+    // row tiles per workgroup: each x~ operand load serves 16 RT weight rows;
+    // keep at least ~128 workgroups in flight
+    const int64_t tiles = (L->n + 15) / 16;
+    const int rt = gv_row_tiles(BPW, tiles);
+    const int64_t grid = (tiles + rt - 1) / rt;
+    const size_t shm = tab + (size_t)rt * GV_WAVES * 16 * 16 * 4;
     const bool g8 = ((L->k / 8) % 8) == 0;
-    auto kern = g8 ? gemv_bf16<BPW, true> : gemv_bf16<BPW, false>;
+    constexpr int RT4 = BPW == 2 ? 4 : 1;            // the only multi-tile variant
+    auto kern = g8 ? (rt == 4 ? gemv_bf16<BPW, true, RT4> : gemv_bf16<BPW, true, 1>)
+                   : (rt == 4 ? gemv_bf16<BPW, false, RT4> : gemv_bf16<BPW, false, 1>);
     int rc = allow_lds(kern, shm);
     if (rc) return rc;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * GV_WAVES), shm, st, L->idx1, L->idx2, blob, xb,

@@ -212,6 +212,21 @@ def test_fused_shapes_bf16(G, cb, bpw, m):
         assert og.relative_error(y, ref) <= TOL_BF16
 
 
+@pytest.mark.parametrize("m,k", [(3, 256), (16, 136)])
+def test_gemv_many_row_tiles(G, cb, m, k):
+    # 2 bpw with more than 1024 tiles of 16 rows: four tiles per workgroup,
+    # the last workgroup ragged
+    n, bpw = 16400, 2
+    i1, i2 = _random_layer(n, k, bpw, 4000 + m + k)
+    s = np.float32(0.013)
+    sn, sk = workloads.signs(n, 51), workloads.signs(k, 52)
+    x = workloads.bf16_round_trip(np.random.default_rng(k).standard_normal((m, k)).astype(np.float32))
+    ref = og.layer_reference(x, i1, i2, bpw, s, sn, sk)
+    for y_dt in ("bf16", "f32"):
+        y = _run_linear(G, cb, i1, i2, s, sn, sk, x, "bf16", y_dt)
+        assert og.relative_error(y, ref) <= TOL_BF16
+
+
 @pytest.mark.parametrize("bpw", [2, 3, 4])
 @pytest.mark.parametrize("m,n,k", [(300, 320, 512), (257, 264, 160), (64, 512, 4160), (40, 136, 72)])
 def test_prefill_tiles(G, cb, bpw, m, n, k):
