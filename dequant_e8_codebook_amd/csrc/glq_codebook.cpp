@@ -297,11 +297,12 @@ bool build_tables(Tables &T) {
   put32(b + 12, (uint32_t)H.entries.size());
   for (uint32_t c = 0; c < kChunks; ++c) put16(b + kCtOff + 2 * c, ct[c]);
   for (size_t r = 0; r < recs.size(); ++r) {
-    uint8_t *p = b + kOtOff + 16 * r;
-    put32(p + 0, recs[r].r_lo);
-    put32(p + 4, recs[r].lo_off);
-    put32(p + 8, recs[r].hi_off);
-    put32(p + 12, recs[r].qw);
+    const int32_t hs = (int32_t)recs[r].hi_off;       // may be negative (wraps in uint32)
+    if (recs[r].r_lo > 31 || recs[r].qw > 31 || recs[r].lo_off >= (1u << 24) || hs < -(1 << 23) || hs >= (1 << 23))
+      return false;
+    uint8_t *p = b + kOtOff + 8 * r;
+    put32(p + 0, recs[r].r_lo | (recs[r].lo_off << 8));
+    put32(p + 4, recs[r].qw | ((uint32_t)hs << 8));
   }
   for (size_t e = 0; e < H.entries.size(); ++e) {
     for (int t = 0; t < 4; ++t) {
@@ -343,8 +344,9 @@ void decode_doubled_via_tables(const uint8_t *blob, uint32_t i, int *y) {
   uint32_t e = rd16(kCtOff + 2 * (ip >> 4));
   uint32_t low = ip & 15u;
   uint32_t rec = (e >> 5) + (low >> (e & 31u));
-  uint32_t r_lo = rd32(kOtOff + 16 * rec), lo_off = rd32(kOtOff + 16 * rec + 4);
-  uint32_t hi_off = rd32(kOtOff + 16 * rec + 8), qw = rd32(kOtOff + 16 * rec + 12);
+  const uint32_t w0 = rd32(kOtOff + 8 * rec), w1 = rd32(kOtOff + 8 * rec + 4);
+  const uint32_t r_lo = w0 & 31u, lo_off = w0 >> 8, qw = w1 & 31u;
+  const uint32_t hi_off = (uint32_t)((int32_t)w1 >> 8);
   uint32_t jlo = ip & ((1u << r_lo) - 1u);
   uint32_t lo_addr = lo_off + 8u * jlo;
   uint32_t qsrc = qw ? (ip & ((1u << qw) - 1u)) : 0u;

@@ -124,15 +124,22 @@ __device__ __forceinline__ uint32_t pk_dec16(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, w) - (u16x2)(1));
 }
 
+// Byte offsets of the low and high signed half-vectors of index i' from its
+// orbit record R (two words, see glq_tables.h): the shift and bit-field
+// extract by R.x / R.y read only bits 0-4 (r_lo, q_width).
+__device__ __forceinline__ void rec_offsets(uint32_t ip, uint2 R, uint32_t &lo, uint32_t &hi) {
+  lo = (R.x >> 8) + (__builtin_amdgcn_ubfe(ip, 0, R.x) << 3);
+  const uint32_t q = __builtin_popcount(__builtin_amdgcn_ubfe(ip, 0, R.y)) & 1u;
+  hi = (uint32_t)((int32_t)R.y >> 8) + ((ip >> (R.x & 31u)) << 3) + (q << 6);
+}
+
 // Table walk for one index, given as i' = i - 1 mod 2^16 (see glq_tables.h):
 // byte offsets of the low and high signed half-vectors within a half table.
 __device__ __forceinline__ void walk(uint32_t ip, uint32_t &lo, uint32_t &hi) {
   const uint32_t e = lds16(kLdsCt + ((ip >> 4) << 1));
   const uint32_t rec = (e >> 5) + ((ip & 15u) >> (e & 31u));
-  const uint4 R = lds128(kLdsOt + (rec << 4));
-  lo = R.y + (__builtin_amdgcn_ubfe(ip, 0, R.x) << 3);
-  const uint32_t q = __builtin_popcount(__builtin_amdgcn_ubfe(ip, 0, R.w)) & 1u;
-  hi = R.z + ((ip >> R.x) << 3) + (q << 6);
+  const uint2 R = lds64(kLdsOt + (rec << 3));
+  rec_offsets(ip, R, lo, hi);
 }
 
 __device__ __forceinline__ uint32_t pk_add16(uint32_t a, uint32_t b) {
@@ -178,7 +185,8 @@ __device__ __forceinline__ uint4 decode_group(uint32_t i1, uint32_t i2, const ui
 template <int BPW>
 struct Dec8 {
   uint32_t e1[8], e2[8];
-  uint4 r3[8], R1[8], R2[8];
+  uint4 r3[8];
+  uint2 R1[8], R2[8];
   uint2 va[8], vb[8], vc[8], vd[8];
 
   __device__ __forceinline__ void p1(const uint32_t (&q1)[8], const uint32_t (&q2)[8]) {
@@ -192,22 +200,20 @@ struct Dec8 {
   __device__ __forceinline__ void p2(const uint32_t (&q1)[8], const uint32_t (&q2)[8]) {
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
-      R1[g] = lds128(kLdsOt + (((e1[g] >> 5) + ((q1[g] & 15u) >> (e1[g] & 31u))) << 4));
-      if constexpr (BPW == 4) R2[g] = lds128(kLdsOt + (((e2[g] >> 5) + ((q2[g] & 15u) >> (e2[g] & 31u))) << 4));
+      R1[g] = lds64(kLdsOt + (((e1[g] >> 5) + ((q1[g] & 15u) >> (e1[g] & 31u))) << 3));
+      if constexpr (BPW == 4) R2[g] = lds64(kLdsOt + (((e2[g] >> 5) + ((q2[g] & 15u) >> (e2[g] & 31u))) << 3));
     }
   }
   __device__ __forceinline__ void p3(const uint32_t (&q1)[8], const uint32_t (&q2)[8]) {
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
-      const uint4 R = R1[g];
-      const uint32_t lo = R.y + (__builtin_amdgcn_ubfe(q1[g], 0, R.x) << 3);
-      const uint32_t hi = R.z + ((q1[g] >> R.x) << 3) + ((__builtin_popcount(__builtin_amdgcn_ubfe(q1[g], 0, R.w)) & 1u) << 6);
+      uint32_t lo, hi;
+      rec_offsets(q1[g], R1[g], lo, hi);
       va[g] = lds64(kLdsHt1 + lo);
       vb[g] = lds64(kLdsHt1 + hi);
       if constexpr (BPW == 4) {
-        const uint4 Q = R2[g];
-        const uint32_t lo2 = Q.y + (__builtin_amdgcn_ubfe(q2[g], 0, Q.x) << 3);
-        const uint32_t hi2 = Q.z + ((q2[g] >> Q.x) << 3) + ((__builtin_popcount(__builtin_amdgcn_ubfe(q2[g], 0, Q.w)) & 1u) << 6);
+        uint32_t lo2, hi2;
+        rec_offsets(q2[g], R2[g], lo2, hi2);
         vc[g] = lds64(kLdsHt2 + lo2);
         vd[g] = lds64(kLdsHt2 + hi2);
       }

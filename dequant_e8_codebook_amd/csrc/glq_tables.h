@@ -11,12 +11,15 @@
 //                                  the orbit size when orbits are smaller than 16
 //                                  (several orbits per chunk), 4 otherwise, 0 for the
 //                                  last chunk (one record per slot)
-//   rec = OT[(e >> 5) + ((i' & 15) >> ls)]   orbit record, 4 x uint32:
-//        .x = r_lo      number of nonzero coordinates among x1..x4
-//        .y = lo_off    byte offset of the block of signed low halves
-//        .z = hi_off'   byte offset of the block of signed high halves, minus
-//                       8 * (orbit_start >> r_lo) (uint32 arithmetic wraps)
-//        .w = q_width   4 for half-integer orbits, 0 for integer orbits
+//   rec = OT[(e >> 5) + ((i' & 15) >> ls)]   orbit record, 2 x uint32:
+//        word 0 = r_lo | lo_off << 8
+//                 r_lo    number of nonzero coordinates among x1..x4 (bits 0-4,
+//                         so a shift or bit-field extract by word 0 uses it)
+//                 lo_off  byte offset of the block of signed low halves
+//        word 1 = q_width | hi_off' << 8   (hi_off' signed, arithmetic shift back)
+//                 q_width 4 for half-integer orbits, 0 for integer orbits
+//                 hi_off' byte offset of the block of signed high halves, minus
+//                         8 * (orbit_start >> r_lo)
 //   lo = HT[lo_off + 8 * (i' & (2^r_lo - 1))]
 //   hi = HT[hi_off' + 8 * (i' >> r_lo) + 64 * (popcount(i' & (2^q_width - 1)) & 1)]
 //
@@ -59,7 +62,7 @@ constexpr uint32_t kHeaderBytes = 256;
 constexpr uint32_t kCtOff = kHeaderBytes;
 constexpr uint32_t kCtBytes = kChunks * 2;
 constexpr uint32_t kOtOff = kCtOff + kCtBytes;
-constexpr uint32_t kOtBytes = kMaxRecords * 16;
+constexpr uint32_t kOtBytes = kMaxRecords * 8;
 constexpr uint32_t kHtBytes = kMaxHalves * 8;
 constexpr uint32_t kHtBf16Off = kOtOff + kOtBytes;
 constexpr uint32_t kHtA3Off = kHtBf16Off + kHtBytes;
@@ -70,7 +73,7 @@ constexpr uint32_t kR3Bytes = 256 * 16;
 constexpr uint32_t kBlobBytes = kR3Off + kR3Bytes;
 
 constexpr uint32_t kMagic0 = 0x43514C47u;  // "GLQC"
-constexpr uint32_t kFormatVersion = 0x00010000u;
+constexpr uint32_t kFormatVersion = 0x00020000u;
 
 static_assert(kCtOff % 16 == 0 && kOtOff % 16 == 0 && kHtBf16Off % 16 == 0 &&
               kHtA3Off % 16 == 0 && kHtA4Off % 16 == 0 && kHtB4Off % 16 == 0 && kR3Off % 16 == 0,

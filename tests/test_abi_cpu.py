@@ -35,7 +35,7 @@ def test_status_strings_and_version():
     for s in (-1, -2, -3, -4):
         assert glq.status_string(s) != "unknown status"
     assert glq.status_string(7) == "unknown status"
-    assert glq.version() == 0x00010000
+    assert glq.version() == 0x00020000
 
 
 def test_codebook_equals_oracle():
@@ -57,17 +57,20 @@ def _walk_blob(blob: bytes):
     table format description (numpy, vectorised), into doubled coordinates."""
     b = np.frombuffer(blob, dtype=np.uint8)
     ct = b[256:256 + 8192].view(np.uint16).astype(np.int64)
-    ot = b[8448:8448 + 1472 * 16].view(np.uint32).reshape(-1, 4).astype(np.int64)
-    a3 = b[8448 + 1472 * 16 + 2368 * 8: 8448 + 1472 * 16 + 2 * 2368 * 8].view(np.int16)
+    ot = b[8448:8448 + 1472 * 8].view(np.uint32).reshape(-1, 2).astype(np.int64)
+    a3 = b[8448 + 1472 * 8 + 2368 * 8: 8448 + 1472 * 8 + 2 * 2368 * 8].view(np.int16)
     i = np.arange(65536, dtype=np.int64)
     ip = (i - 1) & 0xFFFF
     e = ct[ip >> 4]
     rec = (e >> 5) + ((ip & 15) >> (e & 31))
     r = ot[rec]
-    lo = r[:, 1] + 8 * (ip & ((1 << r[:, 0]) - 1))
-    qsrc = ip & ((1 << r[:, 3]) - 1)
+    r_lo, lo_off = r[:, 0] & 31, r[:, 0] >> 8
+    qw = r[:, 1] & 31
+    hi_off = r[:, 1].astype(np.uint32).view(np.int32).astype(np.int64) >> 8   # signed
+    lo = lo_off + 8 * (ip & ((1 << r_lo) - 1))
+    qsrc = ip & ((1 << qw) - 1)
     q = np.array([bin(v).count("1") & 1 for v in qsrc])
-    hi = (r[:, 2] + 8 * (ip >> r[:, 0]) + 64 * q) & 0xFFFFFFFF
+    hi = hi_off + 8 * (ip >> r_lo) + 64 * q
     out = np.zeros((65536, 8), dtype=np.int64)
     for t in range(4):
         out[:, t] = a3[(lo + 2 * t) // 2] // 2
@@ -80,7 +83,7 @@ def test_device_tables_decode_every_index():
     assert np.array_equal(_walk_blob(blob), e8.codebook().astype(np.int64))
     b = np.frombuffer(blob, dtype=np.uint8)
     # value formats agree with each other: bf16 = y/2, A4 = 2 * A3, B4 = 0x4340 + y
-    base = 8448 + 1472 * 16
+    base = 8448 + 1472 * 8
     hb = b[base: base + 2368 * 8].view(np.uint16)
     a3 = b[base + 2368 * 8: base + 2 * 2368 * 8].view(np.int16).astype(np.int64)
     a4 = b[base + 2 * 2368 * 8: base + 3 * 2368 * 8].view(np.int16).astype(np.int64)
