@@ -249,11 +249,17 @@ template <> struct Epi<2> { static constexpr float bias = 0.0f, mul = 1.0f; };
 template <> struct Epi<3> { static constexpr float bias = kBiasValue, mul = 0.25f; };
 template <> struct Epi<4> { static constexpr float bias = kBiasValue, mul = 0.125f; };
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// bf16 bit patterns of two floats (a in bits 0-15), round to nearest even:
+// one v_cvt_pk_bf16_f32 on gfx950
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) { return (uint16_t)bf16x2_rne(f, 0.0f); }
 
 __device__ __forceinline__ void store_out(void *y, glq_dtype dt, size_t off, float v) {
   if (dt == GLQ_F32) reinterpret_cast<float *>(y)[off] = v;
@@ -449,7 +455,8 @@ rht_rows_vec(const void *in, void *out, int64_t rows, int64_t n, int logb, const
         uint32_t w[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const uint16_t h0 = f32_to_bf16_rne(v[2 * t]), h1 = f32_to_bf16_rne(v[2 * t + 1]);
+          const uint32_t hh = bf16x2_rne(v[2 * t], v[2 * t + 1]);
+          const uint16_t h0 = (uint16_t)hh, h1 = (uint16_t)(hh >> 16);
           w[t] = (uint32_t)h0 | ((uint32_t)h1 << 16);
           rs += __uint_as_float((uint32_t)h0 << 16) + __uint_as_float((uint32_t)h1 << 16);
         }
@@ -711,7 +718,14 @@ __device__ __forceinline__ void rr_rows(const void *in, void *out, int64_t rows,
     for (int i = 0; i < E; ++i) {
       x[i] = v[i] * inv;
       if (TRANSPOSE) x[i] *= sg[i];
-      if constexpr (OUT_BF16) x[i] = __uint_as_float((uint32_t)f32_to_bf16_rne(x[i]) << 16);
+    }
+    if constexpr (OUT_BF16) {                        // round to bf16, two at a time
+#pragma unroll
+      for (int i = 0; i < E; i += 2) {
+        const uint32_t hh = bf16x2_rne(x[i], i + 1 < E ? x[i + 1] : 0.0f);
+        x[i] = __uint_as_float(hh << 16);
+        if (i + 1 < E) x[i + 1] = __uint_as_float(hh & 0xFFFF0000u);
+      }
     }
     if (!tr && E >= 2 && e0 + E <= n) {
       // untransposed: the thread's E consecutive outputs in vector stores
@@ -808,7 +822,7 @@ decode_weights_k(const uint16_t *idx1, const void *idx2, const uint8_t *blob, fl
       uint32_t p[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        p[t] = (uint32_t)f32_to_bf16_rne(w[2 * t]) | ((uint32_t)f32_to_bf16_rne(w[2 * t + 1]) << 16);
+        p[t] = bf16x2_rne(w[2 * t], w[2 * t + 1]);
       reinterpret_cast<uint4 *>(out)[g] = make_uint4(p[0], p[1], p[2], p[3]);
     }
   }
@@ -1051,9 +1065,14 @@ __device__ __forceinline__ void ly_input(const uint16_t *x, const int8_t *sign_k
   float rs[4] = {0.f, 0.f, 0.f, 0.f};
   uint16_t h[E];
 #pragma unroll
+  for (int i = 0; i < E; i += 2) {
+    const uint32_t hh = bf16x2_rne(v[i] * inv, i + 1 < E ? v[i + 1] * inv : 0.0f);
+    h[i] = (uint16_t)hh;
+    if (i + 1 < E) h[i + 1] = (uint16_t)(hh >> 16);
+  }
+#pragma unroll
   for (int i = 0; i < E; ++i) {
     const int e = ly_elem<E>(tid, i, tr);
-    h[i] = f32_to_bf16_rne(v[i] * inv);
     if (e < mk) {
       const float hv = __uint_as_float((uint32_t)h[i] << 16);
       const int r = (e >= k) + (e >= 2 * k) + (e >= 3 * k);   // m <= 4
@@ -1330,9 +1349,6 @@ __device__ __forceinline__ uint4 gm_decode_one(const uint2 (&i1)[2], const uint2
   (void)lds;
   return decode_ip<BPW>(a1, a2);
 }
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 // GEMM epilogue: z = post * acc + cz(row) with cz = -post * bias * rowsum(x~),
 // staged through LDS (free once the k-loop has ended) so that every lane
