@@ -3,7 +3,7 @@
 [glq] "How it works" (item 1: 16-bit E8 index per 8-weight group; 3/4 bpw
 add a second-stage residual codebook of 8 or 16 bits), "Bit widths" (global
 scale only, no group size), "Results" (sizes equal the nominal rate).
-Readings (Readings R7-R12):
+Readings (Readings R7-R12, R16):
 
 R7  Global scale s = fp32(sqrt(mean(W~^2))), computed in float64 and rounded
     once; s = 1 when W~ is identically zero.
@@ -20,6 +20,11 @@ R11 Decode: v = C[i1] + 2^-k C_r[i2] (exact in float32), then one IEEE
     w32. Output [n, k] row-major in the rotated basis.
 R12 Layer reference in float64: y = U^T (W32 (V x)) with W32 the float32
     decoded weights (exact in float64) and x as given.
+R16 Per-row scales ("EntroPack", first paragraph: per-row normalized E8
+    quantization; no formula given): s_r = fp32(sqrt(mean_j W~[r, j]^2)) per
+    output row, X[r] = W~[r] / s_r, the same index search; a row's weights
+    decode as fl32(s_r' * v) with s_r' = fl32(scale * s_r) when a global
+    scale multiplies too.
 """
 from __future__ import annotations
 
@@ -45,6 +50,19 @@ def global_scale(wt: np.ndarray) -> np.float32:
     if ms == 0.0:
         return np.float32(1.0)
     return np.float32(np.sqrt(ms))
+
+
+def row_scales(wt: np.ndarray) -> np.ndarray:
+    """Per-row normalisation (EntroPack page, first paragraph: "per-row
+    normalized E8"; the page gives no formula, reading R16): s_r =
+    fp32(sqrt(mean_j W~[r, j]^2)) for each output row r, 1 for a zero row."""
+    wt = np.asarray(wt, dtype=np.float64)
+    if not np.all(np.isfinite(wt)):
+        raise ValueError("non-finite weights")
+    ms = np.mean(wt * wt, axis=1)
+    out = np.sqrt(ms).astype(np.float32)
+    out[ms == 0.0] = np.float32(1.0)
+    return out
 
 
 def groups(wt: np.ndarray) -> np.ndarray:
@@ -122,17 +140,22 @@ def nearest(x: np.ndarray, size: int = e8.CODEBOOK_SIZE, workers: int = -1) -> n
 # --------------------------------------------------------------------------
 
 def encode(w: np.ndarray, bpw: int, sign_n: np.ndarray, sign_k: np.ndarray,
-           scale: float | None = None, search=nearest):
+           scale: float | None = None, search=nearest, per_row: bool = False):
     """Quantise W [n, k] (original basis). Returns (idx1 u16, idx2 | None, s).
 
     W~ = U W V^T (R6); s per R7 unless given; X = W~/s grouped per R8;
-    stage 1 per R9; for 3/4 bpw the residual stage per R10.
+    stage 1 per R9; for 3/4 bpw the residual stage per R10. per_row: s is the
+    float32 vector of row scales (R16) and row r is divided by s[r].
     """
     if bpw not in (2, 3, 4):
         raise ValueError("bpw must be 2, 3 or 4")
     wt = rht.rotate_weights(w, sign_n, sign_k)
-    s = global_scale(wt) if scale is None else np.float32(scale)
-    x = groups(wt) / np.float64(s)
+    if per_row:
+        s = row_scales(wt)
+        x = groups(wt) / s.astype(np.float64)[:, None, None]
+    else:
+        s = global_scale(wt) if scale is None else np.float32(scale)
+        x = groups(wt) / np.float64(s)
     n, g, _ = x.shape
     flat = x.reshape(-1, 8)
     i1 = search(flat)
@@ -144,7 +167,7 @@ def encode(w: np.ndarray, bpw: int, sign_n: np.ndarray, sign_k: np.ndarray,
         # |R - 2^-k c|^2 = 4^-k |2^k R - c|^2 : the same argmin, exactly.
         i2 = search(r * np.float64(1 << k), size=size)
         idx2 = i2.reshape(n, g).astype(np.uint8 if bpw == 3 else np.uint16)
-    return i1.reshape(n, g).astype(np.uint16), idx2, np.float32(s)
+    return i1.reshape(n, g).astype(np.uint16), idx2, (s if per_row else np.float32(s))
 
 
 def decode_values(idx1: np.ndarray, idx2, bpw: int) -> np.ndarray:
@@ -162,10 +185,20 @@ def decode_values(idx1: np.ndarray, idx2, bpw: int) -> np.ndarray:
     return v.reshape(n, g * 8)
 
 
+def effective_scale(scale, row_scale=None):
+    """Scale of each row: the global scale, or fl32(scale * row_scale[r]) (R16)."""
+    if row_scale is None:
+        return np.float32(scale)
+    return np.float32(scale) * np.asarray(row_scale, dtype=np.float32)
+
+
 def decode_f32(idx1, idx2, bpw: int, scale) -> np.ndarray:
-    """w32 = fl32(s * v): one IEEE float32 multiply per weight (R11)."""
+    """w32 = fl32(s * v): one IEEE float32 multiply per weight (R11); scale is
+    one float32 or a float32 vector with one scale per row (R16)."""
     v = decode_values(idx1, idx2, bpw).astype(np.float32)   # exact
-    return np.float32(scale) * v
+    if np.ndim(scale) == 0:
+        return np.float32(scale) * v
+    return np.asarray(scale, dtype=np.float32)[:, None] * v
 
 
 def f32_to_bf16_bits(w32: np.ndarray) -> np.ndarray:

@@ -235,3 +235,66 @@ def test_layer_reference_rotation_flags():
 def test_relative_error_measure():
     assert glq.relative_error(np.array([1.0, 2.0]), np.array([1.0, 2.0])) == 0.0
     assert glq.relative_error(np.array([1.5, 2.0]), np.array([1.0, 2.0])) == 0.25
+
+
+# -------------------------------------------------------- per-row scales ----
+
+def test_row_scales_equal_norm_rows_reduce_to_global_scale():
+    # rows that are signed permutations of one dyadic vector have exactly equal
+    # mean squares, so every row scale is the global scale and the per-row
+    # encoding must give the global-scale indices
+    rng = np.random.default_rng(11)
+    n, k = 12, 64
+    base = rng.integers(-40, 41, k) / 1024.0
+    wt = np.stack([rng.permutation(base) * rng.choice([-1.0, 1.0], k) for _ in range(n)])
+    sn, sk = _signs(n, 3), _signs(k, 4)
+    w = rht.unrotate_weights(wt, sn, sk)
+    rs = glq.row_scales(rht.rotate_weights(w, sn, sk))
+    assert rs.dtype == np.float32 and rs.shape == (n,)
+    g1, g2, gs = glq.encode(w, 4, sn, sk)
+    p1, p2, ps = glq.encode(w, 4, sn, sk, per_row=True)
+    assert np.all(np.abs(ps / gs - 1) < 1e-6)
+    assert np.array_equal(p1, g1) and np.array_equal(p2, g2)
+
+
+def test_row_scales_power_of_two_row_factors():
+    # multiplying row r of W~ by 2^e_r multiplies its scale by 2^e_r and leaves
+    # the indices unchanged
+    rng = np.random.default_rng(12)
+    n, k = 10, 96
+    wt = rng.standard_normal((n, k)) * 0.02
+    e = rng.integers(-6, 7, n)
+    sn, sk = _signs(n, 5), _signs(k, 6)
+    a1, a2, a_s = glq.encode(rht.unrotate_weights(wt, sn, sk), 3, sn, sk, per_row=True)
+    b1, b2, b_s = glq.encode(rht.unrotate_weights(wt * np.ldexp(1.0, e)[:, None], sn, sk), 3, sn, sk, per_row=True)
+    assert np.array_equal(a1, b1) and np.array_equal(a2, b2)
+    assert np.allclose(b_s, a_s * np.ldexp(1.0, e), rtol=2 ** -22, atol=0)
+
+
+def test_row_scales_keep_small_rows():
+    # rows 1000x smaller than the rest vanish under one global scale but are
+    # encoded to the same relative error as the others with row scales
+    rng = np.random.default_rng(13)
+    n, k = 16, 128
+    wt = rng.standard_normal((n, k)) * 0.02
+    wt[::4] *= 1e-3
+    sn, sk = _signs(n, 7), _signs(k, 8)
+    w = rht.unrotate_weights(wt, sn, sk)
+    g1, g2, gs = glq.encode(w, 2, sn, sk)
+    p1, p2, ps = glq.encode(w, 2, sn, sk, per_row=True)
+    def rel(i1, s):
+        wd = glq.decode_f32(i1, None, 2, s).astype(np.float64)
+        return np.linalg.norm(wd - wt, axis=1) / np.linalg.norm(wt, axis=1)
+    assert np.all(rel(g1, gs)[::4] > 0.99)                 # global: small rows decode to ~0
+    assert np.all(rel(p1, ps) < 0.6)                        # per row: every row keeps its shape
+
+
+def test_decode_with_row_scales_is_rowwise_global_decode():
+    rng = np.random.default_rng(14)
+    i1 = rng.integers(0, 65536, (6, 8)).astype(np.uint16)
+    i2 = rng.integers(0, 256, (6, 8)).astype(np.uint8)
+    s = glq.effective_scale(0.5, rng.uniform(0.01, 0.04, 6).astype(np.float32))
+    w = glq.decode_f32(i1, i2, 3, s)
+    for r in range(6):
+        assert np.array_equal(w[r], glq.decode_f32(i1[r:r + 1], i2[r:r + 1], 3, s[r])[0])
+    assert glq.effective_scale(0.5, np.float32([0.3]))[0] == np.float32(np.float32(0.5) * np.float32(0.3))
