@@ -251,7 +251,8 @@ void parallel_for(int64_t count, int nthreads, F fn) {
 extern "C" int glq_encode_ref(const float *w, int64_t n, int64_t k, int32_t bpw,
                               const int8_t *sign_n, const int8_t *sign_k,
                               float scale_in, float *scale_out,
-                              uint16_t *idx1_out, void *idx2_out, int32_t nthreads) {
+                              uint16_t *idx1_out, void *idx2_out, int32_t nthreads,
+                              float *row_scale_out) {
   using namespace glq;
   if (!w || !sign_n || !sign_k || !idx1_out) return GLQ_ERR_ARG;
   if (n < 1 || k < 8 || k % 8 != 0) return GLQ_ERR_ARG;
@@ -290,10 +291,11 @@ extern "C" int glq_encode_ref(const float *w, int64_t n, int64_t k, int32_t bpw,
     }
   });
 
-  float s;
-  if (scale_in > 0.0f) {
-    s = scale_in;
-  } else {
+  // scales: one global s, or one per row (row r divided by srow[r])
+  std::vector<float> srow((size_t)n, 1.0f);
+  float s = 1.0f;
+  const bool per_row = row_scale_out != nullptr;
+  if (per_row || scale_in <= 0.0f) {
     // mean of squares with per-row long double partial sums
     std::vector<long double> part((size_t)n);
     parallel_for(n, nt, [&](int64_t r) {
@@ -302,12 +304,24 @@ extern "C" int glq_encode_ref(const float *w, int64_t n, int64_t k, int32_t bpw,
       for (int64_t c = 0; c < k; ++c) acc += (long double)row[c] * row[c];
       part[r] = acc;
     });
-    long double tot = 0.0L;
-    for (int64_t r = 0; r < n; ++r) tot += part[r];
-    double ms = (double)(tot / (long double)nk);
-    s = ms == 0.0 ? 1.0f : (float)std::sqrt(ms);
+    if (per_row) {
+      for (int64_t r = 0; r < n; ++r) {
+        const double ms = (double)(part[r] / (long double)k);
+        srow[r] = ms == 0.0 ? 1.0f : (float)std::sqrt(ms);
+        row_scale_out[r] = srow[r];
+      }
+    } else {
+      long double tot = 0.0L;
+      for (int64_t r = 0; r < n; ++r) tot += part[r];
+      const double ms = (double)(tot / (long double)nk);
+      s = ms == 0.0 ? 1.0f : (float)std::sqrt(ms);
+    }
+  } else {
+    s = scale_in;
   }
   if (scale_out) *scale_out = s;
+  if (!per_row)
+    for (int64_t r = 0; r < n; ++r) srow[r] = s;
 
   const int64_t g = k / 8;
   const uint32_t rlimit = bpw == 3 ? 256u : kCodebookSize;
@@ -316,7 +330,7 @@ extern "C" int glq_encode_ref(const float *w, int64_t n, int64_t k, int32_t bpw,
   parallel_for(n, nt, [&](int64_t r) {
     for (int64_t q = 0; q < g; ++q) {
       double x[8];
-      for (int t = 0; t < 8; ++t) x[t] = wt[r * k + 8 * q + t] / (double)s;
+      for (int t = 0; t < 8; ++t) x[t] = wt[r * k + 8 * q + t] / (double)srow[r];
       uint32_t i1 = S.nearest(x, kCodebookSize);
       idx1_out[r * g + q] = (uint16_t)i1;
       if (bpw > 2) {

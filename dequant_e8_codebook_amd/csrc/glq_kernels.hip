@@ -797,7 +797,7 @@ rht_rows_reg(const void *in, void *out, int64_t rows, int n, int logb, const int
 template <int BPW, bool OUT_F32>
 __global__ void __launch_bounds__(256)
 decode_weights_k(const uint16_t *idx1, const void *idx2, const uint8_t *blob, float scale,
-                 int64_t groups, void *out) {
+                 const float *row_scale, uint32_t G, int64_t groups, void *out) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   load_tables<BPW>(lds, blob);
   tables_landed();
@@ -808,11 +808,13 @@ decode_weights_k(const uint16_t *idx1, const void *idx2, const uint8_t *blob, fl
     const uint32_t i2 = BPW == 2 ? 0u : load_idx2(idx2, g, BPW);
     const uint4 h = decode_group<BPW>(i1, i2, lds);
     const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
+    // the row's scale s_r = fl32(scale * row_scale[r]) (groups < 2^32)
+    const float sr = row_scale ? scale * row_scale[(uint32_t)g / G] : scale;
     float w[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const float v = operand_value<BPW>((hw[t >> 1] >> (16 * (t & 1))) & 0xFFFFu);
-      w[t] = scale * v;                          // one float32 multiply
+      w[t] = sr * v;                             // one float32 multiply
     }
     if constexpr (OUT_F32) {
       float4 *o = reinterpret_cast<float4 *>(out) + 2 * g;
@@ -902,8 +904,8 @@ __device__ __forceinline__ void gv_unpack(const GvRaw &r, uint32_t (&i1)[8], uin
 template <int BPW, bool G8, int RT>
 __global__ void __launch_bounds__(64 * GV_WAVES, 1)
 gemv_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uint16_t *xt,
-          const float *rowsum, int64_t m, int64_t n, int64_t k, float post, void *out,
-          glq_dtype out_dt) {
+          const float *rowsum, int64_t m, int64_t n, int64_t k, float post, const float *row_scale,
+          void *out, glq_dtype out_dt) {
   // RT tiles of 16 weight rows per workgroup share every x~ operand load
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   float *red = reinterpret_cast<float *>(lds + lds_table_bytes<BPW>());   // [RT][waves][16][16]
@@ -975,7 +977,10 @@ gemv_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
 #pragma unroll
     for (int w = 0; w < GV_WAVES; ++w) v += red[((rt * GV_WAVES + w) * 16 + r) * 16 + col];
     const int64_t nrow = n0 + 16 * rt + col;
-    if (r < m && nrow < n) store_out(out, out_dt, (size_t)r * n + nrow, post * (v - Epi<BPW>::bias * rs_raw));
+    if (r < m && nrow < n) {
+      const float pr = row_scale ? post * row_scale[nrow] : post;
+      store_out(out, out_dt, (size_t)r * n + nrow, pr * (v - Epi<BPW>::bias * rs_raw));
+    }
   }
 }
 
@@ -1131,7 +1136,8 @@ template <int BPW>
 __global__ void __launch_bounds__(LY_THREADS, 1)
 layer_small(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uint16_t *x,
             const int8_t *sign_k, const int8_t *sign_n, int64_t m, int64_t n, int64_t k, int logbk,
-            int logbn, float post, void *y, glq_dtype y_dt, float *z, unsigned int *ctrl) {
+            int logbn, float post, const float *row_scale, void *y, glq_dtype y_dt, float *z,
+            unsigned int *ctrl) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   float *xs = reinterpret_cast<float *>(lds + lds_table_bytes<BPW>());
   float *red = reinterpret_cast<float *>(lds + lds_table_bytes<BPW>() + LY_BUF_BYTES);
@@ -1208,8 +1214,9 @@ layer_small(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const u
       const int64_t nrow = tile * 16 + col;
       if (r < m && nrow < n) {
         if (Epi<BPW>::bias != 0.0f) v -= Epi<BPW>::bias * misc[r];
+        const float pr = row_scale ? post * row_scale[nrow] : post;
         // coherent (write-through) store: visible to every XCD without an L2 writeback
-        __hip_atomic_store(z + (size_t)r * n + nrow, post * v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(z + (size_t)r * n + nrow, pr * v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     __syncthreads();
@@ -1357,8 +1364,8 @@ __device__ __forceinline__ uint4 gm_decode_one(const uint2 (&i1)[2], const uint2
 // aligned (n * element size % 16 == 0 and an aligned output pointer).
 template <int BPW, bool OUT_BF16>
 __device__ __forceinline__ void gm_epilogue(const f32x16 (&acc)[8][2], const float *rowsum, float post,
-                                            void *out, int64_t m, int64_t n, int64_t m0, int64_t n0,
-                                            int lane, int wave, bool vec) {
+                                            const float *row_scale, void *out, int64_t m, int64_t n, int64_t m0,
+                                            int64_t n0, int lane, int wave, bool vec) {
   constexpr int ES = OUT_BF16 ? 2 : 4;              // bytes per output value
   constexpr int CH = OUT_BF16 ? 4 : 2;              // 32-row blocks per chunk
   constexpr uint32_t SB = 64 * ES + 16;             // padded LDS row stride (bytes)
@@ -1369,6 +1376,12 @@ __device__ __forceinline__ void gm_epilogue(const f32x16 (&acc)[8][2], const flo
   const int c = lane & 31, p = lane >> 5;
   const uint32_t wbase = wave * WAVE_BYTES;
   const int64_t rlast4 = ((m - 1) >> 2) << 2;
+  // per output column (weight row) n0 + 32 t + c: post, times its row scale
+  float pt[2] = {post, post};
+  if (row_scale) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) pt[t] = post * row_scale[min(n0 + 32 * t + c, n - 1)];
+  }
 #pragma unroll
   for (int a0 = 0; a0 < 8; a0 += CH) {
 #pragma unroll
@@ -1381,7 +1394,7 @@ __device__ __forceinline__ void gm_epilogue(const f32x16 (&acc)[8][2], const flo
           // inside the 256-byte-aligned row-sum buffer
           const int64_t r0 = min(m0 + 32 * a + 8 * q + 4 * p, rlast4);
           const float4 rs = *reinterpret_cast<const float4 *>(rowsum + r0);
-          const float f = -post * Epi<BPW>::bias;
+          const float f = -Epi<BPW>::bias;
           cz[0] = f * rs.x; cz[1] = f * rs.y; cz[2] = f * rs.z; cz[3] = f * rs.w;
         }
 #pragma unroll
@@ -1389,7 +1402,7 @@ __device__ __forceinline__ void gm_epilogue(const f32x16 (&acc)[8][2], const flo
           const uint32_t base = wbase + (32 * (a - a0) + 8 * q + 4 * p) * SB + (32 * t + c) * ES;
           float v[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) v[j] = fmaf(acc[a][t][4 * q + j], post, cz[j]);
+          for (int j = 0; j < 4; ++j) v[j] = fmaf(acc[a][t][4 * q + j], pt[t], pt[t] * cz[j]);
           if constexpr (OUT_BF16) {
 #pragma unroll
             for (int j = 0; j < 4; j += 2) {
@@ -1435,8 +1448,8 @@ __device__ __forceinline__ void gm_epilogue(const f32x16 (&acc)[8][2], const flo
 template <int BPW, bool G4, bool OUT_BF16>
 __global__ void __launch_bounds__(256, 1)
 gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uint16_t *xt,
-          const float *rowsum, int64_t m, int64_t n, int64_t k, float post, void *out,
-          int vec, int64_t mblocks, int64_t tiles) {
+          const float *rowsum, int64_t m, int64_t n, int64_t k, float post, const float *row_scale,
+          void *out, int vec, int64_t mblocks, int64_t tiles) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   uint16_t *As0 = reinterpret_cast<uint16_t *>(lds + lds_table_bytes<BPW>());
   uint16_t *As1 = As0 + GM_BM * GM_LDA;
@@ -1543,7 +1556,7 @@ gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
     for (int g = 0; g < 8; ++g) bv[g >> 2][g & 3] = bn[g];
     __syncthreads();
   }
-  gm_epilogue<BPW, OUT_BF16>(acc, rowsum, post, out, m, n, m0, n0, lane, wave, vec != 0);
+  gm_epilogue<BPW, OUT_BF16>(acc, rowsum, post, row_scale, out, m, n, m0, n0, lane, wave, vec != 0);
 }
 
 // ---------------------------------------------------------------- float32 path
@@ -1552,7 +1565,8 @@ gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
 template <int BPW>
 __global__ void __launch_bounds__(256)
 gemv_f32(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const float *xt,
-         int64_t m0, int64_t mc, int64_t n, int64_t k, float scale, void *out, glq_dtype out_dt) {
+         int64_t m0, int64_t mc, int64_t n, int64_t k, float scale, const float *row_scale, void *out,
+         glq_dtype out_dt) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   load_tables<BPW>(lds, blob);
   tables_landed();
@@ -1585,7 +1599,8 @@ gemv_f32(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const floa
     for (int r = 0; r < 4; ++r) {
       float t = acc[r];
       for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off);
-      if (lane == 0 && r < mc) store_out(out, out_dt, (size_t)(m0 + r) * n + row, scale * t);
+      if (lane == 0 && r < mc)
+        store_out(out, out_dt, (size_t)(m0 + r) * n + row, (row_scale ? scale * row_scale[row] : scale) * t);
     }
   }
 }
@@ -1740,14 +1755,15 @@ int check_layer(const glq_layer *L, bool need_signs) {
   if (!L->idx1 || !L->cb) return GLQ_ERR_ARG;
   if (L->bpw > 2 && !L->idx2) return GLQ_ERR_ARG;
   if (need_signs && (!L->sign_k || !L->sign_n)) return GLQ_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(L->row_scale) & 3) return GLQ_ERR_ARG;
   if ((double)L->n * (double)L->k > 17179869184.0) return GLQ_ERR_UNSUPPORTED;
   return GLQ_OK;
 }
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-// Workspace: [0, 256) control words (the whole-layer kernel's completion
-// counter: zero before first use, left zero by every call), then x~, row sums
+// Workspace: [0, kCtrlBytes) control words (the whole-layer kernel's ticket
+// counters: zero before first use, left zero by every call), then x~, row sums
 // of x~ and z = s W^ x~.
 struct WsLayout { size_t ctrl, xt, rowsum, z, total; };
 
@@ -1774,10 +1790,10 @@ int launch_decode(const glq_layer *L, void *w_out, glq_dtype out_dt, hipStream_t
   if (rc) return rc;
   if (out_dt == GLQ_F32)
     hipLaunchKernelGGL((decode_weights_k<BPW, true>), dim3((unsigned)grid), dim3(256), shm, st,
-                       L->idx1, L->idx2, blob, L->scale, groups, w_out);
+                       L->idx1, L->idx2, blob, L->scale, L->row_scale, (uint32_t)(L->k / 8), groups, w_out);
   else
     hipLaunchKernelGGL((decode_weights_k<BPW, false>), dim3((unsigned)grid), dim3(256), shm, st,
-                       L->idx1, L->idx2, blob, L->scale, groups, w_out);
+                       L->idx1, L->idx2, blob, L->scale, L->row_scale, (uint32_t)(L->k / 8), groups, w_out);
   return hip_status(hipGetLastError());
 }
 
@@ -1800,8 +1816,8 @@ int launch_matmul(const glq_layer *L, const void *xt, glq_dtype x_dt, const floa
     for (int64_t m0 = 0; m0 < m; m0 += 4) {
       const int64_t mc = m - m0 < 4 ? m - m0 : 4;
       hipLaunchKernelGGL(gemv_f32<BPW>, dim3((unsigned)grid), dim3(256), tab, st, L->idx1, L->idx2,
-                         blob, reinterpret_cast<const float *>(xt), m0, mc, L->n, L->k, L->scale, out,
-                         out_dt);
+                         blob, reinterpret_cast<const float *>(xt), m0, mc, L->n, L->k, L->scale, L->row_scale,
+                         out, out_dt);
       int rc = hip_status(hipGetLastError());
       if (rc) return rc;
     }
@@ -1823,7 +1839,7 @@ int launch_matmul(const glq_layer *L, const void *xt, glq_dtype x_dt, const floa
     int rc = allow_lds(kern, shm);
     if (rc) return rc;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * GV_WAVES), shm, st, L->idx1, L->idx2, blob, xb,
-                       rowsum, m, L->n, L->k, post, out, out_dt);
+                       rowsum, m, L->n, L->k, post, L->row_scale, out, out_dt);
   } else {
     const int64_t mb = (m + GM_BM - 1) / GM_BM, nb = (L->n + GM_BN - 1) / GM_BN;
     const int64_t tiles = mb * nb;
@@ -1837,7 +1853,7 @@ int launch_matmul(const glq_layer *L, const void *xt, glq_dtype x_dt, const floa
     int rc = allow_lds(kern, shm);
     if (rc) return rc;
     hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(256), shm, st, L->idx1, L->idx2, blob, xb, rowsum, m,
-                       L->n, L->k, post, out, vec, mb, tiles);
+                       L->n, L->k, post, L->row_scale, out, vec, mb, tiles);
   }
   return hip_status(hipGetLastError());
 }
@@ -1918,8 +1934,8 @@ extern "C" int glq_fused_linear(const glq_layer *L, const void *x, glq_dtype x_d
     rc = allow_lds(layer_small<B>, ly_lds_bytes<B>());                                                  \
     if (rc) return rc;                                                                                  \
     hipLaunchKernelGGL(layer_small<B>, dim3((unsigned)grid), dim3(64 * GV_WAVES), ly_lds_bytes<B>(), st, \
-                       L->idx1, L->idx2, blob, xb, L->sign_k, L->sign_n, m, L->n, L->k, lbk, lbn, post, y, \
-                       y_dt, z, counter);                                                               \
+                       L->idx1, L->idx2, blob, xb, L->sign_k, L->sign_n, m, L->n, L->k, lbk, lbn, post,   \
+                       L->row_scale, y, y_dt, z, counter);                                                               \
   } while (0)
     if (L->bpw == 2) GLQ_LAYER_SMALL(2);
     else if (L->bpw == 3) GLQ_LAYER_SMALL(3);

@@ -41,11 +41,12 @@ _vp, _i64, _i32, _u32, _f32, _sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_in
 
 class GlqLayerStruct(ctypes.Structure):
     _fields_ = [("n", _i64), ("k", _i64), ("bpw", _i32), ("resid_shift", _i32), ("scale", _f32),
-                ("idx1", _vp), ("idx2", _vp), ("sign_k", _vp), ("sign_n", _vp), ("cb", _vp)]
+                ("idx1", _vp), ("idx2", _vp), ("sign_k", _vp), ("sign_n", _vp), ("cb", _vp),
+                ("row_scale", _vp)]
 
 
 _lib.glq_build_codebook.argtypes = [_i32, _vp, _sz, ctypes.POINTER(_sz)]
-_lib.glq_encode_ref.argtypes = [_vp, _i64, _i64, _i32, _vp, _vp, _f32, ctypes.POINTER(_f32), _vp, _vp, _i32]
+_lib.glq_encode_ref.argtypes = [_vp, _i64, _i64, _i32, _vp, _vp, _f32, ctypes.POINTER(_f32), _vp, _vp, _i32, _vp]
 _lib.glq_rht_apply.argtypes = [_vp, _i32, _vp, _i32, _i64, _i64, _vp, _i32, _vp]
 _lib.glq_decode_weights.argtypes = [ctypes.POINTER(GlqLayerStruct), _vp, _i32, _vp]
 _lib.glq_fused_linear_workspace.argtypes = [ctypes.POINTER(GlqLayerStruct), _i64]
@@ -102,8 +103,9 @@ def codebook_doubled() -> np.ndarray:
 
 
 def encode_ref(w: np.ndarray, bpw: int, sign_n: np.ndarray, sign_k: np.ndarray,
-               scale: float = 0.0, nthreads: int = 0):
-    """CPU encoder: returns (idx1 uint16 [n, k/8], idx2 or None, scale)."""
+               scale: float = 0.0, nthreads: int = 0, per_row: bool = False):
+    """CPU encoder: returns (idx1 uint16 [n, k/8], idx2 or None, scale); with
+    per_row the scale returned is the float32 vector of row scales."""
     w = np.ascontiguousarray(w, dtype=np.float32)
     n, k = w.shape
     sn = np.ascontiguousarray(sign_n, dtype=np.int8)
@@ -113,11 +115,12 @@ def encode_ref(w: np.ndarray, bpw: int, sign_n: np.ndarray, sign_k: np.ndarray,
     if bpw in (3, 4):
         i2 = np.empty((n, k // 8), dtype=np.uint8 if bpw == 3 else np.uint16)
     s = _f32(0.0)
+    rs = np.empty(n, dtype=np.float32) if per_row else None
     rc = _lib.glq_encode_ref(w.ctypes.data, n, k, bpw, sn.ctypes.data, sk.ctypes.data, float(scale),
                              ctypes.byref(s), i1.ctypes.data, None if i2 is None else i2.ctypes.data,
-                             nthreads)
+                             nthreads, None if rs is None else rs.ctypes.data)
     _check(rc, "glq_encode_ref")
-    return i1, i2, np.float32(s.value)
+    return i1, i2, (rs if per_row else np.float32(s.value))
 
 
 # ------------------------------------------------------------------ GPU calls
@@ -161,6 +164,7 @@ class Layer:
     sign_k: object              # torch int8 [k]
     sign_n: object              # torch int8 [n]
     cb: object                  # torch uint8 device tables
+    row_scale: object = None    # torch float32 [n] per-row scales, or None
 
     def struct(self) -> GlqLayerStruct:
         st = self.__dict__.get("_st")
@@ -174,11 +178,17 @@ class Layer:
             self.n, self.k, self.bpw, {2: 0, 3: 1, 4: 2}[self.bpw], float(self.scale),
             self.idx1.data_ptr(), 0 if self.idx2 is None else self.idx2.data_ptr(),
             0 if self.sign_k is None else self.sign_k.data_ptr(),
-            0 if self.sign_n is None else self.sign_n.data_ptr(), self.cb.data_ptr())
+            0 if self.sign_n is None else self.sign_n.data_ptr(), self.cb.data_ptr(),
+            0 if self.row_scale is None else self.row_scale.data_ptr())
 
     @staticmethod
-    def from_numpy(idx1, idx2, scale, sign_n, sign_k, cb, device="cuda") -> "Layer":
+    def from_numpy(idx1, idx2, scale, sign_n, sign_k, cb, device="cuda", row_scale=None) -> "Layer":
+        """scale: one float, or a float32 vector of per-row scales (then the
+        global scale is 1, unless row_scale is given separately)."""
         torch = _torch()
+        if np.ndim(scale) == 1:
+            scale, row_scale = 1.0, scale
+        rs = None if row_scale is None else torch.from_numpy(np.ascontiguousarray(row_scale, np.float32)).to(device)
         idx1 = np.ascontiguousarray(idx1, dtype=np.uint16)
         n, g = idx1.shape
         bpw = 2 if idx2 is None else (3 if np.asarray(idx2).dtype == np.uint8 else 4)
@@ -189,7 +199,7 @@ class Layer:
             t2 = torch.from_numpy(a2 if bpw == 3 else a2.astype(np.uint16).view(np.int16)).to(device)
         sk = None if sign_k is None else torch.from_numpy(np.ascontiguousarray(sign_k, np.int8)).to(device)
         sn = None if sign_n is None else torch.from_numpy(np.ascontiguousarray(sign_n, np.int8)).to(device)
-        return Layer(n, 8 * g, bpw, float(scale), t1, t2, sk, sn, cb)
+        return Layer(n, 8 * g, bpw, float(scale), t1, t2, sk, sn, cb, rs)
 
 
 def rht_apply(inp, out, signs, transpose: bool, stream=None):

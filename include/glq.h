@@ -82,6 +82,10 @@ typedef struct {
     const int8_t *sign_k;     /* [k] input-side signs, each +1 or -1 */
     const int8_t *sign_n;     /* [n] output-side signs, each +1 or -1 */
     const void *cb;           /* device copy of the GLQ_CB_DEVICE tables */
+    const float *row_scale;   /* device float [n] per-row scales, or NULL ("EntroPack" news
+                                 item: per-row normalised E8): row r then decodes with the
+                                 scale s_r = fl32(scale * row_scale[r]) in place of scale;
+                                 each entry finite and > 0 */
 } glq_layer;
 
 /*
@@ -109,12 +113,18 @@ int glq_build_codebook(int32_t form, void *out, size_t out_bytes, size_t *needed
  *   idx1_out   host uint16 [n][k/8]
  *   idx2_out   host uint8 (3 bpw) / uint16 (4 bpw) [n][k/8]; NULL at 2 bpw
  *   nthreads   worker threads (<= 0: hardware concurrency)
+ *   row_scale_out  host float [n], or NULL. When given, every row gets its own
+ *              scale ("EntroPack" news item: per-row normalised E8): s_r =
+ *              fp32(sqrt(mean_j W~[r,j]^2)) (1 for a zero row) is written to
+ *              row_scale_out[r], row r is divided by s_r before the search,
+ *              scale_in is ignored and *scale_out receives 1.
  * Returns GLQ_ERR_ARG for bad sizes/bpw, non-finite weights or signs not +-1.
  */
 int glq_encode_ref(const float *w, int64_t n, int64_t k, int32_t bpw,
                    const int8_t *sign_n, const int8_t *sign_k,
                    float scale_in, float *scale_out,
-                   uint16_t *idx1_out, void *idx2_out, int32_t nthreads);
+                   uint16_t *idx1_out, void *idx2_out, int32_t nthreads,
+                   float *row_scale_out);
 
 /*
  * glq_rht_apply -- randomized Hadamard transform along the last axis of a
@@ -134,8 +144,9 @@ int glq_rht_apply(const void *in, glq_dtype in_dt, void *out, glq_dtype out_dt,
 /*
  * glq_decode_weights -- expand the index planes into the rotated-basis
  * weights W^ [n][k] (the reconstruction the fused kernels do on the fly):
- * v = C[i1] + 2^-k C_r[i2] exactly, w = fl32(s * v) (one float32 multiply),
- * bf16 output = round-to-nearest-even of w.
+ * v = C[i1] + 2^-k C_r[i2] exactly, w = fl32(s * v) (one float32 multiply;
+ * s = s_r of the row when L->row_scale is given), bf16 output =
+ * round-to-nearest-even of w.
  *   w_out      device [n][k] of out_dt
  */
 int glq_decode_weights(const glq_layer *L, void *w_out, glq_dtype out_dt, void *hip_stream);

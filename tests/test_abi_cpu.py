@@ -111,6 +111,22 @@ def test_encode_ref_matches_oracle(bpw):
         assert np.array_equal(a2, b2) and a2.dtype == b2.dtype
 
 
+@pytest.mark.parametrize("bpw", [2, 4])
+def test_encode_ref_row_scales_match_oracle(bpw):
+    # rows of very different magnitude, per-row scales (reading R16)
+    spec = workloads.LayerSpec("t", 24, 128, bpw, 1, "normal", "f32", "f32", 0, 888)
+    w = workloads.weights(spec).astype(np.float32)
+    w *= np.logspace(-2, 1, 24, dtype=np.float32)[:, None]
+    sn, sk = workloads.sign_n(spec), workloads.sign_k(spec)
+    a1, a2, rs = glq.encode_ref(w, bpw, sn, sk, nthreads=3, per_row=True)
+    b1, b2, ro = og.encode(w.astype(np.float64), bpw, sn, sk, per_row=True)
+    assert rs.dtype == np.float32 and rs.shape == (24,)
+    assert np.array_equal(rs, ro)
+    assert np.array_equal(a1, b1)
+    if bpw > 2:
+        assert np.array_equal(a2, b2)
+
+
 def test_encode_ref_explicit_scale_codebook_exact():
     # W = U^T (s C[idx]) V: with the same s, the encoder returns idx
     rng = np.random.default_rng(5)
@@ -134,7 +150,7 @@ def test_encode_ref_errors():
     f = ctypes.c_float(0)
     call = lambda w_, n, k, bpw, sn, sk, i2=None: lib.glq_encode_ref(
         w_.ctypes.data, n, k, bpw, sn.ctypes.data, sk.ctypes.data, 0.0, ctypes.byref(f),
-        i1.ctypes.data, i2, 1)
+        i1.ctypes.data, i2, 1, None)
     assert call(w, 4, 16, 5, s, s) == glq.GLQ_ERR_ARG          # bpw
     assert call(w, 4, 12, 2, s, s) == glq.GLQ_ERR_ARG          # k % 8
     assert call(w, 4, 16, 3, s, s) == glq.GLQ_ERR_ARG          # idx2 missing

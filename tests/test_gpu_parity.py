@@ -359,3 +359,60 @@ def test_small_batch_single_launch(G, cb, bpw, n, k, m):
             ref = og.layer_reference(x, i1, i2, bpw, s, sn, sk)
             assert og.relative_error(y.float().cpu().numpy(), ref) <= TOL_BF16
             assert int(ws[:4352].count_nonzero().item()) == 0     # completion counters left at zero
+
+
+# ------------------------------------------------------ per-row scales ----
+
+def _row_scale_layer(n, k, bpw, seed, scale=0.75):
+    i1, i2 = _random_layer(n, k, bpw, seed)
+    rs = np.random.default_rng(seed).uniform(0.005, 0.05, n).astype(np.float32)
+    return i1, i2, np.float32(scale), rs
+
+
+@pytest.mark.parametrize("bpw", [2, 3, 4])
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_decode_row_scales_bitexact(G, cb, bpw, out):
+    n, k = 300, 264
+    i1, i2, s, rs = _row_scale_layer(n, k, bpw, 500 + bpw)
+    L = G.Layer.from_numpy(i1, i2, s, None, None, cb, row_scale=rs)
+    w = torch.empty((n, k), device="cuda", dtype=torch.bfloat16 if out == "bf16" else torch.float32)
+    G.decode_weights(L, w)
+    torch.cuda.synchronize()
+    se = og.effective_scale(s, rs)
+    ref = og.decode_bf16_bits(i1, i2, bpw, se) if out == "bf16" else og.decode_f32(i1, i2, bpw, se).view(np.uint32)
+    assert np.array_equal(_bits(w), ref)
+
+
+@pytest.mark.parametrize("bpw", [2, 3, 4])
+@pytest.mark.parametrize("m,x_dt", [(1, "bf16"), (3, "bf16"), (12, "bf16"), (40, "bf16"), (300, "bf16"), (3, "f32")])
+def test_fused_row_scales(G, cb, bpw, m, x_dt):
+    # the single-launch layer (m <= 4), the GEMV (m <= 16), the GEMM, the float32 path
+    n, k = 272, 512
+    i1, i2, s, rs = _row_scale_layer(n, k, bpw, 600 + bpw + m)
+    sn, sk = workloads.signs(n, 61), workloads.signs(k, 62)
+    x = np.random.default_rng(m).standard_normal((m, k)).astype(np.float32)
+    if x_dt == "bf16":
+        x = workloads.bf16_round_trip(x)
+    L = G.Layer.from_numpy(i1, i2, s, sn, sk, cb, row_scale=rs)
+    xt = _t(x, torch.float32 if x_dt == "f32" else torch.bfloat16)
+    ref = og.layer_reference(x, i1, i2, bpw, og.effective_scale(s, rs), sn, sk)
+    for y_dt in (("f32",) if x_dt == "f32" else ("bf16", "f32")):
+        y = torch.empty((m, n), device="cuda", dtype=torch.float32 if y_dt == "f32" else torch.bfloat16)
+        ws = torch.zeros(G.workspace_bytes(L, m), device="cuda", dtype=torch.uint8)
+        G.fused_linear(L, xt, y, ws)
+        torch.cuda.synchronize()
+        assert og.relative_error(y.float().cpu().numpy(), ref) <= (TOL_F32 if x_dt == "f32" else TOL_BF16)
+
+
+def test_fused_row_scales_oracle_encoded(G, cb):
+    # rows of very different magnitude encoded with per-row scales by the oracle
+    spec = workloads.layer_specs("batch16")[0]
+    n, k, m = 256, 512, 16
+    w = workloads.weights(workloads.LayerSpec("rs", n, k, 4, m, "normal", "bf16", "bf16", 0, spec.seed_base))
+    w = w * np.logspace(-2, 0, n)[:, None]
+    sn, sk = workloads.signs(n, 71), workloads.signs(k, 72)
+    i1, i2, rs = og.encode(w, 4, sn, sk, per_row=True)
+    x = workloads.bf16_round_trip(np.random.default_rng(3).standard_normal((m, k)).astype(np.float32))
+    y = _run_linear(G, cb, i1, i2, rs, sn, sk, x, "bf16", "f32")
+    ref = og.layer_reference(x, i1, i2, 4, rs, sn, sk)
+    assert og.relative_error(y, ref) <= TOL_BF16
