@@ -76,7 +76,7 @@ def read_traffic(workload, dominant):
 
 # ------------------------------------------------------------------ workload
 
-def build_layers(workload, n_layers, device):
+def build_layers(workload, n_layers, device, row_scale=False):
     import numpy as np
     import torch
     from dequant_e8_codebook_amd import glq
@@ -88,13 +88,13 @@ def build_layers(workload, n_layers, device):
     for spec in specs:
         w = wl.weights(spec).astype(np.float32)
         sn, sk = wl.sign_n(spec), wl.sign_k(spec)
-        i1, i2, s = glq.encode_ref(w, spec.bpw, sn, sk)
+        i1, i2, s = glq.encode_ref(w, spec.bpw, sn, sk, per_row=row_scale)
         base = glq.Layer.from_numpy(i1, i2, s, sn, sk, cb, device=device)
         copies = [base]
         for _ in range(n_layers - 1):
             copies.append(glq.Layer(base.n, base.k, base.bpw, base.scale, base.idx1.clone(),
                                     None if base.idx2 is None else base.idx2.clone(),
-                                    base.sign_k, base.sign_n, cb))
+                                    base.sign_k, base.sign_n, cb, base.row_scale))
         x = wl.activations(spec)
         xdt = torch.float32 if spec.x_dtype == "f32" else torch.bfloat16
         ydt = torch.float32 if spec.y_dtype == "f32" else torch.bfloat16
@@ -132,9 +132,13 @@ def run_bench(args):
     specs = layer_specs(args.workload)
     per_step_layers = len(specs)
     n_rot = args.layers if per_step_layers == 1 else max(1, args.layers // 16)
-    built = build_layers(args.workload, n_rot, dev)
-    comp_bytes = sum(b["layers"][0].idx1.numel() * 2 + (0 if b["layers"][0].idx2 is None else
-                     b["layers"][0].idx2.numel() * b["layers"][0].idx2.element_size()) for b in built)
+    built = build_layers(args.workload, n_rot, dev, row_scale=args.row_scale)
+
+    def layer_bytes(L):
+        # index planes, plus the row-scale vector when there is one
+        return (L.idx1.numel() * 2 + (0 if L.idx2 is None else L.idx2.numel() * L.idx2.element_size())
+                + (0 if L.row_scale is None else L.row_scale.numel() * 4))
+    comp_bytes = sum(layer_bytes(b["layers"][0]) for b in built)
     flops = sum(2.0 * b["spec"].m * b["spec"].n * b["spec"].k for b in built)
 
     def step(i):
@@ -214,7 +218,7 @@ def run_bench(args):
     k_mean = ms_step * 1e-3 if single_launch(spec0) and len(built) == 1 else core_mean
     # rotated-basis launches of 3/4 bpw also run a small row-sum kernel
     L0 = b0["layers"][0]
-    k_bytes = L0.idx1.numel() * 2 + (0 if L0.idx2 is None else L0.idx2.numel() * L0.idx2.element_size())
+    k_bytes = layer_bytes(L0)
     k_flops = 2.0 * spec0.m * spec0.n * spec0.k
     dom = dominant_kernel(spec0)
     hbm_bound = spec0.m <= 16
@@ -251,7 +255,7 @@ def run_bench(args):
         "config": {"workload": args.workload,
                    "layers": [f"{b['spec'].n}x{b['spec'].k}" for b in built],
                    "bpw": spec0.bpw, "m": spec0.m, "x_dtype": spec0.x_dtype,
-                   "distinct_layer_copies": len(b0["layers"]),
+                   "distinct_layer_copies": len(b0["layers"]), "row_scales": bool(args.row_scale),
                    "step": "full layer forward: input RHT + fused decode-matmul + output RHT"},
         "tflops": round(tflops, 4), "compressed_gbs": round(gbs, 2),
         "eager_ms_per_step": round(eager_ms_step, 5),
@@ -283,7 +287,7 @@ def cpu_baseline(built, budget_s):
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    comp = i1.size * 2 + (0 if i2 is None else i2.size * i2.itemsize)
+    comp = i1.size * 2 + (0 if i2 is None else i2.size * i2.itemsize) + (4 * np.size(s) if np.ndim(s) else 0)
     gbs = n_done * comp / dt / 1e9
     return {"value": round(gbs, 5), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{n_done} layer forwards of {spec.n}x{spec.k} at {spec.bpw} bpw, {rows} activation row(s) "
@@ -302,6 +306,55 @@ def _cpu_model():
 
 
 # ------------------------------------------------------------------ profiling helpers
+
+def achievable_peaks():
+    """Measured ceilings on this GPU, for context beside the published peaks:
+    a stream read of 2 GiB (torch sum of float32), a 2 GiB device copy
+    (bytes read plus written) and bf16 torch.matmul
+    (hipBLASLt) on uncompressed weights of the workload shapes."""
+    import torch
+    dev = "cuda:0"
+    out = {}
+    a = torch.ones(512 << 20, dtype=torch.float32, device=dev)      # 2 GiB
+    for _ in range(3):
+        a.sum()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        a.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    out["stream_read_gbs"] = round(a.numel() * 4 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    out["copy_read_plus_write_gbs"] = round(2 * a.numel() * 4 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del a, b
+    shapes = [(2048, 16384, 4096), (4096, 3072, 3072), (4096, 12288, 3072), (4096, 3072, 12288)]
+    mm = {}
+    for m, n, k in shapes:
+        x = torch.randn(m, k, device=dev).to(torch.bfloat16)
+        w = torch.randn(n, k, device=dev).to(torch.bfloat16)
+        wt = w.t().contiguous()
+        for _ in range(3):
+            torch.matmul(x, wt)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(20):
+            torch.matmul(x, wt)
+        e1.record()
+        torch.cuda.synchronize()
+        mm[f"{m}x{n}x{k}"] = round(2.0 * m * n * k * 20 / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+    out["bf16_matmul_tflops"] = mm
+    print(json.dumps(out))
+
 
 def copy_calibration():
     """A plain device-to-device copy of COPY_BYTES (for counter calibration)."""
@@ -375,6 +428,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--achievable", action="store_true", help="measure stream-read and bf16 matmul ceilings")
+    ap.add_argument("--row-scale", action="store_true", help="encode with per-row scales")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("COPY_FETCH", "COPY_WRITE", "BENCH_FETCH", "BENCH_WRITE"))
     ap.add_argument("--pmc-kernel", default="gemv_bf16")
     ap.add_argument("--pmc-kernel-label", default="gemv_bf16<2>")
@@ -392,6 +447,9 @@ def main():
         return 2
     if args.copy_calibration:
         copy_calibration()
+        return 0
+    if args.achievable:
+        achievable_peaks()
         return 0
     out, built = run_bench(args)
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(built, args.cpu_budget)
