@@ -157,17 +157,29 @@ def encode(w: np.ndarray, bpw: int, sign_n: np.ndarray, sign_k: np.ndarray,
         s = global_scale(wt) if scale is None else np.float32(scale)
         x = groups(wt) / np.float64(s)
     n, g, _ = x.shape
-    flat = x.reshape(-1, 8)
+    i1, i2, _ = quantise(x.reshape(-1, 8), bpw, search)
+    idx2 = None if i2 is None else i2.reshape(n, g).astype(np.uint8 if bpw == 3 else np.uint16)
+    return i1.reshape(n, g).astype(np.uint16), idx2, (s if per_row else np.float32(s))
+
+
+def quantise(flat: np.ndarray, bpw: int, search=nearest):
+    """The quantiser Q of one 8-vector per row of flat [G, 8] (already divided
+    by the scale): stage 1 per R9, the residual stage per R10 for 3/4 bpw.
+    Returns (i1 int64 [G], i2 int64 [G] | None, v float64 [G, 8]) with
+    v = C[i1] + 2^-k C_r[i2], the exact decoded vector."""
+    flat = np.asarray(flat, dtype=np.float64).reshape(-1, 8)
+    cb = e8.codebook_f64()
     i1 = search(flat)
-    idx2 = None
+    v = cb[i1]
+    i2 = None
     if bpw > 2:
         k = RESID_SHIFT[bpw]
         size = 1 << RESID_BITS[bpw]
-        r = flat - e8.codebook_f64()[i1]
+        r = flat - v
         # |R - 2^-k c|^2 = 4^-k |2^k R - c|^2 : the same argmin, exactly.
         i2 = search(r * np.float64(1 << k), size=size)
-        idx2 = i2.reshape(n, g).astype(np.uint8 if bpw == 3 else np.uint16)
-    return i1.reshape(n, g).astype(np.uint16), idx2, (s if per_row else np.float32(s))
+        v = v + cb[i2] * (2.0 ** -k)
+    return i1, i2, v
 
 
 def decode_values(idx1: np.ndarray, idx2, bpw: int) -> np.ndarray:

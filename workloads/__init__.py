@@ -21,7 +21,8 @@ weight reconstruction):
 
 Seeds: workload number c (1..5) uses base = 1000*c; the streams are
 W = base+0, x = base+1, sign_k = base+2, sign_n = base+3, outlier
-channels = base+4 (for the DiT block, linear number l adds 100*l).
+channels = base+4, calibration inputs = base+5 (for the DiT block, linear
+number l adds 100*l).
 """
 from __future__ import annotations
 
@@ -32,7 +33,7 @@ import numpy as np
 
 __all__ = [
     "LayerSpec", "WORKLOADS", "layer_specs", "weights", "activations",
-    "signs", "random_indices", "bf16_round_trip",
+    "signs", "random_indices", "bf16_round_trip", "calibration",
 ]
 
 
@@ -121,6 +122,27 @@ def sign_k(spec: LayerSpec) -> np.ndarray:
 
 def sign_n(spec: LayerSpec) -> np.ndarray:
     return signs(spec.n, spec.seed_base + 3)
+
+
+def calibration(spec: LayerSpec, m: int, rho: float = 0.6) -> np.ndarray:
+    """Calibration inputs X [m, k] float64 for a synthetic Hessian X^T X / m.
+
+    Unit normals made first-order autoregressive along k (neighbouring input
+    channels correlated with coefficient rho, unit variance kept), with the
+    same outlier channels as activations() scaled by 20. Stream base+5.
+    """
+    rng = np.random.default_rng(spec.seed_base + 5)
+    z = rng.standard_normal(size=(m, spec.k))
+    x = np.empty_like(z)
+    x[:, 0] = z[:, 0]
+    c = math.sqrt(1.0 - rho * rho)
+    for j in range(1, spec.k):
+        x[:, j] = rho * x[:, j - 1] + c * z[:, j]
+    if spec.outliers:
+        ch = np.random.default_rng(spec.seed_base + 4).choice(
+            spec.k, spec.outliers, replace=False)
+        x[:, ch] *= 20.0
+    return x
 
 
 def random_indices(shape, seed: int, upper: int = 65536, dtype=np.uint16) -> np.ndarray:
