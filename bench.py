@@ -23,6 +23,9 @@ sample of layer forwards of the same workload.
 Other modes (profiling helpers, not bench lines):
   --workload batch16|prefill_up|dit_block|small   time another workload
   --copy-calibration                              a plain device copy of known size
+  --row-scale                                     layers encoded with per-row scales
+  --achievable                                    stream-read, copy and bf16 matmul ceilings
+  --encoder                                       CPU encoder: plain vs LDLQ time and proxy loss
   --pmc-summary DIR                               turn rocprofv3 counter CSVs into a profile file
 """
 from __future__ import annotations
@@ -356,6 +359,51 @@ def achievable_peaks():
     print(json.dumps(out))
 
 
+def encoder_bench(workload, budget_s):
+    """The library's CPU encoders on one layer of the workload: nearest
+    rounding (glq_encode_ref) against LDLQ error feedback (glq_encode_ldlq)
+    with a synthetic Hessian of 2k calibration rows; proxy loss
+    tr((X^ - X) H~ (X^ - X)^T) of both (computed here in float64 from the
+    indices); and the oracle's LDLQ encoder timed on a bounded sample of rows
+    (the first rows of W with the first entries of sign_n)."""
+    import numpy as np
+    import workloads as wl
+    from dequant_e8_codebook_amd import glq
+    from oracle import glq as og, ldlq as ol, rht
+    spec = wl.layer_specs(workload)[0]
+    w = wl.weights(spec).astype(np.float32)
+    sn, sk = wl.sign_n(spec), wl.sign_k(spec)
+    h = ol.hessian_from_inputs(wl.calibration(spec, 2 * spec.k))
+    t0 = time.perf_counter()
+    p1, p2, ps = glq.encode_ref(w, spec.bpw, sn, sk)
+    t_plain = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    l1, l2, ls = glq.encode_ldlq(w, spec.bpw, sn, sk, h)
+    t_ldlq = time.perf_counter() - t0
+    x = rht.rotate_weights(w.astype(np.float64), sn, sk) / np.float64(ps)
+    ht = ol.damp_hessian(ol.rotate_hessian(h, sk))
+    loss_plain = ol.proxy_loss(og.decode_values(p1, p2, spec.bpw), x, ht)
+    loss_ldlq = ol.proxy_loss(og.decode_values(l1, l2, spec.bpw), x, ht)
+    # oracle: row samples of 16, 64, 256 ... rows while they stay within the budget
+    rows_s, t_or, rows = 0, 0.0, 16
+    while rows <= spec.n:
+        t0 = time.perf_counter()
+        ol.encode_ldlq(w[:rows].astype(np.float64), spec.bpw, sn[:rows], sk, h)
+        t_or, rows_s = time.perf_counter() - t0, rows
+        if 4 * t_or > budget_s:
+            break
+        rows *= 4
+    out = {"workload": workload, "n": spec.n, "k": spec.k, "bpw": spec.bpw, "threads": os.cpu_count(),
+           "cpp_plain_s": round(t_plain, 3), "cpp_ldlq_s": round(t_ldlq, 3),
+           "cpp_ldlq_weights_per_s": round(spec.n * spec.k / t_ldlq, 1),
+           "proxy_loss_plain": loss_plain, "proxy_loss_ldlq": loss_ldlq,
+           "loss_ratio": round(loss_ldlq / loss_plain, 4),
+           "indices_changed_frac": round(float((l1 != p1).mean()), 4),
+           "oracle_ldlq_sample": f"{rows_s} rows x {spec.k}", "oracle_ldlq_s": round(t_or, 3),
+           "oracle_ldlq_weights_per_s": round(rows_s * spec.k / t_or, 1)}
+    print(json.dumps(out))
+
+
 def copy_calibration():
     """A plain device-to-device copy of COPY_BYTES (for counter calibration)."""
     import torch
@@ -430,6 +478,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--achievable", action="store_true", help="measure stream-read and bf16 matmul ceilings")
     ap.add_argument("--row-scale", action="store_true", help="encode with per-row scales")
+    ap.add_argument("--encoder", action="store_true", help="time the CPU encoders (plain and LDLQ)")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("COPY_FETCH", "COPY_WRITE", "BENCH_FETCH", "BENCH_WRITE"))
     ap.add_argument("--pmc-kernel", default="gemv_bf16")
     ap.add_argument("--pmc-kernel-label", default="gemv_bf16<2>")
@@ -450,6 +499,9 @@ def main():
         return 0
     if args.achievable:
         achievable_peaks()
+        return 0
+    if args.encoder:
+        encoder_bench(args.workload, args.cpu_budget)
         return 0
     out, built = run_bench(args)
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(built, args.cpu_budget)

@@ -17,6 +17,15 @@
 //     (signs follow x; half-integer orbits with the wrong parity flip their
 //     cheapest coordinate), and every orbit within 1e-9 of the best is
 //     searched point by point for the lowest index at the minimum distance.
+//
+// LDLQ error feedback (glq_encode_ldlq; "How it works", item 3, and GPTQ in
+// "Acknowledgments"): the Hessian is rotated like the weights (item 2),
+// H~ = V H V^T, damped by damp * mean(diag H~) on the diagonal, and factored
+// as H~ = (I + U) D (I + U)^T with U strictly block upper triangular over
+// blocks of 8 inputs (from the last block backward: D_j = the diagonal block,
+// U_ij = H~_ij D_j^-1, Schur complement of the leading part). Every row is
+// then swept block by block along k: T_j = X_j + sum_{i<j} (X_i - X^_i) U_ij
+// and X^_j = the same nearest / residual quantiser applied to T_j.
 #include <algorithm>
 #include <atomic>
 #include <cmath>
@@ -245,25 +254,124 @@ void parallel_for(int64_t count, int nthreads, F fn) {
   for (auto &t : th) t.join();
 }
 
+constexpr int64_t kMaxLdlqK = 16384;
+
+// out = U M V^T in float64 for M [rows][cols] (float or double): every row
+// gets V (signs sign_c over cols), then every column gets U (signs sign_r)
+template <class T>
+void rotate_both(const T *m, int64_t rows, int64_t cols, const int8_t *sign_r, const int8_t *sign_c,
+                 int nt, double *out) {
+  parallel_for(rows, nt, [&](int64_t r) {
+    double *row = out + r * cols;
+    for (int64_t c = 0; c < cols; ++c) row[c] = (double)m[r * cols + c];
+    rht_forward(row, cols, sign_c);
+  });
+  const int64_t cblk = 64;
+  parallel_for((cols + cblk - 1) / cblk, nt, [&](int64_t cb) {
+    std::vector<double> col((size_t)rows);
+    int64_t c1 = std::min(cols, (cb + 1) * cblk);
+    for (int64_t c = cb * cblk; c < c1; ++c) {
+      for (int64_t r = 0; r < rows; ++r) col[r] = out[r * cols + c];
+      rht_forward(col.data(), rows, sign_r);
+      for (int64_t r = 0; r < rows; ++r) out[r * cols + c] = col[r];
+    }
+  });
+}
+
 }  // namespace
 }  // namespace glq
 
-extern "C" int glq_encode_ref(const float *w, int64_t n, int64_t k, int32_t bpw,
-                              const int8_t *sign_n, const int8_t *sign_k,
-                              float scale_in, float *scale_out,
-                              uint16_t *idx1_out, void *idx2_out, int32_t nthreads,
-                              float *row_scale_out) {
-  using namespace glq;
+namespace glq {
+namespace {
+
+// Block factorisation H = (I + U) D (I + U)^T of a symmetric k x k matrix a
+// (row-major, overwritten). Only the block upper part (row block <= column
+// block) of a is read and updated. U is returned packed by column block: the
+// 8j x 8 block U[0:8j, 8j:8j+8] starts at ublk[32 j (j - 1)]. false when a
+// diagonal block of a Schur complement is not positive definite.
+bool block_udu(double *a, int64_t k, int nt, std::vector<double> &ublk) {
+  const int64_t nb = k / 8;
+  ublk.assign((size_t)(32 * nb * (nb - 1)) + 8, 0.0);
+  for (int64_t j = nb - 1; j >= 0; --j) {
+    const int64_t c0 = 8 * j;
+    double d[8][8], l[8][8], inv[8][8];
+    for (int r = 0; r < 8; ++r)
+      for (int c = 0; c < 8; ++c) d[r][c] = a[(c0 + std::min(r, c)) * k + c0 + std::max(r, c)];
+    // Cholesky d = l l^T (positive definiteness test), then inv = d^-1
+    for (int r = 0; r < 8; ++r) {
+      for (int c = 0; c <= r; ++c) {
+        double v = d[r][c];
+        for (int t = 0; t < c; ++t) v -= l[r][t] * l[c][t];
+        if (r == c) {
+          if (!(v > 0.0) || !std::isfinite(v)) return false;
+          l[r][r] = std::sqrt(v);
+        } else {
+          l[r][c] = v / l[c][c];
+        }
+      }
+      for (int c = r + 1; c < 8; ++c) l[r][c] = 0.0;
+    }
+    for (int e = 0; e < 8; ++e) {
+      double y[8], x[8];
+      for (int r = 0; r < 8; ++r) {            // l y = e_e
+        double v = r == e ? 1.0 : 0.0;
+        for (int t = 0; t < r; ++t) v -= l[r][t] * y[t];
+        y[r] = v / l[r][r];
+      }
+      for (int r = 7; r >= 0; --r) {           // l^T x = y
+        double v = y[r];
+        for (int t = r + 1; t < 8; ++t) v -= l[t][r] * x[t];
+        x[r] = v / l[r][r];
+      }
+      for (int r = 0; r < 8; ++r) inv[r][e] = x[r];
+    }
+    if (j == 0) break;
+    double *u = ublk.data() + 32 * j * (j - 1);
+    // U_i,j = H_i,j D_j^-1 for the rows above block j
+    parallel_for(c0, nt > 1 && c0 >= 256 ? nt : 1, [&](int64_t i) {
+      const double *hi = a + i * k + c0;
+      for (int c = 0; c < 8; ++c) {
+        double v = 0.0;
+        for (int t = 0; t < 8; ++t) v += hi[t] * inv[t][c];
+        u[i * 8 + c] = v;
+      }
+    });
+    // Schur complement: a[i][l] -= U_i,j . H_l,j over the block upper part
+    parallel_for(j, nt > 1 && j >= 8 ? nt : 1, [&](int64_t ib) {
+      for (int64_t i = 8 * ib; i < 8 * ib + 8; ++i) {
+        const double *ui = u + i * 8;
+        double *ai = a + i * k;
+        for (int64_t l2 = 8 * ib; l2 < c0; ++l2) {
+          const double *hl = a + l2 * k + c0;
+          double v = 0.0;
+          for (int c = 0; c < 8; ++c) v += ui[c] * hl[c];
+          ai[l2] -= v;
+        }
+      }
+    });
+  }
+  return true;
+}
+
+int encode_impl(const float *w, int64_t n, int64_t k, int32_t bpw,
+                const int8_t *sign_n, const int8_t *sign_k,
+                float scale_in, float *scale_out,
+                uint16_t *idx1_out, void *idx2_out, int32_t nthreads,
+                float *row_scale_out, const double *hessian, double damp) {
   if (!w || !sign_n || !sign_k || !idx1_out) return GLQ_ERR_ARG;
   if (n < 1 || k < 8 || k % 8 != 0) return GLQ_ERR_ARG;
   if (bpw != 2 && bpw != 3 && bpw != 4) return GLQ_ERR_ARG;
   if (bpw > 2 && !idx2_out) return GLQ_ERR_ARG;
   if (!(scale_in <= 0.0f || std::isfinite(scale_in))) return GLQ_ERR_ARG;
   if ((double)n * (double)k > 4.0e9) return GLQ_ERR_UNSUPPORTED;
+  if (hessian && (!std::isfinite(damp) || damp < 0.0)) return GLQ_ERR_ARG;
+  if (hessian && k > kMaxLdlqK) return GLQ_ERR_UNSUPPORTED;
   for (int64_t i = 0; i < n; ++i) if (sign_n[i] != 1 && sign_n[i] != -1) return GLQ_ERR_ARG;
   for (int64_t i = 0; i < k; ++i) if (sign_k[i] != 1 && sign_k[i] != -1) return GLQ_ERR_ARG;
   const int64_t nk = n * k;
   for (int64_t i = 0; i < nk; ++i) if (!std::isfinite(w[i])) return GLQ_ERR_ARG;
+  if (hessian)
+    for (int64_t i = 0; i < k * k; ++i) if (!std::isfinite(hessian[i])) return GLQ_ERR_ARG;
 
   static Searcher S;
   static std::once_flag once;
@@ -273,23 +381,21 @@ extern "C" int glq_encode_ref(const float *w, int64_t n, int64_t k, int32_t bpw,
 
   int nt = nthreads > 0 ? nthreads : (int)std::max(1u, std::thread::hardware_concurrency());
 
-  // W~ = U W V^T in float64: rows get V (over k), then columns get U (over n)
+  // rotated, damped Hessian and its block factorisation (before any output)
+  std::vector<double> ublk;
+  if (hessian) {
+    std::vector<double> ht((size_t)(k * k));
+    rotate_both(hessian, k, k, sign_k, sign_k, nt, ht.data());
+    long double dsum = 0.0L;
+    for (int64_t i = 0; i < k; ++i) dsum += ht[i * k + i];
+    const double add = damp * (double)(dsum / (long double)k);
+    for (int64_t i = 0; i < k; ++i) ht[i * k + i] += add;
+    if (!block_udu(ht.data(), k, nt, ublk)) return GLQ_ERR_ARG;
+  }
+
+  // W~ = U W V^T in float64
   std::vector<double> wt((size_t)nk);
-  parallel_for(n, nt, [&](int64_t r) {
-    double *row = wt.data() + r * k;
-    for (int64_t c = 0; c < k; ++c) row[c] = (double)w[r * k + c];
-    rht_forward(row, k, sign_k);
-  });
-  const int64_t cblk = 64;
-  parallel_for((k + cblk - 1) / cblk, nt, [&](int64_t cb) {
-    std::vector<double> col((size_t)n);
-    int64_t c1 = std::min(k, (cb + 1) * cblk);
-    for (int64_t c = cb * cblk; c < c1; ++c) {
-      for (int64_t r = 0; r < n; ++r) col[r] = wt[r * k + c];
-      rht_forward(col.data(), n, sign_n);
-      for (int64_t r = 0; r < n; ++r) wt[r * k + c] = col[r];
-    }
-  });
+  rotate_both(w, n, k, sign_n, sign_k, nt, wt.data());
 
   // scales: one global s, or one per row (row r divided by srow[r])
   std::vector<float> srow((size_t)n, 1.0f);
@@ -327,20 +433,79 @@ extern "C" int glq_encode_ref(const float *w, int64_t n, int64_t k, int32_t bpw,
   const uint32_t rlimit = bpw == 3 ? 256u : kCodebookSize;
   const double rmul = bpw == 3 ? 2.0 : 4.0;
   const int8_t *cb = S.cb;
-  parallel_for(n, nt, [&](int64_t r) {
+  // Q of one target vector: writes the indices and the exact decoded vector
+  auto quantise = [&](const double *x, int64_t r, int64_t q, double *v) {
+    uint32_t i1 = S.nearest(x, kCodebookSize);
+    idx1_out[r * g + q] = (uint16_t)i1;
+    for (int t = 0; t < 8; ++t) v[t] = 0.5 * cb[8 * i1 + t];
+    if (bpw > 2) {
+      double rr[8];
+      for (int t = 0; t < 8; ++t) rr[t] = (x[t] - v[t]) * rmul;
+      uint32_t i2 = S.nearest(rr, rlimit);
+      if (bpw == 3) ((uint8_t *)idx2_out)[r * g + q] = (uint8_t)i2;
+      else ((uint16_t *)idx2_out)[r * g + q] = (uint16_t)i2;
+      for (int t = 0; t < 8; ++t) v[t] += 0.5 * cb[8 * i2 + t] / rmul;
+    }
+  };
+  if (!hessian) {
+    parallel_for(n, nt, [&](int64_t r) {
+      for (int64_t q = 0; q < g; ++q) {
+        double x[8], v[8];
+        for (int t = 0; t < 8; ++t) x[t] = wt[r * k + 8 * q + t] / (double)srow[r];
+        quantise(x, r, q, v);
+      }
+    });
+    return GLQ_OK;
+  }
+  // LDLQ sweep, rows in tiles of kTile so every U block read serves kTile rows
+  constexpr int64_t kTile = 16;
+  parallel_for((n + kTile - 1) / kTile, nt, [&](int64_t tile) {
+    const int64_t r0 = tile * kTile, nr = std::min(kTile, n - r0);
+    std::vector<double> x((size_t)(kTile * k)), e((size_t)(kTile * k));
+    for (int64_t a = 0; a < nr; ++a)
+      for (int64_t c = 0; c < k; ++c) x[a * k + c] = wt[(r0 + a) * k + c] / (double)srow[r0 + a];
     for (int64_t q = 0; q < g; ++q) {
-      double x[8];
-      for (int t = 0; t < 8; ++t) x[t] = wt[r * k + 8 * q + t] / (double)srow[r];
-      uint32_t i1 = S.nearest(x, kCodebookSize);
-      idx1_out[r * g + q] = (uint16_t)i1;
-      if (bpw > 2) {
-        double rr[8];
-        for (int t = 0; t < 8; ++t) rr[t] = (x[t] - 0.5 * cb[8 * i1 + t]) * rmul;
-        uint32_t i2 = S.nearest(rr, rlimit);
-        if (bpw == 3) ((uint8_t *)idx2_out)[r * g + q] = (uint8_t)i2;
-        else ((uint16_t *)idx2_out)[r * g + q] = (uint16_t)i2;
+      double t[kTile][8];
+      for (int64_t a = 0; a < nr; ++a)
+        for (int c = 0; c < 8; ++c) t[a][c] = 0.0;
+      const double *u = ublk.data() + 32 * q * (q - 1);
+      for (int64_t i = 0; i < 8 * q; ++i) {
+        const double *ui = u + i * 8;
+        for (int64_t a = 0; a < nr; ++a) {
+          const double ei = e[a * k + i];
+          for (int c = 0; c < 8; ++c) t[a][c] += ei * ui[c];
+        }
+      }
+      for (int64_t a = 0; a < nr; ++a) {
+        double tv[8], v[8];
+        for (int c = 0; c < 8; ++c) tv[c] = x[a * k + 8 * q + c] + t[a][c];
+        quantise(tv, r0 + a, q, v);
+        for (int c = 0; c < 8; ++c) e[a * k + 8 * q + c] = x[a * k + 8 * q + c] - v[c];
       }
     }
   });
   return GLQ_OK;
+}
+
+}  // namespace
+}  // namespace glq
+
+extern "C" int glq_encode_ref(const float *w, int64_t n, int64_t k, int32_t bpw,
+                              const int8_t *sign_n, const int8_t *sign_k,
+                              float scale_in, float *scale_out,
+                              uint16_t *idx1_out, void *idx2_out, int32_t nthreads,
+                              float *row_scale_out) {
+  return glq::encode_impl(w, n, k, bpw, sign_n, sign_k, scale_in, scale_out, idx1_out, idx2_out,
+                          nthreads, row_scale_out, nullptr, 0.0);
+}
+
+extern "C" int glq_encode_ldlq(const float *w, int64_t n, int64_t k, int32_t bpw,
+                               const int8_t *sign_n, const int8_t *sign_k,
+                               const double *hessian, double damp,
+                               float scale_in, float *scale_out,
+                               uint16_t *idx1_out, void *idx2_out, int32_t nthreads,
+                               float *row_scale_out) {
+  if (!hessian) return GLQ_ERR_ARG;
+  return glq::encode_impl(w, n, k, bpw, sign_n, sign_k, scale_in, scale_out, idx1_out, idx2_out,
+                          nthreads, row_scale_out, hessian, damp);
 }

@@ -21,7 +21,7 @@ GLQ_F32, GLQ_BF16 = 0, 1
 GLQ_CB_INT8_2X, GLQ_CB_DEVICE = 0, 1
 FLAG_NO_INPUT_RHT, FLAG_NO_OUTPUT_RHT = 1, 2
 
-EXPORTS = ("glq_build_codebook", "glq_encode_ref", "glq_rht_apply", "glq_decode_weights",
+EXPORTS = ("glq_build_codebook", "glq_encode_ref", "glq_encode_ldlq", "glq_rht_apply", "glq_decode_weights",
            "glq_fused_linear_workspace", "glq_fused_linear", "glq_status_string", "glq_last_error",
            "glq_version")
 
@@ -47,6 +47,8 @@ class GlqLayerStruct(ctypes.Structure):
 
 _lib.glq_build_codebook.argtypes = [_i32, _vp, _sz, ctypes.POINTER(_sz)]
 _lib.glq_encode_ref.argtypes = [_vp, _i64, _i64, _i32, _vp, _vp, _f32, ctypes.POINTER(_f32), _vp, _vp, _i32, _vp]
+_lib.glq_encode_ldlq.argtypes = [_vp, _i64, _i64, _i32, _vp, _vp, _vp, ctypes.c_double, _f32,
+                                 ctypes.POINTER(_f32), _vp, _vp, _i32, _vp]
 _lib.glq_rht_apply.argtypes = [_vp, _i32, _vp, _i32, _i64, _i64, _vp, _i32, _vp]
 _lib.glq_decode_weights.argtypes = [ctypes.POINTER(GlqLayerStruct), _vp, _i32, _vp]
 _lib.glq_fused_linear_workspace.argtypes = [ctypes.POINTER(GlqLayerStruct), _i64]
@@ -57,7 +59,7 @@ _lib.glq_status_string.argtypes = [_i32]
 _lib.glq_status_string.restype = ctypes.c_char_p
 _lib.glq_version.restype = _u32
 _lib.glq_last_error.restype = ctypes.c_char_p
-for _name in ("glq_build_codebook", "glq_encode_ref", "glq_rht_apply", "glq_decode_weights",
+for _name in ("glq_build_codebook", "glq_encode_ref", "glq_encode_ldlq", "glq_rht_apply", "glq_decode_weights",
               "glq_fused_linear"):
     getattr(_lib, _name).restype = ctypes.c_int
 
@@ -120,6 +122,32 @@ def encode_ref(w: np.ndarray, bpw: int, sign_n: np.ndarray, sign_k: np.ndarray,
                              ctypes.byref(s), i1.ctypes.data, None if i2 is None else i2.ctypes.data,
                              nthreads, None if rs is None else rs.ctypes.data)
     _check(rc, "glq_encode_ref")
+    return i1, i2, (rs if per_row else np.float32(s.value))
+
+
+def encode_ldlq(w: np.ndarray, bpw: int, sign_n: np.ndarray, sign_k: np.ndarray, hessian: np.ndarray,
+                damp: float = 0.01, scale: float = 0.0, nthreads: int = 0, per_row: bool = False):
+    """CPU encoder with LDLQ error feedback (glq_encode_ldlq); hessian is the
+    float64 [k, k] Hessian over the input features. Returns what encode_ref
+    returns."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    n, k = w.shape
+    h = np.ascontiguousarray(hessian, dtype=np.float64)
+    if h.shape != (k, k):
+        raise ValueError(f"hessian must be [{k}, {k}]")
+    sn = np.ascontiguousarray(sign_n, dtype=np.int8)
+    sk = np.ascontiguousarray(sign_k, dtype=np.int8)
+    i1 = np.empty((n, max(k // 8, 0)), dtype=np.uint16)
+    i2 = None
+    if bpw in (3, 4):
+        i2 = np.empty((n, k // 8), dtype=np.uint8 if bpw == 3 else np.uint16)
+    s = _f32(0.0)
+    rs = np.empty(n, dtype=np.float32) if per_row else None
+    rc = _lib.glq_encode_ldlq(w.ctypes.data, n, k, bpw, sn.ctypes.data, sk.ctypes.data, h.ctypes.data,
+                              float(damp), float(scale), ctypes.byref(s), i1.ctypes.data,
+                              None if i2 is None else i2.ctypes.data, nthreads,
+                              None if rs is None else rs.ctypes.data)
+    _check(rc, "glq_encode_ldlq")
     return i1, i2, (rs if per_row else np.float32(s.value))
 
 

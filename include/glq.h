@@ -28,7 +28,7 @@
  *
  * Conventions for every call:
  *  - All memory is owned and allocated by the caller. No call allocates or
- *    frees memory, device or host (glq_encode_ref allocates host scratch).
+ *    frees memory, device or host (the CPU encoders allocate host scratch).
  *  - Device pointers are HIP device pointers; "host" marks host pointers.
  *  - Every call returns a glq_status. Arguments are validated before any
  *    launch; no error aborts the process or escapes as an exception.
@@ -104,8 +104,8 @@ int glq_build_codebook(int32_t form, void *out, size_t out_bytes, size_t *needed
  * "Bit widths"): W~ = U W V^T in float64, s = fp32(sqrt(mean(W~^2))) unless
  * given, X = W~/s in groups of 8 along k, i1 = nearest codebook entry (float64
  * squared distance, lowest index on ties), and for 3/4 bpw i2 = nearest entry
- * of 2^-k C_r to the residual X - C[i1]. Nearest-neighbour rounding only
- * (the page's LDLQ error feedback needs calibration data and is not done).
+ * of 2^-k C_r to the residual X - C[i1]. Nearest-neighbour rounding of every
+ * group on its own (glq_encode_ldlq adds the page's error feedback).
  *   w          host float [n][k], original (unrotated) basis, finite
  *   sign_n     host int8 [n] (+1/-1),  sign_k  host int8 [k] (+1/-1)
  *   scale_in   > 0: use as s;  <= 0: compute s as above
@@ -125,6 +125,34 @@ int glq_encode_ref(const float *w, int64_t n, int64_t k, int32_t bpw,
                    float scale_in, float *scale_out,
                    uint16_t *idx1_out, void *idx2_out, int32_t nthreads,
                    float *row_scale_out);
+
+/*
+ * glq_encode_ldlq -- CPU encoder with LDLQ error feedback ("glq 0.1.1", "How
+ * it works", item 3: a block LDL decomposition of the Hessian drives a
+ * sequential sweep over 8-weight blocks, each block's quantisation error
+ * corrects the blocks after it, as in GPTQ; item 2: the Hessian is rotated
+ * like the weights). With X = W~/s as in glq_encode_ref:
+ *   H~ = V H V^T + damp * mean(diag(V H V^T)) * I
+ *   H~ = (I + U) D (I + U)^T, U strictly block upper triangular (blocks of 8)
+ *   for j = 0 .. k/8-1, every row:  T_j = X_j + sum_{i<j} (X_i - X^_i) U_ij,
+ *                                   X^_j = Q(T_j)
+ * with Q the nearest-entry / residual quantiser of glq_encode_ref (float64
+ * throughout). Every other argument is as in glq_encode_ref.
+ *   hessian    host double [k][k], symmetric positive semi-definite, over the
+ *              input features in the original basis (e.g. X^T X / m for
+ *              calibration inputs X [m][k]); read only; k <= 16384
+ *   damp       >= 0; GPTQ's dampening fraction (0.01 is its default)
+ * Host scratch of about 1.5 k^2 doubles plus n k doubles is allocated.
+ * Returns GLQ_ERR_ARG as glq_encode_ref does, and also for a NULL or
+ * non-finite Hessian, a negative or non-finite damp, or a damped rotated
+ * Hessian that is not positive definite; GLQ_ERR_UNSUPPORTED for k > 16384.
+ */
+int glq_encode_ldlq(const float *w, int64_t n, int64_t k, int32_t bpw,
+                    const int8_t *sign_n, const int8_t *sign_k,
+                    const double *hessian, double damp,
+                    float scale_in, float *scale_out,
+                    uint16_t *idx1_out, void *idx2_out, int32_t nthreads,
+                    float *row_scale_out);
 
 /*
  * glq_rht_apply -- randomized Hadamard transform along the last axis of a

@@ -140,4 +140,4 @@ def proxy_loss(xhat: np.ndarray, x: np.ndarray, h: np.ndarray) -> float:
     """tr((X^ - X) H (X^ - X)^T), the layer-output error the feedback
     minimises (GPTQ's objective), in the scaled rotated units."""
     e = np.asarray(xhat, dtype=np.float64) - np.asarray(x, dtype=np.float64)
-    return float(np.einsum("ij,jk,ik->", e, h, e))
+    return float(np.sum((e @ np.asarray(h, dtype=np.float64)) * e))

@@ -8,7 +8,7 @@ import re
 import numpy as np
 import pytest
 
-from oracle import e8, glq as og, rht
+from oracle import e8, glq as og, ldlq as ol, rht
 import workloads
 
 glq = pytest.importorskip("dequant_e8_codebook_amd.glq")
@@ -125,6 +125,70 @@ def test_encode_ref_row_scales_match_oracle(bpw):
     assert np.array_equal(a1, b1)
     if bpw > 2:
         assert np.array_equal(a2, b2)
+
+
+def _ldlq_case(n, k, bpw, seed=77, outliers=4):
+    spec = workloads.LayerSpec("t", n, k, bpw, 1, "normal", "f32", "f32", outliers, seed)
+    w = workloads.weights(spec).astype(np.float32)
+    h = ol.hessian_from_inputs(workloads.calibration(spec, 2 * k))
+    return w, workloads.sign_n(spec), workloads.sign_k(spec), h
+
+
+@pytest.mark.parametrize("n,k,bpw,per_row", [(64, 256, 2, False), (40, 192, 3, False), (48, 128, 4, False),
+                                             (33, 128, 3, True), (8, 8, 2, False)])
+def test_encode_ldlq_matches_oracle(n, k, bpw, per_row):
+    # LDLQ error feedback (glq page, "How it works", item 3), readings R17-R19;
+    # k = 192 has Hadamard blocks of 64, k = 8 a single block (no feedback)
+    w, sn, sk, h = _ldlq_case(n, k, bpw)
+    a1, a2, sa = glq.encode_ldlq(w, bpw, sn, sk, h, per_row=per_row, nthreads=3)
+    b1, b2, sb = ol.encode_ldlq(w.astype(np.float64), bpw, sn, sk, h, per_row=per_row)
+    assert np.array_equal(sa, sb)
+    assert np.array_equal(a1, b1)
+    if bpw > 2:
+        assert np.array_equal(a2, b2)
+
+
+def test_encode_ldlq_damping_and_threads():
+    w, sn, sk, h = _ldlq_case(32, 128, 2, seed=5)
+    for damp in (0.0, 0.1):
+        a = glq.encode_ldlq(w, 2, sn, sk, h, damp=damp, nthreads=1)
+        b = glq.encode_ldlq(w, 2, sn, sk, h, damp=damp, nthreads=7)
+        c = ol.encode_ldlq(w.astype(np.float64), 2, sn, sk, h, damp=damp)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[0], c[0])
+
+
+def test_encode_ldlq_identity_hessian_is_plain_encoder():
+    w, sn, sk, _ = _ldlq_case(24, 64, 4)
+    a = glq.encode_ldlq(w, 4, sn, sk, 2.5 * np.eye(64))
+    b = glq.encode_ref(w, 4, sn, sk)
+    assert a[2] == b[2] and np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_encode_ldlq_errors():
+    w, sn, sk, h = _ldlq_case(8, 64, 2)
+    lib = glq.raw()
+    i1 = np.empty((8, 8), np.uint16)
+    s = ctypes.c_float(0)
+
+    def call(hh, damp=0.01):
+        return lib.glq_encode_ldlq(w.ctypes.data, 8, 64, 2, sn.ctypes.data, sk.ctypes.data,
+                                   None if hh is None else hh.ctypes.data, damp, 0.0, ctypes.byref(s),
+                                   i1.ctypes.data, None, 1, None)
+    assert call(np.ascontiguousarray(h)) == glq.GLQ_OK
+    assert call(None) == glq.GLQ_ERR_ARG
+    assert call(np.ascontiguousarray(h), damp=-0.5) == glq.GLQ_ERR_ARG
+    assert call(np.ascontiguousarray(h), damp=float("nan")) == glq.GLQ_ERR_ARG
+    bad = np.ascontiguousarray(h.copy())
+    bad[3, 5] = np.inf
+    assert call(bad) == glq.GLQ_ERR_ARG
+    # not positive definite after damping: -I, and the zero matrix with no damping
+    assert call(np.ascontiguousarray(-np.eye(64))) == glq.GLQ_ERR_ARG
+    assert call(np.zeros((64, 64)), damp=0.0) == glq.GLQ_ERR_ARG
+    # a rank-deficient Hessian is fine once damped
+    v = np.ones((64, 1))
+    assert call(np.ascontiguousarray(v @ v.T)) == glq.GLQ_OK
+    with pytest.raises(ValueError):
+        glq.encode_ldlq(w, 2, sn, sk, np.eye(32))
 
 
 def test_encode_ref_explicit_scale_codebook_exact():

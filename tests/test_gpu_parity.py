@@ -416,3 +416,21 @@ def test_fused_row_scales_oracle_encoded(G, cb):
     y = _run_linear(G, cb, i1, i2, rs, sn, sk, x, "bf16", "f32")
     ref = og.layer_reference(x, i1, i2, 4, rs, sn, sk)
     assert og.relative_error(y, ref) <= TOL_BF16
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("bpw,m", [(2, 1), (3, 64)])
+def test_fused_ldlq_encoded(G, cb, bpw, m):
+    # indices from the oracle's LDLQ encoder (error feedback changes the
+    # indices, not the decode): the fused path still matches the oracle layer
+    from oracle import ldlq as ol
+    n, k = 256, 512
+    spec = workloads.LayerSpec("ldlq", n, k, bpw, m, "student_t", "bf16", "bf16", 4, 6100 + bpw)
+    w = workloads.weights(spec)
+    sn, sk = workloads.sign_n(spec), workloads.sign_k(spec)
+    h = ol.hessian_from_inputs(workloads.calibration(spec, 1024))
+    i1, i2, s = ol.encode_ldlq(w, bpw, sn, sk, h)
+    x = workloads.activations(spec)
+    y = _run_linear(G, cb, i1, i2, s, sn, sk, x, "bf16", "f32")
+    ref = og.layer_reference(x, i1, i2, bpw, s, sn, sk)
+    assert og.relative_error(y, ref) <= TOL_BF16
