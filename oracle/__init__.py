@@ -24,4 +24,4 @@ and collected in DESIGN.md ("Readings"). Parity status of every function
 is listed in the design doc; functions whose result has no independent pin say
 "parity unpinned" in their docstring.
 """
-from . import e8, rht, glq, ldlq  # noqa: F401
+from . import e8, rht, glq, ldlq, entropack  # noqa: F401
