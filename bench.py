@@ -26,6 +26,7 @@ Other modes (profiling helpers, not bench lines):
   --row-scale                                     layers encoded with per-row scales
   --achievable                                    stream-read, copy and bf16 matmul ceilings
   --encoder                                       CPU encoder: plain vs LDLQ time and proxy loss
+  --ep-decode BPP                                 entropy-coded format: decode time at that rate
   --pmc-summary DIR                               turn rocprofv3 counter CSVs into a profile file
 """
 from __future__ import annotations
@@ -404,6 +405,79 @@ def encoder_bench(workload, budget_s):
     print(json.dumps(out))
 
 
+def ep_step_for_rate(w, sn, sk, target_bpp, lane_groups):
+    """Quantiser step whose encoding lands nearest the target actual_bpp
+    (bisection on log(step); the rate falls as the step grows)."""
+    import numpy as np
+    from dequant_e8_codebook_amd import glq
+    n, k = w.shape
+    lo, hi = np.log(0.02), np.log(2.0)
+    best = None
+    for _ in range(14):
+        mid = 0.5 * (lo + hi)
+        try:
+            h = glq.ep_encode(w, sn, sk, float(np.exp(mid)), lane_groups)
+        except glq.GlqError:
+            lo = mid
+            continue
+        bpp = ep_actual_bpp(h)
+        if best is None or abs(bpp - target_bpp) < abs(best[1] - target_bpp):
+            best = (h, bpp)
+        if bpp > target_bpp:
+            lo = mid
+        else:
+            hi = mid
+    return best
+
+
+def ep_actual_bpp(h):
+    """Every stored byte of an entropy-coded layer per weight, times 8."""
+    b = (2 * len(h.words) + 4 * h.states.size + 4 * len(h.offsets) + 40 + 2 * sum(h.model.nsym)
+         + 4 * h.n + 4 + (h.n + 7) // 8 + (h.k + 7) // 8)
+    return 8.0 * b / (h.n * h.k)
+
+
+def ep_decode_bench(workload, target_bpp, lane_groups, launches):
+    """Fused symbol decode + weight reconstruction of the entropy-coded format
+    on the workload's layer shapes: step chosen for the target rate, kernel
+    time from HIP events around back-to-back launches on one stream."""
+    import numpy as np
+    import torch
+    import workloads as wl
+    from dequant_e8_codebook_amd import glq
+    res = []
+    seen = set()
+    for spec in wl.layer_specs(workload):
+        if (spec.n, spec.k) in seen:
+            continue
+        seen.add((spec.n, spec.k))
+        w = wl.weights(spec).astype(np.float32)
+        sn, sk = wl.sign_n(spec), wl.sign_k(spec)
+        h, bpp = ep_step_for_rate(w, sn, sk, target_bpp, lane_groups)
+        L = glq.EpLayer.from_host(h)
+        out = torch.empty((spec.n, spec.k), device="cuda", dtype=torch.bfloat16)
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            for _ in range(5):
+                glq.ep_decode_weights(L, out, stream=s)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            for _ in range(launches):
+                glq.ep_decode_weights(L, out, stream=s)
+            e1.record(s)
+            s.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / launches
+        stored = bpp * spec.n * spec.k / 8.0
+        moved = stored + 2.0 * spec.n * spec.k
+        res.append({"shape": f"{spec.n}x{spec.k}", "step": h.step, "actual_bpp": round(bpp, 4),
+                    "nblocks": h.nblocks, "kernel_us": round(us, 2),
+                    "weights_per_s": round(spec.n * spec.k / (us * 1e-6), 1),
+                    "stored_gbs": round(stored / (us * 1e-6) / 1e9, 1),
+                    "hbm_gbs": round(moved / (us * 1e-6) / 1e9, 1), "hbm_frac": round(moved / (us * 1e-6) / 8e12, 4)})
+    print(json.dumps({"mode": "ep_decode", "workload": workload, "target_bpp": target_bpp,
+                      "lane_groups": lane_groups, "layers": res}))
+
+
 def copy_calibration():
     """A plain device-to-device copy of COPY_BYTES (for counter calibration)."""
     import torch
@@ -479,6 +553,9 @@ def main():
     ap.add_argument("--achievable", action="store_true", help="measure stream-read and bf16 matmul ceilings")
     ap.add_argument("--row-scale", action="store_true", help="encode with per-row scales")
     ap.add_argument("--encoder", action="store_true", help="time the CPU encoders (plain and LDLQ)")
+    ap.add_argument("--ep-decode", type=float, default=0.0, metavar="BPP",
+                    help="time the entropy-coded format's decode at this storage rate")
+    ap.add_argument("--ep-lane-groups", type=int, default=32)
     ap.add_argument("--pmc-summary", nargs=4, metavar=("COPY_FETCH", "COPY_WRITE", "BENCH_FETCH", "BENCH_WRITE"))
     ap.add_argument("--pmc-kernel", default="gemv_bf16")
     ap.add_argument("--pmc-kernel-label", default="gemv_bf16<2>")
@@ -502,6 +579,9 @@ def main():
         return 0
     if args.encoder:
         encoder_bench(args.workload, args.cpu_budget)
+        return 0
+    if args.ep_decode > 0:
+        ep_decode_bench(args.workload, args.ep_decode, args.ep_lane_groups, args.kernel_launches)
         return 0
     out, built = run_bench(args)
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(built, args.cpu_budget)

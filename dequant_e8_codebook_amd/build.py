@@ -19,7 +19,7 @@ LIB = os.path.join(OUT_DIR, "libglq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-HOST_SOURCES = ["glq_codebook.cpp", "glq_encode.cpp"]
+HOST_SOURCES = ["glq_codebook.cpp", "glq_encode.cpp", "glq_ep.cpp"]
 HIP_SOURCES = ["glq_kernels.hip"]
 
 

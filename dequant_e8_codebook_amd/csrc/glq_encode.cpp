@@ -235,25 +235,6 @@ void rht_forward(double *v, int64_t n, const int8_t *sigma) {
   for (int64_t i = 0; i < n; ++i) v[i] *= inv;
 }
 
-template <class F>
-void parallel_for(int64_t count, int nthreads, F fn) {
-  if (nthreads <= 1 || count < 2) {
-    for (int64_t i = 0; i < count; ++i) fn(i);
-    return;
-  }
-  std::atomic<int64_t> next{0};
-  std::vector<std::thread> th;
-  for (int t = 0; t < nthreads; ++t)
-    th.emplace_back([&] {
-      while (true) {
-        int64_t i = next.fetch_add(1);
-        if (i >= count) break;
-        fn(i);
-      }
-    });
-  for (auto &t : th) t.join();
-}
-
 constexpr int64_t kMaxLdlqK = 16384;
 
 // out = U M V^T in float64 for M [rows][cols] (float or double): every row
@@ -488,6 +469,12 @@ int encode_impl(const float *w, int64_t n, int64_t k, int32_t bpw,
 }
 
 }  // namespace
+
+void rotate_weights_f64(const float *w, int64_t n, int64_t k, const int8_t *sign_n,
+                        const int8_t *sign_k, int nthreads, double *out) {
+  rotate_both(w, n, k, sign_n, sign_k, nthreads, out);
+}
+
 }  // namespace glq
 
 extern "C" int glq_encode_ref(const float *w, int64_t n, int64_t k, int32_t bpw,

@@ -1605,6 +1605,169 @@ gemv_f32(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const floa
   }
 }
 
+// ------------------------------------------------ entropy-coded lattice layers
+// Fused symbol decode and weight reconstruction of the entropy-coded E8
+// format ("Transformers Proposes EntroPack Integration ...", first two
+// paragraphs; the format is this library's reading, defined in glq.h).
+// One wave per coded block: lane l holds the rANS state of the block's lane
+// l and all 64 step through their groups' 8 symbols in lockstep. The words a
+// step needs are taken from the block's stream in lane order (ballot, then a
+// prefix count with mbcnt) out of a per-wave ring of 2048 words in LDS. The
+// ring is filled on a fixed schedule: the prologue publishes the first 1024
+// words (from the 8-aligned start) and loads 512 more; every round (8 steps)
+// ends by publishing the loaded 512 and loading the next 512 (16 bytes per
+// lane), so each load has a round to land. The fill position advances by 512
+// per round but stays within 1024 words of the (8-aligned) read position:
+// then the ring holds a round's words (at most 512) before the round starts
+// and never overwrites a word not yet read. Next round's row scale is loaded
+// just before the words, so waiting for it leaves the word load in flight.
+// The five
+// decode tables (slot -> symbol | (frequency - 1) << 8 |
+// (slot - cumulative) << 20, 4096 slots each) are copied to LDS once per
+// workgroup with global-to-LDS loads.
+constexpr uint32_t kEpWaves = 8;
+constexpr uint32_t kEpLutHdr = 64;                    // vmin[5], padded
+constexpr uint32_t kEpLutBytes = 5 * 4096 * 4;        // in LDS at offset 0
+constexpr uint32_t kEpRing = 2048;                    // words per wave
+constexpr uint32_t kEpLds = kEpLutBytes + kEpWaves * kEpRing * 2;
+
+typedef __attribute__((address_space(3))) const uint32_t lds_u32;
+typedef __attribute__((address_space(3))) u32x4_t lds_u128_w;
+__device__ __forceinline__ uint32_t lds32(uint32_t addr) {
+  return *reinterpret_cast<lds_u32 *>(static_cast<uintptr_t>(addr));
+}
+__device__ __forceinline__ void lds_st128(uint32_t addr, uint4 v) {
+  u32x4_t t = {v.x, v.y, v.z, v.w};
+  *reinterpret_cast<lds_u128_w *>(static_cast<uintptr_t>(addr)) = t;
+}
+
+template <bool F32>
+__global__ __launch_bounds__(512) void ep_decode_k(const uint32_t *__restrict__ states,
+                                                   const uint32_t *__restrict__ offsets,
+                                                   const uint16_t *__restrict__ words, uint32_t nwords,
+                                                   const uint8_t *__restrict__ lut,
+                                                   const float *__restrict__ row_scale, float step,
+                                                   uint32_t total_groups, uint32_t gpr, uint32_t lane_groups,
+                                                   uint32_t nblocks, uint32_t k, void *__restrict__ out) {
+  const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (uint32_t r = wave; r < kEpLutBytes / 1024; r += kEpWaves)
+    __builtin_amdgcn_global_load_lds((glb_void_t *)(lut + kEpLutHdr + 1024 * r + 16 * lane),
+                                     (lds_void_t *)(uintptr_t)(1024 * r), 16, 0, 0);
+  const int32_t *vm = reinterpret_cast<const int32_t *>(lut);
+  const int32_t vm0 = vm[0], vm1 = vm[1], vm2 = vm[2], vm3 = vm[3], vm4 = vm[4];
+  tables_landed();
+  __syncthreads();
+  const uint32_t blk = blockIdx.x * kEpWaves + wave;
+  if (blk >= nblocks) return;
+
+  const uint32_t ring = kEpLutBytes + wave * kEpRing * 2;   // this wave's ring (bytes)
+  const uint32_t bg = 64 * lane_groups;
+  const uint32_t g0 = blk * bg;
+  const uint32_t ng = min(bg, total_groups - g0);
+  uint32_t x = states[(size_t)blk * 64 + lane];
+  uint32_t pos = __builtin_amdgcn_readfirstlane(offsets[blk]);   // next word (wave-uniform)
+  // 16-byte loads of 8 words at 8-aligned positions, clamped to the last
+  // 8-aligned start below nwords (the buffer is padded to a multiple of 8
+  // words, at least 8); positions past the stream get stale words, which a
+  // valid stream never reads
+  const uint32_t lastq = nwords > 0 ? ((nwords - 1) & ~7u) : 0u;
+  auto ld8 = [&](uint32_t at) -> uint4 {
+    return *reinterpret_cast<const uint4 *>(words + min(at + 8 * lane, lastq));
+  };
+  // prologue: words [f0, f0 + 1024) published, [f0 + 1024, f0 + 1536) loading
+  uint32_t f = pos & ~7u;                             // fill position of pend
+  lds_st128(ring + ((f + 8 * lane) & (kEpRing - 1)) * 2, ld8(f));
+  lds_st128(ring + ((f + 512 + 8 * lane) & (kEpRing - 1)) * 2, ld8(f + 512));
+  // the start state is waited for here: left to the loop, the wait at the
+  // loop head would also hold every later round on its last store
+  asm volatile("" ::"v"(x));
+  f += 1024;
+  float rs = row_scale[min(g0 + lane, total_groups - 1) / gpr];   // round 0's row scale
+  __builtin_amdgcn_sched_barrier(0);
+  uint4 pend = ld8(f);
+  __builtin_amdgcn_sched_barrier(0);
+
+  const uint32_t rounds = (ng + 63) / 64;
+  for (uint32_t p = 0; p < rounds; ++p) {
+    const uint32_t j = p * 64 + lane;
+    const bool act = j < ng;
+    const uint32_t gi = min(g0 + j, total_groups - 1);
+    int32_t z[8];
+    int32_t b = 0, s7 = 0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint32_t tb = c == 0 ? 0u : (c < 7 ? 1u + (uint32_t)b : 3u + (uint32_t)b);
+      const uint32_t e = lds32(tb * 16384u + (x & 4095u) * 4u);
+      const uint32_t xn = (((e >> 8) & 0xFFFu) + 1u) * (x >> 12) + (e >> 20);
+      const int32_t sym = (int32_t)(e & 0xFFu);
+      x = act ? xn : x;
+      if (c == 0) {
+        z[0] = sym + vm0;
+        b = z[0] & 1;
+        s7 = z[0];
+      } else if (c < 7) {
+        z[c] = 2 * (sym + (b ? vm2 : vm1)) + b;
+        s7 += z[c];
+      } else {
+        z[7] = 4 * (sym + (b ? vm4 : vm3)) + ((-s7) & 3);
+      }
+      const bool need = act && x < 65536u;
+      const uint64_t mask = __ballot(need);
+      const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+      const uint32_t wd = lds16(ring + ((pos + below) & (kEpRing - 1)) * 2);
+      x = need ? ((x << 16) | wd) : x;
+      pos += (uint32_t)__popcll(mask);
+    }
+    // Stores and the row-scale load are issued by every lane (lanes past the
+    // block's end repeat lane 0's store: same bytes, same address), so the
+    // count of vector-memory operations per round is fixed and the next
+    // round waits for its word load alone, not for this round's stores.
+    // Groups are row-major, so group gi's 8 weights start at element 8 gi.
+    const float er = __fmul_rn(step, rs);
+    float v[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[c] = __fmul_rn(er, (float)z[c] * 0.5f);
+    // lane 0 is active in every round: its group is g0 + 64 p, and its values
+    // are read with readlane(., 0), which (unlike readfirstlane) does not
+    // depend on which lanes are enabled where the compiler places it
+    const uint32_t gs = act ? gi : g0 + p * 64;
+    if constexpr (F32) {
+      float u[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float l = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v[c]), 0));
+        u[c] = act ? v[c] : l;
+      }
+      float4 *dst = reinterpret_cast<float4 *>(reinterpret_cast<float *>(out) + (size_t)gs * 8);
+      dst[0] = make_float4(u[0], u[1], u[2], u[3]);
+      dst[1] = make_float4(u[4], u[5], u[6], u[7]);
+    } else {
+      uint32_t h0 = bf16x2_rne(v[0], v[1]), h1 = bf16x2_rne(v[2], v[3]);
+      uint32_t h2 = bf16x2_rne(v[4], v[5]), h3 = bf16x2_rne(v[6], v[7]);
+      const uint32_t l0 = __builtin_amdgcn_readlane((int)h0, 0), l1 = __builtin_amdgcn_readlane((int)h1, 0);
+      const uint32_t l2 = __builtin_amdgcn_readlane((int)h2, 0), l3 = __builtin_amdgcn_readlane((int)h3, 0);
+      h0 = act ? h0 : l0;
+      h1 = act ? h1 : l1;
+      h2 = act ? h2 : l2;
+      h3 = act ? h3 : l3;
+      *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(out) + (size_t)gs * 8) = make_uint4(h0, h1, h2, h3);
+    }
+    // publish the words loaded a round ago; next round's row scale, then
+    // the next 512 words (scheduling barriers keep this order: the word load
+    // must be the youngest vector-memory operation)
+    const uint32_t rsi = min(g0 + j + 64, total_groups - 1) / gpr;
+    const uint32_t fn = min(f + 512, (pos & ~7u) + 1024);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_st128(ring + ((f + 8 * lane) & (kEpRing - 1)) * 2, pend);
+    rs = row_scale[rsi];
+    __builtin_amdgcn_sched_barrier(0);
+    f = fn;
+    pend = ld8(f);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // ---------------------------------------------------------------- host helpers
 thread_local char g_last_error[256] = "";
 
@@ -1977,4 +2140,28 @@ extern "C" int glq_fused_linear(const glq_layer *L, const void *x, glq_dtype x_d
   if (rc) return rc;
   if (out_rht) return launch_rht(z, mm_dt, y, y_dt, m, L->n, L->sign_n, 1, nullptr, st);
   return GLQ_OK;
+}
+
+extern "C" int glq_ep_decode_weights(const glq_ep_layer *L, void *w_out, glq_dtype out_dt, void *hip_stream) {
+  if (!L || !w_out || !valid_dtype(out_dt)) return GLQ_ERR_ARG;
+  if (L->n < 1 || L->k < 8 || L->k % 8 != 0 || L->lane_groups < 1 || L->lane_groups > (1 << 20)) return GLQ_ERR_ARG;
+  if (!(L->step > 0.0f) || !std::isfinite(L->step)) return GLQ_ERR_ARG;
+  if (!L->row_scale || !L->states || !L->offsets || !L->lut) return GLQ_ERR_ARG;
+  if (L->nwords < 0 || L->nwords > 0xFFFFFFF0ll || !L->words) return GLQ_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(w_out) & 15) || (reinterpret_cast<uintptr_t>(L->lut) & 15) ||
+      (reinterpret_cast<uintptr_t>(L->words) & 15))
+    return GLQ_ERR_ARG;
+  if ((double)L->n * (double)L->k / 8.0 >= 2147483648.0) return GLQ_ERR_UNSUPPORTED;
+  const uint32_t total = (uint32_t)(L->n * (L->k / 8));
+  const uint64_t bg = 64ull * (uint64_t)L->lane_groups;
+  const uint32_t nblocks = (uint32_t)((total + bg - 1) / bg);
+  const uint32_t grid = (nblocks + kEpWaves - 1) / kEpWaves;
+  hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+  auto kern = out_dt == GLQ_F32 ? ep_decode_k<true> : ep_decode_k<false>;
+  int rc = allow_lds(kern, kEpLds);
+  if (rc) return rc;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kEpWaves), kEpLds, st, L->states, L->offsets, L->words,
+                     (uint32_t)L->nwords, reinterpret_cast<const uint8_t *>(L->lut), L->row_scale, L->step, total,
+                     (uint32_t)(L->k / 8), (uint32_t)L->lane_groups, nblocks, (uint32_t)L->k, w_out);
+  return hip_status(hipGetLastError());
 }

@@ -23,7 +23,9 @@ FLAG_NO_INPUT_RHT, FLAG_NO_OUTPUT_RHT = 1, 2
 
 EXPORTS = ("glq_build_codebook", "glq_encode_ref", "glq_encode_ldlq", "glq_rht_apply", "glq_decode_weights",
            "glq_fused_linear_workspace", "glq_fused_linear", "glq_status_string", "glq_last_error",
-           "glq_version")
+           "glq_version", "glq_ep_encode", "glq_ep_build_lut", "glq_ep_decode_weights")
+EP_LANES, EP_TABLES, EP_MAX_SYMS = 64, 5, 256
+EP_LUT_BYTES = 64 + EP_TABLES * 4096 * 4
 
 # torch's wheel bundles its own HIP runtime (libamdhip64.so, same soname as
 # /opt/rocm's). Load torch first so libglq.so binds to that one runtime:
@@ -45,6 +47,16 @@ class GlqLayerStruct(ctypes.Structure):
                 ("row_scale", _vp)]
 
 
+class EpModel(ctypes.Structure):
+    _fields_ = [("vmin", ctypes.c_int32 * EP_TABLES), ("nsym", ctypes.c_int32 * EP_TABLES),
+                ("freq", (ctypes.c_uint16 * EP_MAX_SYMS) * EP_TABLES)]
+
+
+class EpLayerStruct(ctypes.Structure):
+    _fields_ = [("n", _i64), ("k", _i64), ("lane_groups", _i32), ("step", _f32), ("row_scale", _vp),
+                ("states", _vp), ("offsets", _vp), ("words", _vp), ("nwords", _i64), ("lut", _vp)]
+
+
 _lib.glq_build_codebook.argtypes = [_i32, _vp, _sz, ctypes.POINTER(_sz)]
 _lib.glq_encode_ref.argtypes = [_vp, _i64, _i64, _i32, _vp, _vp, _f32, ctypes.POINTER(_f32), _vp, _vp, _i32, _vp]
 _lib.glq_encode_ldlq.argtypes = [_vp, _i64, _i64, _i32, _vp, _vp, _vp, ctypes.c_double, _f32,
@@ -55,12 +67,16 @@ _lib.glq_fused_linear_workspace.argtypes = [ctypes.POINTER(GlqLayerStruct), _i64
 _lib.glq_fused_linear_workspace.restype = _sz
 _lib.glq_fused_linear.argtypes = [ctypes.POINTER(GlqLayerStruct), _vp, _i32, _i64, _vp, _i32, _vp, _sz,
                                   _u32, _vp]
+_lib.glq_ep_encode.argtypes = [_vp, _i64, _i64, _vp, _vp, _f32, _i32, _i32, _vp, ctypes.POINTER(EpModel), _vp, _vp,
+                               _vp, _i64, ctypes.POINTER(_i64)]
+_lib.glq_ep_build_lut.argtypes = [ctypes.POINTER(EpModel), _vp, _sz]
+_lib.glq_ep_decode_weights.argtypes = [ctypes.POINTER(EpLayerStruct), _vp, _i32, _vp]
 _lib.glq_status_string.argtypes = [_i32]
 _lib.glq_status_string.restype = ctypes.c_char_p
 _lib.glq_version.restype = _u32
 _lib.glq_last_error.restype = ctypes.c_char_p
 for _name in ("glq_build_codebook", "glq_encode_ref", "glq_encode_ldlq", "glq_rht_apply", "glq_decode_weights",
-              "glq_fused_linear"):
+              "glq_fused_linear", "glq_ep_encode", "glq_ep_build_lut", "glq_ep_decode_weights"):
     getattr(_lib, _name).restype = ctypes.c_int
 
 
@@ -151,6 +167,55 @@ def encode_ldlq(w: np.ndarray, bpw: int, sign_n: np.ndarray, sign_k: np.ndarray,
     return i1, i2, (rs if per_row else np.float32(s.value))
 
 
+@dataclass
+class EpHost:
+    """An entropy-coded layer on the host (glq_ep_encode's outputs)."""
+    n: int
+    k: int
+    lane_groups: int
+    step: float
+    row_scale: np.ndarray      # float32 [n]
+    model: EpModel
+    states: np.ndarray         # uint32 [nblocks, 64]
+    offsets: np.ndarray        # uint32 [nblocks + 1]
+    words: np.ndarray          # uint16 [nwords]
+
+    @property
+    def nblocks(self) -> int:
+        return len(self.offsets) - 1
+
+
+def ep_encode(w: np.ndarray, sign_n: np.ndarray, sign_k: np.ndarray, step: float, lane_groups: int = 32,
+              nthreads: int = 0) -> EpHost:
+    """CPU encoder of the entropy-coded E8 lattice format (glq_ep_encode)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    n, k = w.shape
+    sn = np.ascontiguousarray(sign_n, dtype=np.int8)
+    sk = np.ascontiguousarray(sign_k, dtype=np.int8)
+    total = n * (k // 8)
+    nb = max(0, -(-total // (EP_LANES * lane_groups))) if lane_groups > 0 else 0
+    rs = np.empty(n, dtype=np.float32)
+    model = EpModel()
+    states = np.empty((max(nb, 1), EP_LANES), dtype=np.uint32)
+    offsets = np.empty(nb + 1, dtype=np.uint32)
+    cap = n * k
+    words = np.empty(max(cap, 1), dtype=np.uint16)
+    nw = _i64(0)
+    rc = _lib.glq_ep_encode(w.ctypes.data, n, k, sn.ctypes.data, sk.ctypes.data, float(step), lane_groups,
+                            nthreads, rs.ctypes.data, ctypes.byref(model), states.ctypes.data, offsets.ctypes.data,
+                            words.ctypes.data, cap, ctypes.byref(nw))
+    _check(rc, "glq_ep_encode")
+    return EpHost(n, k, lane_groups, float(np.float32(step)), rs, model, states[:nb].copy(), offsets,
+                  words[:nw.value].copy())
+
+
+def ep_build_lut(model: EpModel) -> np.ndarray:
+    """Decode tables of a model (glq_ep_build_lut), uint8 [EP_LUT_BYTES]."""
+    out = np.zeros(EP_LUT_BYTES, dtype=np.uint8)
+    _check(_lib.glq_ep_build_lut(ctypes.byref(model), out.ctypes.data, out.size), "glq_ep_build_lut")
+    return out
+
+
 # ------------------------------------------------------------------ GPU calls
 
 def _torch():
@@ -228,6 +293,50 @@ class Layer:
         sk = None if sign_k is None else torch.from_numpy(np.ascontiguousarray(sign_k, np.int8)).to(device)
         sn = None if sign_n is None else torch.from_numpy(np.ascontiguousarray(sign_n, np.int8)).to(device)
         return Layer(n, 8 * g, bpw, float(scale), t1, t2, sk, sn, cb, rs)
+
+
+@dataclass
+class EpLayer:
+    """Device tensors of one entropy-coded layer, and its glq_ep_layer struct."""
+    n: int
+    k: int
+    lane_groups: int
+    step: float
+    row_scale: object           # torch float32 [n]
+    states: object              # torch int32 [nblocks, 64] (uint32 bits)
+    offsets: object             # torch int32 [nblocks + 1] (uint32 bits)
+    words: object               # torch int16, nwords rounded up to 8 (>= 8), 16-byte aligned (uint16 bits)
+    nwords: int
+    lut: object                 # torch uint8 [EP_LUT_BYTES]
+
+    def struct(self) -> EpLayerStruct:
+        st = self.__dict__.get("_st")
+        if st is None:
+            st = EpLayerStruct(self.n, self.k, self.lane_groups, float(self.step), self.row_scale.data_ptr(),
+                               self.states.data_ptr(), self.offsets.data_ptr(), self.words.data_ptr(), self.nwords,
+                               self.lut.data_ptr())
+            self.__dict__["_st"] = st
+        return st
+
+    @staticmethod
+    def from_host(h: EpHost, device="cuda") -> "EpLayer":
+        torch = _torch()
+
+        def dev(a):
+            return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+        words = np.zeros(max(8, (len(h.words) + 7) // 8 * 8), np.uint16)    # 16-byte reads
+        words[:len(h.words)] = h.words
+        return EpLayer(h.n, h.k, h.lane_groups, h.step, dev(h.row_scale.astype(np.float32)),
+                       dev(h.states.view(np.int32)), dev(h.offsets.view(np.int32)), dev(words.view(np.int16)),
+                       len(h.words), dev(ep_build_lut(h.model)))
+
+
+def ep_decode_weights(layer: EpLayer, out, stream=None):
+    """Fused symbol decode + weight reconstruction (glq_ep_decode_weights)."""
+    st = layer.struct()
+    _check(_lib.glq_ep_decode_weights(ctypes.byref(st), out.data_ptr(), _dtype_code(out), _stream_ptr(stream)),
+           "glq_ep_decode_weights")
+    return out
 
 
 def rht_apply(inp, out, signs, transpose: bool, stream=None):

@@ -205,6 +205,100 @@ int glq_fused_linear(const glq_layer *L, const void *x, glq_dtype x_dt, int64_t 
                      void *y, glq_dtype y_dt, void *workspace, size_t ws_bytes,
                      uint32_t flags, void *hip_stream);
 
+/* ------------------------------------------------------------------------
+ * Entropy-coded E8 lattice layers ("Transformers Proposes EntroPack
+ * Integration ...", first two paragraphs: per-row normalised E8 lattice
+ * quantisation, a conditional probability model and entropy coding give any
+ * non-integer average storage rate; the coded coordinates are cut into
+ * independently decodable blocks; the GPU decodes the symbols and rebuilds
+ * the weights in one fused step; actual_bpp counts metadata). The page gives
+ * no formulas; the format below is this library's reading of it.
+ *
+ *  quantiser   s_r = fp32(sqrt(mean_j W~[r,j]^2)) per row (W~ = U W V^T as in
+ *              glq_encode_ref), z = 2 * (nearest point of the whole E8
+ *              lattice to (W~[r] / s_r) / step), one 8-vector per group of 8
+ *              inputs. Decoded weight fl32(fl32(step * s_r) * (z / 2)); bf16 =
+ *              round to nearest even of it.
+ *  symbols     per group: z_1 (table 0; b = z_1 mod 2), (z_c - b)/2 for
+ *              c = 2..7 (table 1 + b), (z_8 - t)/4 with t = -(z_1+..+z_7) mod 4
+ *              (table 3 + b). Static per-layer frequencies, 12-bit precision.
+ *  coder       rANS, 32-bit state in [2^16, 2^32), 16-bit words.
+ *  blocks      groups in row-major order (row r, group q), 64 * lane_groups
+ *              per block (the last may be short); group j of a block belongs to
+ *              lane j mod 64; the 64 lanes decode in lockstep and take the
+ *              words of one step from the block's stream in lane order.
+ * ---------------------------------------------------------------------- */
+#define GLQ_EP_LANES 64
+#define GLQ_EP_TABLES 5
+#define GLQ_EP_MAX_SYMS 256
+#define GLQ_EP_LUT_BYTES (64 + GLQ_EP_TABLES * 4096 * 4)
+
+/* The probability model: per table the value of symbol 0, the span of
+ * values (0 = table unused) and the frequencies (sum 4096 when used). */
+typedef struct {
+    int32_t vmin[GLQ_EP_TABLES];
+    int32_t nsym[GLQ_EP_TABLES];
+    uint16_t freq[GLQ_EP_TABLES][GLQ_EP_MAX_SYMS];
+} glq_ep_model;
+
+/* One coded layer on the device. nblocks = ceil(n k / 8 / (64 lane_groups)). */
+typedef struct {
+    int64_t n, k;                /* out, in features; k % 8 == 0; n k / 8 < 2^31 */
+    int32_t lane_groups;         /* groups per lane, >= 1 */
+    float   step;                /* quantiser step (> 0) */
+    const float    *row_scale;   /* device float [n]: s_r */
+    const uint32_t *states;      /* device [nblocks][64]: rANS start state of every lane */
+    const uint32_t *offsets;     /* device [nblocks + 1]: first word of each block's stream */
+    const uint16_t *words;       /* device, 16-byte aligned, [nwords rounded up to a multiple of 8, at least 8] */
+    int64_t nwords;              /* offsets[nblocks] */
+    const void     *lut;         /* device, GLQ_EP_LUT_BYTES from glq_ep_build_lut */
+} glq_ep_layer;
+
+/*
+ * glq_ep_encode -- CPU encoder of the format above (float64 arithmetic; the
+ * nearest lattice point by Conway & Sloane's decoder: coordinates rounded half
+ * to even, the parity fixed on the first coordinate with the largest
+ * rounding error, the integer coset kept on equal distances).
+ *   w, sign_n, sign_k   as in glq_encode_ref
+ *   step                > 0, finite: the rate control (smaller = more bits)
+ *   lane_groups         >= 1 (32 keeps the per-lane state near 2% of the stream
+ *                       at 3-4 bits per weight)
+ *   row_scale_out       host float [n]
+ *   model_out           host
+ *   states_out          host uint32 [nblocks][64]
+ *   offsets_out         host uint32 [nblocks + 1]
+ *   words_out           host uint16 [words_capacity]; n k words always suffice
+ *   words_written       host, receives the number of words
+ * Returns GLQ_ERR_ARG for bad arguments, GLQ_ERR_UNSUPPORTED when a table
+ * would span more than 256 values (step too small for the weights) or
+ * n k / 8 >= 2^31, GLQ_ERR_WORKSPACE when words_capacity is too small
+ * (*words_written then holds the number needed).
+ */
+int glq_ep_encode(const float *w, int64_t n, int64_t k, const int8_t *sign_n, const int8_t *sign_k,
+                  float step, int32_t lane_groups, int32_t nthreads,
+                  float *row_scale_out, glq_ep_model *model_out, uint32_t *states_out,
+                  uint32_t *offsets_out, uint16_t *words_out, int64_t words_capacity,
+                  int64_t *words_written);
+
+/*
+ * glq_ep_build_lut -- CPU: the decode table blob of a model (GLQ_EP_LUT_BYTES;
+ * copy it to device memory unchanged): the five vmin values, then per table
+ * 4096 slots, slot -> (symbol, frequency, slot - cumulative frequency).
+ * Returns GLQ_ERR_ARG for a model whose used tables do not sum to 4096 or a
+ * buffer smaller than GLQ_EP_LUT_BYTES.
+ */
+int glq_ep_build_lut(const glq_ep_model *model, void *lut_out, size_t lut_bytes);
+
+/*
+ * glq_ep_decode_weights -- GPU: fused symbol decode and weight reconstruction
+ * of every group, w_out [n][k] row-major in the rotated basis, bf16 or float32
+ * (16-byte aligned). One wave per block. The words buffer is read 16 bytes at
+ * a time: it must be 16-byte aligned and hold nwords entries rounded up to a
+ * multiple of 8 (at least 8); reads are clamped to it, so a corrupt stream
+ * gives wrong weights, never an access outside the buffers.
+ */
+int glq_ep_decode_weights(const glq_ep_layer *L, void *w_out, glq_dtype out_dt, void *hip_stream);
+
 /* Static text for a status code. */
 const char *glq_status_string(int status);
 

@@ -54,7 +54,8 @@ def _apply_h(v: np.ndarray, b: int) -> np.ndarray:
     n = shp[-1]
     blocks = v.reshape(-1, n // b, b)
     if b <= DENSE_MAX:
-        out = blocks @ hadamard(b)          # H symmetric: row-vector form
+        # H symmetric: row-vector form, every block one row of a single product
+        out = blocks.reshape(-1, b) @ hadamard(b)
     else:
         b2 = DENSE_MAX
         b1 = b // b2

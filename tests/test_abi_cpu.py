@@ -259,3 +259,98 @@ def test_gpu_entry_points_validate_before_launch():
     big = glq.GlqLayerStruct(16, 65536 * 2, 2, 0, 1.0, 1, 0, 1, 1, 1)                          # Hadamard block 131072
     nb = lib.glq_fused_linear_workspace(ctypes.byref(big), 1)
     assert lib.glq_fused_linear(ctypes.byref(big), 1, 0, 1, 1, 0, 256, nb, 0, None) == glq.GLQ_ERR_UNSUPPORTED
+
+
+# ------------------------------------------------ entropy-coded lattice format
+
+def _ep_case(n, k, seed, dist="student_t"):
+    spec = workloads.LayerSpec("ep", n, k, 2, 1, dist, "f32", "f32", 0, seed)
+    return workloads.weights(spec).astype(np.float32), workloads.sign_n(spec), workloads.sign_k(spec)
+
+
+@pytest.mark.parametrize("n,k,step,lane_groups", [(8, 64, 0.4, 1), (13, 96, 0.25, 3), (32, 256, 0.15, 8),
+                                                  (5, 8, 0.3, 2), (64, 512, 0.2, 32), (48, 192, 0.7, 4)])
+def test_ep_encode_matches_oracle(n, k, step, lane_groups):
+    # EntroPack news item (readings R20-R24): the library's stream is the
+    # oracle's, byte for byte
+    from oracle import entropack as oep
+    w, sn, sk = _ep_case(n, k, n * k + 1)
+    h = glq.ep_encode(w, sn, sk, step, lane_groups, nthreads=3)
+    o = oep.encode(w.astype(np.float64), sn, sk, step, lane_groups)
+    assert np.array_equal(h.row_scale, o.row_scale)
+    for t in range(5):
+        assert h.model.nsym[t] == len(o.model.freq[t])
+        if h.model.nsym[t]:
+            assert h.model.vmin[t] == o.model.vmin[t]
+            assert list(h.model.freq[t][:h.model.nsym[t]]) == list(o.model.freq[t])
+    assert np.array_equal(h.states, o.states)
+    assert np.array_equal(h.offsets, o.offsets)
+    assert np.array_equal(h.words, o.words)
+
+
+def test_ep_lut_matches_model():
+    from oracle import entropack as oep
+    w, sn, sk = _ep_case(32, 256, 5)
+    h = glq.ep_encode(w, sn, sk, 0.2, 4)
+    lut = glq.ep_build_lut(h.model)
+    assert np.array_equal(lut[:20].view(np.int32), np.array(h.model.vmin))
+    ent = lut[64:].view(np.uint32).reshape(5, 4096)
+    for t in range(5):
+        ns = h.model.nsym[t]
+        if ns == 0:
+            continue
+        f = np.array(h.model.freq[t][:ns], dtype=np.int64)
+        cum = np.concatenate([[0], np.cumsum(f)[:-1]])
+        slot = np.arange(4096)
+        s = np.searchsorted(cum, slot, side="right") - 1
+        assert np.array_equal(ent[t] & 0xFF, s)
+        assert np.array_equal(((ent[t] >> 8) & 0xFFF) + 1, f[s])
+        assert np.array_equal(ent[t] >> 20, slot - cum[s])
+    bad = glq.EpModel()
+    bad.nsym[0] = 2
+    bad.freq[0][0] = 5
+    with pytest.raises(glq.GlqError):
+        glq.ep_build_lut(bad)
+
+
+def test_ep_encode_errors():
+    w, sn, sk = _ep_case(8, 64, 3)
+    with pytest.raises(glq.GlqError) as e:
+        glq.ep_encode(w, sn, sk, 0.0)
+    assert e.value.status == glq.GLQ_ERR_ARG
+    with pytest.raises(glq.GlqError) as e:
+        glq.ep_encode(w, sn, sk, float("nan"))
+    assert e.value.status == glq.GLQ_ERR_ARG
+    with pytest.raises(glq.GlqError) as e:
+        glq.ep_encode(w, sn, sk, 0.003)              # a table would span more than 256 values
+    assert e.value.status == glq.GLQ_ERR_UNSUPPORTED
+    with pytest.raises(glq.GlqError) as e:
+        glq.ep_encode(w, sn, sk, 0.3, lane_groups=0)
+    assert e.value.status == glq.GLQ_ERR_ARG
+    # too small a word buffer: GLQ_ERR_WORKSPACE and the count needed
+    lib = glq.raw()
+    rs = np.empty(8, np.float32)
+    model = glq.EpModel()
+    states = np.empty((1, 64), np.uint32)
+    offs = np.empty(2, np.uint32)
+    words = np.empty(4, np.uint16)
+    nw = ctypes.c_int64(0)
+    rc = lib.glq_ep_encode(w.ctypes.data, 8, 64, sn.ctypes.data, sk.ctypes.data, 0.2, 1, 1, rs.ctypes.data,
+                           ctypes.byref(model), states.ctypes.data, offs.ctypes.data, words.ctypes.data, 4,
+                           ctypes.byref(nw))
+    assert rc == glq.GLQ_ERR_WORKSPACE and nw.value > 4
+    assert glq.ep_encode(w, sn, sk, 0.2, 1).words.size == nw.value
+
+
+def test_ep_decode_validation_before_launch():
+    lib = glq.raw()
+    st = glq.EpLayerStruct(8, 64, 1, 0.5, 16, 16, 16, 16, 4, 16)
+    assert lib.glq_ep_decode_weights(None, ctypes.c_void_p(16), glq.GLQ_BF16, None) == glq.GLQ_ERR_ARG
+    assert lib.glq_ep_decode_weights(ctypes.byref(st), None, glq.GLQ_BF16, None) == glq.GLQ_ERR_ARG
+    assert lib.glq_ep_decode_weights(ctypes.byref(st), ctypes.c_void_p(16), 7, None) == glq.GLQ_ERR_ARG
+    assert lib.glq_ep_decode_weights(ctypes.byref(st), ctypes.c_void_p(24), glq.GLQ_BF16, None) == glq.GLQ_ERR_ARG
+    for field, val in (("k", 12), ("lane_groups", 0), ("step", 0.0), ("row_scale", None), ("nwords", -1),
+                       ("lut", 8)):
+        bad = glq.EpLayerStruct(8, 64, 1, 0.5, 16, 16, 16, 16, 4, 16)
+        setattr(bad, field, val)
+        assert lib.glq_ep_decode_weights(ctypes.byref(bad), ctypes.c_void_p(16), glq.GLQ_BF16, None) == glq.GLQ_ERR_ARG

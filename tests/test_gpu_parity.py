@@ -434,3 +434,88 @@ def test_fused_ldlq_encoded(G, cb, bpw, m):
     y = _run_linear(G, cb, i1, i2, s, sn, sk, x, "bf16", "f32")
     ref = og.layer_reference(x, i1, i2, bpw, s, sn, sk)
     assert og.relative_error(y, ref) <= TOL_BF16
+
+
+# ------------------------------------------- entropy-coded lattice layers ----
+
+def _ep_weights(n, k, seed, dist="student_t"):
+    spec = workloads.LayerSpec("ep", n, k, 2, 1, dist, "f32", "f32", 0, seed)
+    return workloads.weights(spec).astype(np.float32), workloads.sign_n(spec), workloads.sign_k(spec)
+
+
+def _ep_decode(G, layer, dt):
+    out = torch.empty((layer.n, layer.k), device="cuda", dtype=dt)
+    G.ep_decode_weights(layer, out)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("n,k,step,lane_groups", [(8, 64, 0.4, 1), (13, 96, 0.25, 3), (5, 8, 0.3, 2),
+                                                  (64, 512, 0.2, 32), (100, 1032, 0.12, 5)])
+def test_ep_decode_oracle_stream_bitexact(G, n, k, step, lane_groups):
+    # the oracle's own stream (EntroPack readings R20-R23), decoded on the GPU,
+    # gives the oracle's weights bit for bit
+    from oracle import entropack as oep
+    w, sn, sk = _ep_weights(n, k, 7 * n + k)
+    o = oep.encode(w.astype(np.float64), sn, sk, step, lane_groups)
+    h = G.EpHost(n, k, lane_groups, float(o.step), o.row_scale, G.EpModel(), o.states, o.offsets, o.words)
+    for t in range(5):
+        h.model.nsym[t] = len(o.model.freq[t])
+        h.model.vmin[t] = int(o.model.vmin[t])
+        for s_, f in enumerate(o.model.freq[t]):
+            h.model.freq[t][s_] = int(f)
+    L = G.EpLayer.from_host(h)
+    z, s = oep.quantise_lattice(w.astype(np.float64), sn, sk, step)
+    ref = oep.weights_f32(z, s, step)
+    assert np.array_equal(_bits(_ep_decode(G, L, torch.float32)), ref.view(np.uint32))
+    assert np.array_equal(_bits(_ep_decode(G, L, torch.bfloat16)), og.f32_to_bf16_bits(ref))
+
+
+@pytest.mark.parametrize("n,k,step,lane_groups", [(256, 4096, 0.19, 32), (3072, 1024, 0.3, 7), (1, 8, 0.5, 1)])
+def test_ep_decode_library_stream_lossless(G, n, k, step, lane_groups):
+    # row scales 1 and step 2 make the float32 output z itself: the lattice
+    # points come back exactly as the oracle's quantiser chose them
+    from oracle import entropack as oep
+    w, sn, sk = _ep_weights(n, k, n + k)
+    h = G.ep_encode(w, sn, sk, step, lane_groups)
+    L = G.EpLayer.from_host(h)
+    L.row_scale.fill_(1.0)
+    L.step = 2.0
+    out = _ep_decode(G, L, torch.float32).cpu().numpy()
+    z, s = oep.quantise_lattice(w.astype(np.float64), sn, sk, step)
+    assert np.array_equal(out, z.reshape(n, k).astype(np.float32))
+    assert np.array_equal(h.row_scale, s)
+
+
+@pytest.mark.parametrize("shape,step", [((4096, 4096), 0.25), ((12288, 3072), 0.35)])
+def test_ep_decode_full_size(G, shape, step):
+    # full-size layers: every weight against the oracle's quantiser
+    from oracle import entropack as oep
+    n, k = shape
+    w, sn, sk = _ep_weights(n, k, 7000 + n)
+    h = G.ep_encode(w, sn, sk, step, 32)
+    L = G.EpLayer.from_host(h)
+    got = _bits(_ep_decode(G, L, torch.bfloat16))
+    z, s = oep.quantise_lattice(w.astype(np.float64), sn, sk, step)
+    assert np.array_equal(got, og.f32_to_bf16_bits(oep.weights_f32(z, s, step)))
+
+
+def test_ep_decode_graph_replays(G):
+    # several replays of a captured decode, each equal to the eager result
+    w, sn, sk = _ep_weights(512, 2048, 99)
+    L = G.EpLayer.from_host(G.ep_encode(w, sn, sk, 0.22, 16))
+    ref = _ep_decode(G, L, torch.bfloat16)
+    out = torch.empty_like(ref)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        G.ep_decode_weights(L, out, stream=s)
+        s.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            G.ep_decode_weights(L, out, stream=s)
+    for _ in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
