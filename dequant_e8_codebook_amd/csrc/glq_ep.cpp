@@ -11,8 +11,8 @@
 //    of x - 1/2, keep the nearer coset).
 //  - 8 symbols per group under 5 tables: z_1; (z_c - b)/2 given the coset b;
 //    (z_8 - t)/4 with t the residue the even-sum rule leaves.
-//  - static frequencies per table, 12-bit precision: each seen symbol gets
-//    1 + floor(c (4096 - nz) / N); the rest go one each to the largest
+//  - static frequencies per table, 11-bit precision: each seen symbol gets
+//    1 + floor(c (2048 - nz) / N); the rest go one each to the largest
 //    remainders, ties to the smaller value.
 //  - range ANS (J. Duda, "Asymmetric numeral systems", 2013): 32-bit state
 //    in [2^16, 2^32), 16-bit words; a block's 64 lanes are coded so that a
@@ -34,7 +34,7 @@ namespace {
 constexpr int kLanes = GLQ_EP_LANES;
 constexpr int kTables = GLQ_EP_TABLES;
 constexpr int kMaxSyms = GLQ_EP_MAX_SYMS;
-constexpr uint32_t kPrecBits = 12;
+constexpr uint32_t kPrecBits = 11;
 constexpr uint32_t kM = 1u << kPrecBits;
 constexpr uint32_t kL = 1u << 16;
 
@@ -211,7 +211,7 @@ extern "C" int glq_ep_encode(const float *w, int64_t n, int64_t k, const int8_t 
           const int s = (int)(vals[i] - lo[t]);
           const uint32_t f = model_out->freq[t][s];
           uint32_t xs = x[l];
-          if ((uint64_t)xs >= ((uint64_t)f << 20)) {   // at most one word: then xs < 2^16 <= f 2^20
+          if ((uint64_t)xs >= ((uint64_t)f << (32 - kPrecBits))) {   // at most one word: then xs < 2^16
             o.push_back((uint16_t)(xs & 0xFFFFu));
             xs >>= 16;
           }

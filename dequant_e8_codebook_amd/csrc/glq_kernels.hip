@@ -1623,11 +1623,11 @@ gemv_f32(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const floa
 // just before the words, so waiting for it leaves the word load in flight.
 // The five
 // decode tables (slot -> symbol | (frequency - 1) << 8 |
-// (slot - cumulative) << 20, 4096 slots each) are copied to LDS once per
+// (slot - cumulative) << 20, 2048 slots each) are copied to LDS once per
 // workgroup with global-to-LDS loads.
 constexpr uint32_t kEpWaves = 8;
 constexpr uint32_t kEpLutHdr = 64;                    // vmin[5], padded
-constexpr uint32_t kEpLutBytes = 5 * 4096 * 4;        // in LDS at offset 0
+constexpr uint32_t kEpLutBytes = 5 * 2048 * 4;        // in LDS at offset 0
 constexpr uint32_t kEpRing = 2048;                    // words per wave
 constexpr uint32_t kEpLds = kEpLutBytes + kEpWaves * kEpRing * 2;
 
@@ -1697,8 +1697,8 @@ __global__ __launch_bounds__(512) void ep_decode_k(const uint32_t *__restrict__ 
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const uint32_t tb = c == 0 ? 0u : (c < 7 ? 1u + (uint32_t)b : 3u + (uint32_t)b);
-      const uint32_t e = lds32(tb * 16384u + (x & 4095u) * 4u);
-      const uint32_t xn = (((e >> 8) & 0xFFFu) + 1u) * (x >> 12) + (e >> 20);
+      const uint32_t e = lds32(tb * 8192u + (x & 2047u) * 4u);
+      const uint32_t xn = (((e >> 8) & 0xFFFu) + 1u) * (x >> 11) + (e >> 20);
       const int32_t sym = (int32_t)(e & 0xFFu);
       x = act ? xn : x;
       if (c == 0) {

@@ -25,7 +25,7 @@ EXPORTS = ("glq_build_codebook", "glq_encode_ref", "glq_encode_ldlq", "glq_rht_a
            "glq_fused_linear_workspace", "glq_fused_linear", "glq_status_string", "glq_last_error",
            "glq_version", "glq_ep_encode", "glq_ep_build_lut", "glq_ep_decode_weights")
 EP_LANES, EP_TABLES, EP_MAX_SYMS = 64, 5, 256
-EP_LUT_BYTES = 64 + EP_TABLES * 4096 * 4
+EP_LUT_BYTES = 64 + EP_TABLES * 2048 * 4
 
 # torch's wheel bundles its own HIP runtime (libamdhip64.so, same soname as
 # /opt/rocm's). Load torch first so libglq.so binds to that one runtime:

@@ -221,7 +221,7 @@ int glq_fused_linear(const glq_layer *L, const void *x, glq_dtype x_dt, int64_t 
  *              round to nearest even of it.
  *  symbols     per group: z_1 (table 0; b = z_1 mod 2), (z_c - b)/2 for
  *              c = 2..7 (table 1 + b), (z_8 - t)/4 with t = -(z_1+..+z_7) mod 4
- *              (table 3 + b). Static per-layer frequencies, 12-bit precision.
+ *              (table 3 + b). Static per-layer frequencies, 11-bit precision.
  *  coder       rANS, 32-bit state in [2^16, 2^32), 16-bit words.
  *  blocks      groups in row-major order (row r, group q), 64 * lane_groups
  *              per block (the last may be short); group j of a block belongs to
@@ -231,10 +231,10 @@ int glq_fused_linear(const glq_layer *L, const void *x, glq_dtype x_dt, int64_t 
 #define GLQ_EP_LANES 64
 #define GLQ_EP_TABLES 5
 #define GLQ_EP_MAX_SYMS 256
-#define GLQ_EP_LUT_BYTES (64 + GLQ_EP_TABLES * 4096 * 4)
+#define GLQ_EP_LUT_BYTES (64 + GLQ_EP_TABLES * 2048 * 4)
 
 /* The probability model: per table the value of symbol 0, the span of
- * values (0 = table unused) and the frequencies (sum 4096 when used). */
+ * values (0 = table unused) and the frequencies (sum 2048 when used). */
 typedef struct {
     int32_t vmin[GLQ_EP_TABLES];
     int32_t nsym[GLQ_EP_TABLES];
@@ -283,8 +283,8 @@ int glq_ep_encode(const float *w, int64_t n, int64_t k, const int8_t *sign_n, co
 /*
  * glq_ep_build_lut -- CPU: the decode table blob of a model (GLQ_EP_LUT_BYTES;
  * copy it to device memory unchanged): the five vmin values, then per table
- * 4096 slots, slot -> (symbol, frequency, slot - cumulative frequency).
- * Returns GLQ_ERR_ARG for a model whose used tables do not sum to 4096 or a
+ * 2048 slots, slot -> (symbol, frequency, slot - cumulative frequency).
+ * Returns GLQ_ERR_ARG for a model whose used tables do not sum to 2048 or a
  * buffer smaller than GLQ_EP_LUT_BYTES.
  */
 int glq_ep_build_lut(const glq_ep_model *model, void *lut_out, size_t lut_bytes);

@@ -294,14 +294,14 @@ def test_ep_lut_matches_model():
     h = glq.ep_encode(w, sn, sk, 0.2, 4)
     lut = glq.ep_build_lut(h.model)
     assert np.array_equal(lut[:20].view(np.int32), np.array(h.model.vmin))
-    ent = lut[64:].view(np.uint32).reshape(5, 4096)
+    ent = lut[64:].view(np.uint32).reshape(5, 2048)
     for t in range(5):
         ns = h.model.nsym[t]
         if ns == 0:
             continue
         f = np.array(h.model.freq[t][:ns], dtype=np.int64)
         cum = np.concatenate([[0], np.cumsum(f)[:-1]])
-        slot = np.arange(4096)
+        slot = np.arange(2048)
         s = np.searchsorted(cum, slot, side="right") - 1
         assert np.array_equal(ent[t] & 0xFF, s)
         assert np.array_equal(((ent[t] >> 8) & 0xFFF) + 1, f[s])
