@@ -254,7 +254,7 @@ extern "C" int glq_ep_build_lut(const glq_ep_model *model, void *lut_out, size_t
     for (int s = 0; s < model->nsym[t]; ++s) {
       const uint32_t f = model->freq[t][s];
       for (uint32_t u = 0; u < f; ++u)
-        lut[t * kM + c + u] = (uint32_t)s | ((f - 1u) << 8) | (u << 20);
+        lut[t * kM + c + u] = (uint32_t)s | (f << 8) | (u << 20);
       c += f;
     }
   }

@@ -1622,8 +1622,8 @@ gemv_f32(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const floa
 // and never overwrites a word not yet read. Next round's row scale is loaded
 // just before the words, so waiting for it leaves the word load in flight.
 // The five
-// decode tables (slot -> symbol | (frequency - 1) << 8 |
-// (slot - cumulative) << 20, 2048 slots each) are copied to LDS once per
+// decode tables (slot -> symbol | frequency << 8 | (slot - cumulative) << 20,
+// 2048 slots each) are copied to LDS once per
 // workgroup with global-to-LDS loads.
 constexpr uint32_t kEpWaves = 8;
 constexpr uint32_t kEpLutHdr = 64;                    // vmin[5], padded
@@ -1698,9 +1698,10 @@ __global__ __launch_bounds__(512) void ep_decode_k(const uint32_t *__restrict__ 
     for (int c = 0; c < 8; ++c) {
       const uint32_t tb = c == 0 ? 0u : (c < 7 ? 1u + (uint32_t)b : 3u + (uint32_t)b);
       const uint32_t e = lds32(tb * 8192u + (x & 2047u) * 4u);
-      const uint32_t xn = (((e >> 8) & 0xFFFu) + 1u) * (x >> 11) + (e >> 20);
+      // lanes past the block's end decode garbage: they read no words and
+      // their values are never stored
+      x = ((e >> 8) & 0xFFFu) * (x >> 11) + (e >> 20);
       const int32_t sym = (int32_t)(e & 0xFFu);
-      x = act ? xn : x;
       if (c == 0) {
         z[0] = sym + vm0;
         b = z[0] & 1;
@@ -1712,7 +1713,7 @@ __global__ __launch_bounds__(512) void ep_decode_k(const uint32_t *__restrict__ 
         z[7] = 4 * (sym + (b ? vm4 : vm3)) + ((-s7) & 3);
       }
       const bool need = act && x < 65536u;
-      const uint64_t mask = __ballot(need);
+      const uint64_t mask = __builtin_amdgcn_ballot_w64(need);
       const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
       const uint32_t wd = lds16(ring + ((pos + below) & (kEpRing - 1)) * 2);

@@ -283,7 +283,7 @@ int glq_ep_encode(const float *w, int64_t n, int64_t k, const int8_t *sign_n, co
 /*
  * glq_ep_build_lut -- CPU: the decode table blob of a model (GLQ_EP_LUT_BYTES;
  * copy it to device memory unchanged): the five vmin values, then per table
- * 2048 slots, slot -> (symbol, frequency, slot - cumulative frequency).
+ * 2048 slots, slot -> symbol | frequency << 8 | (slot - cumulative) << 20.
  * Returns GLQ_ERR_ARG for a model whose used tables do not sum to 2048 or a
  * buffer smaller than GLQ_EP_LUT_BYTES.
  */

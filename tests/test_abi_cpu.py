@@ -304,7 +304,7 @@ def test_ep_lut_matches_model():
         slot = np.arange(2048)
         s = np.searchsorted(cum, slot, side="right") - 1
         assert np.array_equal(ent[t] & 0xFF, s)
-        assert np.array_equal(((ent[t] >> 8) & 0xFFF) + 1, f[s])
+        assert np.array_equal((ent[t] >> 8) & 0xFFF, f[s])
         assert np.array_equal(ent[t] >> 20, slot - cum[s])
     bad = glq.EpModel()
     bad.nsym[0] = 2
