@@ -469,11 +469,29 @@ def ep_decode_bench(workload, target_bpp, lane_groups, launches):
         us = e0.elapsed_time(e1) * 1e3 / launches
         stored = bpp * spec.n * spec.k / 8.0
         moved = stored + 2.0 * spec.n * spec.k
+        # the whole layer y = U^T W^ (V x) at the workload's batch (bf16 in/out)
+        L.sign_k, L.sign_n = (torch.from_numpy(np.ascontiguousarray(a, np.int8)).to("cuda") for a in (sk, sn))
+        L.__dict__.pop("_st", None)
+        x = torch.randn(spec.m, spec.k, device="cuda").to(torch.bfloat16)
+        y = torch.empty(spec.m, spec.n, device="cuda", dtype=torch.bfloat16)
+        ws = torch.zeros(glq.ep_workspace_bytes(L, spec.m), device="cuda", dtype=torch.uint8)
+        reps = max(3, min(50, launches // 4))
+        with torch.cuda.stream(s):
+            for _ in range(3):
+                glq.ep_fused_linear(L, x, y, ws, stream=s)
+            e0.record(s)
+            for _ in range(reps):
+                glq.ep_fused_linear(L, x, y, ws, stream=s)
+            e1.record(s)
+            s.synchronize()
+        lus = e0.elapsed_time(e1) * 1e3 / reps
         res.append({"shape": f"{spec.n}x{spec.k}", "step": h.step, "actual_bpp": round(bpp, 4),
                     "nblocks": h.nblocks, "kernel_us": round(us, 2),
                     "weights_per_s": round(spec.n * spec.k / (us * 1e-6), 1),
                     "stored_gbs": round(stored / (us * 1e-6) / 1e9, 1),
-                    "hbm_gbs": round(moved / (us * 1e-6) / 1e9, 1), "hbm_frac": round(moved / (us * 1e-6) / 8e12, 4)})
+                    "hbm_gbs": round(moved / (us * 1e-6) / 1e9, 1), "hbm_frac": round(moved / (us * 1e-6) / 8e12, 4),
+                    "layer_m": spec.m, "layer_us": round(lus, 2),
+                    "layer_tflops": round(2.0 * spec.m * spec.n * spec.k / (lus * 1e-6) / 1e12, 1)})
     print(json.dumps({"mode": "ep_decode", "workload": workload, "target_bpp": target_bpp,
                       "lane_groups": lane_groups, "layers": res}))
 

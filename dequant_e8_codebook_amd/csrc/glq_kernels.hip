@@ -1559,6 +1559,150 @@ gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
   gm_epilogue<BPW, OUT_BF16>(acc, rowsum, post, row_scale, out, m, n, m0, n0, lane, wave, vec != 0);
 }
 
+// Dense GEMM z = post * x~ W^T with the weights already in memory as bf16
+// [n][k] row-major (the entropy-coded layers' decoded weights): the tiling,
+// x~ staging and epilogue of gemm_bf16. The 256 x 64 weight tile of a step
+// has the shape of the x~ tile, so it is staged the same way (loaded into
+// registers one step ahead, stored to a second double-buffered LDS tile);
+// in MFMA block u, lane (c, p) reads inputs 32 p + 8 u .. + 7 of its weight
+// row, the order in which it reads its A operands (the k order inside a step
+// is a permutation shared by A and B). Past k both tiles are zero.
+template <bool OUT_BF16>
+__global__ void __launch_bounds__(256, 1)
+gemm_w_bf16(const uint16_t *w, const uint16_t *xt, int64_t m, int64_t n, int64_t k, float post, void *out,
+            int vec, int64_t mblocks, int64_t tiles) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  uint16_t *As0 = reinterpret_cast<uint16_t *>(lds);
+  uint16_t *As1 = As0 + GM_BM * GM_LDA;
+  uint16_t *Bs0 = As1 + GM_BM * GM_LDA;
+  uint16_t *Bs1 = Bs0 + GM_BN * GM_LDA;
+  int64_t tile = blockIdx.x;
+  if (tiles % 8 == 0) tile = (blockIdx.x % 8) * (tiles / 8) + blockIdx.x / 8;
+  const int64_t m0 = (tile % mblocks) * GM_BM;
+  const int64_t nb0 = (tile / mblocks) * GM_BN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 31, p = lane >> 5;
+  const int64_t n0 = nb0 + 64 * wave;
+  const int64_t S = (k + GM_BK - 1) / GM_BK;
+
+  uint4 ra[8], rb[8];
+  gm_load_a(xt, m, k, m0, 0, ra);
+  gm_load_a(w, n, k, nb0, 0, rb);
+  gm_store_a(As0, ra, k);
+  gm_store_a(Bs0, rb, k);
+  gm_load_a(xt, m, k, m0, min((int64_t)1, S - 1), ra);
+  gm_load_a(w, n, k, nb0, min((int64_t)1, S - 1), rb);
+  __syncthreads();
+
+  f32x16 acc[8][2];
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][t][e] = 0.f;
+
+  for (int64_t st = 0; st < S; ++st) {
+    const uint16_t *Acur = (st & 1) ? As1 : As0;
+    const uint16_t *Bcur = ((st & 1) ? Bs1 : Bs0) + (64 * wave) * GM_LDA;
+    uint4 av[8], an[8], bv[2];
+#pragma unroll
+    for (int a = 0; a < 8; ++a) av[a] = *reinterpret_cast<const uint4 *>(Acur + (32 * a + c) * GM_LDA + 32 * p);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        bv[t] = *reinterpret_cast<const uint4 *>(Bcur + (32 * t + c) * GM_LDA + 32 * p + 8 * u);
+      if (u < 3) {
+#pragma unroll
+        for (int a = 0; a < 8; ++a)
+          an[a] = *reinterpret_cast<const uint4 *>(Acur + (32 * a + c) * GM_LDA + 32 * p + 8 * (u + 1));
+      }
+#pragma unroll
+      for (int a = 0; a < 8; ++a) {
+        acc[a][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[a]),
+                                                            __builtin_bit_cast(bf16x8, bv[0]), acc[a][0], 0, 0, 0);
+        acc[a][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[a]),
+                                                            __builtin_bit_cast(bf16x8, bv[1]), acc[a][1], 0, 0, 0);
+      }
+      if (u < 3) {
+#pragma unroll
+        for (int a = 0; a < 8; ++a) av[a] = an[a];
+      }
+    }
+    const int64_t kv = k - GM_BK * (st + 1);
+    gm_store_a((st & 1) ? As0 : As1, ra, kv);          // tiles st + 1 (unused past the end)
+    gm_store_a((st & 1) ? Bs0 : Bs1, rb, kv);
+    gm_load_a(xt, m, k, m0, min(st + 2, S - 1), ra);
+    gm_load_a(w, n, k, nb0, min(st + 2, S - 1), rb);
+    __syncthreads();
+  }
+  gm_epilogue<2, OUT_BF16>(acc, nullptr, post, nullptr, out, m, n, m0, n0, lane, wave, vec != 0);
+}
+
+// Dense GEMV for m <= 16 on weights in memory (bf16 [n][k]): one 16-row
+// weight tile per workgroup of 16 waves; the k axis is cut in chunks of 32
+// inputs and wave w takes chunks w, w + 16, ... Lane l (row j = l & 15,
+// slot q = l >> 4) loads inputs 8 q .. 8 q + 7 of the chunk from x~ row j
+// (clamped to m - 1: rows past m feed only outputs that are not stored) and
+// from weight row n0 + j, and one MFMA 16x16x32 contracts the chunk (A = x~
+// rows, B = weight rows). Four chunks' loads are issued before their MFMAs;
+// a partial last chunk (k % 32 != 0) is taken apart, with its weights past k
+// zeroed. Partial sums of the 16 waves meet in LDS.
+constexpr int GW_WAVES = 16;
+
+__global__ void __launch_bounds__(64 * GW_WAVES)
+gemv_w_bf16(const uint16_t *w, const uint16_t *xt, int64_t m, int64_t n, int64_t k, float post, void *out,
+            glq_dtype out_dt) {
+  __shared__ float red[GW_WAVES * 256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = lane & 15, q = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const uint16_t *xr = xt + (size_t)min((int64_t)j, m - 1) * k + 8 * q;
+  const uint16_t *wr = w + (size_t)min(n0 + j, n - 1) * k + 8 * q;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int64_t full = k / 32;
+  int64_t c = wave;
+  for (; c + 3 * GW_WAVES < full; c += 4 * GW_WAVES) {
+    uint4 a[4], b[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      a[u] = *reinterpret_cast<const uint4 *>(xr + 32 * (c + u * GW_WAVES));
+      b[u] = *reinterpret_cast<const uint4 *>(wr + 32 * (c + u * GW_WAVES));
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[u]), __builtin_bit_cast(bf16x8, b[u]),
+                                                    acc, 0, 0, 0);
+  }
+  for (; c < full; c += GW_WAVES) {
+    const uint4 a = *reinterpret_cast<const uint4 *>(xr + 32 * c);
+    const uint4 b = *reinterpret_cast<const uint4 *>(wr + 32 * c);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc,
+                                                  0, 0, 0);
+  }
+  if ((k & 31) && wave == (int)(full % GW_WAVES)) {       // the partial last chunk
+    const int64_t kk = 32 * full + 8 * q;
+    const int64_t kc = min(kk, k - 8) - 8 * q;          // clamped, in-bounds load position
+    const uint4 a = *reinterpret_cast<const uint4 *>(xr + kc);
+    uint4 b = *reinterpret_cast<const uint4 *>(wr + kc);
+    if (kk >= k) b = make_uint4(0u, 0u, 0u, 0u);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc,
+                                                  0, 0, 0);
+  }
+  // D[r][col]: lane holds rows 4 q + t (activation row), column j (weight row)
+#pragma unroll
+  for (int t = 0; t < 4; ++t) red[(wave * 16 + 4 * q + t) * 16 + j] = acc[t];
+  __syncthreads();
+  if (threadIdx.x < 256) {
+    const int r = threadIdx.x >> 4, col = threadIdx.x & 15;
+    float v = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < GW_WAVES; ++ww) v += red[(ww * 16 + r) * 16 + col];
+    if (r < m && n0 + col < n) store_out(out, out_dt, (size_t)r * n + n0 + col, post * v);
+  }
+}
+
 // ---------------------------------------------------------------- float32 path
 // One wave per weight row (grid-stride); lanes split the groups of the row;
 // up to 4 activation rows per pass (the host loops over passes).
@@ -2165,4 +2309,79 @@ extern "C" int glq_ep_decode_weights(const glq_ep_layer *L, void *w_out, glq_dty
                      (uint32_t)L->nwords, reinterpret_cast<const uint8_t *>(L->lut), L->row_scale, L->step, total,
                      (uint32_t)(L->k / 8), (uint32_t)L->lane_groups, nblocks, (uint32_t)L->k, w_out);
   return hip_status(hipGetLastError());
+}
+
+int launch_gemm_w(const uint16_t *w, const uint16_t *xt, int64_t m, int64_t n, int64_t k, void *out,
+                  glq_dtype out_dt, hipStream_t st) {
+  if (m <= 16) {
+    const int64_t grid = (n + 15) / 16;
+    if (grid > 0x7FFFFFFF) return GLQ_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(gemv_w_bf16, dim3((unsigned)grid), dim3(64 * GW_WAVES), 0, st, w, xt, m, n, k, 1.0f, out,
+                       out_dt);
+    return hip_status(hipGetLastError());
+  }
+  const int64_t mb = (m + GM_BM - 1) / GM_BM, nb = (n + GM_BN - 1) / GM_BN;
+  const int64_t tiles = mb * nb;
+  if (tiles > 0x7FFFFFFF) return GLQ_ERR_UNSUPPORTED;
+  const size_t shm = 4 * GM_A_BYTES;                 // x~ and W tiles, double-buffered
+  const bool ob = out_dt == GLQ_BF16;
+  const int vec = ((n * (ob ? 2 : 4)) % 16 == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0) ? 1 : 0;
+  auto kern = ob ? gemm_w_bf16<true> : gemm_w_bf16<false>;
+  int rc = allow_lds(kern, shm);
+  if (rc) return rc;
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(256), shm, st, w, xt, m, n, k, 1.0f, out, vec, mb, tiles);
+  return hip_status(hipGetLastError());
+}
+
+// Workspace of the entropy-coded layer: decoded W^ (bf16), x~ (bf16), z.
+struct EpWs { size_t w, xt, z, total; };
+
+EpWs ep_ws_layout(int64_t n, int64_t k, int64_t m) {
+  EpWs e;
+  e.w = 0;
+  e.xt = align256((size_t)n * (size_t)k * 2);
+  e.z = e.xt + align256((size_t)m * (size_t)k * 2);
+  e.total = e.z + align256((size_t)m * (size_t)n * 4);
+  return e;
+}
+
+extern "C" size_t glq_ep_fused_linear_workspace(const glq_ep_layer *L, int64_t m) {
+  if (!L || m <= 0 || L->n < 1 || L->k < 8) return 0;
+  return ep_ws_layout(L->n, L->k, m).total;
+}
+
+extern "C" int glq_ep_fused_linear(const glq_ep_layer *L, const void *x, glq_dtype x_dt, int64_t m, void *y,
+                                   glq_dtype y_dt, void *workspace, size_t ws_bytes, uint32_t flags,
+                                   void *hip_stream) {
+  const bool in_rht = !(flags & GLQ_FLAG_NO_INPUT_RHT);
+  const bool out_rht = !(flags & GLQ_FLAG_NO_OUTPUT_RHT);
+  if (!L || (flags & ~3u) || !valid_dtype(x_dt) || !valid_dtype(y_dt) || m < 0) return GLQ_ERR_ARG;
+  if ((in_rht && !L->sign_k) || (out_rht && !L->sign_n)) return GLQ_ERR_ARG;
+  if (m == 0) return GLQ_OK;
+  if (!x || !y) return GLQ_ERR_ARG;
+  if (!in_rht && (x_dt != GLQ_BF16 || (reinterpret_cast<uintptr_t>(x) & 15))) return GLQ_ERR_UNSUPPORTED;
+  if (in_rht && log2_block(L->k) > kMaxLogBlock) return GLQ_ERR_UNSUPPORTED;
+  if (out_rht && log2_block(L->n) > kMaxLogBlock) return GLQ_ERR_UNSUPPORTED;
+  if (L->n < 1 || L->k < 8 || L->k % 8 != 0) return GLQ_ERR_ARG;
+  const EpWs ws = ep_ws_layout(L->n, L->k, m);
+  if (!workspace || ws_bytes < ws.total || (reinterpret_cast<uintptr_t>(workspace) & 255)) return GLQ_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+  uint8_t *wsb = reinterpret_cast<uint8_t *>(workspace);
+  uint16_t *w = reinterpret_cast<uint16_t *>(wsb + ws.w);
+  uint16_t *xt = reinterpret_cast<uint16_t *>(wsb + ws.xt);
+  void *z = wsb + ws.z;
+  int rc = glq_ep_decode_weights(L, w, GLQ_BF16, hip_stream);
+  if (rc) return rc;
+  const uint16_t *xt_use = reinterpret_cast<const uint16_t *>(x);
+  if (in_rht) {
+    rc = launch_rht(x, x_dt, xt, GLQ_BF16, m, L->k, L->sign_k, 0, nullptr, st);
+    if (rc) return rc;
+    xt_use = xt;
+  }
+  void *mm_out = out_rht ? z : y;
+  const glq_dtype mm_dt = !out_rht ? y_dt : (y_dt == GLQ_BF16 && m > 16) ? GLQ_BF16 : GLQ_F32;
+  rc = launch_gemm_w(w, xt_use, m, L->n, L->k, mm_out, mm_dt, st);
+  if (rc) return rc;
+  if (out_rht) return launch_rht(z, mm_dt, y, y_dt, m, L->n, L->sign_n, 1, nullptr, st);
+  return GLQ_OK;
 }

@@ -23,7 +23,8 @@ FLAG_NO_INPUT_RHT, FLAG_NO_OUTPUT_RHT = 1, 2
 
 EXPORTS = ("glq_build_codebook", "glq_encode_ref", "glq_encode_ldlq", "glq_rht_apply", "glq_decode_weights",
            "glq_fused_linear_workspace", "glq_fused_linear", "glq_status_string", "glq_last_error",
-           "glq_version", "glq_ep_encode", "glq_ep_build_lut", "glq_ep_decode_weights")
+           "glq_version", "glq_ep_encode", "glq_ep_build_lut", "glq_ep_decode_weights",
+           "glq_ep_fused_linear_workspace", "glq_ep_fused_linear")
 EP_LANES, EP_TABLES, EP_MAX_SYMS = 64, 5, 256
 EP_LUT_BYTES = 64 + EP_TABLES * 2048 * 4
 
@@ -54,7 +55,8 @@ class EpModel(ctypes.Structure):
 
 class EpLayerStruct(ctypes.Structure):
     _fields_ = [("n", _i64), ("k", _i64), ("lane_groups", _i32), ("step", _f32), ("row_scale", _vp),
-                ("states", _vp), ("offsets", _vp), ("words", _vp), ("nwords", _i64), ("lut", _vp)]
+                ("states", _vp), ("offsets", _vp), ("words", _vp), ("nwords", _i64), ("lut", _vp),
+                ("sign_k", _vp), ("sign_n", _vp)]
 
 
 _lib.glq_build_codebook.argtypes = [_i32, _vp, _sz, ctypes.POINTER(_sz)]
@@ -71,12 +73,16 @@ _lib.glq_ep_encode.argtypes = [_vp, _i64, _i64, _vp, _vp, _f32, _i32, _i32, _vp,
                                _vp, _i64, ctypes.POINTER(_i64)]
 _lib.glq_ep_build_lut.argtypes = [ctypes.POINTER(EpModel), _vp, _sz]
 _lib.glq_ep_decode_weights.argtypes = [ctypes.POINTER(EpLayerStruct), _vp, _i32, _vp]
+_lib.glq_ep_fused_linear_workspace.argtypes = [ctypes.POINTER(EpLayerStruct), _i64]
+_lib.glq_ep_fused_linear_workspace.restype = _sz
+_lib.glq_ep_fused_linear.argtypes = [ctypes.POINTER(EpLayerStruct), _vp, _i32, _i64, _vp, _i32, _vp, _sz, _u32, _vp]
 _lib.glq_status_string.argtypes = [_i32]
 _lib.glq_status_string.restype = ctypes.c_char_p
 _lib.glq_version.restype = _u32
 _lib.glq_last_error.restype = ctypes.c_char_p
 for _name in ("glq_build_codebook", "glq_encode_ref", "glq_encode_ldlq", "glq_rht_apply", "glq_decode_weights",
-              "glq_fused_linear", "glq_ep_encode", "glq_ep_build_lut", "glq_ep_decode_weights"):
+              "glq_fused_linear", "glq_ep_encode", "glq_ep_build_lut", "glq_ep_decode_weights",
+              "glq_ep_fused_linear"):
     getattr(_lib, _name).restype = ctypes.c_int
 
 
@@ -308,18 +314,21 @@ class EpLayer:
     words: object               # torch int16, nwords rounded up to 8 (>= 8), 16-byte aligned (uint16 bits)
     nwords: int
     lut: object                 # torch uint8 [EP_LUT_BYTES]
+    sign_k: object = None       # torch int8 [k] (the layer product only)
+    sign_n: object = None       # torch int8 [n]
 
     def struct(self) -> EpLayerStruct:
         st = self.__dict__.get("_st")
         if st is None:
             st = EpLayerStruct(self.n, self.k, self.lane_groups, float(self.step), self.row_scale.data_ptr(),
                                self.states.data_ptr(), self.offsets.data_ptr(), self.words.data_ptr(), self.nwords,
-                               self.lut.data_ptr())
+                               self.lut.data_ptr(), 0 if self.sign_k is None else self.sign_k.data_ptr(),
+                               0 if self.sign_n is None else self.sign_n.data_ptr())
             self.__dict__["_st"] = st
         return st
 
     @staticmethod
-    def from_host(h: EpHost, device="cuda") -> "EpLayer":
+    def from_host(h: EpHost, device="cuda", sign_k=None, sign_n=None) -> "EpLayer":
         torch = _torch()
 
         def dev(a):
@@ -328,7 +337,9 @@ class EpLayer:
         words[:len(h.words)] = h.words
         return EpLayer(h.n, h.k, h.lane_groups, h.step, dev(h.row_scale.astype(np.float32)),
                        dev(h.states.view(np.int32)), dev(h.offsets.view(np.int32)), dev(words.view(np.int16)),
-                       len(h.words), dev(ep_build_lut(h.model)))
+                       len(h.words), dev(ep_build_lut(h.model)),
+                       None if sign_k is None else dev(np.asarray(sign_k, np.int8)),
+                       None if sign_n is None else dev(np.asarray(sign_n, np.int8)))
 
 
 def ep_decode_weights(layer: EpLayer, out, stream=None):
@@ -337,6 +348,21 @@ def ep_decode_weights(layer: EpLayer, out, stream=None):
     _check(_lib.glq_ep_decode_weights(ctypes.byref(st), out.data_ptr(), _dtype_code(out), _stream_ptr(stream)),
            "glq_ep_decode_weights")
     return out
+
+
+def ep_workspace_bytes(layer: EpLayer, m: int) -> int:
+    st = layer.struct()
+    return int(_lib.glq_ep_fused_linear_workspace(ctypes.byref(st), m))
+
+
+def ep_fused_linear(layer: EpLayer, x, y, workspace, flags: int = 0, stream=None):
+    """y = U^T W^ (V x) on an entropy-coded layer (glq_ep_fused_linear)."""
+    st = layer.struct()
+    rc = _lib.glq_ep_fused_linear(ctypes.byref(st), x.data_ptr(), _dtype_code(x), x.shape[0], y.data_ptr(),
+                                  _dtype_code(y), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                  flags, _stream_ptr(stream))
+    _check(rc, "glq_ep_fused_linear")
+    return y
 
 
 def rht_apply(inp, out, signs, transpose: bool, stream=None):

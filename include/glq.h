@@ -252,6 +252,7 @@ typedef struct {
     const uint16_t *words;       /* device, 16-byte aligned, [nwords rounded up to a multiple of 8, at least 8] */
     int64_t nwords;              /* offsets[nblocks] */
     const void     *lut;         /* device, GLQ_EP_LUT_BYTES from glq_ep_build_lut */
+    const int8_t   *sign_k, *sign_n;  /* device [k], [n] (+1/-1); used by glq_ep_fused_linear only */
 } glq_ep_layer;
 
 /*
@@ -298,6 +299,22 @@ int glq_ep_build_lut(const glq_ep_model *model, void *lut_out, size_t lut_bytes)
  * gives wrong weights, never an access outside the buffers.
  */
 int glq_ep_decode_weights(const glq_ep_layer *L, void *w_out, glq_dtype out_dt, void *hip_stream);
+
+/*
+ * glq_ep_fused_linear -- the layer on an entropy-coded weight set:
+ * y = U^T (W^ (V x)) with W^ from glq_ep_decode_weights (the weights carry
+ * their row scales and step), computed as: W^ decoded to bf16 in the
+ * workspace, x~ = V x rounded to bf16, z = x~ W^T on bf16 matrix cores with
+ * float32 accumulation (kept in float32, or bf16 for bf16 y when m > 16), then
+ * y = U^T z. Flags, dtypes and m as in glq_fused_linear; with
+ * GLQ_FLAG_NO_INPUT_RHT, x must be bf16 and 16-byte aligned
+ * (GLQ_ERR_UNSUPPORTED otherwise).
+ *   workspace   device, >= glq_ep_fused_linear_workspace(L, m) bytes (2 n k +
+ *               2 m k + 4 m n, each part 256-byte aligned), 256-byte aligned
+ */
+size_t glq_ep_fused_linear_workspace(const glq_ep_layer *L, int64_t m);
+int glq_ep_fused_linear(const glq_ep_layer *L, const void *x, glq_dtype x_dt, int64_t m, void *y,
+                        glq_dtype y_dt, void *workspace, size_t ws_bytes, uint32_t flags, void *hip_stream);
 
 /* Static text for a status code. */
 const char *glq_status_string(int status);

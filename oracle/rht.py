@@ -57,10 +57,13 @@ def _apply_h(v: np.ndarray, b: int) -> np.ndarray:
         # H symmetric: row-vector form, every block one row of a single product
         out = blocks.reshape(-1, b) @ hadamard(b)
     else:
+        # H_b1 on the left, H_b2 on the right of each b1 x b2 block, each as
+        # one matrix product over all blocks
         b2 = DENSE_MAX
         b1 = b // b2
-        m = blocks.reshape(-1, n // b, b1, b2)
-        out = np.einsum("ij,gbjk,kl->gbil", hadamard(b1), m, hadamard(b2))
+        m = blocks.reshape(-1, b2) @ hadamard(b2)                        # rows of every block times H_b2
+        m = m.reshape(-1, b1, b2).transpose(0, 2, 1).reshape(-1, b1) @ hadamard(b1)
+        out = m.reshape(-1, b2, b1).transpose(0, 2, 1)                   # back to b1 x b2 blocks
     return out.reshape(shp)
 
 

@@ -344,13 +344,38 @@ def test_ep_encode_errors():
 
 def test_ep_decode_validation_before_launch():
     lib = glq.raw()
-    st = glq.EpLayerStruct(8, 64, 1, 0.5, 16, 16, 16, 16, 4, 16)
+    st = glq.EpLayerStruct(8, 64, 1, 0.5, 16, 16, 16, 16, 4, 16, 0, 0)
     assert lib.glq_ep_decode_weights(None, ctypes.c_void_p(16), glq.GLQ_BF16, None) == glq.GLQ_ERR_ARG
     assert lib.glq_ep_decode_weights(ctypes.byref(st), None, glq.GLQ_BF16, None) == glq.GLQ_ERR_ARG
     assert lib.glq_ep_decode_weights(ctypes.byref(st), ctypes.c_void_p(16), 7, None) == glq.GLQ_ERR_ARG
     assert lib.glq_ep_decode_weights(ctypes.byref(st), ctypes.c_void_p(24), glq.GLQ_BF16, None) == glq.GLQ_ERR_ARG
     for field, val in (("k", 12), ("lane_groups", 0), ("step", 0.0), ("row_scale", None), ("nwords", -1),
                        ("lut", 8)):
-        bad = glq.EpLayerStruct(8, 64, 1, 0.5, 16, 16, 16, 16, 4, 16)
+        bad = glq.EpLayerStruct(8, 64, 1, 0.5, 16, 16, 16, 16, 4, 16, 0, 0)
         setattr(bad, field, val)
         assert lib.glq_ep_decode_weights(ctypes.byref(bad), ctypes.c_void_p(16), glq.GLQ_BF16, None) == glq.GLQ_ERR_ARG
+
+
+def test_ep_fused_linear_validation_before_launch():
+    lib = glq.raw()
+
+    def st(**kw):
+        s = glq.EpLayerStruct(8, 64, 1, 0.5, 16, 16, 16, 16, 4, 16, 16, 16)
+        for a, v in kw.items():
+            setattr(s, a, v)
+        return s
+    ok = st()
+    a256 = lambda v: (v + 255) // 256 * 256
+    assert lib.glq_ep_fused_linear_workspace(ctypes.byref(ok), 4) == a256(2 * 8 * 64) + a256(2 * 4 * 64) + a256(4 * 4 * 8)
+    call = lambda s, x_dt=glq.GLQ_BF16, m=4, ws=1 << 20, flags=0, x=16: lib.glq_ep_fused_linear(
+        None if s is None else ctypes.byref(s), x, x_dt, m, 16, glq.GLQ_BF16, 256, ws, flags, None)
+    assert call(None) == glq.GLQ_ERR_ARG
+    assert call(ok, flags=4) == glq.GLQ_ERR_ARG
+    assert call(ok, x_dt=5) == glq.GLQ_ERR_ARG
+    assert call(ok, m=-1) == glq.GLQ_ERR_ARG
+    assert call(ok, m=0) == glq.GLQ_OK                        # no-op, no launch
+    assert call(st(sign_k=None)) == glq.GLQ_ERR_ARG
+    assert call(st(sign_n=None)) == glq.GLQ_ERR_ARG
+    assert call(ok, x_dt=glq.GLQ_F32, flags=1) == glq.GLQ_ERR_UNSUPPORTED
+    assert call(ok, flags=1, x=24) == glq.GLQ_ERR_UNSUPPORTED   # x not 16-byte aligned
+    assert call(ok, ws=100) == glq.GLQ_ERR_WORKSPACE

@@ -519,3 +519,64 @@ def test_ep_decode_graph_replays(G):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+def _ep_layer_case(G, n, k, step, seed, lane_groups=8):
+    from oracle import entropack as oep
+    w, sn, sk = _ep_weights(n, k, seed)
+    h = G.ep_encode(w, sn, sk, step, lane_groups)
+    L = G.EpLayer.from_host(h, sign_k=sk, sign_n=sn)
+    z, s = oep.quantise_lattice(w.astype(np.float64), sn, sk, step)
+    return L, oep.weights_f32(z, s, step).astype(np.float64), sn, sk
+
+
+def _ep_run(G, L, x, x_dt, y_dt, flags=0):
+    m = x.shape[0]
+    xt = _t(x.astype(np.float32), torch.float32 if x_dt == "f32" else torch.bfloat16)
+    ncol = L.n
+    y = torch.empty((m, ncol), device="cuda", dtype=torch.float32 if y_dt == "f32" else torch.bfloat16)
+    ws = torch.zeros(max(G.ep_workspace_bytes(L, max(m, 1)), 256), device="cuda", dtype=torch.uint8)
+    G.ep_fused_linear(L, xt, y, ws, flags)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy()
+
+
+@pytest.mark.parametrize("n,k,m,x_dt,y_dt", [(256, 512, 1, "bf16", "bf16"), (256, 512, 16, "f32", "f32"),
+                                            (300, 264, 5, "bf16", "f32"), (40, 8, 3, "f32", "f32"),
+                                            (300, 264, 37, "bf16", "f32"), (1024, 4096, 300, "bf16", "bf16"),
+                                            (520, 3072, 257, "f32", "bf16")])
+def test_ep_fused_linear(G, n, k, m, x_dt, y_dt):
+    # y = U^T W^ (V x) on entropy-coded weights: bf16 matrix cores against
+    # the float64 product of the oracle's weights and transforms
+    L, w32, sn, sk = _ep_layer_case(G, n, k, 0.3, 11 * n + k)
+    x = np.random.default_rng(n + m).standard_normal((m, k)).astype(np.float32)
+    if x_dt == "bf16":
+        x = workloads.bf16_round_trip(x)
+    y = _ep_run(G, L, x, x_dt, y_dt)
+    ref = rht.rht_transpose(rht.rht_forward(x.astype(np.float64), sk) @ w32.T, sn)
+    assert og.relative_error(y, ref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("flags", [1, 2, 3])
+def test_ep_fused_linear_flags(G, flags):
+    n, k, m = 256, 1024, 24
+    L, w32, sn, sk = _ep_layer_case(G, n, k, 0.25, 77)
+    x = workloads.bf16_round_trip(np.random.default_rng(flags).standard_normal((m, k)).astype(np.float32))
+    y = _ep_run(G, L, x, "bf16", "f32", flags)
+    xt = x.astype(np.float64) if flags & 1 else rht.rht_forward(x.astype(np.float64), sk)
+    ref = xt @ w32.T
+    if not flags & 2:
+        ref = rht.rht_transpose(ref, sn)
+    assert og.relative_error(y, ref) <= TOL_BF16
+
+
+def test_ep_fused_linear_full_size_sampled(G):
+    # the prefill up-projection shape, 16384 x 4096 at m = 2048: sampled rows
+    # of y against the oracle (row r of y needs only row r of x)
+    n, k, m = 16384, 4096, 2048
+    L, w32, sn, sk = _ep_layer_case(G, n, k, 0.28, 4242, lane_groups=32)
+    x = workloads.bf16_round_trip(np.random.default_rng(5).standard_normal((m, k)).astype(np.float32))
+    y = _ep_run(G, L, x, "bf16", "bf16")
+    rows = np.array([0, 1, 255, 256, 1023, 1500, 2046, 2047])
+    ref = rht.rht_transpose(rht.rht_forward(x[rows].astype(np.float64), sk) @ w32.T, sn)
+    assert og.relative_error(y[rows], ref) <= TOL_BF16
