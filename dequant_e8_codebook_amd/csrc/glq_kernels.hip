@@ -396,7 +396,46 @@ __device__ __forceinline__ void rv_signs(const int8_t *signs, int64_t i0, float 
   for (int t = 0; t < 8; ++t) sg[t] = (float)(int8_t)(((t < 4 ? u.x : u.y) >> (8 * (t & 3))) & 0xFF);
 }
 
-template <bool IN_BF16, bool OUT_BF16, bool TRANSPOSE>
+// Pieces of 8 consecutive inputs as loaded (bf16: one 16-byte word; float32:
+// two), kept packed until they are written to LDS.
+template <bool IN_BF16> struct RvRaw { uint4 a, b; };
+
+template <bool IN_BF16>
+__device__ __forceinline__ void rv_fetch(const void *in, size_t e0, RvRaw<IN_BF16> &r) {
+  if constexpr (IN_BF16) {
+    r.a = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(in) + e0);
+  } else {
+    r.a = *reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(in) + e0);
+    r.b = *reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(in) + e0 + 4);
+  }
+}
+
+template <bool IN_BF16>
+__device__ __forceinline__ void rv_unpack(const RvRaw<IN_BF16> &r, float (&v)[8]) {
+  if constexpr (IN_BF16) {
+    const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      v[2 * t] = __uint_as_float(w[t] << 16);
+      v[2 * t + 1] = __uint_as_float(w[t] & 0xFFFF0000u);
+    }
+  } else {
+    const uint32_t w[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v[t] = __uint_as_float(w[t]);
+  }
+}
+
+__device__ __forceinline__ float rv_sign(uint2 u, int t) {
+  return (float)(int8_t)(((t < 4 ? u.x : u.y) >> (8 * (t & 3))) & 0xFF);
+}
+
+// Rows of n (multiple of 8) through LDS radix-16 passes, 256 threads per row,
+// grid-stride over rows. Thread t owns pieces t, t + 256, ... (PT at most) of
+// every row. The next row's pieces are loaded into registers right after the
+// current row is written to LDS, so they arrive during its passes and
+// stores; the signs (the same for every row) are loaded once, packed.
+template <bool IN_BF16, bool OUT_BF16, bool TRANSPOSE, int PT>
 __global__ void __launch_bounds__(256)
 rht_rows_vec(const void *in, void *out, int64_t rows, int64_t n, int logb, const int8_t *signs,
              float *rowsum) {
@@ -405,29 +444,36 @@ rht_rows_vec(const void *in, void *out, int64_t rows, int64_t n, int logb, const
   const int b = 1 << logb;
   const float inv = 1.0f / sqrtf((float)b);   // exact for even logb
   const int pieces = (int)(n >> 3);
-  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+  const int tid = threadIdx.x;
+  uint2 sgp[PT];
+  RvRaw<IN_BF16> raw[PT];
+#pragma unroll
+  for (int u = 0; u < PT; ++u) {
+    const int pc = min(tid + 256 * u, pieces - 1);     // clamped: pieces past n are not used
+    sgp[u] = *reinterpret_cast<const uint2 *>(signs + 8 * (int64_t)pc);
+  }
+  int64_t row = blockIdx.x;
+  if (row < rows) {
+#pragma unroll
+    for (int u = 0; u < PT; ++u) rv_fetch<IN_BF16>(in, (size_t)row * n + 8 * (size_t)min(tid + 256 * u, pieces - 1), raw[u]);
+  }
+  for (; row < rows; row += gridDim.x) {
     const size_t base = (size_t)row * n;
     __syncthreads();                           // previous row's readers are done with buf
-    for (int p0 = threadIdx.x; p0 < pieces; p0 += 4 * 256) {
-      float v[4][8], sg[4][8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int pc = min(p0 + 256 * u, pieces - 1);
-        rv_load_piece<IN_BF16>(in, base + 8 * (size_t)pc, v[u]);
-        if (!TRANSPOSE) rv_signs(signs, 8 * (int64_t)pc, sg[u]);
+    for (int u = 0; u < PT; ++u) {
+      const int pc = tid + 256 * u;
+      if (pc < pieces) {
+        float v[8];
+        rv_unpack<IN_BF16>(raw[u], v);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) buf[pidx(8 * pc + t)] = TRANSPOSE ? v[t] : v[t] * rv_sign(sgp[u], t);
       }
+    }
+    if (row + gridDim.x < rows) {              // next row, in flight during this row's passes
+      const size_t nb = base + (size_t)gridDim.x * n;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int pc = p0 + 256 * u;
-        if (pc < pieces) {
-          if (!TRANSPOSE) {
-#pragma unroll
-            for (int t = 0; t < 8; ++t) v[u][t] *= sg[u][t];
-          }
-#pragma unroll
-          for (int t = 0; t < 8; ++t) buf[pidx(8 * pc + t)] = v[u][t];
-        }
-      }
+      for (int u = 0; u < PT; ++u) rv_fetch<IN_BF16>(in, nb + 8 * (size_t)min(tid + 256 * u, pieces - 1), raw[u]);
     }
     __syncthreads();
     int lo = 0;
@@ -440,41 +486,43 @@ rht_rows_vec(const void *in, void *out, int64_t rows, int64_t n, int logb, const
     }
     __syncthreads();
     float rs = 0.0f;
-    for (int pc = threadIdx.x; pc < pieces; pc += 256) {
-      float sg[8];
-      if (TRANSPOSE) rv_signs(signs, 8 * (int64_t)pc, sg);      // issued before the LDS reads
-      float v[8];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) v[t] = buf[pidx(8 * pc + t)];
+    for (int u = 0; u < PT; ++u) {
+      const int pc = tid + 256 * u;
+      if (pc < pieces) {
+        float v[8];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        v[t] *= inv;
-        if (TRANSPOSE) v[t] *= sg[t];
-      }
-      if constexpr (OUT_BF16) {
-        uint32_t w[4];
+        for (int t = 0; t < 8; ++t) v[t] = buf[pidx(8 * pc + t)];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const uint32_t hh = bf16x2_rne(v[2 * t], v[2 * t + 1]);
-          const uint16_t h0 = (uint16_t)hh, h1 = (uint16_t)(hh >> 16);
-          w[t] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-          rs += __uint_as_float((uint32_t)h0 << 16) + __uint_as_float((uint32_t)h1 << 16);
+        for (int t = 0; t < 8; ++t) {
+          v[t] *= inv;
+          if (TRANSPOSE) v[t] *= rv_sign(sgp[u], t);
         }
-        *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(out) + base + 8 * (size_t)pc) =
-            make_uint4(w[0], w[1], w[2], w[3]);
-      } else {
-        float *o = reinterpret_cast<float *>(out) + base + 8 * (size_t)pc;
-        reinterpret_cast<float4 *>(o)[0] = make_float4(v[0], v[1], v[2], v[3]);
-        reinterpret_cast<float4 *>(o)[1] = make_float4(v[4], v[5], v[6], v[7]);
+        if constexpr (OUT_BF16) {
+          uint32_t w[4];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) rs += v[t];
+          for (int t = 0; t < 4; ++t) {
+            const uint32_t hh = bf16x2_rne(v[2 * t], v[2 * t + 1]);
+            const uint16_t h0 = (uint16_t)hh, h1 = (uint16_t)(hh >> 16);
+            w[t] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+            rs += __uint_as_float((uint32_t)h0 << 16) + __uint_as_float((uint32_t)h1 << 16);
+          }
+          *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(out) + base + 8 * (size_t)pc) =
+              make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+          float *o = reinterpret_cast<float *>(out) + base + 8 * (size_t)pc;
+          reinterpret_cast<float4 *>(o)[0] = make_float4(v[0], v[1], v[2], v[3]);
+          reinterpret_cast<float4 *>(o)[1] = make_float4(v[4], v[5], v[6], v[7]);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) rs += v[t];
+        }
       }
     }
     if (rowsum) {
       for (int off = 32; off > 0; off >>= 1) rs += __shfl_xor(rs, off);
-      if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = rs;
+      if ((tid & 63) == 0) red[tid >> 6] = rs;
       __syncthreads();
-      if (threadIdx.x == 0) rowsum[row] = red[0] + red[1] + red[2] + red[3];
+      if (tid == 0) rowsum[row] = red[0] + red[1] + red[2] + red[3];
     }
   }
 }
@@ -1967,16 +2015,28 @@ int cu_count() {
   return cus;
 }
 
+template <bool IB, bool OB, bool TR, int PT>
+int launch_rht_vec_pt(const void *in, void *out, int64_t rows, int64_t n, int lb, const int8_t *signs,
+                      float *rowsum, hipStream_t st) {
+  const int64_t grid = rows < 8192 ? rows : 8192;
+  const size_t shm = sizeof(float) * padded_floats((size_t)n);
+  const int rc = allow_lds(rht_rows_vec<IB, OB, TR, PT>, shm + 1024);
+  if (rc) return rc;
+  hipLaunchKernelGGL((rht_rows_vec<IB, OB, TR, PT>), dim3((unsigned)grid), dim3(256), shm, st, in, out, rows, n,
+                     lb, signs, rowsum);
+  return hip_status(hipGetLastError());
+}
+
+// pieces of 8 per thread: n / 8 / 256 rounded up to a power of two
 template <bool IB, bool OB, bool TR>
 int launch_rht_vec(const void *in, void *out, int64_t rows, int64_t n, int lb, const int8_t *signs,
                    float *rowsum, hipStream_t st) {
-  const int64_t grid = rows < 8192 ? rows : 8192;
-  const size_t shm = sizeof(float) * padded_floats((size_t)n);
-  const int rc = allow_lds(rht_rows_vec<IB, OB, TR>, shm + 1024);
-  if (rc) return rc;
-  hipLaunchKernelGGL((rht_rows_vec<IB, OB, TR>), dim3((unsigned)grid), dim3(256), shm, st, in, out, rows, n, lb,
-                     signs, rowsum);
-  return hip_status(hipGetLastError());
+  const int64_t pt = (n / 8 + 255) / 256;
+  if (pt <= 1) return launch_rht_vec_pt<IB, OB, TR, 1>(in, out, rows, n, lb, signs, rowsum, st);
+  if (pt <= 2) return launch_rht_vec_pt<IB, OB, TR, 2>(in, out, rows, n, lb, signs, rowsum, st);
+  if (pt <= 4) return launch_rht_vec_pt<IB, OB, TR, 4>(in, out, rows, n, lb, signs, rowsum, st);
+  if (pt <= 8) return launch_rht_vec_pt<IB, OB, TR, 8>(in, out, rows, n, lb, signs, rowsum, st);
+  return launch_rht_vec_pt<IB, OB, TR, 16>(in, out, rows, n, lb, signs, rowsum, st);
 }
 
 // rows of n <= 4096 on 256-thread workgroups, longer rows on 512 or 1024
