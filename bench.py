@@ -293,9 +293,20 @@ def cpu_baseline(built, budget_s):
     dt = time.perf_counter() - t0
     comp = i1.size * 2 + (0 if i2 is None else i2.size * i2.itemsize) + (4 * np.size(s) if np.ndim(s) else 0)
     gbs = n_done * comp / dt / 1e9
+    # the oracle's decode alone (float32 weights from the indices), a quarter of the budget
+    n_dec = 0
+    t1 = time.perf_counter()
+    while True:
+        og.decode_f32(i1, i2, spec.bpw, s)
+        n_dec += 1
+        if time.perf_counter() - t1 >= budget_s / 4:
+            break
+    dd = time.perf_counter() - t1
     return {"value": round(gbs, 5), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{n_done} layer forwards of {spec.n}x{spec.k} at {spec.bpw} bpw, {rows} activation row(s) "
                       f"each (decode + float64 RHTs + matmul), {dt:.1f} s; compressed bytes per second",
+            "decode_only": {"value": round(n_dec * comp / dd / 1e9, 5), "unit": "GB/s",
+                            "sample": f"{n_dec} float32 decodes of the layer, {dd:.1f} s"},
             "cpu_model": _cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
