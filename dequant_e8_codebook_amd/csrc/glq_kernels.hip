@@ -1817,11 +1817,10 @@ gemv_f32(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const floa
 // decode tables (slot -> symbol | frequency << 8 | (slot - cumulative) << 20,
 // 2048 slots each) are copied to LDS once per
 // workgroup with global-to-LDS loads.
-constexpr uint32_t kEpWaves = 8;
 constexpr uint32_t kEpLutHdr = 64;                    // vmin[5], padded
 constexpr uint32_t kEpLutBytes = 5 * 2048 * 4;        // in LDS at offset 0
 constexpr uint32_t kEpRing = 2048;                    // words per wave
-constexpr uint32_t kEpLds = kEpLutBytes + kEpWaves * kEpRing * 2;
+constexpr uint32_t ep_lds(uint32_t waves) { return kEpLutBytes + waves * kEpRing * 2; }
 
 typedef __attribute__((address_space(3))) const uint32_t lds_u32;
 typedef __attribute__((address_space(3))) u32x4_t lds_u128_w;
@@ -1833,8 +1832,8 @@ __device__ __forceinline__ void lds_st128(uint32_t addr, uint4 v) {
   *reinterpret_cast<lds_u128_w *>(static_cast<uintptr_t>(addr)) = t;
 }
 
-template <bool F32>
-__global__ __launch_bounds__(512) void ep_decode_k(const uint32_t *__restrict__ states,
+template <bool F32, uint32_t kEpWaves>
+__global__ __launch_bounds__(64 * kEpWaves) void ep_decode_k(const uint32_t *__restrict__ states,
                                                    const uint32_t *__restrict__ offsets,
                                                    const uint16_t *__restrict__ words, uint32_t nwords,
                                                    const uint8_t *__restrict__ lut,
@@ -2360,12 +2359,17 @@ extern "C" int glq_ep_decode_weights(const glq_ep_layer *L, void *w_out, glq_dty
   const uint32_t total = (uint32_t)(L->n * (L->k / 8));
   const uint64_t bg = 64ull * (uint64_t)L->lane_groups;
   const uint32_t nblocks = (uint32_t)((total + bg - 1) / bg);
-  const uint32_t grid = (nblocks + kEpWaves - 1) / kEpWaves;
+  // one wave per block: 4-wave workgroups spread a layer of at most one
+  // wave per SIMD over every CU; larger layers take 8 (two per CU fit)
+  const bool wide = nblocks > (uint32_t)cu_count() * 4;
+  const uint32_t waves = wide ? 8 : 4;
+  const uint32_t grid = (nblocks + waves - 1) / waves;
   hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
-  auto kern = out_dt == GLQ_F32 ? ep_decode_k<true> : ep_decode_k<false>;
-  int rc = allow_lds(kern, kEpLds);
+  auto kern = wide ? (out_dt == GLQ_F32 ? ep_decode_k<true, 8> : ep_decode_k<false, 8>)
+                   : (out_dt == GLQ_F32 ? ep_decode_k<true, 4> : ep_decode_k<false, 4>);
+  int rc = allow_lds(kern, ep_lds(waves));
   if (rc) return rc;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kEpWaves), kEpLds, st, L->states, L->offsets, L->words,
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * waves), ep_lds(waves), st, L->states, L->offsets, L->words,
                      (uint32_t)L->nwords, reinterpret_cast<const uint8_t *>(L->lut), L->row_scale, L->step, total,
                      (uint32_t)(L->k / 8), (uint32_t)L->lane_groups, nblocks, (uint32_t)L->k, w_out);
   return hip_status(hipGetLastError());
