@@ -379,3 +379,20 @@ def test_ep_fused_linear_validation_before_launch():
     assert call(ok, x_dt=glq.GLQ_F32, flags=1) == glq.GLQ_ERR_UNSUPPORTED
     assert call(ok, flags=1, x=24) == glq.GLQ_ERR_UNSUPPORTED   # x not 16-byte aligned
     assert call(ok, ws=100) == glq.GLQ_ERR_WORKSPACE
+
+
+def test_ep_encode_zero_layer():
+    # all-zero weights: row scales 1, every used table a single value of
+    # frequency 2048, no words at all; the oracle agrees
+    from oracle import entropack as oep
+    w = np.zeros((4, 64), np.float32)
+    sn, sk = workloads.signs(4, 1), workloads.signs(64, 2)
+    h = glq.ep_encode(w, sn, sk, 0.3, 1)
+    o = oep.encode(w.astype(np.float64), sn, sk, 0.3, 1)
+    assert len(h.words) == 0 and len(o.words) == 0
+    assert np.all(h.row_scale == 1.0)
+    assert np.array_equal(h.states, o.states) and np.all(h.states == 1 << 16)
+    for t in range(5):
+        if h.model.nsym[t]:
+            assert h.model.nsym[t] == 1 and h.model.freq[t][0] == 2048
+    assert np.array_equal(oep.decode_z(o), np.zeros((4, 8, 8), np.int64))

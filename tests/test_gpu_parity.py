@@ -580,3 +580,16 @@ def test_ep_fused_linear_full_size_sampled(G):
     rows = np.array([0, 1, 255, 256, 1023, 1500, 2046, 2047])
     ref = rht.rht_transpose(rht.rht_forward(x[rows].astype(np.float64), sk) @ w32.T, sn)
     assert og.relative_error(y[rows], ref) <= TOL_BF16
+
+
+def test_ep_decode_zero_layer(G):
+    # a stream with no words (every symbol certain) decodes to zeros
+    w = np.zeros((64, 256), np.float32)
+    sn, sk = workloads.signs(64, 3), workloads.signs(256, 4)
+    h = G.ep_encode(w, sn, sk, 0.25, 4)
+    assert len(h.words) == 0
+    L = G.EpLayer.from_host(h, sign_k=sk, sign_n=sn)
+    out = _ep_decode(G, L, torch.float32)
+    assert not out.any()
+    y = _ep_run(G, L, np.ones((3, 256), np.float32), "f32", "f32")
+    assert not np.any(y)
