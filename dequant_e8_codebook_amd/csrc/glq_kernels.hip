@@ -20,9 +20,15 @@
 //   gemm_bf16       m > 16: 256 x 256 output tiles, x~ double-buffered in LDS,
 //                   weights decoded per wave straight into MFMA B operands.
 //   gemv_f32        float32 path: exact float32 weights, float32 FMAs.
+//   layer_small     m <= 4: the whole layer (both transforms and the
+//                   decode-GEMV) in one launch.
+//   ep_decode_k     entropy-coded layers: rANS symbol decode and weight
+//                   reconstruction, one wave per 64-lane block.
+//   gemm_w_bf16,    entropy-coded layers: the product on decoded bf16 weights
+//   gemv_w_bf16     (m > 16 / m <= 16).
 //
-// Every kernel that decodes first copies the decode tables (glq_tables.h) from
-// the caller's GLQ_CB_DEVICE buffer into LDS.
+// Every kernel that decodes first copies its decode tables (glq_tables.h, or
+// the entropy-coded layer's symbol tables) from the caller's buffer into LDS.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
