@@ -593,3 +593,19 @@ def test_ep_decode_zero_layer(G):
     assert not out.any()
     y = _ep_run(G, L, np.ones((3, 256), np.float32), "f32", "f32")
     assert not np.any(y)
+
+
+@pytest.mark.parametrize("m,x_dt,y_dt,bpw", [(1, "bf16", "bf16", 2), (3, "f32", "f32", 2), (16, "bf16", "f32", 4),
+                                            (40, "bf16", "bf16", 3)])
+def test_largest_hadamard_block_along_k(G, cb, m, x_dt, y_dt, bpw):
+    # k = 16384: the largest supported Hadamard block, 2048 groups per row
+    n, k = 64, 16384
+    i1, i2 = _random_layer(n, k, bpw, 161 + bpw)
+    s = np.float32(2.1e-3)
+    sn, sk = workloads.signs(n, 5), workloads.signs(k, 6)
+    x = np.random.default_rng(m).standard_normal((m, k)).astype(np.float32)
+    if x_dt == "bf16":
+        x = workloads.bf16_round_trip(x)
+    y = _run_linear(G, cb, i1, i2, s, sn, sk, x, x_dt, y_dt)
+    ref = og.layer_reference(x, i1, i2, bpw, s, sn, sk)
+    assert og.relative_error(y, ref) <= (TOL_F32 if x_dt == "f32" and y_dt == "f32" else TOL_BF16)
