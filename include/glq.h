@@ -310,7 +310,10 @@ int glq_ep_decode_weights(const glq_ep_layer *L, void *w_out, glq_dtype out_dt, 
  * GLQ_FLAG_NO_INPUT_RHT, x must be bf16 and 16-byte aligned
  * (GLQ_ERR_UNSUPPORTED otherwise).
  *   workspace   device, >= glq_ep_fused_linear_workspace(L, m) bytes (2 n k +
- *               2 m k + 4 m n, each part 256-byte aligned), 256-byte aligned
+ *               2 m k + 4 m n, each part 256-byte aligned), 256-byte aligned;
+ *               owned by the caller, overwritten on every call, and must not
+ *               overlap x or y (calls that share one workspace on concurrent
+ *               streams race)
  */
 size_t glq_ep_fused_linear_workspace(const glq_ep_layer *L, int64_t m);
 int glq_ep_fused_linear(const glq_ep_layer *L, const void *x, glq_dtype x_dt, int64_t m, void *y,
