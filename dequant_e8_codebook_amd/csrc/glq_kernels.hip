@@ -552,7 +552,12 @@ row_sums_bf16(const uint16_t *x, int64_t rows, int64_t n, float *rowsum) {
 // v of lane (lane ^ mask) within the wave, mask a power of two <= 32 known at
 // compile time: DPP moves for masks below 16 (quad_perm for 1 and 2; a half-row
 // mirror (lane ^ 7) then quad_perm [3,2,1,0] (lane ^ 3) for 4; a row mirror
-// (lane ^ 15) then a half-row mirror for 8), a swizzle for 16, a permute for 32.
+// (lane ^ 15) then a half-row mirror for 8); for 16 and 32 the gfx950 lane
+// swaps, VALU operations that need no trip through the LDS unit.
+// v_permlane16_swap(a, b) exchanges the odd 16-lane rows of a with the even
+// rows of b, v_permlane32_swap(a, b) the upper half of a with the lower half
+// of b; with a = b = v, lane l finds v of lane l ^ 16 (l ^ 32) in the second
+// result where bit 4 (bit 5) of l is clear and in the first where it is set.
 #define GLQ_DPP(v, ctrl) __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xF, 0xF, false))
 __device__ __forceinline__ float lane_xor(float v, int mask) {
   switch (mask) {
@@ -560,8 +565,14 @@ __device__ __forceinline__ float lane_xor(float v, int mask) {
     case 2: return GLQ_DPP(v, 0x4E);
     case 4: return GLQ_DPP(GLQ_DPP(v, 0x141), 0x1B);
     case 8: return GLQ_DPP(GLQ_DPP(v, 0x140), 0x141);
-    case 16: return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
-    default: return __shfl_xor(v, 32);
+    case 16: {
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+      return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+    }
+    default: {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+      return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+    }
   }
 }
 #undef GLQ_DPP
@@ -1041,21 +1052,78 @@ gemv_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
 // ---------------------------------------------------------------- whole layer (m <= 4)
 // One launch for y = U^T (s W^) (V x) at a few activation rows (decode-time
 // batch sizes), where separate RHT launches would cost more than the
-// decode-GEMV itself. Every workgroup: issues its first index loads and the
-// table copy, loads x (with the input signs) into registers and rotates it
-// (block FWHT along k in registers and lane shuffles, one LDS transpose,
-// 1/sqrt(b), bf16 rounding, row sums), runs the 16-wave decode-GEMV of
-// gemv_bf16 over its 16-row weight tiles with the x~ operands read from LDS,
-// and writes z (float32) to the workspace with write-through stores. Tickets
-// on 16 group counters and one top counter (each reset by its last taker)
-// pick the last workgroup, which loads all of z, applies U^T (block FWHT
-// along n, then signs) and writes y.
+// decode-GEMV itself. Every workgroup: issues its x and input-sign loads, then
+// its first index loads and the table copy, rotates x while the tables are
+// in flight (block FWHT along k in registers and lane exchanges, one LDS
+// transpose, 1/sqrt(b), bf16 rounding, row sums at 3 and 4 bpw), runs the
+// 16-wave decode-GEMV of gemv_bf16 over its 16-row weight tiles with the x~
+// operands read from LDS, and writes z (float32) to the workspace with
+// write-through stores. Tickets on 16 group counters and one top counter
+// (each reset by its last taker) pick the last workgroup, which loads all of
+// z and the output signs, applies U^T (block FWHT along n, then signs) and
+// writes y.
 constexpr int LY_MAXE = 16384;                       // m*k and m*n limit (64 KiB of float32)
 constexpr int LY_THREADS = 64 * GV_WAVES;            // 1024
 constexpr size_t LY_BUF_BYTES = (LY_MAXE + 4 * 16) * 4;   // float32 transpose buffer (padded)
 
+// The table image rounded up to whole 1 KiB copy runs (the tail of the last
+// run lands in padding that nothing reads).
 template <int BPW>
-constexpr size_t ly_lds_bytes() { return lds_table_bytes<BPW>() + LY_BUF_BYTES + GV_WAVES * 256 * 4 + 64; }
+constexpr uint32_t ly_tab_bytes() { return (lds_table_bytes<BPW>() + 1023) / 1024 * 1024; }
+
+template <int BPW>
+constexpr size_t ly_lds_bytes() { return ly_tab_bytes<BPW>() + LY_BUF_BYTES + GV_WAVES * 256 * 4 + 64; }
+
+// Table copy of the single-launch layer, staged through registers: global
+// loads that the rotation of x, issued after the x loads, does not wait for
+// (a copy straight to LDS counts as a different kind of load, after which the
+// compiler waits for all loads at the first use of any), written to LDS once
+// x~ is done. Every wave copies the same fixed number of 1 KiB runs with no
+// branch; lanes past the image read clamped blob addresses and write the
+// padding, and waves past the last run repeat it (the same bytes to the same
+// place). Workgroups start at different runs (rot), so that the 32 workgroups
+// of an XCD do not all ask the same L2 channel for the same lines at once.
+template <int BPW> struct LyTab {   // named members: an array here ended up on the stack
+  static constexpr uint32_t runs = ly_tab_bytes<BPW>() / 1024, per_wave = (runs + GV_WAVES - 1) / GV_WAVES;
+  static_assert(per_wave <= 4, "table runs per wave");
+  uint4 v0, v1, v2, v3;
+};
+
+template <int BPW>
+__device__ __forceinline__ uint32_t ly_run(uint32_t u, uint32_t rot) {
+  constexpr uint32_t runs = LyTab<BPW>::runs;
+  const uint32_t r = min((uint32_t)(threadIdx.x >> 6) + GV_WAVES * u, runs - 1) + rot;   // rot < runs
+  return r >= runs ? r - runs : r;
+}
+
+template <int BPW>
+__device__ __forceinline__ uint4 ly_fetch_run(const uint8_t *blob, uint32_t u, uint32_t rot) {
+  constexpr uint32_t b01 = kCtBytes + kOtBytes, b2 = b01 + kHtBytes;
+  static_assert(kLdsCt == 0 && kLdsOt == kCtBytes && kLdsHt1 == b01, "LDS table order");
+  const uint32_t pos = 1024 * ly_run<BPW>(u, rot) + 16 * (threadIdx.x & 63);
+  const uint32_t src = pos < b01 ? kCtOff + pos : pos < b2 ? TabCfg<BPW>::ht1 + (pos - b01)
+                                                           : TabCfg<BPW>::ht2 + (pos - b2);
+  return *reinterpret_cast<const uint4 *>(blob + min(src, kBlobBytes - 16));
+}
+
+template <int BPW>
+__device__ __forceinline__ void ly_fetch_tables(const uint8_t *blob, uint32_t rot, LyTab<BPW> &t) {
+  constexpr uint32_t pw = LyTab<BPW>::per_wave;
+  t.v0 = ly_fetch_run<BPW>(blob, 0, rot);
+  if constexpr (pw > 1) t.v1 = ly_fetch_run<BPW>(blob, 1, rot);
+  if constexpr (pw > 2) t.v2 = ly_fetch_run<BPW>(blob, 2, rot);
+  if constexpr (pw > 3) t.v3 = ly_fetch_run<BPW>(blob, 3, rot);
+}
+
+template <int BPW>
+__device__ __forceinline__ void ly_store_tables(uint8_t *lds, uint32_t rot, const LyTab<BPW> &t) {
+  constexpr uint32_t pw = LyTab<BPW>::per_wave;
+  const uint32_t l16 = 16 * (threadIdx.x & 63);
+  *reinterpret_cast<uint4 *>(lds + 1024 * ly_run<BPW>(0, rot) + l16) = t.v0;
+  if constexpr (pw > 1) *reinterpret_cast<uint4 *>(lds + 1024 * ly_run<BPW>(1, rot) + l16) = t.v1;
+  if constexpr (pw > 2) *reinterpret_cast<uint4 *>(lds + 1024 * ly_run<BPW>(2, rot) + l16) = t.v2;
+  if constexpr (pw > 3) *reinterpret_cast<uint4 *>(lds + 1024 * ly_run<BPW>(3, rot) + l16) = t.v3;
+}
 
 // Control words of the single-launch layer at the start of the workspace:
 // group counters g = 0 .. 15 at byte 256 g, the top counter at byte 4096 (each
@@ -1064,64 +1132,51 @@ constexpr int LY_GROUPS = 16;
 constexpr size_t kCtrlBytes = GLQ_WS_CTRL_BYTES;
 static_assert(kCtrlBytes % 256 == 0 && kCtrlBytes >= 4096 + 4, "ticket counters fit");
 
-// E consecutive bf16 values of x from element e (16-byte aligned x; e % E == 0)
-template <int E>
-__device__ __forceinline__ void ly_load_x(const uint16_t *x, int e, float (&v)[E]) {
-  uint32_t w[(E + 1) / 2];
-  if constexpr (E == 1) w[0] = x[e];
-  else if constexpr (E == 2) w[0] = *reinterpret_cast<const uint32_t *>(x + e);
-  else if constexpr (E == 4) { const uint2 u = *reinterpret_cast<const uint2 *>(x + e); w[0] = u.x; w[1] = u.y; }
-  else {
-#pragma unroll
-    for (int c = 0; c < E / 8; ++c) {
-      const uint4 u = *reinterpret_cast<const uint4 *>(x + e + 8 * c);
-      w[4 * c] = u.x; w[4 * c + 1] = u.y; w[4 * c + 2] = u.z; w[4 * c + 3] = u.w;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < E; ++i) v[i] = __uint_as_float(((w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) << 16);
-}
-
-// E consecutive signs from index c (8-byte aligned signs; c % E == 0)
-template <int E>
-__device__ __forceinline__ void ly_load_signs(const int8_t *sg, int c, float (&v)[E]) {
-  uint32_t w[(E + 3) / 4];
-  if constexpr (E == 1) w[0] = (uint8_t)sg[c];
-  else if constexpr (E == 2) w[0] = *reinterpret_cast<const uint16_t *>(sg + c);
-  else if constexpr (E == 4) w[0] = *reinterpret_cast<const uint32_t *>(sg + c);
-  else {
-#pragma unroll
-    for (int q = 0; q < E / 8; ++q) {
-      const uint2 u = *reinterpret_cast<const uint2 *>(sg + c + 8 * q);
-      w[2 * q] = u.x; w[2 * q + 1] = u.y;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < E; ++i) v[i] = (float)(int8_t)((w[i >> 2] >> (8 * (i & 3))) & 0xFFu);
-}
-
-// Input side: x~ = bf16( H (sign_k . x) / sqrt(b) ) into xb (LDS, [m][k] bf16),
-// per-wave row-sum partials into red[wave * 4 + r]. Ends with a barrier.
-template <int E>
+// Input side. Issue order: this thread's x and input-sign loads, the first
+// index loads of the decode (raw), the table loads; then x~ = bf16( H (sign_k
+// . x) / sqrt(b) ) into xb (LDS, [m][k] bf16), which waits for the x loads
+// only, and (ROWSUM) per-wave row-sum partials into red[wave * 4 + r]. Ends
+// with this wave's table runs written to LDS and the barrier that publishes
+// tables, xb and red. Loads use clamped in-bounds addresses; elements past m k are zeroed
+// and, being whole Hadamard blocks of their own, never reach a stored value.
+// xb lies past the transpose buffer for E <= 8 and on top of it for E = 16.
+template <int BPW, int E, bool ROWSUM>
 __device__ __forceinline__ void ly_input(const uint16_t *x, const int8_t *sign_k, int mk, int k, int logbk,
-                                         float *buf, uint16_t *xb, float *red, int tid) {
-  float v[E];
-  const int e0 = E * tid;
-  if (e0 < mk) {
-    float sg[E];
-    ly_load_x<E>(x, e0, v);
-    ly_load_signs<E>(sign_k, e0 % k, sg);
-#pragma unroll
-    for (int i = 0; i < E; ++i) v[i] *= sg[i];
+                                         uint8_t *lds, float *buf, uint16_t *xb, float *red, int tid, const uint16_t *idx1,
+                                         const void *idx2, const uint8_t *blob, uint32_t rot, int64_t irow,
+                                         int64_t G, int64_t ig0, GvRaw &raw) {
+  const int e0 = E * tid, el = min(e0, mk - E);      // mk % E == 0
+  uint32_t xw[(E + 1) / 2], sw[(E + 3) / 4];
+  if constexpr (E == 1) { xw[0] = x[el]; sw[0] = (uint8_t)sign_k[el % k]; }
+  else if constexpr (E == 2) {
+    xw[0] = *reinterpret_cast<const uint32_t *>(x + el);
+    sw[0] = *reinterpret_cast<const uint16_t *>(sign_k + el % k);
+  } else if constexpr (E == 4) {
+    const uint2 u = *reinterpret_cast<const uint2 *>(x + el);
+    xw[0] = u.x; xw[1] = u.y;
+    sw[0] = *reinterpret_cast<const uint32_t *>(sign_k + el % k);
   } else {
 #pragma unroll
-    for (int i = 0; i < E; ++i) v[i] = 0.0f;
+    for (int c = 0; c < E / 8; ++c) {
+      const uint4 u = *reinterpret_cast<const uint4 *>(x + el + 8 * c);
+      xw[4 * c] = u.x; xw[4 * c + 1] = u.y; xw[4 * c + 2] = u.z; xw[4 * c + 3] = u.w;
+      const uint2 g = *reinterpret_cast<const uint2 *>(sign_k + (el + 8 * c) % k);
+      sw[2 * c] = g.x; sw[2 * c + 1] = g.y;
+    }
   }
-  tables_landed();                                   // this wave's table copies: published by the next barrier
+  raw = gv_load_raw<BPW, true>(idx1, idx2, irow, G, ig0);
+  LyTab<BPW> tab;
+  ly_fetch_tables<BPW>(blob, rot, tab);
+  __builtin_amdgcn_sched_barrier(0);                 // everything above is issued before the first wait
+  const float keep = e0 < mk ? 1.0f : 0.0f;
+  float v[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const float sg = (float)(int8_t)((sw[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+    v[i] = __uint_as_float(((xw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) << 16) * (sg * keep);
+  }
   const bool tr = ly_fwht<E>(v, buf, logbk, tid);
-  if (!tr) __syncthreads();                          // tables visible
   const float inv = 1.0f / sqrtf((float)(1 << logbk));
-  float rs[4] = {0.f, 0.f, 0.f, 0.f};
   uint16_t h[E];
 #pragma unroll
   for (int i = 0; i < E; i += 2) {
@@ -1129,43 +1184,56 @@ __device__ __forceinline__ void ly_input(const uint16_t *x, const int8_t *sign_k
     h[i] = (uint16_t)hh;
     if (i + 1 < E) h[i + 1] = (uint16_t)(hh >> 16);
   }
+  float rs[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (ROWSUM) {
 #pragma unroll
-  for (int i = 0; i < E; ++i) {
-    const int e = ly_elem<E>(tid, i, tr);
-    if (e < mk) {
-      const float hv = __uint_as_float((uint32_t)h[i] << 16);
-      const int r = (e >= k) + (e >= 2 * k) + (e >= 3 * k);   // m <= 4
+    for (int i = 0; i < E; ++i) {
+      const int e = ly_elem<E>(tid, i, tr);
+      if (e < mk) {
+        const float hv = __uint_as_float((uint32_t)h[i] << 16);
+        const int r = (e >= k) + (e >= 2 * k) + (e >= 3 * k);   // m <= 4
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) rs[rr] += rr == r ? hv : 0.0f;
+        for (int rr = 0; rr < 4; ++rr) rs[rr] += rr == r ? hv : 0.0f;
+      }
     }
   }
-  if (tr) __syncthreads();                           // every thread has read buf (xb aliases it)
+  if (E == 16 && tr) __syncthreads();                // every thread has read buf (xb aliases it)
 #pragma unroll
   for (int i = 0; i < E; ++i) {
     const int e = ly_elem<E>(tid, i, tr);
     if (e < mk) xb[e] = h[i];
   }
+  if constexpr (ROWSUM) {
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    if (rr * k >= mk) break;                          // rows past m
-    float t = rs[rr];
+    for (int rr = 0; rr < 4; ++rr) {
+      if (rr * k >= mk) break;                        // rows past m
+      float t = rs[rr];
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) t += lane_xor(t, off);
-    if ((tid & 63) == 0) red[(tid >> 6) * 4 + rr] = t;
+      for (int off = 1; off < 64; off <<= 1) t += lane_xor(t, off);
+      if ((tid & 63) == 0) red[(tid >> 6) * 4 + rr] = t;
+    }
   }
+  ly_store_tables<BPW>(lds, rot, tab);
   __syncthreads();
 }
 
-// Output side (last workgroup): y = sign_n . H z / sqrt(b); sn = this thread's
-// signs (raw bytes) for ly_elem(tid, i, logbn > L), loaded at the start.
+// Output side (last workgroup): y = sign_n . H z / sqrt(b). The signs this
+// thread applies (to elements ly_elem(tid, i, logbn > L)) are loaded after z,
+// so that the first butterflies wait for z alone.
 template <int E>
-__device__ __forceinline__ void ly_output(const float *z, const int (&sn)[16], int mn, int logbn, float *buf,
-                                          void *y, glq_dtype y_dt, int tid) {
+__device__ __forceinline__ void ly_output(const float *z, const int8_t *sign_n, int n, int mn, int logbn,
+                                          float *buf, void *y, glq_dtype y_dt, int tid) {
   float v[E];
   const int e0 = E * tid;
 #pragma unroll
   for (int i = 0; i < E; ++i)   // padding elements form whole blocks of their own
     v[i] = e0 + i < mn ? __hip_atomic_load(z + e0 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0f;
+  int sn[E];
+  {
+    const bool str = logbn > LyF<E>::L;
+#pragma unroll
+    for (int i = 0; i < E; ++i) sn[i] = sign_n[min(ly_elem<E>(tid, i, str), mn - 1) % n];
+  }
   const bool tr = ly_fwht<E>(v, buf, logbn, tid);
   const float inv = 1.0f / sqrtf((float)(1 << logbn));
 #pragma unroll
@@ -1175,17 +1243,6 @@ __device__ __forceinline__ void ly_output(const float *z, const int (&sn)[16], i
   }
 }
 
-template <int E>
-__device__ __forceinline__ void ly_out_signs(const int8_t *sign_n, int n, int mn, int logbn, int tid, int (&sn)[16]) {
-  const bool tr = logbn > LyF<E>::L;
-#pragma unroll
-  for (int i = 0; i < E; ++i) {
-    const int e = ly_elem<E>(tid, i, tr);
-    sn[i] = sign_n[min(e, mn - 1) % n];
-  }
-}
-
-
 template <int BPW>
 __global__ void __launch_bounds__(LY_THREADS, 1)
 layer_small(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uint16_t *x,
@@ -1193,43 +1250,39 @@ layer_small(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const u
             int logbn, float post, const float *row_scale, void *y, glq_dtype y_dt, float *z,
             unsigned int *ctrl) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  float *xs = reinterpret_cast<float *>(lds + lds_table_bytes<BPW>());
-  float *red = reinterpret_cast<float *>(lds + lds_table_bytes<BPW>() + LY_BUF_BYTES);
+  float *xs = reinterpret_cast<float *>(lds + ly_tab_bytes<BPW>());
+  float *red = reinterpret_cast<float *>(lds + ly_tab_bytes<BPW>() + LY_BUF_BYTES);
   float *misc = red + GV_WAVES * 256;                 // [0..3] row sums, [8] last-workgroup flag
-  uint16_t *xb = reinterpret_cast<uint16_t *>(xs);   // x~ as bf16 [m][k] after rotation
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 15, q = lane >> 4;
   const int64_t G = k / 8, chunks = (G + 31) / 32;
-  const int64_t tiles = (n + 15) / 16;
+  const int64_t tiles = (n + 15) / 16;               // >= gridDim.x
   const int mk = (int)(m * k), mn = (int)(m * n);
+  const int ei = ly_e(mk);
+  // x~ as bf16 [m][k] after rotation: past the transpose buffer's 1024 E + 64
+  // floats when E <= 8, on top of it at E = 16
+  uint16_t *xb = reinterpret_cast<uint16_t *>(ei <= 8 ? xs + 1024 * ei + 64 : xs);
 
-  // 1. first index loads and the table copy in flight before anything else
+  // 1. x, the first index loads and the table copy; x~ into LDS while the
+  // tables land (the barrier at its end publishes tables, x~ and row sums)
   int64_t tile = blockIdx.x, c = wave;
   GvRaw raw;
-  if (tile < tiles && c < chunks) raw = gv_load_raw<BPW, true>(idx1, idx2, min(tile * 16 + j, n - 1), G, 32 * c + 8 * q);
-  load_tables<BPW, LY_THREADS>(lds, blob);
-  // the output signs this thread will apply if its workgroup finishes last
-  const int eo = ly_e(mn);
-  int sn[16];
-  switch (eo) {
-    case 1: ly_out_signs<1>(sign_n, (int)n, mn, logbn, tid, sn); break;
-    case 2: ly_out_signs<2>(sign_n, (int)n, mn, logbn, tid, sn); break;
-    case 4: ly_out_signs<4>(sign_n, (int)n, mn, logbn, tid, sn); break;
-    case 8: ly_out_signs<8>(sign_n, (int)n, mn, logbn, tid, sn); break;
-    default: ly_out_signs<16>(sign_n, (int)n, mn, logbn, tid, sn); break;
-  }
-  // 2. x~ into LDS (the barriers inside also publish the tables)
-  switch (ly_e(mk)) {
-    case 1: ly_input<1>(x, sign_k, mk, (int)k, logbk, xs, xb, red, tid); break;
-    case 2: ly_input<2>(x, sign_k, mk, (int)k, logbk, xs, xb, red, tid); break;
-    case 4: ly_input<4>(x, sign_k, mk, (int)k, logbk, xs, xb, red, tid); break;
-    case 8: ly_input<8>(x, sign_k, mk, (int)k, logbk, xs, xb, red, tid); break;
-    default: ly_input<16>(x, sign_k, mk, (int)k, logbk, xs, xb, red, tid); break;
-  }
-  if (tid < m) {
-    float t = 0.0f;
-    for (int w = 0; w < GV_WAVES; ++w) t += red[w * 4 + tid];
-    misc[tid] = t;                                   // read after the next barrier
+  {
+    constexpr bool RS = Epi<BPW>::bias != 0.0f;
+    const uint32_t rot = (blockIdx.x >> 3) % (ly_tab_bytes<BPW>() / 1024);
+    const int64_t irow = min(tile * 16 + j, n - 1), ig0 = 32 * min(c, chunks - 1) + 8 * q;
+    switch (ei) {
+      case 1: ly_input<BPW, 1, RS>(x, sign_k, mk, (int)k, logbk, lds, xs, xb, red, tid, idx1, idx2, blob, rot, irow, G, ig0, raw); break;
+      case 2: ly_input<BPW, 2, RS>(x, sign_k, mk, (int)k, logbk, lds, xs, xb, red, tid, idx1, idx2, blob, rot, irow, G, ig0, raw); break;
+      case 4: ly_input<BPW, 4, RS>(x, sign_k, mk, (int)k, logbk, lds, xs, xb, red, tid, idx1, idx2, blob, rot, irow, G, ig0, raw); break;
+      case 8: ly_input<BPW, 8, RS>(x, sign_k, mk, (int)k, logbk, lds, xs, xb, red, tid, idx1, idx2, blob, rot, irow, G, ig0, raw); break;
+      default: ly_input<BPW, 16, RS>(x, sign_k, mk, (int)k, logbk, lds, xs, xb, red, tid, idx1, idx2, blob, rot, irow, G, ig0, raw); break;
+    }
+    if (RS && tid < m) {
+      float t = 0.0f;
+      for (int w = 0; w < GV_WAVES; ++w) t += red[w * 4 + tid];
+      misc[tid] = t;                                 // read after the next barrier
+    }
   }
   // 3. decode-GEMV over this workgroup's tiles
   const uint16_t *xrow = xb + (size_t)min((int64_t)j, m - 1) * k;
@@ -1300,12 +1353,12 @@ layer_small(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const u
   __syncthreads();
   if (misc[8] == 0.0f) return;
   // 5. the last workgroup: y = U^T z
-  switch (eo) {
-    case 1: ly_output<1>(z, sn, mn, logbn, xs, y, y_dt, tid); break;
-    case 2: ly_output<2>(z, sn, mn, logbn, xs, y, y_dt, tid); break;
-    case 4: ly_output<4>(z, sn, mn, logbn, xs, y, y_dt, tid); break;
-    case 8: ly_output<8>(z, sn, mn, logbn, xs, y, y_dt, tid); break;
-    default: ly_output<16>(z, sn, mn, logbn, xs, y, y_dt, tid); break;
+  switch (ly_e(mn)) {
+    case 1: ly_output<1>(z, sign_n, (int)n, mn, logbn, xs, y, y_dt, tid); break;
+    case 2: ly_output<2>(z, sign_n, (int)n, mn, logbn, xs, y, y_dt, tid); break;
+    case 4: ly_output<4>(z, sign_n, (int)n, mn, logbn, xs, y, y_dt, tid); break;
+    case 8: ly_output<8>(z, sign_n, (int)n, mn, logbn, xs, y, y_dt, tid); break;
+    default: ly_output<16>(z, sign_n, (int)n, mn, logbn, xs, y, y_dt, tid); break;
   }
 }
 
