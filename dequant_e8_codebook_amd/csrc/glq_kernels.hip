@@ -629,17 +629,51 @@ __device__ __forceinline__ void ly_stage_lanes(float (&v)[E], int mask, bool upp
   for (int i = 0; i < E; ++i) v[i] = fmaf(v[i], sg, lane_xor(v[i], mask));
 }
 
-template <int E, int NW = 16>
-__device__ __forceinline__ bool ly_fwht(float (&v)[E], float *buf, int logb, int tid) {
+// One butterfly stage across lane bit 4 (R16) or lane bit 5 for register
+// pairs (a, b): the lane swap (16-lane rows, or 32-lane halves) exchanges the
+// odd rows of a with the even rows of b, after which every lane holds both
+// members of one butterfly pair in its two results (a pair of a in the even
+// rows, a pair of b in the odd ones). The butterflies run in registers, and
+// the same swap of the sums and differences puts every result back in place:
+// four operations per two elements instead of a copy, a swap, a select and an
+// fma per element.
+template <int E, bool R16>
+__device__ __forceinline__ void ly_stage_swap(float (&v)[E]) {
+  static_assert(E >= 2 && E % 2 == 0, "register pairs");
+#pragma unroll
+  for (int p = 0; p < E; p += 2) {
+    const auto r = R16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(v[p]), __float_as_uint(v[p + 1]), false, false)
+                       : __builtin_amdgcn_permlane32_swap(__float_as_uint(v[p]), __float_as_uint(v[p + 1]), false, false);
+    const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+    const float sum = a + b, dif = a - b;
+    const auto t = R16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(sum), __float_as_uint(dif), false, false)
+                       : __builtin_amdgcn_permlane32_swap(__float_as_uint(sum), __float_as_uint(dif), false, false);
+    v[p] = __uint_as_float(t[0]);
+    v[p + 1] = __uint_as_float(t[1]);
+  }
+}
+
+// FULL: the block is all 64 NW E elements (logb = L + log2 NW), so that every
+// stage runs and none is tested at run time.
+template <int E, int NW = 16, bool FULL = false>
+__device__ __forceinline__ bool ly_fwht(float (&v)[E], float *buf, int logb_rt, int tid) {
   using F = LyF<E, NW>;
   constexpr int LE = F::LE, L = F::L;
+  const int logb = FULL ? L + F::WB : logb_rt;
   const int lane = tid & 63;
 #pragma unroll
   for (int s = 0; s < LE; ++s)
     if (s < logb) ly_stage_regs<E>(v, s);
 #pragma unroll
-  for (int s = 0; s < 6; ++s)
-    if (LE + s < logb) ly_stage_lanes<E>(v, 1 << s, (lane >> s) & 1);
+  for (int s = 0; s < 6; ++s) {
+    if (LE + s < logb) {
+      if constexpr (E >= 2) {
+        if (s == 4) { ly_stage_swap<E, true>(v); continue; }
+        if (s == 5) { ly_stage_swap<E, false>(v); continue; }
+      }
+      ly_stage_lanes<E>(v, 1 << s, (lane >> s) & 1);
+    }
+  }
   if (logb <= L) return false;
   {
     float *w = buf + E * tid + 4 * (tid >> 6);         // element E tid + i at e + 4 (e >> L)
@@ -1140,7 +1174,7 @@ static_assert(kCtrlBytes % 256 == 0 && kCtrlBytes >= 4096 + 4, "ticket counters 
 // tables, xb and red. Loads use clamped in-bounds addresses; elements past m k are zeroed
 // and, being whole Hadamard blocks of their own, never reach a stored value.
 // xb lies past the transpose buffer for E <= 8 and on top of it for E = 16.
-template <int BPW, int E, bool ROWSUM>
+template <int BPW, int E, bool ROWSUM, bool FULL>
 __device__ __forceinline__ void ly_input(const uint16_t *x, const int8_t *sign_k, int mk, int k, int logbk,
                                          uint8_t *lds, float *buf, uint16_t *xb, float *red, int tid, const uint16_t *idx1,
                                          const void *idx2, const uint8_t *blob, uint32_t rot, int64_t irow,
@@ -1168,14 +1202,15 @@ __device__ __forceinline__ void ly_input(const uint16_t *x, const int8_t *sign_k
   LyTab<BPW> tab;
   ly_fetch_tables<BPW>(blob, rot, tab);
   __builtin_amdgcn_sched_barrier(0);                 // everything above is issued before the first wait
-  const float keep = e0 < mk ? 1.0f : 0.0f;
+  const float keep = FULL || e0 < mk ? 1.0f : 0.0f;    // FULL: m k = 1024 E
   float v[E];
 #pragma unroll
   for (int i = 0; i < E; ++i) {
     const float sg = (float)(int8_t)((sw[i >> 2] >> (8 * (i & 3))) & 0xFFu);
-    v[i] = __uint_as_float(((xw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) << 16) * (sg * keep);
+    const float xv = __uint_as_float(((xw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) << 16);
+    v[i] = FULL ? xv * sg : xv * (sg * keep);
   }
-  const bool tr = ly_fwht<E>(v, buf, logbk, tid);
+  const bool tr = ly_fwht<E, 16, FULL>(v, buf, logbk, tid);
   const float inv = 1.0f / sqrtf((float)(1 << logbk));
   uint16_t h[E];
 #pragma unroll
@@ -1220,7 +1255,7 @@ __device__ __forceinline__ void ly_input(const uint16_t *x, const int8_t *sign_k
 // Output side (last workgroup): y = sign_n . H z / sqrt(b). The signs this
 // thread applies (to elements ly_elem(tid, i, logbn > L)) are loaded after z,
 // so that the first butterflies wait for z alone.
-template <int E>
+template <int E, bool FULL>
 __device__ __forceinline__ void ly_output(const float *z, const int8_t *sign_n, int n, int mn, int logbn,
                                           float *buf, void *y, glq_dtype y_dt, int tid) {
   float v[E];
@@ -1234,7 +1269,7 @@ __device__ __forceinline__ void ly_output(const float *z, const int8_t *sign_n, 
 #pragma unroll
     for (int i = 0; i < E; ++i) sn[i] = sign_n[min(ly_elem<E>(tid, i, str), mn - 1) % n];
   }
-  const bool tr = ly_fwht<E>(v, buf, logbn, tid);
+  const bool tr = ly_fwht<E, 16, FULL>(v, buf, logbn, tid);
   const float inv = 1.0f / sqrtf((float)(1 << logbn));
 #pragma unroll
   for (int i = 0; i < E; ++i) {
@@ -1271,13 +1306,17 @@ layer_small(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const u
     constexpr bool RS = Epi<BPW>::bias != 0.0f;
     const uint32_t rot = (blockIdx.x >> 3) % (ly_tab_bytes<BPW>() / 1024);
     const int64_t irow = min(tile * 16 + j, n - 1), ig0 = 32 * min(c, chunks - 1) + 8 * q;
+#define GLQ_LY_IN(E, F) ly_input<BPW, E, RS, F>(x, sign_k, mk, (int)k, logbk, lds, xs, xb, red, tid, idx1, idx2, \
+                                              blob, rot, irow, G, ig0, raw)
+    // FULL variants for one row whose block is all of k (k = 4096, 8192, 16384)
     switch (ei) {
-      case 1: ly_input<BPW, 1, RS>(x, sign_k, mk, (int)k, logbk, lds, xs, xb, red, tid, idx1, idx2, blob, rot, irow, G, ig0, raw); break;
-      case 2: ly_input<BPW, 2, RS>(x, sign_k, mk, (int)k, logbk, lds, xs, xb, red, tid, idx1, idx2, blob, rot, irow, G, ig0, raw); break;
-      case 4: ly_input<BPW, 4, RS>(x, sign_k, mk, (int)k, logbk, lds, xs, xb, red, tid, idx1, idx2, blob, rot, irow, G, ig0, raw); break;
-      case 8: ly_input<BPW, 8, RS>(x, sign_k, mk, (int)k, logbk, lds, xs, xb, red, tid, idx1, idx2, blob, rot, irow, G, ig0, raw); break;
-      default: ly_input<BPW, 16, RS>(x, sign_k, mk, (int)k, logbk, lds, xs, xb, red, tid, idx1, idx2, blob, rot, irow, G, ig0, raw); break;
+      case 1: GLQ_LY_IN(1, false); break;
+      case 2: GLQ_LY_IN(2, false); break;
+      case 4: if (logbk == LyF<4>::L + 4) GLQ_LY_IN(4, true); else GLQ_LY_IN(4, false); break;
+      case 8: if (logbk == LyF<8>::L + 4) GLQ_LY_IN(8, true); else GLQ_LY_IN(8, false); break;
+      default: if (logbk == LyF<16>::L + 4) GLQ_LY_IN(16, true); else GLQ_LY_IN(16, false); break;
     }
+#undef GLQ_LY_IN
     if (RS && tid < m) {
       float t = 0.0f;
       for (int w = 0; w < GV_WAVES; ++w) t += red[w * 4 + tid];
@@ -1353,13 +1392,15 @@ layer_small(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const u
   __syncthreads();
   if (misc[8] == 0.0f) return;
   // 5. the last workgroup: y = U^T z
+#define GLQ_LY_OUT(E, F) ly_output<E, F>(z, sign_n, (int)n, mn, logbn, xs, y, y_dt, tid)
   switch (ly_e(mn)) {
-    case 1: ly_output<1>(z, sign_n, (int)n, mn, logbn, xs, y, y_dt, tid); break;
-    case 2: ly_output<2>(z, sign_n, (int)n, mn, logbn, xs, y, y_dt, tid); break;
-    case 4: ly_output<4>(z, sign_n, (int)n, mn, logbn, xs, y, y_dt, tid); break;
-    case 8: ly_output<8>(z, sign_n, (int)n, mn, logbn, xs, y, y_dt, tid); break;
-    default: ly_output<16>(z, sign_n, (int)n, mn, logbn, xs, y, y_dt, tid); break;
+    case 1: GLQ_LY_OUT(1, false); break;
+    case 2: GLQ_LY_OUT(2, false); break;
+    case 4: if (logbn == LyF<4>::L + 4) GLQ_LY_OUT(4, true); else GLQ_LY_OUT(4, false); break;
+    case 8: if (logbn == LyF<8>::L + 4) GLQ_LY_OUT(8, true); else GLQ_LY_OUT(8, false); break;
+    default: if (logbn == LyF<16>::L + 4) GLQ_LY_OUT(16, true); else GLQ_LY_OUT(16, false); break;
   }
+#undef GLQ_LY_OUT
 }
 
 // ---------------------------------------------------------------- GEMM (m > 16)
