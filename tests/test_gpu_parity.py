@@ -361,6 +361,20 @@ def test_small_batch_single_launch(G, cb, bpw, n, k, m):
             assert int(ws[:4352].count_nonzero().item()) == 0     # completion counters left at zero
 
 
+@pytest.mark.parametrize("n,k,bpw", [(1024, 8192, 2), (8192, 1024, 4), (16384, 1024, 2)])
+def test_one_row_whole_block_layers(G, cb, n, k, bpw):
+    # one activation row whose Hadamard block is all of k (8192) or all of n
+    # (8192, 16384): the single-launch layer's transforms with every stage
+    # fixed at compile time (4096 is covered above, 16384 along k below)
+    i1, i2 = _random_layer(n, k, bpw, 7000 + n + k)
+    s = np.float32(0.013)
+    sn, sk = workloads.signs(n, 51), workloads.signs(k, 52)
+    x = workloads.bf16_round_trip(np.random.default_rng(n + k).standard_normal((1, k)).astype(np.float32))
+    y = _run_linear(G, cb, i1, i2, s, sn, sk, x, "bf16", "bf16")
+    ref = og.layer_reference(x, i1, i2, bpw, s, sn, sk)
+    assert og.relative_error(y, ref) <= TOL_BF16
+
+
 # ------------------------------------------------------ per-row scales ----
 
 def _row_scale_layer(n, k, bpw, seed, scale=0.75):
