@@ -12,6 +12,10 @@
 //                   float32 in LDS (x~ = V x on inputs, y = U^T z on outputs);
 //                   optionally rounds to bf16 and records each row's sum of the
 //                   rounded values (needed by the biased 3/4 bpw operands).
+//   rht_rows_vec,   the same for 16-byte aligned rows, out of place: radix-16
+//   rht_rows_reg    passes through LDS (thousands of rows of 3072 .. 12288), or
+//                   butterflies in registers and lane exchanges with one LDS
+//                   transpose (rows of 16384, and a few rows of any width).
 //   decode_weights  indices -> W^ (rotated basis) as float32 or bf16.
 //   gemv_bf16       m <= 16: one 16-row weight tile per workgroup, 16 waves split
 //                   k, bf16 MFMA 16x16x32 with x~ rows as the M side (the few
@@ -2146,7 +2150,10 @@ int launch_rht_reg_nw(const void *in, void *out, int64_t rows, int64_t n, int lb
   int64_t e = 1;
   while (e * 64 * NW < n) e <<= 1;
   const size_t shm = sizeof(float) * (size_t)(64 * NW * e + 64);
-  const int64_t cap = (int64_t)cu_count() * (32 / NW);
+  // 1024 threads of 100+ registers each fill a CU: one resident workgroup per
+  // CU, each streaming its rows with the next row's loads in flight (a second
+  // round of workgroups measured 10% slower at 2048 x 16384)
+  const int64_t cap = (int64_t)cu_count() * (NW == 16 ? 1 : 32 / NW);
   const int64_t grid = rows < cap ? rows : cap;
   const int rc = allow_lds(rht_rows_reg<IB, OB, TR, NW>, shm + 64);
   if (rc) return rc;
