@@ -535,6 +535,47 @@ def test_ep_decode_graph_replays(G):
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
 
 
+@pytest.mark.parametrize("m,bpw", [(1, 2), (3, 4), (16, 4), (40, 3)])
+def test_fused_graph_replays(G, cb, m, bpw):
+    # a captured layer forward (single launch with its completion tickets at
+    # m <= 4, transform + GEMV + transform at 16, the GEMM path at 40),
+    # replayed several times with eager calls on the same workspace in
+    # between: every replay and every eager call give the eager result bit
+    # for bit, and the ticket counters are left at zero
+    n, k = 512, 1024
+    i1, i2 = _random_layer(n, k, bpw, 900 + m)
+    s = np.float32(0.02)
+    sn, sk = workloads.signs(n, 61), workloads.signs(k, 62)
+    L = G.Layer.from_numpy(i1, i2, s, sn, sk, cb)
+    x = _t(workloads.bf16_round_trip(np.random.default_rng(m).standard_normal((m, k)).astype(np.float32)),
+           torch.bfloat16)
+    ws = torch.zeros(G.workspace_bytes(L, m), device="cuda", dtype=torch.uint8)
+    ref = torch.empty((m, n), device="cuda", dtype=torch.bfloat16)
+    G.fused_linear(L, x, ref, ws)
+    torch.cuda.synchronize()
+    out = torch.empty_like(ref)
+    eager = torch.empty_like(ref)
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        G.fused_linear(L, x, out, ws, stream=st)
+        st.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=st):
+            G.fused_linear(L, x, out, ws, stream=st)
+    for _ in range(4):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+        G.fused_linear(L, x, eager, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(eager.view(torch.int16), ref.view(torch.int16))
+        assert int(ws[:4352].count_nonzero().item()) == 0
+    y = ref.float().cpu().numpy()
+    assert og.relative_error(y, og.layer_reference(x.float().cpu().numpy(), i1, i2, bpw, s, sn, sk)) <= TOL_BF16
+
+
 def _ep_layer_case(G, n, k, step, seed, lane_groups=8):
     from oracle import entropack as oep
     w, sn, sk = _ep_weights(n, k, seed)
