@@ -117,6 +117,14 @@ def single_launch(spec):
             and spec.m * spec.n <= 16384 and (spec.k // 8) % 8 == 0)
 
 
+def operand_layout(spec):
+    """True when the library writes x~ in the small-batch GEMV's operand
+    layout (its input transform does it): bf16 x, m <= 16 and k a multiple of
+    256 and at most 16384, outside the single-launch shapes."""
+    return (spec.x_dtype == "bf16" and spec.m <= 16 and spec.k % 256 == 0 and spec.k <= 16384
+            and not single_launch(spec))
+
+
 def dominant_kernel(spec):
     if spec.x_dtype == "f32":
         return f"gemv_f32<{spec.bpw}>"
@@ -208,16 +216,38 @@ def run_bench(args):
         for L in b0["layers"]:
             glq.fused_linear(L, xr, z, b0["ws"], flags)
     krep = max(1, args.kernel_launches // len(b0["layers"]))
-    kgraph.replay()
-    torch.cuda.synchronize()
-    k0 = torch.cuda.Event(enable_timing=True)
-    k1 = torch.cuda.Event(enable_timing=True)
-    k0.record()
-    for _ in range(krep):
-        kgraph.replay()
-    k1.record()
-    torch.cuda.synchronize()
-    core_mean = k0.elapsed_time(k1) * 1e-3 / (krep * len(b0["layers"]))
+
+    def graph_seconds(g):
+        g.replay()
+        torch.cuda.synchronize()
+        k0 = torch.cuda.Event(enable_timing=True)
+        k1 = torch.cuda.Event(enable_timing=True)
+        k0.record()
+        for _ in range(krep):
+            g.replay()
+        k1.record()
+        torch.cuda.synchronize()
+        return k0.elapsed_time(k1) * 1e-3
+
+    core_mean = graph_seconds(kgraph) / (krep * len(b0["layers"]))
+    tiled = operand_layout(spec0)
+    if tiled:
+        # the step's GEMV reads x~ in the operand layout its input transform
+        # writes, which a pre-rotated x cannot give: time input transform +
+        # GEMV and subtract the row-major transform of the same rows (the
+        # same kernel writing row-major, without the row sums)
+        zt = torch.empty_like(b0["y"])
+        for L in b0["layers"]:
+            glq.fused_linear(L, b0["x"], zt, b0["ws"], glq.FLAG_NO_OUTPUT_RHT)
+        ga = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(ga):
+            for L in b0["layers"]:
+                glq.fused_linear(L, b0["x"], zt, b0["ws"], glq.FLAG_NO_OUTPUT_RHT)
+        gb = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gb):
+            for L in b0["layers"]:
+                glq.rht_apply(b0["x"], xr, L.sign_k, False)
+        core_mean = (graph_seconds(ga) - graph_seconds(gb)) / (krep * len(b0["layers"]))
     # the whole-layer kernel is the step itself: its mean launch is the step time
     k_mean = ms_step * 1e-3 if single_launch(spec0) and len(built) == 1 else core_mean
     # rotated-basis launches of 3/4 bpw also run a small row-sum kernel
@@ -244,6 +274,9 @@ def run_bench(args):
         roof["matmul_core"] = {"kernel": f"gemv_bf16<{spec0.bpw}>", "mean_us": round(core_mean * 1e6, 3),
                                "achieved_gbs": round(k_bytes / core_mean / 1e9, 2),
                                "note": "decode-GEMV alone (x already rotated, z left rotated), as in the multi-kernel path"}
+    elif tiled:
+        roof["timing"] = (f"HIP events around {krep} replays of a graph of {len(b0['layers'])} (input transform into "
+                          "the operand layout + GEMV) pairs, minus the same for the row-major input transform alone")
     else:
         roof["timing"] = f"HIP events around {krep} replays of a graph of {len(b0['layers'])} launches"
     roof["algorithmic_bytes_per_launch"] = k_bytes

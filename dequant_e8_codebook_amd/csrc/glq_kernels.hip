@@ -724,6 +724,17 @@ __device__ __forceinline__ int ly_e(int count) {    // elements per thread for c
   return e;
 }
 
+// Element (r, e) of x~ (r < 16 activation rows, e < k, k a multiple of 256)
+// in the layout the small-batch GEMV reads its MFMA 16x16x32 A operands in:
+// for chunk c (32 groups of 8 elements) and step s (0..7) one KiB holds lane
+// l = j + 16 q's 16 bytes, the 8 elements of group 32 c + 8 q + s of row j.
+// A wave then loads each operand as one contiguous KiB instead of 16 rows x
+// 64 bytes (16 cache lines), which bound the GEMV's load phase.
+__device__ __forceinline__ size_t tile16_index(int64_t r, int e) {
+  const int g = e >> 3;
+  return ((size_t)((((g >> 5) << 3) + (g & 7)) * 64 + (int)r + 16 * ((g >> 3) & 3)) << 3) + (e & 7);
+}
+
 // RHT of rows of length n <= 16384 (n % 8 == 0, 16-byte aligned rows and
 // pointers, in != out): one row per workgroup of 64 NW threads (grid-stride),
 // the block FWHT in registers and lane exchanges (ly_fwht).
@@ -787,7 +798,7 @@ __device__ __forceinline__ void rr_unpack(const RrRaw<E, IN_BF16> &r, float (&v)
 
 
 
-template <int E, int NW, bool IN_BF16, bool OUT_BF16, bool TRANSPOSE>
+template <int E, int NW, bool IN_BF16, bool OUT_BF16, bool TRANSPOSE, bool TILE16>
 __device__ __forceinline__ void rr_rows(const void *in, void *out, int64_t rows, int n, int logb,
                                         const int8_t *signs, float *rowsum, float *buf, float *red) {
   const int tid = threadIdx.x;
@@ -830,7 +841,7 @@ __device__ __forceinline__ void rr_rows(const void *in, void *out, int64_t rows,
         if (i + 1 < E) x[i + 1] = __uint_as_float(hh & 0xFFFF0000u);
       }
     }
-    if (!tr && E >= 2 && e0 + E <= n) {
+    if (!TILE16 && !tr && E >= 2 && e0 + E <= n) {
       // untransposed: the thread's E consecutive outputs in vector stores
       if constexpr (OUT_BF16) {
         uint32_t w[E / 2 > 0 ? E / 2 : 1];
@@ -860,8 +871,9 @@ __device__ __forceinline__ void rr_rows(const void *in, void *out, int64_t rows,
       for (int i = 0; i < E; ++i) {
         const int e = ly_elem<E, NW>(tid, i, tr);
         if (e < n) {
-          if constexpr (OUT_BF16) reinterpret_cast<uint16_t *>(out)[base + e] = (uint16_t)(__float_as_uint(x[i]) >> 16);
-          else reinterpret_cast<float *>(out)[base + e] = x[i];
+          const size_t o = TILE16 ? tile16_index(row, e) : base + e;
+          if constexpr (OUT_BF16) reinterpret_cast<uint16_t *>(out)[o] = (uint16_t)(__float_as_uint(x[i]) >> 16);
+          else reinterpret_cast<float *>(out)[o] = x[i];
           rs += x[i];
         }
       }
@@ -880,7 +892,7 @@ __device__ __forceinline__ void rr_rows(const void *in, void *out, int64_t rows,
   }
 }
 
-template <bool IN_BF16, bool OUT_BF16, bool TRANSPOSE, int NW>
+template <bool IN_BF16, bool OUT_BF16, bool TRANSPOSE, int NW, bool TILE16 = false>
 __global__ void __launch_bounds__(64 * NW)
 rht_rows_reg(const void *in, void *out, int64_t rows, int n, int logb, const int8_t *signs, float *rowsum) {
   extern __shared__ __attribute__((aligned(16))) float rr_buf[];   // 64 NW E + 64 floats
@@ -888,11 +900,11 @@ rht_rows_reg(const void *in, void *out, int64_t rows, int n, int logb, const int
   int e = 1;
   while (e * 64 * NW < n) e <<= 1;
   switch (e) {
-    case 1: rr_rows<1, NW, IN_BF16, OUT_BF16, TRANSPOSE>(in, out, rows, n, logb, signs, rowsum, rr_buf, red); break;
-    case 2: rr_rows<2, NW, IN_BF16, OUT_BF16, TRANSPOSE>(in, out, rows, n, logb, signs, rowsum, rr_buf, red); break;
-    case 4: rr_rows<4, NW, IN_BF16, OUT_BF16, TRANSPOSE>(in, out, rows, n, logb, signs, rowsum, rr_buf, red); break;
-    case 8: rr_rows<8, NW, IN_BF16, OUT_BF16, TRANSPOSE>(in, out, rows, n, logb, signs, rowsum, rr_buf, red); break;
-    default: rr_rows<16, NW, IN_BF16, OUT_BF16, TRANSPOSE>(in, out, rows, n, logb, signs, rowsum, rr_buf, red); break;
+    case 1: rr_rows<1, NW, IN_BF16, OUT_BF16, TRANSPOSE, TILE16>(in, out, rows, n, logb, signs, rowsum, rr_buf, red); break;
+    case 2: rr_rows<2, NW, IN_BF16, OUT_BF16, TRANSPOSE, TILE16>(in, out, rows, n, logb, signs, rowsum, rr_buf, red); break;
+    case 4: rr_rows<4, NW, IN_BF16, OUT_BF16, TRANSPOSE, TILE16>(in, out, rows, n, logb, signs, rowsum, rr_buf, red); break;
+    case 8: rr_rows<8, NW, IN_BF16, OUT_BF16, TRANSPOSE, TILE16>(in, out, rows, n, logb, signs, rowsum, rr_buf, red); break;
+    default: rr_rows<16, NW, IN_BF16, OUT_BF16, TRANSPOSE, TILE16>(in, out, rows, n, logb, signs, rowsum, rr_buf, red); break;
   }
 }
 
@@ -1004,7 +1016,9 @@ __device__ __forceinline__ void gv_unpack(const GvRaw &r, uint32_t (&i1)[8], uin
   }
 }
 
-template <int BPW, bool G8, int RT>
+// TILED: x~ in the operand layout of tile16_index (k a multiple of 256), so
+// that each operand load is one contiguous KiB; otherwise x~ row-major [m][k].
+template <int BPW, bool G8, int RT, bool TILED>
 __global__ void __launch_bounds__(64 * GV_WAVES, 1)
 gemv_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uint16_t *xt,
           const float *rowsum, int64_t m, int64_t n, int64_t k, float post, const float *row_scale,
@@ -1033,7 +1047,10 @@ gemv_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) raw[rt] = gv_load_raw<BPW, G8>(idx1, idx2, min(n0 + 16 * rt + j, n - 1), G, g0);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) av[s] = *reinterpret_cast<const uint4 *>(xrow + 8 * min(g0 + s, G - 1));
+    for (int s = 0; s < 8; ++s) {
+      if constexpr (TILED) av[s] = *reinterpret_cast<const uint4 *>(xt + ((size_t)((cc * 8 + s) * 64 + lane) << 3));
+      else av[s] = *reinterpret_cast<const uint4 *>(xrow + 8 * min(g0 + s, G - 1));
+    }
   };
   if (c < chunks) load_chunk(c);
   // row sum of the activation row this thread reduces at the end (loaded
@@ -2144,7 +2161,7 @@ int launch_rht_vec(const void *in, void *out, int64_t rows, int64_t n, int lb, c
 
 // rows of n <= 4096 on 256-thread workgroups, longer rows on 512 or 1024
 // threads (16 elements per thread)
-template <bool IB, bool OB, bool TR, int NW>
+template <bool IB, bool OB, bool TR, int NW, bool TILE16 = false>
 int launch_rht_reg_nw(const void *in, void *out, int64_t rows, int64_t n, int lb, const int8_t *signs,
                       float *rowsum, hipStream_t st) {
   int64_t e = 1;
@@ -2155,11 +2172,24 @@ int launch_rht_reg_nw(const void *in, void *out, int64_t rows, int64_t n, int lb
   // round of workgroups measured 10% slower at 2048 x 16384)
   const int64_t cap = (int64_t)cu_count() * (NW == 16 ? 1 : 32 / NW);
   const int64_t grid = rows < cap ? rows : cap;
-  const int rc = allow_lds(rht_rows_reg<IB, OB, TR, NW>, shm + 64);
+  const int rc = allow_lds(rht_rows_reg<IB, OB, TR, NW, TILE16>, shm + 64);
   if (rc) return rc;
-  hipLaunchKernelGGL((rht_rows_reg<IB, OB, TR, NW>), dim3((unsigned)grid), dim3(64 * NW), shm, st, in, out,
+  hipLaunchKernelGGL((rht_rows_reg<IB, OB, TR, NW, TILE16>), dim3((unsigned)grid), dim3(64 * NW), shm, st, in, out,
                      rows, (int)n, lb, signs, rowsum);
   return hip_status(hipGetLastError());
+}
+
+// x~ of at most 16 rows written in the small-batch GEMV's operand layout
+// (tile16_index): bf16 in and out, n a multiple of 256 and at most 16384,
+// 16-byte aligned pointers, in != out (rht_tile16_ok).
+bool rht_tile16_ok(const void *in, const void *out, const int8_t *signs, int64_t rows, int64_t n) {
+  return rows <= 16 && n % 256 == 0 && n <= 16384 && in != out &&
+         ((reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(signs)) & 15) == 0;
+}
+
+int launch_rht_tile16(const void *in, void *out, int64_t rows, int64_t n, const int8_t *signs, float *rowsum,
+                      hipStream_t st) {
+  return launch_rht_reg_nw<true, true, false, 16, true>(in, out, rows, n, log2_block(n), signs, rowsum, st);
 }
 
 template <bool IB, bool OB, bool TR>
@@ -2245,7 +2275,9 @@ WsLayout ws_layout(int64_t n, int64_t k, int64_t m) {
   WsLayout w;
   w.ctrl = 0;
   w.xt = kCtrlBytes;
-  w.rowsum = w.xt + align256((size_t)m * (size_t)k * 4);
+  // x~: float32 [m][k], or bf16 in the 16-row operand layout when m <= 16
+  const size_t xt_bytes = (size_t)(m <= 16 ? 16 : m) * (size_t)k * 4;
+  w.rowsum = w.xt + align256(xt_bytes);
   w.z = w.rowsum + align256((size_t)m * 4);
   w.total = w.z + align256((size_t)m * (size_t)n * 4);
   return w;
@@ -2278,7 +2310,7 @@ int gv_row_tiles(int bpw, int64_t tiles) { return bpw == 2 && tiles >= 1024 ? 4 
 
 template <int BPW>
 int launch_matmul(const glq_layer *L, const void *xt, glq_dtype x_dt, const float *rowsum, int64_t m,
-                  void *out, glq_dtype out_dt, hipStream_t st) {
+                  void *out, glq_dtype out_dt, hipStream_t st, bool tiled = false) {
   const uint8_t *blob = reinterpret_cast<const uint8_t *>(L->cb);
   const size_t tab = lds_table_bytes<BPW>();
   if (x_dt == GLQ_F32) {
@@ -2308,8 +2340,9 @@ int launch_matmul(const glq_layer *L, const void *xt, glq_dtype x_dt, const floa
     const size_t shm = tab + (size_t)rt * GV_WAVES * 16 * 16 * 4;
     const bool g8 = ((L->k / 8) % 8) == 0;
     constexpr int RT4 = BPW == 2 ? 4 : 1;            // the only multi-tile variant
-    auto kern = g8 ? (rt == 4 ? gemv_bf16<BPW, true, RT4> : gemv_bf16<BPW, true, 1>)
-                   : (rt == 4 ? gemv_bf16<BPW, false, RT4> : gemv_bf16<BPW, false, 1>);
+    auto kern = tiled ? (rt == 4 ? gemv_bf16<BPW, true, RT4, true> : gemv_bf16<BPW, true, 1, true>)
+              : g8 ? (rt == 4 ? gemv_bf16<BPW, true, RT4, false> : gemv_bf16<BPW, true, 1, false>)
+                   : (rt == 4 ? gemv_bf16<BPW, false, RT4, false> : gemv_bf16<BPW, false, 1, false>);
     int rc = allow_lds(kern, shm);
     if (rc) return rc;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * GV_WAVES), shm, st, L->idx1, L->idx2, blob, xb,
@@ -2418,6 +2451,7 @@ extern "C" int glq_fused_linear(const glq_layer *L, const void *x, glq_dtype x_d
     return hip_status(hipGetLastError());
   }
   const void *xt_use = x;
+  bool tiled = false;
   if (x_dt == GLQ_F32) {
     if (in_rht) {
       rc = launch_rht(x, GLQ_F32, xt, GLQ_F32, m, L->k, L->sign_k, 0, nullptr, st);
@@ -2425,7 +2459,13 @@ extern "C" int glq_fused_linear(const glq_layer *L, const void *x, glq_dtype x_d
       xt_use = xt;
     }
   } else {
-    if (in_rht) {
+    if (in_rht && rht_tile16_ok(x, xt, L->sign_k, m, L->k)) {
+      // at most 16 rows: x~ straight into the GEMV's operand layout
+      rc = launch_rht_tile16(x, xt, m, L->k, L->sign_k, rowsum, st);
+      if (rc) return rc;
+      xt_use = xt;
+      tiled = true;
+    } else if (in_rht) {
       rc = launch_rht(x, GLQ_BF16, xt, GLQ_BF16, m, L->k, L->sign_k, 0, rowsum, st);
       if (rc) return rc;
       xt_use = xt;
@@ -2444,9 +2484,9 @@ extern "C" int glq_fused_linear(const glq_layer *L, const void *x, glq_dtype x_d
   void *mm_out = out_rht ? (void *)z : y;
   const glq_dtype mm_dt = !out_rht ? y_dt : (x_dt == GLQ_BF16 && y_dt == GLQ_BF16 && m > 16) ? GLQ_BF16 : GLQ_F32;
   switch (L->bpw) {
-    case 2: rc = launch_matmul<2>(L, xt_use, x_dt, rowsum, m, mm_out, mm_dt, st); break;
-    case 3: rc = launch_matmul<3>(L, xt_use, x_dt, rowsum, m, mm_out, mm_dt, st); break;
-    default: rc = launch_matmul<4>(L, xt_use, x_dt, rowsum, m, mm_out, mm_dt, st); break;
+    case 2: rc = launch_matmul<2>(L, xt_use, x_dt, rowsum, m, mm_out, mm_dt, st, tiled); break;
+    case 3: rc = launch_matmul<3>(L, xt_use, x_dt, rowsum, m, mm_out, mm_dt, st, tiled); break;
+    default: rc = launch_matmul<4>(L, xt_use, x_dt, rowsum, m, mm_out, mm_dt, st, tiled); break;
   }
   if (rc) return rc;
   if (out_rht) return launch_rht(z, mm_dt, y, y_dt, m, L->n, L->sign_n, 1, nullptr, st);

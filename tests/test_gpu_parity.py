@@ -361,6 +361,31 @@ def test_small_batch_single_launch(G, cb, bpw, n, k, m):
             assert int(ws[:4352].count_nonzero().item()) == 0     # completion counters left at zero
 
 
+@pytest.mark.parametrize("bpw", [2, 3, 4])
+@pytest.mark.parametrize("m,n,k,flags", [(2, 150, 512, 2), (7, 300, 768, 0), (16, 64, 2048, 0), (9, 1000, 256, 2),
+                                         (1, 40, 4096, 2)])
+def test_small_batch_operand_layout(G, cb, bpw, m, n, k, flags):
+    # at most 16 rows, k a multiple of 256, bf16 x: the input transform writes
+    # x~ in the GEMV's operand layout; the operand rows past m keep whatever
+    # the workspace held (here all-ones bytes, NaN as bf16) and feed no stored
+    # output. flags = 2 (no output transform) keeps m <= 4 off the
+    # single-launch layer.
+    i1, i2 = _random_layer(n, k, bpw, 4000 + m + k)
+    s = np.float32(0.03)
+    sn, sk = workloads.signs(n, 71), workloads.signs(k, 72)
+    x = workloads.bf16_round_trip(np.random.default_rng(m + k).standard_normal((m, k)).astype(np.float32))
+    L = G.Layer.from_numpy(i1, i2, s, sn, sk, cb)
+    ws = torch.full((G.workspace_bytes(L, m),), 255, device="cuda", dtype=torch.uint8)
+    ws[:4352] = 0                                      # completion counters start at zero
+    y = torch.empty((m, n), device="cuda", dtype=torch.float32)
+    G.fused_linear(L, _t(x, torch.bfloat16), y, ws, flags)
+    torch.cuda.synchronize()
+    yy = y.cpu().numpy()
+    assert np.all(np.isfinite(yy))
+    ref = og.layer_reference(x, i1, i2, bpw, s, sn, sk, output_rht=not (flags & 2))
+    assert og.relative_error(yy, ref) <= TOL_BF16
+
+
 @pytest.mark.parametrize("n,k,bpw", [(1024, 8192, 2), (8192, 1024, 4), (16384, 1024, 2)])
 def test_one_row_whole_block_layers(G, cb, n, k, bpw):
     # one activation row whose Hadamard block is all of k (8192) or all of n
