@@ -19,9 +19,9 @@ follows:
         precision; GPU fused decode + weight reconstruction; actual_bpp
         includes metadata.
 
-Readings of points the pages leave open are stated where they are used
-and collected in DESIGN.md ("Readings"). Parity status of every function
-is listed in the design doc; functions whose result has no independent pin say
-"parity unpinned" in their docstring.
+Readings of points the pages leave open are stated, each under a label
+(R1, R2, ...), in the docstring of the module that uses them. Functions
+whose result has no independent pin say "parity unpinned" in their
+docstring.
 """
 from . import e8, rht, glq, ldlq, entropack  # noqa: F401

@@ -2,7 +2,7 @@
 
 [glq] "How it works", item 1: the codebook holds 65536 vectors taken from
 the first 7 shells of the E8 lattice. The pages fix neither coordinates,
-nor which 65536 points, nor their order. Readings (Readings R1-R3):
+nor which 65536 points, nor their order. Readings:
 
 R1  Standard coordinates: x is in E8 iff all x_i are integers or all are
     integers + 1/2, and sum(x) is even. Minimum squared norm 2. Points are

@@ -9,7 +9,7 @@ conditional probability model; the coded coordinates are split into
 independently decodable blocks; a GPU decodes the symbols and rebuilds the
 weights in one fused step; the storage rate is set freely (non-integer)
 and reported with metadata as actual_bpp. The page gives no formulas.
-Readings (DESIGN.md, R20-R24):
+Readings of what the page leaves open:
 
 R20 Quantiser: s_r per row as in R16, X = W~ / s_r, y = the nearest point
     of the whole (untruncated) E8 lattice to X / step (Conway & Sloane's

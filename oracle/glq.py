@@ -3,7 +3,7 @@
 [glq] "How it works" (item 1: 16-bit E8 index per 8-weight group; 3/4 bpw
 add a second-stage residual codebook of 8 or 16 bits), "Bit widths" (global
 scale only, no group size), "Results" (sizes equal the nominal rate).
-Readings (Readings R7-R12, R16):
+Readings of what the pages leave open:
 
 R7  Global scale s = fp32(sqrt(mean(W~^2))), computed in float64 and rounded
     once; s = 1 when W~ is identically zero.

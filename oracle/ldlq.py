@@ -8,7 +8,9 @@ drives a sequential sweep over 8-weight blocks, and the quantisation error
 of each block is carried forward to correct the blocks after it (the error
 feedback of GPTQ, "Acknowledgments", with 8-dimensional blocks in place of
 single columns). Item 2: the Hessian is rotated by the same randomized
-Hadamard transform as the weights. Readings (R15, R17-R19):
+Hadamard transform as the weights. Readings of what the pages leave open
+(R15: the error feedback is optional; the plain encoder rounds every group
+on its own, this one adds the feedback below given a Hessian):
 
 R17 Hessian: H [k, k], symmetric positive semi-definite, over the input
     features in the original basis (H = X^T X / m for calibration inputs

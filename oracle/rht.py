@@ -3,7 +3,7 @@
 [glq] "How it works", item 2: random sign flips followed by a fast
 Walsh-Hadamard transform, applied to the weights so the Hessian becomes
 roughly proportional to the identity and Euclidean nearest neighbour is
-close to optimal. Readings (Readings R4-R6):
+close to optimal. Readings of what the pages leave open:
 
 R4  Hadamard matrix: Sylvester construction in natural order,
     H_1 = [1], H_2b = [[H_b, H_b], [H_b, -H_b]]  (= scipy.linalg.hadamard).
