@@ -629,8 +629,8 @@ def main():
         pmc_summary(args)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(rows of x or output features would shard with no exchange; see the design notes).",
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
+              "(rows of x or output features would shard across GPUs with no exchange).",
               file=sys.stderr)
         return 2
     if args.copy_calibration:
