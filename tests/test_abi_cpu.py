@@ -247,6 +247,9 @@ def test_gpu_entry_points_validate_before_launch():
     po = ctypes.byref(ok)
     need = lib.glq_fused_linear_workspace(po, 4)
     assert need >= 4 * 64 * 4 + 4 * 16 * 4
+    # up to 16 rows the workspace has room for x~ of 16 rows (the GEMV's
+    # operand layout pads the activation rows to 16)
+    assert lib.glq_fused_linear_workspace(po, 1) >= 4352 + 16 * 64 * 2 + 16 * 4
     assert lib.glq_fused_linear(po, 1, 0, 4, 1, 0, 256, need - 1, 0, None) == glq.GLQ_ERR_WORKSPACE
     assert lib.glq_fused_linear(po, 1, 0, 4, 1, 0, 0, need, 0, None) == glq.GLQ_ERR_WORKSPACE
     assert lib.glq_fused_linear(po, 1, 0, 4, 1, 0, 257, need, 0, None) == glq.GLQ_ERR_WORKSPACE  # alignment
