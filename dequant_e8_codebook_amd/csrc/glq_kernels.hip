@@ -318,6 +318,40 @@ __device__ __forceinline__ void fwht_pass(float *buf, int b, int lo) {
   }
 }
 
+// The same pass with the stride 2^LO known at compile time, LO a multiple of
+// 4. Under pidx's padding, element base + m 2^LO of a thread's R lies at
+// pidx(base) + m (2^LO + 2^LO / 16) for LO >= 4 (m 2^LO is a multiple of 16),
+// and at pidx(base) + m for LO = 0 (base = q R with R dividing 16, so the R
+// elements share one 16-float run): one address register and constant
+// offsets instead of a shift and two adds per element.
+template <int R, int LO>
+__device__ __forceinline__ void fwht_pass_c(float *buf, int b) {
+  constexpr int h = 1 << LO;
+  constexpr int step = LO == 0 ? 1 : h + h / 16;
+  static_assert(LO % 4 == 0 && 16 % R == 0, "stride a multiple of 16, radix dividing 16");
+  const int nsub = b / R;
+  for (int q = threadIdx.x; q < nsub; q += blockDim.x) {
+    float *p = buf + pidx((q >> LO) * (h * R) + (q & (h - 1)));
+    float v[R];
+#pragma unroll
+    for (int m = 0; m < R; ++m) v[m] = p[m * step];
+    fwht_regs<R>(v);
+#pragma unroll
+    for (int m = 0; m < R; ++m) p[m * step] = v[m];
+  }
+}
+
+template <int R>
+__device__ __forceinline__ void fwht_pass_at(float *buf, int b, int lo) {
+  switch (lo) {
+    case 0: fwht_pass_c<R, 0>(buf, b); break;
+    case 4: fwht_pass_c<R, 4>(buf, b); break;
+    case 8: fwht_pass_c<R, 8>(buf, b); break;
+    case 12: fwht_pass_c<R, 12>(buf, b); break;
+    default: fwht_pass<R>(buf, b, lo); break;
+  }
+}
+
 __device__ __forceinline__ float load_elem(const void *p, glq_dtype dt, size_t off) {
   if (dt == GLQ_F32) return reinterpret_cast<const float *>(p)[off];
   return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(p)[off] << 16);
@@ -462,6 +496,19 @@ rht_rows_vec(const void *in, void *out, int64_t rows, int64_t n, int logb, const
     const int pc = min(tid + 256 * u, pieces - 1);     // clamped: pieces past n are not used
     sgp[u] = *reinterpret_cast<const uint2 *>(signs + 8 * (int64_t)pc);
   }
+  // Up to 4 pieces a thread: the factor of each element (the same for every
+  // row) as floats once, the sign before the transform or sign / sqrt(b)
+  // after it (transposed), and passes with compile-time strides. With 8
+  // pieces, the 8 more registers these take cost a resident wave per SIMD
+  // (175 against 167), so those rows keep runtime strides.
+  constexpr bool SGF = PT <= 4;
+  float sgf[SGF ? PT : 1][8];
+  if constexpr (SGF) {
+#pragma unroll
+    for (int u = 0; u < PT; ++u)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) sgf[u][t] = TRANSPOSE ? rv_sign(sgp[u], t) * inv : rv_sign(sgp[u], t);
+  }
   int64_t row = blockIdx.x;
   if (row < rows) {
 #pragma unroll
@@ -476,8 +523,13 @@ rht_rows_vec(const void *in, void *out, int64_t rows, int64_t n, int logb, const
       if (pc < pieces) {
         float v[8];
         rv_unpack<IN_BF16>(raw[u], v);
+        float *pp = buf + pidx(8 * pc);                // a piece never crosses a 16-float run
 #pragma unroll
-        for (int t = 0; t < 8; ++t) buf[pidx(8 * pc + t)] = TRANSPOSE ? v[t] : v[t] * rv_sign(sgp[u], t);
+        for (int t = 0; t < 8; ++t) {
+          float f = 1.0f;
+          if constexpr (!TRANSPOSE) f = SGF ? sgf[SGF ? u : 0][t] : rv_sign(sgp[u], t);
+          pp[t] = TRANSPOSE ? v[t] : v[t] * f;
+        }
       }
     }
     if (row + gridDim.x < rows) {              // next row, in flight during this row's passes
@@ -487,12 +539,22 @@ rht_rows_vec(const void *in, void *out, int64_t rows, int64_t n, int logb, const
     }
     __syncthreads();
     int lo = 0;
-    for (; lo + 4 <= logb; lo += 4) { fwht_pass<16>(buf, (int)n, lo); __syncthreads(); }
-    switch (logb - lo) {
-      case 1: fwht_pass<2>(buf, (int)n, lo); break;
-      case 2: fwht_pass<4>(buf, (int)n, lo); break;
-      case 3: fwht_pass<8>(buf, (int)n, lo); break;
-      default: break;
+    if constexpr (SGF) {
+      for (; lo + 4 <= logb; lo += 4) { fwht_pass_at<16>(buf, (int)n, lo); __syncthreads(); }
+      switch (logb - lo) {
+        case 1: fwht_pass_at<2>(buf, (int)n, lo); break;
+        case 2: fwht_pass_at<4>(buf, (int)n, lo); break;
+        case 3: fwht_pass_at<8>(buf, (int)n, lo); break;
+        default: break;
+      }
+    } else {                                   // longer rows: the register budget of 3 waves per SIMD
+      for (; lo + 4 <= logb; lo += 4) { fwht_pass<16>(buf, (int)n, lo); __syncthreads(); }
+      switch (logb - lo) {
+        case 1: fwht_pass<2>(buf, (int)n, lo); break;
+        case 2: fwht_pass<4>(buf, (int)n, lo); break;
+        case 3: fwht_pass<8>(buf, (int)n, lo); break;
+        default: break;
+      }
     }
     __syncthreads();
     float rs = 0.0f;
@@ -501,12 +563,16 @@ rht_rows_vec(const void *in, void *out, int64_t rows, int64_t n, int logb, const
       const int pc = tid + 256 * u;
       if (pc < pieces) {
         float v[8];
+        const float *pp = buf + pidx(8 * pc);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) v[t] = buf[pidx(8 * pc + t)];
+        for (int t = 0; t < 8; ++t) v[t] = pp[t];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          v[t] *= inv;
-          if (TRANSPOSE) v[t] *= rv_sign(sgp[u], t);
+          if constexpr (TRANSPOSE && SGF) v[t] *= sgf[SGF ? u : 0][t];
+          else {
+            v[t] *= inv;
+            if (TRANSPOSE) v[t] *= rv_sign(sgp[u], t);
+          }
         }
         if constexpr (OUT_BF16) {
           uint32_t w[4];
