@@ -864,20 +864,25 @@ __device__ __forceinline__ void rr_unpack(const RrRaw<E, IN_BF16> &r, float (&v)
 
 
 
-template <int E, int NW, bool IN_BF16, bool OUT_BF16, bool TRANSPOSE, bool TILE16>
+// FULL: the row is one block of all 64 NW E elements (n = 2^logb = 64 NW E),
+// so every FWHT stage runs (none tested at run time) and every element is in
+// the row (no bounds test per store).
+template <int E, int NW, bool IN_BF16, bool OUT_BF16, bool TRANSPOSE, bool TILE16, bool FULL>
 __device__ __forceinline__ void rr_rows(const void *in, void *out, int64_t rows, int n, int logb,
                                         const int8_t *signs, float *rowsum, float *buf, float *red) {
   const int tid = threadIdx.x;
   const int e0 = E * tid;
   const float inv = 1.0f / sqrtf((float)(1 << logb));
   // signs of this thread's elements before (sign then FWHT) or after the
-  // transform (FWHT then sign); the element map is the same for every row
-  const bool trx = logb > LyF<E, NW>::L;
+  // transform (FWHT then sign, folded with 1 / sqrt(b): an exact product);
+  // the element map is the same for every row
+  const bool trx = FULL || logb > LyF<E, NW>::L;
   float sg[E];
 #pragma unroll
   for (int i = 0; i < E; ++i) {
     const int e = TRANSPOSE ? ly_elem<E, NW>(tid, i, trx) : e0 + i;
-    sg[i] = e < n ? (float)signs[e] : 0.0f;
+    sg[i] = (FULL || e < n) ? (float)signs[e] : 0.0f;
+    if (TRANSPOSE) sg[i] *= inv;
   }
   RrRaw<E, IN_BF16> raw;
   if ((int64_t)blockIdx.x < rows) rr_fetch<E, IN_BF16>(in, (size_t)blockIdx.x * n, e0, n, raw);
@@ -891,14 +896,11 @@ __device__ __forceinline__ void rr_rows(const void *in, void *out, int64_t rows,
       for (int i = 0; i < E; ++i) v[i] *= sg[i];
     }
     __syncthreads();                                 // the previous row is out of buf and red
-    const bool tr = ly_fwht<E, NW>(v, buf, logb, tid);
+    const bool tr = ly_fwht<E, NW, FULL>(v, buf, logb, tid);
     float rs = 0.0f;
     float x[E];
 #pragma unroll
-    for (int i = 0; i < E; ++i) {
-      x[i] = v[i] * inv;
-      if (TRANSPOSE) x[i] *= sg[i];
-    }
+    for (int i = 0; i < E; ++i) x[i] = v[i] * (TRANSPOSE ? sg[i] : inv);
     if constexpr (OUT_BF16) {                        // round to bf16, two at a time
 #pragma unroll
       for (int i = 0; i < E; i += 2) {
@@ -936,7 +938,7 @@ __device__ __forceinline__ void rr_rows(const void *in, void *out, int64_t rows,
 #pragma unroll
       for (int i = 0; i < E; ++i) {
         const int e = ly_elem<E, NW>(tid, i, tr);
-        if (e < n) {
+        if (FULL || e < n) {
           const size_t o = TILE16 ? tile16_index(row, e) : base + e;
           if constexpr (OUT_BF16) reinterpret_cast<uint16_t *>(out)[o] = (uint16_t)(__float_as_uint(x[i]) >> 16);
           else reinterpret_cast<float *>(out)[o] = x[i];
@@ -965,13 +967,21 @@ rht_rows_reg(const void *in, void *out, int64_t rows, int n, int logb, const int
   __shared__ float red[NW];
   int e = 1;
   while (e * 64 * NW < n) e <<= 1;
+#define GLQ_RR(E_)                                                                                          \
+  do {                                                                                                      \
+    if (n == 64 * NW * (E_) && logb == LyF<E_, NW>::L + LyF<E_, NW>::WB)                                    \
+      rr_rows<E_, NW, IN_BF16, OUT_BF16, TRANSPOSE, TILE16, true>(in, out, rows, n, logb, signs, rowsum, rr_buf, red); \
+    else                                                                                                    \
+      rr_rows<E_, NW, IN_BF16, OUT_BF16, TRANSPOSE, TILE16, false>(in, out, rows, n, logb, signs, rowsum, rr_buf, red); \
+  } while (0)
   switch (e) {
-    case 1: rr_rows<1, NW, IN_BF16, OUT_BF16, TRANSPOSE, TILE16>(in, out, rows, n, logb, signs, rowsum, rr_buf, red); break;
-    case 2: rr_rows<2, NW, IN_BF16, OUT_BF16, TRANSPOSE, TILE16>(in, out, rows, n, logb, signs, rowsum, rr_buf, red); break;
-    case 4: rr_rows<4, NW, IN_BF16, OUT_BF16, TRANSPOSE, TILE16>(in, out, rows, n, logb, signs, rowsum, rr_buf, red); break;
-    case 8: rr_rows<8, NW, IN_BF16, OUT_BF16, TRANSPOSE, TILE16>(in, out, rows, n, logb, signs, rowsum, rr_buf, red); break;
-    default: rr_rows<16, NW, IN_BF16, OUT_BF16, TRANSPOSE, TILE16>(in, out, rows, n, logb, signs, rowsum, rr_buf, red); break;
+    case 1: GLQ_RR(1); break;
+    case 2: GLQ_RR(2); break;
+    case 4: GLQ_RR(4); break;
+    case 8: GLQ_RR(8); break;
+    default: GLQ_RR(16); break;
   }
+#undef GLQ_RR
 }
 
 // ---------------------------------------------------------------- decode only
