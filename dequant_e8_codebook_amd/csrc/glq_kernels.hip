@@ -2283,11 +2283,15 @@ int launch_rht(const void *in, glq_dtype in_dt, void *out, glq_dtype out_dt, int
   if (lb > kMaxLogBlock) return GLQ_ERR_UNSUPPORTED;
   const bool aligned = ((reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out) |
                          reinterpret_cast<uintptr_t>(signs)) & 15) == 0;
-  // the register kernel where it measured faster: rows of 16384, and a few
-  // rows (decode-time batches, latency-bound: 1024 threads per row); the LDS
-  // radix-16 kernel below for thousands of rows of 3072 .. 12288
+  // the register kernel where it measured faster: rows that are one whole
+  // block of 1024 .. 16384 (its full-block variant; level with the LDS kernel
+  // at 4096, faster at 1024, 2048, 8192 and 16384), and a few rows
+  // (decode-time batches, latency-bound: 1024 threads per row); the LDS
+  // radix-16 kernel below for thousands of rows of several blocks (3072,
+  // 12288)
   const bool few = rows <= 64 && n % 8 == 0 && n <= 16384;
-  if ((n == 16384 || few) && aligned && in != out) {
+  const bool one_block = n >= 1024 && n <= 16384 && (n & (n - 1)) == 0;
+  if ((one_block || few) && aligned && in != out) {
     const bool ib = in_dt == GLQ_BF16, ob = out_dt == GLQ_BF16;
     if (transpose) {
       if (ib) return ob ? launch_rht_reg<true, true, true>(in, out, rows, n, lb, signs, rowsum, st)

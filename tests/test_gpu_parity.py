@@ -131,11 +131,12 @@ def test_rht_f32(G, n, rows, transpose):
     assert np.max(np.abs(got - ref)) <= 1e-6 * np.max(np.abs(ref)) * np.log2(max(rht.block_size(n), 2))
 
 
-@pytest.mark.parametrize("n", [3072, 4096, 16384, 8200])
+@pytest.mark.parametrize("n", [3072, 4096, 16384, 8200, 1024, 8192])
 @pytest.mark.parametrize("transpose", [0, 1])
 def test_rht_many_rows(G, n, transpose):
     # more rows than the few-row path takes: the LDS radix-16 kernel (3072,
-    # 4096, 8200) and the register kernel on 256 .. 1024 threads (16384)
+    # 8200) and the full-block register kernel on 256 .. 1024 threads (1024,
+    # 4096, 8192, 16384)
     rows = 96
     rng = np.random.default_rng(n + transpose)
     x = rng.standard_normal((rows, n)).astype(np.float32)
