@@ -13,9 +13,10 @@
 //                   optionally rounds to bf16 and records each row's sum of the
 //                   rounded values (needed by the biased 3/4 bpw operands).
 //   rht_rows_vec,   the same for 16-byte aligned rows, out of place: radix-16
-//   rht_rows_reg    passes through LDS (thousands of rows of 3072 .. 12288), or
-//                   butterflies in registers and lane exchanges with one LDS
-//                   transpose (rows of 16384, and a few rows of any width).
+//   rht_rows_reg    passes through LDS (thousands of rows of several blocks,
+//                   3072 or 12288), or butterflies in registers and lane
+//                   exchanges with one LDS transpose (rows that are one block
+//                   of 1024 .. 16384, and a few rows of any width).
 //   decode_weights  indices -> W^ (rotated basis) as float32 or bf16.
 //   gemv_bf16       m <= 16: one 16-row weight tile per workgroup, 16 waves split
 //                   k, bf16 MFMA 16x16x32 with x~ rows as the M side (the few
@@ -297,6 +298,34 @@ __device__ __forceinline__ void fwht_regs(float *v) {
         v[t + s] = a - c;
       }
 }
+
+// v of lane (lane ^ mask) within the wave, mask a power of two <= 32 known at
+// compile time: DPP moves for masks below 16 (quad_perm for 1 and 2; a half-row
+// mirror (lane ^ 7) then quad_perm [3,2,1,0] (lane ^ 3) for 4; a row mirror
+// (lane ^ 15) then a half-row mirror for 8); for 16 and 32 the gfx950 lane
+// swaps, VALU operations that need no trip through the LDS unit.
+// v_permlane16_swap(a, b) exchanges the odd 16-lane rows of a with the even
+// rows of b, v_permlane32_swap(a, b) the upper half of a with the lower half
+// of b; with a = b = v, lane l finds v of lane l ^ 16 (l ^ 32) in the second
+// result where bit 4 (bit 5) of l is clear and in the first where it is set.
+#define GLQ_DPP(v, ctrl) __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xF, 0xF, false))
+__device__ __forceinline__ float lane_xor(float v, int mask) {
+  switch (mask) {
+    case 1: return GLQ_DPP(v, 0xB1);
+    case 2: return GLQ_DPP(v, 0x4E);
+    case 4: return GLQ_DPP(GLQ_DPP(v, 0x141), 0x1B);
+    case 8: return GLQ_DPP(GLQ_DPP(v, 0x140), 0x141);
+    case 16: {
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+      return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+    }
+    default: {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+      return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+    }
+  }
+}
+#undef GLQ_DPP
 
 // LDS layout of every FWHT buffer: one pad float after each 16, so that the
 // radix-16 passes (element strides 1, 16, 256, ...) hit distinct banks.
@@ -595,7 +624,8 @@ rht_rows_vec(const void *in, void *out, int64_t rows, int64_t n, int logb, const
       }
     }
     if (rowsum) {
-      for (int off = 32; off > 0; off >>= 1) rs += __shfl_xor(rs, off);
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) rs += lane_xor(rs, off);   // DPP / lane swaps, no LDS
       if ((tid & 63) == 0) red[tid >> 6] = rs;
       __syncthreads();
       if (tid == 0) rowsum[row] = red[0] + red[1] + red[2] + red[3];
@@ -611,7 +641,8 @@ row_sums_bf16(const uint16_t *x, int64_t rows, int64_t n, float *rowsum) {
     float rs = 0.0f;
     for (int64_t i = threadIdx.x; i < n; i += blockDim.x)
       rs += __uint_as_float((uint32_t)x[(size_t)row * n + i] << 16);
-    for (int off = 32; off > 0; off >>= 1) rs += __shfl_xor(rs, off);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) rs += lane_xor(rs, off);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = rs;
     __syncthreads();
     if (threadIdx.x == 0) rowsum[row] = red[0] + red[1] + red[2] + red[3];
@@ -619,33 +650,6 @@ row_sums_bf16(const uint16_t *x, int64_t rows, int64_t n, float *rowsum) {
   }
 }
 
-// v of lane (lane ^ mask) within the wave, mask a power of two <= 32 known at
-// compile time: DPP moves for masks below 16 (quad_perm for 1 and 2; a half-row
-// mirror (lane ^ 7) then quad_perm [3,2,1,0] (lane ^ 3) for 4; a row mirror
-// (lane ^ 15) then a half-row mirror for 8); for 16 and 32 the gfx950 lane
-// swaps, VALU operations that need no trip through the LDS unit.
-// v_permlane16_swap(a, b) exchanges the odd 16-lane rows of a with the even
-// rows of b, v_permlane32_swap(a, b) the upper half of a with the lower half
-// of b; with a = b = v, lane l finds v of lane l ^ 16 (l ^ 32) in the second
-// result where bit 4 (bit 5) of l is clear and in the first where it is set.
-#define GLQ_DPP(v, ctrl) __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xF, 0xF, false))
-__device__ __forceinline__ float lane_xor(float v, int mask) {
-  switch (mask) {
-    case 1: return GLQ_DPP(v, 0xB1);
-    case 2: return GLQ_DPP(v, 0x4E);
-    case 4: return GLQ_DPP(GLQ_DPP(v, 0x141), 0x1B);
-    case 8: return GLQ_DPP(GLQ_DPP(v, 0x140), 0x141);
-    case 16: {
-      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-      return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
-    }
-    default: {
-      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-      return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
-    }
-  }
-}
-#undef GLQ_DPP
 
 // Block FWHT over bits 0 .. logb - 1 of the flat index of 64 NW E elements
 // (E = 1, 2, 4, 8, 16 per thread, NW = 4, 8 or 16 waves; 2^logb <= 64 NW E)
