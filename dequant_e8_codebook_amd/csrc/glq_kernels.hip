@@ -509,7 +509,7 @@ __device__ __forceinline__ float rv_sign(uint2 u, int t) {
 // current row is written to LDS, so they arrive during its passes and
 // stores; the signs (the same for every row) are loaded once, packed.
 template <bool IN_BF16, bool OUT_BF16, bool TRANSPOSE, int PT>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PT == 8 && IN_BF16 ? 3 : 1)))
 rht_rows_vec(const void *in, void *out, int64_t rows, int64_t n, int logb, const int8_t *signs,
              float *rowsum) {
   extern __shared__ float buf[];
@@ -527,9 +527,11 @@ rht_rows_vec(const void *in, void *out, int64_t rows, int64_t n, int logb, const
   }
   // Up to 4 pieces a thread: the factor of each element (the same for every
   // row) as floats once, the sign before the transform or sign / sqrt(b)
-  // after it (transposed), and passes with compile-time strides. With 8
-  // pieces, the 8 more registers these take cost a resident wave per SIMD
-  // (175 against 167), so those rows keep runtime strides.
+  // after it (transposed). Passes with compile-time strides up to 4 pieces,
+  // and at 8 for bf16 input under a 3-waves-per-SIMD register cap (the
+  // kernel attribute): uncapped they take 175 registers, one resident wave
+  // per SIMD fewer than the 167 of runtime strides. Float32 input at 8
+  // pieces (198 registers either way) keeps runtime strides.
   constexpr bool SGF = PT <= 4;
   float sgf[SGF ? PT : 1][8];
   if constexpr (SGF) {
@@ -568,7 +570,7 @@ rht_rows_vec(const void *in, void *out, int64_t rows, int64_t n, int logb, const
     }
     __syncthreads();
     int lo = 0;
-    if constexpr (SGF) {
+    if constexpr (SGF || (PT == 8 && IN_BF16)) {
       for (; lo + 4 <= logb; lo += 4) { fwht_pass_at<16>(buf, (int)n, lo); __syncthreads(); }
       switch (logb - lo) {
         case 1: fwht_pass_at<2>(buf, (int)n, lo); break;

@@ -148,6 +148,22 @@ def test_rht_many_rows(G, n, transpose):
     assert np.max(np.abs(out.cpu().numpy() - ref)) <= 1e-6 * np.max(np.abs(ref)) * np.log2(rht.block_size(n))
 
 
+@pytest.mark.parametrize("n", [3072, 12288])
+@pytest.mark.parametrize("transpose", [0, 1])
+def test_rht_many_rows_bf16(G, n, transpose):
+    # the LDS kernel on bf16 rows of several blocks: 2 pieces a thread (3072)
+    # and 8 (12288, compile-time pass strides under a 3-wave register cap)
+    rows = 96
+    x = workloads.bf16_round_trip(np.random.default_rng(n + 7 * transpose).standard_normal((rows, n)).astype(np.float32))
+    sig = workloads.signs(n, n + 9)
+    out = torch.empty((rows, n), device="cuda", dtype=torch.bfloat16)
+    G.rht_apply(_t(x, torch.bfloat16), out, _t(sig), bool(transpose))
+    torch.cuda.synchronize()
+    ref = (rht.rht_transpose if transpose else rht.rht_forward)(x.astype(np.float64), sig)
+    got = out.float().cpu().numpy()
+    assert np.max(np.abs(got - ref) / np.maximum(np.abs(ref), 1e-3)) <= 2.0 ** -8   # one bf16 rounding
+
+
 def test_rht_bf16_in_out(G):
     n, rows = 4096, 3
     x = workloads.bf16_round_trip(np.random.default_rng(1).standard_normal((rows, n)).astype(np.float32))
