@@ -578,7 +578,7 @@ rht_rows_vec(const void *in, void *out, int64_t rows, int64_t n, int logb, const
         case 3: fwht_pass_at<8>(buf, (int)n, lo); break;
         default: break;
       }
-    } else {                                   // longer rows: the register budget of 3 waves per SIMD
+    } else {                                   // float32 rows of 8 pieces, rows of 16: runtime strides
       for (; lo + 4 <= logb; lo += 4) { fwht_pass<16>(buf, (int)n, lo); __syncthreads(); }
       switch (logb - lo) {
         case 1: fwht_pass<2>(buf, (int)n, lo); break;
