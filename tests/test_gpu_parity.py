@@ -131,6 +131,29 @@ def test_rht_f32(G, n, rows, transpose):
     assert np.max(np.abs(got - ref)) <= 1e-6 * np.max(np.abs(ref)) * np.log2(max(rht.block_size(n), 2))
 
 
+@pytest.mark.parametrize("n", [1024, 2048, 8192])
+@pytest.mark.parametrize("rows", [1, 16, 64])
+@pytest.mark.parametrize("transpose", [0, 1])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_rht_few_rows_whole_block(G, n, rows, transpose, dt):
+    # a few rows that are one block filling 1024 threads with 1, 2 or 8
+    # elements a thread: the register kernel's full-block variant
+    x = np.random.default_rng(n + rows + 5 * transpose).standard_normal((rows, n)).astype(np.float32)
+    if dt == "bf16":
+        x = workloads.bf16_round_trip(x)
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    sig = workloads.signs(n, n + 11)
+    out = torch.empty((rows, n), device="cuda", dtype=tdt)
+    G.rht_apply(_t(x, tdt), out, _t(sig), bool(transpose))
+    torch.cuda.synchronize()
+    ref = (rht.rht_transpose if transpose else rht.rht_forward)(x.astype(np.float64), sig)
+    got = out.float().cpu().numpy()
+    if dt == "f32":
+        assert np.max(np.abs(got - ref)) <= 1e-6 * np.max(np.abs(ref)) * np.log2(n)
+    else:
+        assert np.max(np.abs(got - ref) / np.maximum(np.abs(ref), 1e-3)) <= 2.0 ** -8   # one bf16 rounding
+
+
 @pytest.mark.parametrize("n", [3072, 4096, 16384, 8200, 1024, 8192])
 @pytest.mark.parametrize("transpose", [0, 1])
 def test_rht_many_rows(G, n, transpose):
