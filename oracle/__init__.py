@@ -19,6 +19,10 @@ follows:
         precision; GPU fused decode + weight reconstruction; actual_bpp
         includes metadata.
 
+nearest_bf.c (loaded by cnative.py) is the brute-force nearest-entry
+search written out as a plain C loop, used to check the faster numpy search
+on large samples.
+
 Readings of points the pages leave open are stated, each under a label
 (R1, R2, ...), in the docstring of the module that uses them. Functions
 whose result has no independent pin say "parity unpinned" in their

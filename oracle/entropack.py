@@ -300,3 +300,60 @@ def actual_bpp(st: Stream) -> float:
     b = (2 * len(st.words) + 4 * st.states.size + 4 * len(st.offsets) + st.model.stored_bytes()
          + 4 * st.n + 4 + (st.n + 7) // 8 + (st.k + 7) // 8)
     return 8.0 * b / (st.n * st.k)
+
+
+def serialise_stream(st: Stream, sign_n: np.ndarray, sign_k: np.ndarray) -> bytes:
+    """Every stored byte of a coded layer, in one buffer: start states
+    (uint32), block offsets (uint32), the model (per table int32 vmin and
+    int32 span, then the uint16 frequencies of every table), the float32
+    row scales and step, the sign vectors at one bit per entry (bit set =
+    -1), then the words (uint16); all little-endian. The shape (n, k) and
+    the groups per lane travel beside the buffer, as a tensor header would
+    carry them."""
+    spans = [len(f) for f in st.model.freq]
+    hdr = np.empty(2 * NTAB, dtype="<i4")
+    hdr[0::2] = st.model.vmin
+    hdr[1::2] = spans
+    parts = [np.ascontiguousarray(st.states, dtype="<u4").tobytes(),
+             np.ascontiguousarray(st.offsets, dtype="<u4").tobytes(),
+             hdr.tobytes()]
+    parts += [np.asarray(f, dtype="<u2").tobytes() for f in st.model.freq]
+    parts.append(np.asarray(st.row_scale, dtype="<f4").tobytes())
+    parts.append(np.asarray([st.step], dtype="<f4").tobytes())
+    for sg in (sign_n, sign_k):
+        parts.append(np.packbits(np.asarray(sg) < 0, bitorder="little").tobytes())
+    parts.append(np.ascontiguousarray(st.words, dtype="<u2").tobytes())
+    return b"".join(parts)
+
+
+def deserialise_stream(blob: bytes, n: int, k: int, lane_groups: int):
+    """Inverse of serialise_stream: (Stream, sign_n, sign_k). Raises
+    ValueError when the buffer is not exactly one coded layer long."""
+    pos = 0
+
+    def take(count, dtype):
+        nonlocal pos
+        size = count * np.dtype(dtype).itemsize
+        if pos + size > len(blob):
+            raise ValueError("buffer too short")
+        a = np.frombuffer(blob, dtype=dtype, count=count, offset=pos)
+        pos += size
+        return a
+
+    total = n * (k // 8)
+    nb = -(-total // (LANES * lane_groups))
+    states = take(nb * LANES, "<u4").astype(np.uint32).reshape(nb, LANES)
+    offsets = take(nb + 1, "<u4").astype(np.uint32)
+    hdr = take(2 * NTAB, "<i4").astype(np.int64)
+    freq = [take(int(hdr[2 * t + 1]), "<u2").astype(np.int64) for t in range(NTAB)]
+    model = Model(hdr[0::2].copy(), freq)
+    row_scale = take(n, "<f4").astype(np.float32)
+    step = np.float32(take(1, "<f4")[0])
+    signs = []
+    for length in (n, k):
+        bits = np.unpackbits(take((length + 7) // 8, np.uint8), bitorder="little")[:length]
+        signs.append(np.where(bits == 1, -1, 1).astype(np.int8))
+    words = take(int(offsets[-1]), "<u2").astype(np.uint16)
+    if pos != len(blob):
+        raise ValueError("trailing bytes")
+    return Stream(n, k, lane_groups, step, row_scale, model, states, offsets, words), signs[0], signs[1]

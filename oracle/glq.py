@@ -262,6 +262,53 @@ def actual_bpw(n: int, k: int, bpw: int) -> float:
     return 8.0 * (compressed_bytes(n, k, bpw) + meta) / (n * k)
 
 
+def serialise_layer(idx1, idx2, scale, sign_n, sign_k) -> bytes:
+    """Every stored byte of a compressed layer, in one buffer: the index
+    planes (little-endian uint16, then uint8 / uint16 residuals), the float32
+    scale and the two sign vectors at one bit per entry (bit set = -1, bits
+    little-endian within a byte). The shape and the bit width travel beside
+    the buffer, as a tensor header would carry them."""
+    parts = [np.ascontiguousarray(idx1, dtype="<u2").tobytes()]
+    if idx2 is not None:
+        i2 = np.asarray(idx2)
+        parts.append(np.ascontiguousarray(i2, dtype="<u1" if i2.dtype == np.uint8 else "<u2").tobytes())
+    parts.append(np.asarray([scale], dtype="<f4").tobytes())
+    for sg in (sign_n, sign_k):
+        parts.append(np.packbits(np.asarray(sg) < 0, bitorder="little").tobytes())
+    return b"".join(parts)
+
+
+def deserialise_layer(blob: bytes, n: int, k: int, bpw: int):
+    """Inverse of serialise_layer: (idx1, idx2 | None, scale, sign_n, sign_k).
+    Raises ValueError when the buffer is not exactly one layer long."""
+    g = n * (k // 8)
+    pos = 0
+
+    def take(count, dtype):
+        nonlocal pos
+        size = count * np.dtype(dtype).itemsize
+        if pos + size > len(blob):
+            raise ValueError("buffer too short")
+        a = np.frombuffer(blob, dtype=dtype, count=count, offset=pos)
+        pos += size
+        return a
+
+    idx1 = take(g, "<u2").astype(np.uint16).reshape(n, k // 8)
+    idx2 = None
+    if bpw == 3:
+        idx2 = take(g, "<u1").astype(np.uint8).reshape(n, k // 8)
+    elif bpw == 4:
+        idx2 = take(g, "<u2").astype(np.uint16).reshape(n, k // 8)
+    scale = np.float32(take(1, "<f4")[0])
+    signs = []
+    for length in (n, k):
+        bits = np.unpackbits(take((length + 7) // 8, np.uint8), bitorder="little")[:length]
+        signs.append(np.where(bits == 1, -1, 1).astype(np.int8))
+    if pos != len(blob):
+        raise ValueError("trailing bytes")
+    return idx1, idx2, scale, signs[0], signs[1]
+
+
 def relative_error(y: np.ndarray, y_ref: np.ndarray) -> float:
     """max|y - y_ref| / max|y_ref| over the whole output (the tolerance
     measure for layer outputs)."""

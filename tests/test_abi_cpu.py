@@ -399,3 +399,68 @@ def test_ep_encode_zero_layer():
         if h.model.nsym[t]:
             assert h.model.nsym[t] == 1 and h.model.freq[t][0] == 2048
     assert np.array_equal(oep.decode_z(o), np.zeros((4, 8, 8), np.int64))
+
+
+def test_ep_encode_exact_ties_match_oracle():
+    # rotated weights that are exact ties of the lattice quantiser (half-way
+    # roundings, equal worst errors under the parity fix, equally distant
+    # cosets): the library's stream is still the oracle's, byte for byte
+    from oracle import entropack as oep
+    from tie_layers import ep_tie_rows, exact_layer, lattice_ties
+    _, _, zg = lattice_ties()
+    wt, pos = ep_tie_rows()
+    sn = np.array([-1, 1, 1], dtype=np.int8)
+    sk = np.where(np.arange(48) % 5 == 2, -1, 1).astype(np.int8)
+    w = exact_layer(wt * 2.0 ** -5, sn, sk)
+    h = glq.ep_encode(w, sn, sk, 1.0, 1, nthreads=2)
+    o = oep.encode(w.astype(np.float64), sn, sk, 1.0, 1)
+    z = oep.decode_z(o)
+    for (r, j), p in pos.items():
+        assert np.array_equal(z[r, j], zg[p])
+    assert np.array_equal(h.row_scale, o.row_scale)
+    assert np.array_equal(h.states, o.states)
+    assert np.array_equal(h.offsets, o.offsets)
+    assert np.array_equal(h.words, o.words)
+
+
+@pytest.mark.parametrize("bpw", [2, 3, 4])
+def test_encode_ref_exact_ties_lowest_index(bpw):
+    # codebook-index ties (reading: lowest index wins): group midpoints of two
+    # entries, and at 3/4 bpw residuals half-way between two residual entries;
+    # the library's indices equal the oracle's and the definition's
+    from oracle import cnative
+    from tie_layers import exact_layer
+    cb = e8.codebook_f64()
+    rng = np.random.default_rng(40 + bpw)
+    n, k = 3, 48
+    kk = og.RESID_SHIFT.get(bpw, 0)
+    groups = []
+    for g in range(n * k // 8):
+        if g % 3 == 0:                                   # origin / root midpoint
+            x = cb[1 + rng.integers(240)] / 2.0
+        elif g % 3 == 1:                                 # two neighbouring entries
+            a = int(rng.integers(1, 9000))
+            d = ((cb - cb[a]) ** 2).sum(1)
+            d[a] = np.inf
+            x = (cb[a] + cb[int(np.argmin(d))]) / 2.0
+        else:                                            # residual tie at 3/4 bpw
+            i1 = int(rng.integers(1, 2401))
+            r = cb[1 + rng.integers(240)] / 2.0          # midpoint of entry 0 and a root
+            x = cb[i1] + (2.0 ** -kk) * r if bpw > 2 else cb[i1]
+        groups.append(x)
+    wt = np.array(groups).reshape(n, k)
+    alpha = 2.0 ** -7
+    sn = np.array([1, -1, -1], dtype=np.int8)
+    sk = np.where(np.arange(k) % 4 == 3, -1, 1).astype(np.int8)
+    w = exact_layer(wt * alpha, sn, sk)
+    i1, i2, s = glq.encode_ref(w, bpw, sn, sk, scale=alpha)
+    o1, o2, _ = og.encode(w.astype(np.float64), bpw, sn, sk, scale=alpha)
+    assert np.array_equal(i1, o1)
+    flat = wt.reshape(-1, 8)
+    assert np.array_equal(o1.reshape(-1), cnative.nearest_bruteforce(flat, cb))
+    if bpw > 2:
+        assert np.array_equal(i2, o2)
+        size = 1 << og.RESID_BITS[bpw]
+        res = (flat - cb[o1.reshape(-1).astype(np.int64)]) * 2.0 ** kk
+        assert np.array_equal(o2.reshape(-1).astype(np.int64), cnative.nearest_bruteforce(res, cb[:size]))
+        assert np.all(o2.reshape(-1)[2::3] == 0)         # the residual ties resolve to entry 0

@@ -138,11 +138,31 @@ def test_orbit_structure_of_stated_order():
 
 
 def test_nearest_matches_bruteforce_random():
+    # the fast search (Conway-Sloane prefilter, k-d tree candidates, margin
+    # fallback) against the definition on 12,000 groups per run: typical
+    # weights, points far outside the codebook, heavy tails; and the
+    # 256-entry residual search on 4,000 more
+    from oracle import cnative
     rng = np.random.default_rng(7)
-    x = np.concatenate([rng.standard_normal((600, 8)),
-                        2.5 * rng.standard_normal((300, 8)),        # many outside the codebook
-                        rng.standard_t(3, (300, 8))])
-    assert np.array_equal(glq.nearest(x), glq.nearest_bruteforce(x))
+    x = np.concatenate([rng.standard_normal((5000, 8)),
+                        2.5 * rng.standard_normal((3000, 8)),        # many outside the codebook
+                        rng.standard_t(3, (2000, 8)),
+                        0.35 * rng.standard_normal((2000, 8))])     # near the origin's cell
+    cb = e8.codebook_f64()
+    assert np.array_equal(glq.nearest(x), cnative.nearest_bruteforce(x, cb))
+    r = 1.2 * rng.standard_normal((4000, 8))
+    assert np.array_equal(glq.nearest(r, size=256), cnative.nearest_bruteforce(r, cb[:256]))
+
+
+def test_bruteforce_in_c_equals_numpy_definition():
+    # the C loop and the numpy expression of the same definition agree,
+    # exact ties included (midpoints between the origin and roots)
+    from oracle import cnative
+    rng = np.random.default_rng(8)
+    cb = e8.codebook_f64()
+    x = np.concatenate([rng.standard_normal((120, 8)), cb[1:31] / 2.0])
+    assert np.array_equal(cnative.nearest_bruteforce(x, cb), glq.nearest_bruteforce(x))
+    assert np.all(cnative.nearest_bruteforce(cb[1:31] / 2.0, cb) == 0)
 
 
 def test_nearest_tie_rule_lowest_index():

@@ -139,15 +139,60 @@ def test_code_length_identity():
     assert abs(used - ideal) < 0.002 * ideal
 
 
-def test_actual_bpp_counts_every_byte():
-    w, sn, sk = _layer(16, 128)
-    st = ep.encode(w, sn, sk, 0.3, lane_groups=2)
-    by = (2 * len(st.words) + 4 * st.states.size + 4 * (st.nblocks + 1) + st.model.stored_bytes()
-          + 4 * 16 + 4 + 2 + 16)
-    assert ep.actual_bpp(st) == pytest.approx(8.0 * by / (16 * 128))
+@pytest.mark.parametrize("n,k,step,lane_groups", [(16, 128, 0.3, 2), (7, 264, 0.5, 1), (40, 64, 0.2, 4)])
+def test_actual_bpp_is_the_serialised_length(n, k, step, lane_groups):
+    # actual_bpp against the length of the coded layer actually written out
+    # and read back: the buffer alone (plus the shape) decodes to the same
+    # lattice points, and every byte of it is counted
+    w, sn, sk = _layer(n, k, "student_t", seed=n + k)
+    st = ep.encode(w, sn, sk, step, lane_groups=lane_groups)
+    blob = ep.serialise_stream(st, sn, sk)
+    assert ep.actual_bpp(st) == 8.0 * len(blob) / (n * k)
+    back, bn, bk = ep.deserialise_stream(blob, n, k, lane_groups)
+    assert np.array_equal(bn, sn) and np.array_equal(bk, sk)
+    assert np.array_equal(ep.decode_z(back), ep.quantise_lattice(w, sn, sk, step)[0])
+    assert np.array_equal(ep.weights_f32(ep.decode_z(back), back.row_scale, back.step),
+                          ep.weights_f32(ep.decode_z(st), st.row_scale, st.step))
+    with pytest.raises(ValueError):
+        ep.deserialise_stream(blob + b"\0", n, k, lane_groups)
 
 
 def test_too_fine_step_rejected():
     w, sn, sk = _layer(4, 64, "student_t")
     with pytest.raises(ValueError):
         ep.encode(w, sn, sk, 0.004)
+
+
+# ------------------------------------------------------------- exact ties ----
+
+def test_closest_point_exact_ties_follow_stated_rule():
+    # hand-derived outcomes of the decoder's tie rules (tests/golden/
+    # e8_lattice_ties.txt): half-to-even rounding, parity fixed on the first
+    # largest error, integer coset on equal distance
+    from tie_layers import lattice_ties
+    names, x, z = lattice_ties()
+    y, dist, _ = e8.closest_e8(x)
+    for nm, a, b in zip(names, y, z):
+        assert np.array_equal(a, b), nm
+    # each is a genuine tie: another lattice point is exactly as far
+    rel = _rel() / 2.0
+    for xi, yi, di in zip(x, y, dist):
+        d = ((xi[None] - (yi / 2.0)[None] - rel) ** 2).sum(axis=1)
+        assert d.min() == di
+
+
+def test_quantiser_exact_ties_through_the_layer():
+    # the same ties reached through the whole quantiser: exact rotation,
+    # row scale exactly 1, step 1
+    from tie_layers import ep_tie_rows, exact_layer, lattice_ties
+    _, _, zg = lattice_ties()
+    wt, pos = ep_tie_rows()
+    sn = np.array([1, -1, 1], dtype=np.int8)
+    sk = np.where(np.arange(48) % 3 == 1, -1, 1).astype(np.int8)
+    w = exact_layer(wt * 2.0 ** -6, sn, sk)
+    z, s = ep.quantise_lattice(w, sn, sk, 1.0)
+    assert np.all(s == np.float32(2.0 ** -6))
+    for (r, j), p in pos.items():
+        assert np.array_equal(z[r, j], zg[p])
+    st = ep.encode(w.astype(np.float64), sn, sk, 1.0, lane_groups=1)
+    assert np.array_equal(ep.decode_z(st), z)

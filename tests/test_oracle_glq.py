@@ -42,11 +42,32 @@ def test_results_table_sizes_follow_nominal_rate():
         assert abs(bf16_mb * bpw / 16 - mb) <= 1.0       # 1537.5, 1153.1, 768.75
 
 
-def test_actual_bpw_includes_metadata():
-    # 4096x4096 at 2 bpw: 4 MiB of indices + 4 B scale + 1024 B of packed signs
-    a = glq.actual_bpw(4096, 4096, 2)
-    assert a == 8 * (4194304 + 4 + 1024) / (4096 * 4096)
-    assert 2.0 < a < 2.001
+@pytest.mark.parametrize("n,k,bpw", [(4096, 4096, 2), (37, 136, 3), (64, 256, 4), (1, 8, 2)])
+def test_actual_bpw_is_the_serialised_length(n, k, bpw):
+    # actual_bpw against the length of a layer actually written out (index
+    # planes, scale, packed signs) and read back losslessly: the stored
+    # bytes are enough to rebuild every weight, and they are all counted
+    rng = np.random.default_rng(n + k + bpw)
+    i1 = rng.integers(0, 65536, (n, k // 8)).astype(np.uint16)
+    i2 = None
+    if bpw == 3:
+        i2 = rng.integers(0, 256, (n, k // 8)).astype(np.uint8)
+    elif bpw == 4:
+        i2 = rng.integers(0, 65536, (n, k // 8)).astype(np.uint16)
+    s = np.float32(0.0173)
+    sn = np.where(rng.random(n) < 0.5, -1, 1).astype(np.int8)
+    sk = np.where(rng.random(k) < 0.5, -1, 1).astype(np.int8)
+    blob = glq.serialise_layer(i1, i2, s, sn, sk)
+    assert glq.actual_bpw(n, k, bpw) == 8.0 * len(blob) / (n * k)
+    j1, j2, t, tn, tk = glq.deserialise_layer(blob, n, k, bpw)
+    assert np.array_equal(j1, i1) and t == s and np.array_equal(tn, sn) and np.array_equal(tk, sk)
+    if bpw > 2:
+        assert np.array_equal(j2, i2)
+    assert np.array_equal(glq.decode_bf16_bits(j1, j2, bpw, t), glq.decode_bf16_bits(i1, i2, bpw, s))
+    with pytest.raises(ValueError):
+        glq.deserialise_layer(blob[:-1], n, k, bpw)
+    if n * k == 4096 * 4096:
+        assert 2.0 < glq.actual_bpw(n, k, bpw) < 2.001
 
 
 # ---------------------------------------------------------------- scale ----
