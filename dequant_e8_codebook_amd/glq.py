@@ -244,6 +244,116 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+# ------------------------------------------------ argument checks (no launch)
+# The C entry points check pointers, sizes and enums; only the caller knows
+# how large each buffer is. These checks run before every GPU call so a
+# wrong shape, a strided view or a host tensor raises ValueError instead of
+# reaching a kernel.
+
+def _dev_tensor(t, name, device=None, shape=None, numel=None, min_numel=None, dtypes=None):
+    if t is None:
+        raise ValueError(f"{name}: missing")
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name}: must be a device (cuda) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name}: {t.numel()} elements, expected {numel}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name}: {t.numel()} elements, expected at least {min_numel}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected one of {dtypes}")
+    return t
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _check_layer(layer, need_sign_k=True, need_sign_n=True):
+    torch = _torch()
+    dev = layer.idx1.device if getattr(layer.idx1, "is_cuda", False) else None
+    if dev is None:
+        raise ValueError("idx1: must be a device (cuda) tensor")
+    g = layer.k // 8
+    if layer.bpw not in (2, 3, 4) or layer.k % 8 or layer.n < 1 or layer.k < 8:
+        raise ValueError("layer: bad n, k or bpw")
+    _dev_tensor(layer.idx1, "idx1", dev, shape=(layer.n, g), dtypes=(torch.int16,))
+    if layer.bpw == 2:
+        if layer.idx2 is not None:
+            raise ValueError("idx2: must be None at 2 bpw")
+    else:
+        _dev_tensor(layer.idx2, "idx2", dev, shape=(layer.n, g),
+                    dtypes=((torch.uint8,) if layer.bpw == 3 else (torch.int16,)))
+    _dev_tensor(layer.cb, "cb", dev, min_numel=_codebook_bytes(), dtypes=(torch.uint8,))
+    if need_sign_k:
+        _dev_tensor(layer.sign_k, "sign_k", dev, numel=layer.k, dtypes=(torch.int8,))
+    if need_sign_n:
+        _dev_tensor(layer.sign_n, "sign_n", dev, numel=layer.n, dtypes=(torch.int8,))
+    if layer.row_scale is not None:
+        _dev_tensor(layer.row_scale, "row_scale", dev, numel=layer.n, dtypes=(torch.float32,))
+    return dev
+
+
+def _check_ep_layer(layer, need_sign_k=False, need_sign_n=False):
+    torch = _torch()
+    dev = layer.words.device if getattr(layer.words, "is_cuda", False) else None
+    if dev is None:
+        raise ValueError("words: must be a device (cuda) tensor")
+    total = layer.n * (layer.k // 8)
+    if layer.k % 8 or layer.n < 1 or layer.k < 8 or layer.lane_groups < 1:
+        raise ValueError("layer: bad n, k or lane_groups")
+    nb = -(-total // (EP_LANES * layer.lane_groups))
+    _dev_tensor(layer.row_scale, "row_scale", dev, numel=layer.n, dtypes=(torch.float32,))
+    _dev_tensor(layer.states, "states", dev, numel=nb * EP_LANES, dtypes=(torch.int32,))
+    _dev_tensor(layer.offsets, "offsets", dev, numel=nb + 1, dtypes=(torch.int32,))
+    _dev_tensor(layer.words, "words", dev, min_numel=max(8, (layer.nwords + 7) // 8 * 8), dtypes=(torch.int16,))
+    _dev_tensor(layer.lut, "lut", dev, numel=EP_LUT_BYTES, dtypes=(torch.uint8,))
+    if layer.words.numel() % 8 or layer.words.data_ptr() % 16:
+        raise ValueError("words: must hold a multiple of 8 entries and be 16-byte aligned")
+    if need_sign_k:
+        _dev_tensor(layer.sign_k, "sign_k", dev, numel=layer.k, dtypes=(torch.int8,))
+    if need_sign_n:
+        _dev_tensor(layer.sign_n, "sign_n", dev, numel=layer.n, dtypes=(torch.int8,))
+    return dev
+
+
+def _check_linear_io(dev, n, k, x, y, workspace, flags):
+    torch = _torch()
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError(f"x: shape {tuple(x.shape)}, expected (m, {k})")
+    m = x.shape[0]
+    _dev_tensor(x, "x", dev, dtypes=(torch.float32, torch.bfloat16))
+    _dev_tensor(y, "y", dev, shape=(m, n), dtypes=(torch.float32, torch.bfloat16))
+    _dev_tensor(workspace, "workspace", dev)
+    if workspace.data_ptr() % 256:
+        raise ValueError("workspace: must be 256-byte aligned")
+    if flags & ~(FLAG_NO_INPUT_RHT | FLAG_NO_OUTPUT_RHT):
+        raise ValueError("flags: unknown bits")
+    for t, nm in ((x, "x"), (y, "y")):
+        a0, a1 = t.data_ptr(), t.data_ptr() + _nbytes(t)
+        b0, b1 = workspace.data_ptr(), workspace.data_ptr() + _nbytes(workspace)
+        if _nbytes(t) and a0 < b1 and b0 < a1:
+            raise ValueError(f"{nm}: overlaps the workspace")
+    return m
+
+
+_CB_BYTES = None
+
+
+def _codebook_bytes() -> int:
+    global _CB_BYTES
+    if _CB_BYTES is None:
+        need = _sz(0)
+        _check(_lib.glq_build_codebook(GLQ_CB_DEVICE, None, 0, ctypes.byref(need)), "glq_build_codebook")
+        _CB_BYTES = int(need.value)
+    return _CB_BYTES
+
+
 def device_codebook(device="cuda"):
     """The GLQ_CB_DEVICE tables copied into a device uint8 tensor."""
     torch = _torch()
@@ -344,6 +454,11 @@ class EpLayer:
 
 def ep_decode_weights(layer: EpLayer, out, stream=None):
     """Fused symbol decode + weight reconstruction (glq_ep_decode_weights)."""
+    torch = _torch()
+    dev = _check_ep_layer(layer)
+    _dev_tensor(out, "out", dev, shape=(layer.n, layer.k), dtypes=(torch.float32, torch.bfloat16))
+    if out.data_ptr() % 16:
+        raise ValueError("out: must be 16-byte aligned")
     st = layer.struct()
     _check(_lib.glq_ep_decode_weights(ctypes.byref(st), out.data_ptr(), _dtype_code(out), _stream_ptr(stream)),
            "glq_ep_decode_weights")
@@ -357,8 +472,10 @@ def ep_workspace_bytes(layer: EpLayer, m: int) -> int:
 
 def ep_fused_linear(layer: EpLayer, x, y, workspace, flags: int = 0, stream=None):
     """y = U^T W^ (V x) on an entropy-coded layer (glq_ep_fused_linear)."""
+    dev = _check_ep_layer(layer, not (flags & FLAG_NO_INPUT_RHT), not (flags & FLAG_NO_OUTPUT_RHT))
+    m = _check_linear_io(dev, layer.n, layer.k, x, y, workspace, flags)
     st = layer.struct()
-    rc = _lib.glq_ep_fused_linear(ctypes.byref(st), x.data_ptr(), _dtype_code(x), x.shape[0], y.data_ptr(),
+    rc = _lib.glq_ep_fused_linear(ctypes.byref(st), x.data_ptr(), _dtype_code(x), m, y.data_ptr(),
                                   _dtype_code(y), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                   flags, _stream_ptr(stream))
     _check(rc, "glq_ep_fused_linear")
@@ -367,8 +484,21 @@ def ep_fused_linear(layer: EpLayer, x, y, workspace, flags: int = 0, stream=None
 
 def rht_apply(inp, out, signs, transpose: bool, stream=None):
     """out = RHT(inp) along the last axis (glq_rht_apply)."""
+    torch = _torch()
+    if inp.dim() < 1 or inp.shape[-1] < 1:
+        raise ValueError("inp: needs a last axis of length >= 1")
     n = inp.shape[-1]
-    rows = inp.numel() // n if n else 0
+    rows = inp.numel() // n
+    dev = _dev_tensor(inp, "inp", dtypes=(torch.float32, torch.bfloat16)).device
+    _dev_tensor(out, "out", dev, shape=tuple(inp.shape), dtypes=(torch.float32, torch.bfloat16))
+    _dev_tensor(signs, "signs", dev, numel=n, dtypes=(torch.int8,))
+    if out.data_ptr() != inp.data_ptr() and _nbytes(inp) and _nbytes(out):
+        a0, a1 = inp.data_ptr(), inp.data_ptr() + _nbytes(inp)
+        b0, b1 = out.data_ptr(), out.data_ptr() + _nbytes(out)
+        if a0 < b1 and b0 < a1:
+            raise ValueError("out: partly overlaps inp (only the same buffer is allowed)")
+    if out.data_ptr() == inp.data_ptr() and out.dtype != inp.dtype:
+        raise ValueError("out: in place needs the same dtype")
     rc = _lib.glq_rht_apply(inp.data_ptr(), _dtype_code(inp), out.data_ptr(), _dtype_code(out), rows, n,
                             signs.data_ptr(), int(bool(transpose)), _stream_ptr(stream))
     _check(rc, "glq_rht_apply")
@@ -376,6 +506,10 @@ def rht_apply(inp, out, signs, transpose: bool, stream=None):
 
 
 def decode_weights(layer: Layer, out, stream=None):
+    """W^ [n, k] in the rotated basis (glq_decode_weights)."""
+    torch = _torch()
+    dev = _check_layer(layer, False, False)
+    _dev_tensor(out, "out", dev, shape=(layer.n, layer.k), dtypes=(torch.float32, torch.bfloat16))
     st = layer.struct()
     _check(_lib.glq_decode_weights(ctypes.byref(st), out.data_ptr(), _dtype_code(out), _stream_ptr(stream)),
            "glq_decode_weights")
@@ -389,8 +523,9 @@ def workspace_bytes(layer: Layer, m: int) -> int:
 
 def fused_linear(layer: Layer, x, y, workspace, flags: int = 0, stream=None):
     """y = U^T (s W^) (V x) (glq_fused_linear); x [m, k], y [m, n]."""
+    dev = _check_layer(layer, not (flags & FLAG_NO_INPUT_RHT), not (flags & FLAG_NO_OUTPUT_RHT))
+    m = _check_linear_io(dev, layer.n, layer.k, x, y, workspace, flags)
     st = layer.struct()
-    m = x.shape[0]
     rc = _lib.glq_fused_linear(ctypes.byref(st), x.data_ptr(), _dtype_code(x), m, y.data_ptr(),
                                _dtype_code(y), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                flags, _stream_ptr(stream))

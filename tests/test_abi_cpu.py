@@ -464,3 +464,21 @@ def test_encode_ref_exact_ties_lowest_index(bpw):
         res = (flat - cb[o1.reshape(-1).astype(np.int64)]) * 2.0 ** kk
         assert np.array_equal(o2.reshape(-1).astype(np.int64), cnative.nearest_bruteforce(res, cb[:size]))
         assert np.all(o2.reshape(-1)[2::3] == 0)         # the residual ties resolve to entry 0
+
+
+def test_binding_rejects_host_tensors_before_any_call():
+    # the binding checks device, shape and contiguity before the C call: host
+    # tensors never reach a kernel
+    import torch
+    i1 = np.zeros((16, 8), np.uint16)
+    cbh = torch.zeros(glq._codebook_bytes(), dtype=torch.uint8)
+    L = glq.Layer.from_numpy(i1, None, 1.0, np.ones(16, np.int8), np.ones(64, np.int8), cbh, device="cpu")
+    x = torch.zeros((2, 64), dtype=torch.bfloat16)
+    y = torch.zeros((2, 16), dtype=torch.bfloat16)
+    ws = torch.zeros(1 << 16, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        glq.fused_linear(L, x, y, ws)
+    with pytest.raises(ValueError):
+        glq.decode_weights(L, torch.zeros((16, 64), dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        glq.rht_apply(x, x, torch.ones(64, dtype=torch.int8), False)

@@ -63,7 +63,8 @@ def _run_linear(G, cb, i1, i2, s, sn, sk, x, x_dt, y_dt, flags=0):
     L = G.Layer.from_numpy(i1, i2, s, sn, sk, cb)
     m = x.shape[0]
     xt = _t(x.astype(np.float32), torch.float32 if x_dt == "f32" else torch.bfloat16)
-    y = torch.empty((m, L.n), device="cuda", dtype=torch.float32 if y_dt == "f32" else torch.bfloat16)
+    # NaN-filled so that an output element no kernel writes fails the finiteness checks
+    y = torch.full((m, L.n), float("nan"), device="cuda", dtype=torch.float32 if y_dt == "f32" else torch.bfloat16)
     ws = torch.zeros(max(G.workspace_bytes(L, max(m, 1)), 256), device="cuda", dtype=torch.uint8)
     G.fused_linear(L, xt, y, ws, flags)
     torch.cuda.synchronize()
@@ -268,11 +269,13 @@ def test_gemv_many_row_tiles(G, cb, m, k):
 
 
 @pytest.mark.parametrize("bpw", [2, 3, 4])
-@pytest.mark.parametrize("m,n,k", [(300, 320, 512), (257, 264, 160), (64, 512, 4160), (40, 136, 72)])
+@pytest.mark.parametrize("m,n,k", [(300, 320, 512), (257, 264, 160), (64, 512, 4160), (40, 136, 72),
+                                   (512, 1024, 136), (1000, 1024, 264)])
 def test_prefill_tiles(G, cb, bpw, m, n, k):
     # several 256 x 256 output tiles with ragged row and column tails, the
     # 16-byte-store epilogue (n * element size % 16 == 0) and its per-element
-    # fallback, and a k that is not a multiple of the 64-input k-step
+    # fallback, a k that is not a multiple of the 64-input k-step, and 8 and
+    # 16 tiles (every XCD dealt whole tiles), all rows checked
     i1, i2 = _random_layer(n, k, bpw, 3000 + m + n + k)
     s = np.float32(0.017)
     sn, sk = workloads.signs(n, 41), workloads.signs(k, 42)
@@ -352,28 +355,36 @@ def test_m_zero_is_noop(G, cb):
 
 # ------------------------------------------------- full-size workloads ----
 
-def _full_check(G, cb, spec, rows_to_check):
+def _tile_rows(m, tile=256):
+    """One row in every 256-row output tile (the prefill GEMM's M tiles, at a
+    different offset in each), the last row, and a few more."""
+    rows = {min(m - 1, t + (t // tile * 37 + 11) % tile) for t in range(0, m, tile)}
+    return sorted(rows | {0, m - 1, m // 2})
+
+
+def _full_check(G, cb, spec, rows):
     i1, i2 = _random_layer(spec.n, spec.k, spec.bpw, spec.seed_base + 7)
     s = np.float32(0.02)
     sn, sk = workloads.sign_n(spec), workloads.sign_k(spec)
     x = workloads.activations(spec)
     y = _run_linear(G, cb, i1, i2, s, sn, sk, x, spec.x_dtype, spec.y_dtype)
-    rows = sorted(set(r % spec.m for r in rows_to_check))
+    assert np.all(np.isfinite(y))                      # every element written (y starts as NaN)
+    rows = sorted(set(r % spec.m for r in rows))
     ref = og.layer_reference(x[rows], i1, i2, spec.bpw, s, sn, sk)
     assert og.relative_error(y[rows], ref) <= TOL_BF16
-    assert np.all(np.isfinite(y))
 
 
 @pytest.mark.parametrize("name", ["gemv", "batch16", "prefill_up"])
 def test_full_size_workload(G, cb, name):
     spec = workloads.layer_specs(name)[0]
-    _full_check(G, cb, spec, [0, 1, spec.m // 2, spec.m - 1, 977])
+    rows = range(spec.m) if spec.m <= 16 else _tile_rows(spec.m) + [977]
+    _full_check(G, cb, spec, rows)
 
 
 @pytest.mark.parametrize("which", range(6))
 def test_full_size_dit_block(G, cb, which):
     spec = workloads.layer_specs("dit_block")[which]
-    _full_check(G, cb, spec, [0, 2047, 4095])
+    _full_check(G, cb, spec, _tile_rows(spec.m))
 
 
 # ------------------------------------- single-launch layer at small batch ----
@@ -729,3 +740,40 @@ def test_largest_hadamard_block_along_k(G, cb, m, x_dt, y_dt, bpw):
     y = _run_linear(G, cb, i1, i2, s, sn, sk, x, x_dt, y_dt)
     ref = og.layer_reference(x, i1, i2, bpw, s, sn, sk)
     assert og.relative_error(y, ref) <= (TOL_F32 if x_dt == "f32" and y_dt == "f32" else TOL_BF16)
+
+
+# ------------------------------------------------------ binding checks ----
+
+def test_binding_rejects_bad_arguments(G, cb):
+    # wrong shapes, strided or mismatched tensors raise ValueError in the
+    # binding before any launch; the good call afterwards still works
+    n, k, m = 32, 64, 3
+    i1, i2 = _random_layer(n, k, 4, 5)
+    L = G.Layer.from_numpy(i1, i2, 0.01, workloads.signs(n, 1), workloads.signs(k, 2), cb)
+    x = torch.randn(m, k, device="cuda").to(torch.bfloat16)
+    y = torch.empty(m, n, device="cuda", dtype=torch.bfloat16)
+    ws = torch.zeros(G.workspace_bytes(L, m), device="cuda", dtype=torch.uint8)
+    bad = [
+        dict(x=torch.randn(m, k + 8, device="cuda").to(torch.bfloat16)),          # k mismatch
+        dict(x=torch.randn(k, device="cuda").to(torch.bfloat16)),                 # 1-D x
+        dict(x=torch.randn(k, m, device="cuda").to(torch.bfloat16).t()),          # strided x
+        dict(y=torch.empty(m, n + 1, device="cuda", dtype=torch.bfloat16)),       # y shape
+        dict(y=torch.empty(m + 1, n, device="cuda", dtype=torch.bfloat16)),
+        dict(x=x.cpu()),                                                          # host x
+        dict(ws=ws[1:]),                                                          # misaligned workspace
+        dict(y=ws[:m * n * 2].view(torch.bfloat16).view(m, n)),                   # y inside the workspace
+    ]
+    for b in bad:
+        with pytest.raises(ValueError):
+            G.fused_linear(L, b.get("x", x), b.get("y", y), b.get("ws", ws))
+    short = G.Layer(L.n, L.k, L.bpw, L.scale, L.idx1, L.idx2, L.sign_k[:k - 1], L.sign_n, L.cb)
+    with pytest.raises(ValueError):
+        G.fused_linear(short, x, y, ws)
+    G.fused_linear(short, x, y, ws, G.FLAG_NO_INPUT_RHT)          # signs along k not needed then
+    with pytest.raises(ValueError):
+        G.decode_weights(L, torch.empty(n, k + 8, device="cuda", dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        G.rht_apply(x, torch.empty(m, k, device="cuda"), torch.ones(k - 1, device="cuda", dtype=torch.int8), False)
+    G.fused_linear(L, x, y, ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y.float()).all()
