@@ -730,7 +730,7 @@ def main():
     ap.add_argument("--layers", type=int, default=128, help="distinct copies of the index planes rotated through")
     ap.add_argument("--kernel-launches", type=int, default=1024)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU work (small-batch runs)")
-    ap.add_argument("--cpu-rows", type=int, default=256,
+    ap.add_argument("--cpu-rows", type=int, default=1024,
                     help="activation rows per linear in the oracle's timed sample (prefill / DiT runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")

@@ -14,7 +14,7 @@ from dataclasses import dataclass
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "lib", "libglq.so")
+LIB_PATH = os.environ.get("GLQ_LIBRARY") or os.path.join(_PKG, "lib", "libglq.so")   # override: another build
 
 GLQ_OK, GLQ_ERR_ARG, GLQ_ERR_UNSUPPORTED, GLQ_ERR_HIP, GLQ_ERR_WORKSPACE = 0, -1, -2, -3, -4
 GLQ_F32, GLQ_BF16 = 0, 1
