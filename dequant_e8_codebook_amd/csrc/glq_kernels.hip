@@ -1696,6 +1696,23 @@ __device__ __forceinline__ void gm_epilogue(const f32x16 (&acc)[8][2], const flo
   }
 }
 
+// Issue pattern of one MFMA block of the decode-GEMM: 16 rounds of one MFMA
+// followed by up to D LDS reads, V VALU operations, W LDS writes and M
+// global loads. A wave issues in order and each MFMA 32x32x16 keeps the
+// matrix core busy for 32 cycles, so the decode work placed between two
+// MFMAs runs in their shadow instead of after a run of back-to-back MFMAs.
+template <int V, int D, int W = 0, int M = 0>
+__device__ __forceinline__ void gm_interleave16() {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (D > 0) __builtin_amdgcn_sched_group_barrier(0x100, D, 0);
+    if constexpr (V > 0) __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+    if constexpr (W > 0) __builtin_amdgcn_sched_group_barrier(0x200, W, 0);
+    if constexpr (M > 0) __builtin_amdgcn_sched_group_barrier(0x020, M, 0);
+  }
+}
+
 template <int BPW, bool G4, bool OUT_BF16>
 __global__ void __launch_bounds__(256, 1)
 gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uint16_t *xt,
@@ -1788,21 +1805,27 @@ gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
       }
     };
 
+    // walks per step: 8 groups, two table walks each at 4 bpw
+    constexpr int NW = BPW == 4 ? 16 : 8;
     Dec8<BPW> D;
     D.p1(q1, q2);
     mfma_block(0);
+    gm_interleave16<3, (NW + 8 + 15) / 16>();
     __builtin_amdgcn_sched_barrier(0);
     D.p2(q1, q2);
     mfma_block(1);
+    gm_interleave16<(5 * NW + 15) / 16, (NW + 8 + 15) / 16>();
     __builtin_amdgcn_sched_barrier(0);
     D.p3(q1, q2);
     mfma_block(2);
+    gm_interleave16<(9 * NW + 15) / 16, (2 * NW + 8 + 15) / 16>();
     __builtin_amdgcn_sched_barrier(0);
     uint4 bn[8];
     D.p4(bn);
     mfma_block(3);
     gm_store_a((s & 1) ? As0 : As1, ra, k - GM_BK * (s + 1));   // tile s + 1 (unused past the end)
     gm_load_a(xt, m, k, m0, min(s + 2, S - 1), ra);
+    gm_interleave16<3, 1, 1, 1>();
 #pragma unroll
     for (int g = 0; g < 8; ++g) bv[g >> 2][g & 3] = bn[g];
     __syncthreads();
