@@ -7,7 +7,8 @@
 //   (|x|^2, -orbit size, max|x_i|, |x| lexicographic, sign counter j)
 // with orbit = points sharing |x| (2^nnz points when integer, 128 when
 // half-integer), j over the nonzero coordinates in order (integer points) or
-// over x1..x7 (half-integer points, the sign of x8 fixed by parity).
+// over x1, x2, x3, x5, .., x8 (half-integer points, the sign of x4 fixed by
+// the even-sum rule). Format 3 of the tables (glq_tables.h).
 //
 // Points are held doubled, y = 2x in int8.
 #include <algorithm>
@@ -61,7 +62,8 @@ Point make_point(const int8_t *y) {
   p.size = half ? 128 : (1 << nnz);
   p.j = 0;
   if (half) {
-    for (int t = 0; t < 7; ++t) if (y[t] < 0) p.j |= 1u << t;
+    static const int coord[7] = {0, 1, 2, 4, 5, 6, 7};   // bit -> coordinate; x4 by parity
+    for (int b = 0; b < 7; ++b) if (y[coord[b]] < 0) p.j |= 1u << b;
   } else {
     int r = 0;
     for (int t = 0; t < 8; ++t) {
@@ -114,18 +116,6 @@ std::vector<Point> build_points() {
   return pts;
 }
 
-struct Orbit {
-  uint32_t start;   // first index i
-  uint32_t count;   // entries inside the codebook
-  uint32_t size;    // full orbit size
-  bool half;
-  std::array<int, 8> a;   // |y|
-};
-
-uint64_t abs_key4(const int *a) {
-  return (uint64_t)a[0] | ((uint64_t)a[1] << 8) | ((uint64_t)a[2] << 16) | ((uint64_t)a[3] << 24);
-}
-
 uint16_t bf16_of_half(int y) {  // bf16 bits of y / 2 (exact: |y| <= 6)
   float f = 0.5f * (float)y;
   uint32_t u;
@@ -135,57 +125,94 @@ uint16_t bf16_of_half(int y) {  // bf16 bits of y / 2 (exact: |y| <= 6)
 
 struct Tables {
   std::vector<Point> pts;
-  std::vector<Orbit> orbits;
   std::vector<uint8_t> blob;      // GLQ_CB_DEVICE
   std::vector<int8_t> flat;       // GLQ_CB_INT8_2X
   bool ok = false;
 };
 
-// Signed half-vectors: y values of 4 coordinates.
-struct HalfTable {
-  std::vector<std::array<int, 4>> entries;
-  std::map<uint64_t, uint32_t> natural;   // abs pattern -> first entry
-  std::map<uint64_t, uint32_t> qblock;    // half-integer abs pattern -> first entry (24 entries)
+typedef std::array<int, 4> Half;  // doubled coordinates of 4 consecutive coordinates
 
-  uint32_t natural_block(const int *a) {
-    uint64_t key = abs_key4(a);
-    auto it = natural.find(key);
-    if (it != natural.end()) return it->second;
+// The half-vector table: blocks appended in order, and an index of every
+// run of 1, 2 or 4 consecutive entries (content -> first position), so that
+// the record of a chunk points into an existing block whenever one holds
+// the run it needs.
+struct HalfTable {
+  std::vector<Half> entries;
+  std::map<std::vector<int>, std::vector<uint32_t>> runs;    // content -> positions, increasing
+  std::map<std::vector<int>, uint32_t> aligned_runs;         // first position with start % 4 == 0
+  std::map<std::pair<int, std::vector<int>>, uint32_t> blocks;  // (kind, |pattern|) -> first entry
+
+  static std::vector<int> key(const std::vector<Half> &r) {
+    std::vector<int> k;
+    for (const Half &h : r) k.insert(k.end(), h.begin(), h.end());
+    return k;
+  }
+  void index_from(size_t first) {
+    for (size_t p = first >= 3 ? first - 3 : 0; p < entries.size(); ++p)
+      for (size_t len : {1u, 2u, 4u}) {
+        if (p + len > entries.size()) continue;
+        std::vector<Half> r(entries.begin() + p, entries.begin() + p + len);
+        auto k = key(r);
+        auto &v = runs[k];
+        if (v.empty() || v.back() < p) v.push_back((uint32_t)p);
+        if (p % 4 == 0) aligned_runs.emplace(k, (uint32_t)p);
+      }
+  }
+  uint32_t append(const std::vector<Half> &r) {    // at a multiple of 4
+    while (entries.size() % 4) entries.push_back(Half{0, 0, 0, 0});
+    const size_t first = entries.size();
+    entries.insert(entries.end(), r.begin(), r.end());
+    index_from(first);
+    return (uint32_t)first;
+  }
+  uint32_t find_aligned(const std::vector<Half> &r) {
+    auto it = aligned_runs.find(key(r));
+    return it != aligned_runs.end() ? it->second : append(r);
+  }
+  uint32_t find_from(const std::vector<Half> &r, uint32_t min_pos) {   // first position >= min_pos
+    auto it = runs.find(key(r));
+    if (it != runs.end())
+      for (uint32_t p : it->second)
+        if (p >= min_pos) return p;
+    return append(r);
+  }
+  // every sign pattern of the nonzero coordinates of |a|, coordinate r of
+  // the nonzeros negative iff bit r of the entry number is set
+  void natural_block(const Half &a) {
+    const auto bk = std::make_pair(0, std::vector<int>(a.begin(), a.end()));
+    if (blocks.count(bk)) return;
     int pos[4], nnz = 0;
     for (int t = 0; t < 4; ++t) if (a[t]) pos[nnz++] = t;
-    uint32_t base = (uint32_t)entries.size();
-    for (uint32_t s = 0; s < (1u << nnz); ++s) {
-      std::array<int, 4> e{a[0], a[1], a[2], a[3]};
-      for (int r = 0; r < nnz; ++r) if (s >> r & 1) e[pos[r]] = -e[pos[r]];
-      entries.push_back(e);
+    std::vector<Half> blk;
+    for (uint32_t sg = 0; sg < (1u << nnz); ++sg) {
+      Half e = a;
+      for (int r = 0; r < nnz; ++r) if (sg >> r & 1) e[pos[r]] = -e[pos[r]];
+      blk.push_back(e);
     }
-    natural[key] = base;
-    return base;
+    blocks[bk] = append(blk);
   }
-
-  // Entry e in [0, 24): q = (e >> 3) & 1, j3 = e & 7 gives the signs of
-  // coordinates 0..2; coordinate 3 is negative iff q xor parity(j3) (the
-  // parity constant P = 0; P = 1 orbits start 8 entries later).
-  uint32_t q_block(const int *a) {
-    uint64_t key = abs_key4(a);
-    auto it = qblock.find(key);
-    if (it != qblock.end()) return it->second;
-    uint32_t base = (uint32_t)entries.size();
-    for (uint32_t e = 0; e < 24; ++e) {
-      uint32_t q = (e >> 3) & 1, j3 = e & 7;
-      std::array<int, 4> v{a[0], a[1], a[2], a[3]};
+  // half-integer low halves: entry (q << 3) | j3, the signs of x1..x3 from
+  // j3 and the sign of x4 negative iff q xor parity(j3)
+  void q_block(const Half &a) {
+    const auto bk = std::make_pair(1, std::vector<int>(a.begin(), a.end()));
+    if (blocks.count(bk)) return;
+    std::vector<Half> blk;
+    for (uint32_t e = 0; e < 16; ++e) {
+      uint32_t q = e >> 3, j3 = e & 7;
+      Half v = a;
       for (int t = 0; t < 3; ++t) if (j3 >> t & 1) v[t] = -v[t];
-      uint32_t par = (j3 ^ (j3 >> 1) ^ (j3 >> 2)) & 1;
-      if (q ^ par) v[3] = -v[3];
-      entries.push_back(v);
+      if ((q ^ j3 ^ (j3 >> 1) ^ (j3 >> 2)) & 1) v[3] = -v[3];
+      blk.push_back(v);
     }
-    qblock[key] = base;
-    return base;
+    blocks[bk] = append(blk);
   }
 };
 
 void put16(uint8_t *p, uint16_t v) { std::memcpy(p, &v, 2); }
 void put32(uint8_t *p, uint32_t v) { std::memcpy(p, &v, 4); }
+
+Half lo_half(const Point &p) { return Half{p.y[0], p.y[1], p.y[2], p.y[3]}; }
+Half hi_half(const Point &p) { return Half{p.y[4], p.y[5], p.y[6], p.y[7]}; }
 
 bool build_tables(Tables &T) {
   T.pts = build_points();
@@ -196,125 +223,68 @@ bool build_tables(Tables &T) {
   for (uint32_t i = 0; i < kCodebookSize; ++i)
     for (int t = 0; t < 8; ++t) T.flat[i * 8 + t] = P[i].y[t];
 
-  // orbits (runs of equal |y|), the origin included as orbit 0
-  for (uint32_t i = 0; i < kCodebookSize;) {
-    Orbit o;
-    o.start = i;
-    for (int t = 0; t < 8; ++t) o.a[t] = std::abs(P[i].y[t]);
-    o.half = (P[i].y[0] & 1) != 0;
-    o.size = (uint32_t)P[i].size;
-    uint32_t e = i;
-    while (e < kCodebookSize) {
-      bool same = true;
-      for (int t = 0; t < 8; ++t) same &= std::abs(P[e].y[t]) == o.a[t];
-      if (!same) break;
-      ++e;
-    }
-    o.count = e - i;
-    T.orbits.push_back(o);
-    i = e;
-  }
-
+  // Blocks first (the zero half at entry 0): the natural sign blocks of
+  // every integer half pattern and of every half-integer high half, and the
+  // parity blocks of the half-integer low halves; the chunks' runs are then
+  // found inside them.
   HalfTable H;
-  // records: one per orbit except the origin, in order; then 16 for the last chunk
-  struct Rec { uint32_t r_lo, lo_off, hi_off, qw; };
-  std::vector<Rec> recs;
-  std::vector<uint32_t> rec_of_orbit(T.orbits.size(), 0xFFFFFFFFu);
-  auto make_rec = [&](const Orbit &o) {
-    Rec r;
-    int lo[4] = {o.a[0], o.a[1], o.a[2], o.a[3]};
-    int hi[4] = {o.a[4], o.a[5], o.a[6], o.a[7]};
-    uint32_t sp = (o.start - 1u) & 0xFFFFu;       // start in i'
-    if (o.half) {
-      uint32_t par = 0;
-      for (int t = 0; t < 8; ++t) par += (uint32_t)o.a[t];
-      uint32_t P8 = (par % 4) != 0;               // x8 negative when x1..x7 positive
-      r.r_lo = 4;
-      r.lo_off = 8u * H.natural_block(lo);
-      uint32_t hb = 8u * H.q_block(hi) + 64u * P8;
-      r.hi_off = hb - 8u * (sp >> 4);
-      r.qw = 4;
-    } else {
-      int nlo = 0;
-      for (int t = 0; t < 4; ++t) nlo += lo[t] != 0;
-      r.r_lo = (uint32_t)nlo;
-      r.lo_off = 8u * H.natural_block(lo);
-      uint32_t hb = 8u * H.natural_block(hi);
-      r.hi_off = hb - 8u * (sp >> r.r_lo);
-      r.qw = 0;
-    }
-    return r;
-  };
-  for (size_t oi = 1; oi < T.orbits.size(); ++oi) {
-    rec_of_orbit[oi] = (uint32_t)recs.size();
-    recs.push_back(make_rec(T.orbits[oi]));
-  }
-  Rec origin_rec;
-  {
-    Orbit o = T.orbits[0];          // the origin: start 0 -> i' = 65535
-    int z[4] = {0, 0, 0, 0};
-    origin_rec.r_lo = 0;
-    origin_rec.lo_off = 8u * H.natural_block(z);
-    origin_rec.hi_off = 8u * H.natural_block(z) - 8u * ((o.start - 1u) & 0xFFFFu);
-    origin_rec.qw = 0;
+  H.append({Half{0, 0, 0, 0}});
+  for (uint32_t i = 0; i < kCodebookSize; ++i) {
+    Half lo = lo_half(P[i]), hi = hi_half(P[i]);
+    for (int t = 0; t < 4; ++t) { lo[t] = std::abs(lo[t]); hi[t] = std::abs(hi[t]); }
+    if (P[i].y[0] & 1) H.q_block(lo);
+    else H.natural_block(lo);
+    H.natural_block(hi);
   }
 
-  // orbit containing each index
-  std::vector<uint32_t> orbit_of(kCodebookSize);
-  for (size_t oi = 0; oi < T.orbits.size(); ++oi)
-    for (uint32_t i = T.orbits[oi].start; i < T.orbits[oi].start + T.orbits[oi].count; ++i)
-      orbit_of[i] = (uint32_t)oi;
-
-  std::vector<uint16_t> ct(kChunks);
+  std::vector<uint32_t> rt(kChunks);
   for (uint32_t c = 0; c < kChunks; ++c) {
-    uint32_t i0 = 16 * c + 1;                      // i of slot 0 (i' = 16c)
-    if (c == kChunks - 1) {
-      uint32_t first = (uint32_t)recs.size();
-      for (uint32_t s = 0; s < 16; ++s) {
-        uint32_t ip = 16 * c + s;
-        Rec r = ip == 0xFFFFu ? origin_rec : recs[rec_of_orbit[orbit_of[ip + 1]]];
-        recs.push_back(r);
-      }
-      ct[c] = (uint16_t)((first << 5) | 0u);
-      continue;
+    Half L[4], Hh[4];
+    for (uint32_t m = 0; m < 4; ++m) {
+      const uint32_t i = (4 * c + m + 1) & 0xFFFFu;
+      L[m] = lo_half(P[i]);
+      Hh[m] = hi_half(P[i]);
     }
-    const Orbit &o = T.orbits[orbit_of[i0]];
-    uint32_t ls = 4;
-    if (o.size < 16) {
-      ls = 0;
-      while ((1u << ls) < o.size) ++ls;
-    }
-    ct[c] = (uint16_t)((rec_of_orbit[orbit_of[i0]] << 5) | ls);
+    // low half: the smallest window width whose 2^t values repeat across the chunk
+    uint32_t t_lo = 2;
+    if (L[0] == L[1] && L[0] == L[2] && L[0] == L[3]) t_lo = 0;
+    else if (L[0] == L[2] && L[1] == L[3]) t_lo = 1;
+    // high half: the largest window offset the chunk allows
+    uint32_t Toff = 0;
+    if (Hh[0] == Hh[1] && Hh[0] == Hh[2] && Hh[0] == Hh[3]) Toff = 2;
+    else if (Hh[0] == Hh[1] && Hh[2] == Hh[3]) Toff = 1;
+    std::vector<Half> lrun(L, L + (1u << t_lo));
+    const uint32_t lo_entry = H.find_aligned(lrun);
+    std::vector<Half> hrun;
+    if (Toff == 2) hrun = {Hh[0]};
+    else if (Toff == 1) hrun = {Hh[0], Hh[2]};
+    else hrun = {Hh[0], Hh[1], Hh[2], Hh[3]};
+    // the window (i' >> T) & 3 also covers bits of i' that are constant in
+    // the chunk: subtract their value at m = 0
+    const uint32_t base_off = ((4 * c) >> Toff) & 3u;
+    const uint32_t hrun_entry = H.find_from(hrun, base_off);
+    const uint32_t hi_entry = hrun_entry - base_off;
+    if (lo_entry % 4 || 8 * lo_entry >= 65536 || hi_entry >= kMaxHalves) return false;
+    rt[c] = rec_pack(t_lo, 8 * lo_entry, Toff, hi_entry);
   }
-  if (recs.size() > kMaxRecords || H.entries.size() > kMaxHalves) return false;
+  if (H.entries.size() > kMaxHalves) return false;
 
   // blob
   T.blob.assign(kBlobBytes, 0);
   uint8_t *b = T.blob.data();
   put32(b + 0, kMagic0);
   put32(b + 4, kFormatVersion);
-  put32(b + 8, (uint32_t)recs.size());
-  put32(b + 12, (uint32_t)H.entries.size());
-  for (uint32_t c = 0; c < kChunks; ++c) put16(b + kCtOff + 2 * c, ct[c]);
-  for (size_t r = 0; r < recs.size(); ++r) {
-    const int32_t hs = (int32_t)recs[r].hi_off;       // may be negative (wraps in uint32)
-    if (recs[r].r_lo > 31 || recs[r].qw > 31 || recs[r].lo_off >= (1u << 24) || hs < -(1 << 23) || hs >= (1 << 23))
-      return false;
-    uint8_t *p = b + kOtOff + 8 * r;
-    put32(p + 0, recs[r].r_lo | (recs[r].lo_off << 8));
-    put32(p + 4, recs[r].qw | ((uint32_t)hs << 8));
-  }
+  put32(b + 8, (uint32_t)H.entries.size());
+  for (uint32_t c = 0; c < kChunks; ++c) put32(b + kRtOff + 4 * c, rt[c]);
   for (size_t e = 0; e < H.entries.size(); ++e) {
     for (int t = 0; t < 4; ++t) {
       int y = H.entries[e][t];
       put16(b + kHtBf16Off + 8 * e + 2 * t, bf16_of_half(y));
-      put16(b + kHtA3Off + 8 * e + 2 * t, (uint16_t)(int16_t)(2 * y));
-      put16(b + kHtA4Off + 8 * e + 2 * t, (uint16_t)(int16_t)(4 * y));
-      put16(b + kHtB4Off + 8 * e + 2 * t, (uint16_t)(kBias + y));
+      put16(b + kHtTOff + 8 * e + 2 * t, (uint16_t)((kHtBase + (uint32_t)y) & 0xFFFFu));
     }
   }
   for (uint32_t i = 0; i < 256; ++i)
-    for (int t = 0; t < 8; ++t) put16(b + kR3Off + 16 * i + 2 * t, (uint16_t)(kBias + P[i].y[t]));
+    for (int t = 0; t < 8; ++t) put16(b + kR3Off + 16 * i + 2 * t, (uint16_t)((kR3Base + (uint32_t)P[i].y[t]) & 0xFFFFu));
 
   // self-check: decode every index through the tables exactly as the kernels do
   for (uint32_t i = 0; i < kCodebookSize; ++i) {
@@ -340,21 +310,14 @@ Tables &tables() {
 void decode_doubled_via_tables(const uint8_t *blob, uint32_t i, int *y) {
   auto rd16 = [&](uint32_t off) { uint16_t v; std::memcpy(&v, blob + off, 2); return (uint32_t)v; };
   auto rd32 = [&](uint32_t off) { uint32_t v; std::memcpy(&v, blob + off, 4); return v; };
-  uint32_t ip = (i - 1u) & 0xFFFFu;
-  uint32_t e = rd16(kCtOff + 2 * (ip >> 4));
-  uint32_t low = ip & 15u;
-  uint32_t rec = (e >> 5) + (low >> (e & 31u));
-  const uint32_t w0 = rd32(kOtOff + 8 * rec), w1 = rd32(kOtOff + 8 * rec + 4);
-  const uint32_t r_lo = w0 & 31u, lo_off = w0 >> 8, qw = w1 & 31u;
-  const uint32_t hi_off = (uint32_t)((int32_t)w1 >> 8);
-  uint32_t jlo = ip & ((1u << r_lo) - 1u);
-  uint32_t lo_addr = lo_off + 8u * jlo;
-  uint32_t qsrc = qw ? (ip & ((1u << qw) - 1u)) : 0u;
-  uint32_t q = (uint32_t)__builtin_popcount(qsrc) & 1u;
-  uint32_t hi_addr = hi_off + 8u * (ip >> r_lo) + 64u * q;
+  const uint32_t ip = (i - 1u) & 0xFFFFu;
+  const uint32_t rec = rd32(kRtOff + 4 * (ip >> 2));
+  const uint32_t t_lo = rec & 31u, wh = rec >> 16;
+  const uint32_t lo_byte = (rec & 0xFFE0u) + 8u * (ip & ((1u << t_lo) - 1u));
+  const uint32_t hi_byte = (wh >> 2) + 8u * ((ip >> (wh & 31u)) & 3u);
   for (int t = 0; t < 4; ++t) {
-    y[t] = (int16_t)rd16(kHtA3Off + lo_addr + 2 * t) / 2;
-    y[4 + t] = (int16_t)rd16(kHtA3Off + hi_addr + 2 * t) / 2;
+    y[t] = (int)(int16_t)(uint16_t)(rd16(kHtTOff + lo_byte + 2 * t) - kHtBase);
+    y[4 + t] = (int)(int16_t)(uint16_t)(rd16(kHtTOff + hi_byte + 2 * t) - kHtBase);
   }
 }
 

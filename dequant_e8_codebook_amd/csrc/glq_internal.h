@@ -15,7 +15,7 @@ const int8_t *codebook_doubled();
 // The GLQ_CB_DEVICE blob (kBlobBytes bytes), or NULL.
 const uint8_t *device_blob();
 
-// Decode index i through the chunk/record/half tables of a GLQ_CB_DEVICE blob
+// Decode index i through the record and half-vector tables of a GLQ_CB_DEVICE blob
 // (host version of the kernels' table walk) into doubled coordinates y[8].
 void decode_doubled_via_tables(const uint8_t *blob, uint32_t i, int *y);
 

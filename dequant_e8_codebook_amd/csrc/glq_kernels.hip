@@ -56,43 +56,43 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- LDS tables
-// LDS layout of the decode tables: [CT][OT][HT stage 1][HT stage 2 | R3]
-constexpr uint32_t kLdsCt = 0;
-constexpr uint32_t kLdsOt = kLdsCt + kCtBytes;
-constexpr uint32_t kLdsHt1 = kLdsOt + kOtBytes;
-constexpr uint32_t kLdsHt2 = kLdsHt1 + kHtBytes;
+// LDS layout of the decode tables: [RT][HT][R3 at 3 bpw]
+constexpr uint32_t kLdsRt = 0;
+constexpr uint32_t kLdsHt = kLdsRt + kRtBytes;
+constexpr uint32_t kLdsR3 = kLdsHt + kHtBytes;
 
 template <int BPW> struct TabCfg;
-template <> struct TabCfg<2> { static constexpr uint32_t ht1 = kHtBf16Off, ht2 = 0, ht2_bytes = 0; };
-template <> struct TabCfg<3> { static constexpr uint32_t ht1 = kHtA3Off, ht2 = kR3Off, ht2_bytes = kR3Bytes; };
-template <> struct TabCfg<4> { static constexpr uint32_t ht1 = kHtA4Off, ht2 = kHtB4Off, ht2_bytes = kHtBytes; };
+template <> struct TabCfg<2> { static constexpr uint32_t ht = kHtBf16Off, r3_bytes = 0; };
+template <> struct TabCfg<3> { static constexpr uint32_t ht = kHtTOff, r3_bytes = kR3Bytes; };
+template <> struct TabCfg<4> { static constexpr uint32_t ht = kHtTOff, r3_bytes = 0; };
 
 template <int BPW>
-constexpr uint32_t lds_table_bytes() { return kLdsHt2 + TabCfg<BPW>::ht2_bytes; }
+constexpr uint32_t lds_table_bytes() { return kLdsR3 + TabCfg<BPW>::r3_bytes; }
+
+// blob offset of LDS table byte pos
+template <int BPW>
+__device__ __forceinline__ uint32_t table_src(uint32_t pos) {
+  return pos < kLdsHt ? kRtOff + pos : pos < kLdsR3 ? TabCfg<BPW>::ht + (pos - kLdsHt) : kR3Off + (pos - kLdsR3);
+}
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
-// Copy CT + OT + the two value tables of this bit width into LDS (bytes
+// Copy RT + the value table of this bit width (+ R3 at 3 bpw) into LDS (bytes
 // 0 .. lds_table_bytes) with global-to-LDS loads: no registers held, nothing
 // waited for here. Run r (1 KiB of the LDS image) is copied by wave r mod the
 // wave count, lane i writing its bytes 16 i .. 16 i + 15. The caller waits
 // with tables_landed() before the barrier that publishes the tables.
 template <int BPW, int NT = 256>
 __device__ __forceinline__ void load_tables(uint8_t *, const uint8_t *blob) {
-  constexpr uint32_t b01 = kCtBytes + kOtBytes;                 // CT + OT (contiguous in both)
-  constexpr uint32_t b2 = b01 + kHtBytes;                       // + stage-1 half table
   constexpr uint32_t total = lds_table_bytes<BPW>();
-  constexpr uint32_t runs = (total + 1023) / 1024;
-  static_assert(kLdsCt == 0 && kLdsOt == kCtBytes && kLdsHt1 == b01 && total % 16 == 0, "LDS table order");
+  constexpr uint32_t runs = total / 1024;
+  static_assert(total % 1024 == 0 && kLdsHt % 1024 == 0 && kLdsR3 % 1024 == 0, "LDS table runs");
   const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (uint32_t r = wave; r < runs; r += NT / 64) {
     const uint32_t pos = 1024 * r + 16 * lane;
-    if (pos < total) {
-      const uint32_t src = pos < b01 ? kCtOff + pos : pos < b2 ? TabCfg<BPW>::ht1 + (pos - b01)
-                                                               : TabCfg<BPW>::ht2 + (pos - b2);
-      __builtin_amdgcn_global_load_lds((glb_void_t *)(blob + src), (lds_void_t *)(uintptr_t)(1024 * r), 16, 0, 0);
-    }
+    __builtin_amdgcn_global_load_lds((glb_void_t *)(blob + table_src<BPW>(pos)), (lds_void_t *)(uintptr_t)(1024 * r),
+                                     16, 0, 0);
   }
 }
 
@@ -109,8 +109,12 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) const uint16_t lds_u16;
 typedef __attribute__((address_space(3))) const u32x2_t lds_u64;
 typedef __attribute__((address_space(3))) const u32x4_t lds_u128;
+typedef __attribute__((address_space(3))) const uint32_t lds_u32;
 __device__ __forceinline__ uint32_t lds16(uint32_t addr) {
   return *reinterpret_cast<lds_u16 *>(static_cast<uintptr_t>(addr));
+}
+__device__ __forceinline__ uint32_t lds_rd32(uint32_t addr) {
+  return *reinterpret_cast<lds_u32 *>(static_cast<uintptr_t>(addr));
 }
 __device__ __forceinline__ uint2 lds64(uint32_t addr) {
   const u32x2_t v = *reinterpret_cast<lds_u64 *>(static_cast<uintptr_t>(addr));
@@ -135,26 +139,28 @@ __device__ __forceinline__ uint32_t pk_dec16(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, w) - (u16x2)(1));
 }
 
-// Byte offsets of the low and high signed half-vectors of index i' from its
-// orbit record R (two words, see glq_tables.h): the shift and bit-field
-// extract by R.x / R.y read only bits 0-4 (r_lo, q_width).
-__device__ __forceinline__ void rec_offsets(uint32_t ip, uint2 R, uint32_t &lo, uint32_t &hi) {
-  lo = (R.x >> 8) + (__builtin_amdgcn_ubfe(ip, 0, R.x) << 3);
-  const uint32_t q = __builtin_popcount(__builtin_amdgcn_ubfe(ip, 0, R.y)) & 1u;
-  hi = (uint32_t)((int32_t)R.y >> 8) + ((ip >> (R.x & 31u)) << 3) + (q << 6);
+// Byte offsets (inside HT) of the low and high half-vectors of index i',
+// from the record of its chunk (glq_tables.h): the low window is
+// bfe(i', 0, t_lo) with t_lo in bits 0-4 of the record, the high window
+// bfe(i', T, 2) with T in bits 0-4 of rec >> 16, and (rec >> 16) >> 2 is 8 HI.
+__device__ __forceinline__ void rec_offsets(uint32_t ip, uint32_t rec, uint32_t &lo, uint32_t &hi) {
+  lo = (rec & 0xFFE0u) + (__builtin_amdgcn_ubfe(ip, 0, rec) << 3);
+  const uint32_t wh = rec >> 16;
+  hi = (wh >> 2) + (__builtin_amdgcn_ubfe(ip, wh, 2) << 3);
 }
 
-// Table walk for one index, given as i' = i - 1 mod 2^16 (see glq_tables.h):
-// byte offsets of the low and high signed half-vectors within a half table.
-__device__ __forceinline__ void walk(uint32_t ip, uint32_t &lo, uint32_t &hi) {
-  const uint32_t e = lds16(kLdsCt + ((ip >> 4) << 1));
-  const uint32_t rec = (e >> 5) + ((ip & 15u) >> (e & 31u));
-  const uint2 R = lds64(kLdsOt + (rec << 3));
-  rec_offsets(ip, R, lo, hi);
-}
+// record of index i' = i - 1 mod 2^16 (RT entry i' >> 2 at byte i' & ~3)
+__device__ __forceinline__ uint32_t rec_of(uint32_t ip) { return lds_rd32(kLdsRt + (ip & 0xFFFCu)); }
 
 __device__ __forceinline__ uint32_t pk_add16(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, a) + __builtin_bit_cast(u16x2, b));
+}
+
+// Stage-1 and stage-2 halves into operand form: 16-bit lanes M * a + b
+// (mod 2^16), M = 2 at 3 bpw and 4 at 4 bpw (one packed multiply-add).
+template <uint16_t M>
+__device__ __forceinline__ uint32_t pk_comb(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, a) * (u16x2)(M) + __builtin_bit_cast(u16x2, b));
 }
 
 // Decode one group into 8 x 16-bit operand values, coordinate t in half t of
@@ -164,21 +170,21 @@ __device__ __forceinline__ uint32_t pk_add16(uint32_t a, uint32_t b) {
 template <int BPW>
 __device__ __forceinline__ uint4 decode_ip(uint32_t ip1, uint32_t a2) {
   uint32_t lo, hi;
-  walk(ip1, lo, hi);
-  const uint2 a = lds64(kLdsHt1 + lo);
-  const uint2 b = lds64(kLdsHt1 + hi);
+  rec_offsets(ip1, rec_of(ip1), lo, hi);
+  const uint2 a = lds64(kLdsHt + lo);
+  const uint2 b = lds64(kLdsHt + hi);
   if constexpr (BPW == 2) {
     (void)a2;
     return make_uint4(a.x, a.y, b.x, b.y);
   } else if constexpr (BPW == 3) {
-    const uint4 r = lds128(kLdsHt2 + (a2 << 4));
-    return make_uint4(pk_add16(a.x, r.x), pk_add16(a.y, r.y), pk_add16(b.x, r.z), pk_add16(b.y, r.w));
+    const uint4 r = lds128(kLdsR3 + (a2 << 4));
+    return make_uint4(pk_comb<2>(a.x, r.x), pk_comb<2>(a.y, r.y), pk_comb<2>(b.x, r.z), pk_comb<2>(b.y, r.w));
   } else {
     uint32_t lo2, hi2;
-    walk(a2, lo2, hi2);
-    const uint2 c = lds64(kLdsHt2 + lo2);
-    const uint2 d = lds64(kLdsHt2 + hi2);
-    return make_uint4(pk_add16(a.x, c.x), pk_add16(a.y, c.y), pk_add16(b.x, d.x), pk_add16(b.y, d.y));
+    rec_offsets(a2, rec_of(a2), lo2, hi2);
+    const uint2 c = lds64(kLdsHt + lo2);
+    const uint2 d = lds64(kLdsHt + hi2);
+    return make_uint4(pk_comb<4>(a.x, c.x), pk_comb<4>(a.y, c.y), pk_comb<4>(b.x, d.x), pk_comb<4>(b.y, d.y));
   }
 }
 
@@ -188,59 +194,61 @@ __device__ __forceinline__ uint4 decode_group(uint32_t i1, uint32_t i2, const ui
   return decode_ip<BPW>((i1 - 1u) & 0xFFFFu, BPW == 4 ? ((i2 - 1u) & 0xFFFFu) : i2);
 }
 
-// Table walk of 8 groups split into phases, so that the LDS reads of one
-// phase for all 8 groups are in flight together: p1 chunk-table entries (and
-// the direct residual rows at 3 bpw), p2 orbit records, p3 the signed
-// half-vectors, p4 the combine into operand form (as decode_ip). q1 / q2 hold
-// the indices as decode_ip takes them.
+// Decode of 8 groups split into phases, so that the LDS reads of one phase
+// are in flight together: p1 the chunk records (and the direct residual rows
+// at 3 bpw), p2 the half-vector offsets and reads, p3 the combine into
+// operand form (as decode_ip). Each phase takes a range [G0, G1) of the
+// groups, so a caller can stagger them. q1 / q2 hold the indices as
+// decode_ip takes them.
 template <int BPW>
 struct Dec8 {
-  uint32_t e1[8], e2[8];
+  uint32_t R1[8], R2[8];
   uint4 r3[8];
-  uint2 R1[8], R2[8];
   uint2 va[8], vb[8], vc[8], vd[8];
 
+  template <int G0 = 0, int G1 = 8>
   __device__ __forceinline__ void p1(const uint32_t (&q1)[8], const uint32_t (&q2)[8]) {
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      e1[g] = lds16(kLdsCt + ((q1[g] >> 4) << 1));
-      if constexpr (BPW == 4) e2[g] = lds16(kLdsCt + ((q2[g] >> 4) << 1));
-      if constexpr (BPW == 3) r3[g] = lds128(kLdsHt2 + (q2[g] << 4));
+    for (int g = G0; g < G1; ++g) {
+      R1[g] = rec_of(q1[g]);
+      if constexpr (BPW == 4) R2[g] = rec_of(q2[g]);
+      if constexpr (BPW == 3) r3[g] = lds128(kLdsR3 + (q2[g] << 4));
     }
   }
+  template <int G0 = 0, int G1 = 8>
   __device__ __forceinline__ void p2(const uint32_t (&q1)[8], const uint32_t (&q2)[8]) {
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      R1[g] = lds64(kLdsOt + (((e1[g] >> 5) + ((q1[g] & 15u) >> (e1[g] & 31u))) << 3));
-      if constexpr (BPW == 4) R2[g] = lds64(kLdsOt + (((e2[g] >> 5) + ((q2[g] & 15u) >> (e2[g] & 31u))) << 3));
-    }
-  }
-  __device__ __forceinline__ void p3(const uint32_t (&q1)[8], const uint32_t (&q2)[8]) {
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
+    for (int g = G0; g < G1; ++g) {
       uint32_t lo, hi;
       rec_offsets(q1[g], R1[g], lo, hi);
-      va[g] = lds64(kLdsHt1 + lo);
-      vb[g] = lds64(kLdsHt1 + hi);
+      va[g] = lds64(kLdsHt + lo);
+      vb[g] = lds64(kLdsHt + hi);
       if constexpr (BPW == 4) {
         uint32_t lo2, hi2;
         rec_offsets(q2[g], R2[g], lo2, hi2);
-        vc[g] = lds64(kLdsHt2 + lo2);
-        vd[g] = lds64(kLdsHt2 + hi2);
+        vc[g] = lds64(kLdsHt + lo2);
+        vd[g] = lds64(kLdsHt + hi2);
       }
     }
   }
-  __device__ __forceinline__ void p4(uint4 (&out)[8]) {
+  template <int G0 = 0, int G1 = 8>
+  __device__ __forceinline__ void p3(uint4 (&out)[8]) {
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
+    for (int g = G0; g < G1; ++g) {
       if constexpr (BPW == 2) out[g] = make_uint4(va[g].x, va[g].y, vb[g].x, vb[g].y);
       else if constexpr (BPW == 3)
-        out[g] = make_uint4(pk_add16(va[g].x, r3[g].x), pk_add16(va[g].y, r3[g].y),
-                            pk_add16(vb[g].x, r3[g].z), pk_add16(vb[g].y, r3[g].w));
+        out[g] = make_uint4(pk_comb<2>(va[g].x, r3[g].x), pk_comb<2>(va[g].y, r3[g].y),
+                            pk_comb<2>(vb[g].x, r3[g].z), pk_comb<2>(vb[g].y, r3[g].w));
       else
-        out[g] = make_uint4(pk_add16(va[g].x, vc[g].x), pk_add16(va[g].y, vc[g].y),
-                            pk_add16(vb[g].x, vd[g].x), pk_add16(vb[g].y, vd[g].y));
+        out[g] = make_uint4(pk_comb<4>(va[g].x, vc[g].x), pk_comb<4>(va[g].y, vc[g].y),
+                            pk_comb<4>(vb[g].x, vd[g].x), pk_comb<4>(vb[g].y, vd[g].y));
     }
+  }
+  // all phases at once
+  __device__ __forceinline__ void run(const uint32_t (&q1)[8], const uint32_t (&q2)[8], uint4 (&out)[8]) {
+    p1(q1, q2);
+    p2(q1, q2);
+    p3(out);
   }
 };
 
@@ -1153,10 +1161,7 @@ gemv_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
       gv_unpack<BPW>(raw[rt], i1, i2);
       Dec8<BPW> D;
       uint4 bv[8];
-      D.p1(i1, i2);
-      D.p2(i1, i2);
-      D.p3(i1, i2);
-      D.p4(bv);
+      D.run(i1, i2, bv);
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const uint4 b = g0 + s < G ? bv[s] : make_uint4(0, 0, 0, 0);
@@ -1201,7 +1206,9 @@ gemv_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
 // writes y.
 constexpr int LY_MAXE = 16384;                       // m*k and m*n limit (64 KiB of float32)
 constexpr int LY_THREADS = 64 * GV_WAVES;            // 1024
-constexpr size_t LY_BUF_BYTES = (LY_MAXE + 4 * 16) * 4;   // float32 transpose buffer (padded)
+// float32 transpose buffer (padded); it also holds x~ in bf16 and, past
+// x~, the cross-wave reduction rows and the row sums (see layer_small)
+constexpr size_t LY_BUF_BYTES = (LY_MAXE + 4 * 16) * 4 + 64;
 
 // The table image rounded up to whole 1 KiB copy runs (the tail of the last
 // run lands in padding that nothing reads).
@@ -1209,7 +1216,8 @@ template <int BPW>
 constexpr uint32_t ly_tab_bytes() { return (lds_table_bytes<BPW>() + 1023) / 1024 * 1024; }
 
 template <int BPW>
-constexpr size_t ly_lds_bytes() { return ly_tab_bytes<BPW>() + LY_BUF_BYTES + GV_WAVES * 256 * 4 + 64; }
+constexpr size_t ly_lds_bytes() { return ly_tab_bytes<BPW>() + LY_BUF_BYTES; }
+static_assert(ly_lds_bytes<3>() <= 160 * 1024, "single-launch layer fits the LDS of a CU");
 
 // Table copy of the single-launch layer, staged through registers: global
 // loads that the rotation of x, issued after the x loads, does not wait for
@@ -1222,8 +1230,8 @@ constexpr size_t ly_lds_bytes() { return ly_tab_bytes<BPW>() + LY_BUF_BYTES + GV
 // of an XCD do not all ask the same L2 channel for the same lines at once.
 template <int BPW> struct LyTab {   // named members: an array here ended up on the stack
   static constexpr uint32_t runs = ly_tab_bytes<BPW>() / 1024, per_wave = (runs + GV_WAVES - 1) / GV_WAVES;
-  static_assert(per_wave <= 4, "table runs per wave");
-  uint4 v0, v1, v2, v3;
+  static_assert(per_wave <= 6, "table runs per wave");
+  uint4 v0, v1, v2, v3, v4, v5;
 };
 
 template <int BPW>
@@ -1235,12 +1243,8 @@ __device__ __forceinline__ uint32_t ly_run(uint32_t u, uint32_t rot) {
 
 template <int BPW>
 __device__ __forceinline__ uint4 ly_fetch_run(const uint8_t *blob, uint32_t u, uint32_t rot) {
-  constexpr uint32_t b01 = kCtBytes + kOtBytes, b2 = b01 + kHtBytes;
-  static_assert(kLdsCt == 0 && kLdsOt == kCtBytes && kLdsHt1 == b01, "LDS table order");
   const uint32_t pos = 1024 * ly_run<BPW>(u, rot) + 16 * (threadIdx.x & 63);
-  const uint32_t src = pos < b01 ? kCtOff + pos : pos < b2 ? TabCfg<BPW>::ht1 + (pos - b01)
-                                                           : TabCfg<BPW>::ht2 + (pos - b2);
-  return *reinterpret_cast<const uint4 *>(blob + min(src, kBlobBytes - 16));
+  return *reinterpret_cast<const uint4 *>(blob + min(table_src<BPW>(pos), kBlobBytes - 16));
 }
 
 template <int BPW>
@@ -1250,6 +1254,8 @@ __device__ __forceinline__ void ly_fetch_tables(const uint8_t *blob, uint32_t ro
   if constexpr (pw > 1) t.v1 = ly_fetch_run<BPW>(blob, 1, rot);
   if constexpr (pw > 2) t.v2 = ly_fetch_run<BPW>(blob, 2, rot);
   if constexpr (pw > 3) t.v3 = ly_fetch_run<BPW>(blob, 3, rot);
+  if constexpr (pw > 4) t.v4 = ly_fetch_run<BPW>(blob, 4, rot);
+  if constexpr (pw > 5) t.v5 = ly_fetch_run<BPW>(blob, 5, rot);
 }
 
 template <int BPW>
@@ -1260,6 +1266,8 @@ __device__ __forceinline__ void ly_store_tables(uint8_t *lds, uint32_t rot, cons
   if constexpr (pw > 1) *reinterpret_cast<uint4 *>(lds + 1024 * ly_run<BPW>(1, rot) + l16) = t.v1;
   if constexpr (pw > 2) *reinterpret_cast<uint4 *>(lds + 1024 * ly_run<BPW>(2, rot) + l16) = t.v2;
   if constexpr (pw > 3) *reinterpret_cast<uint4 *>(lds + 1024 * ly_run<BPW>(3, rot) + l16) = t.v3;
+  if constexpr (pw > 4) *reinterpret_cast<uint4 *>(lds + 1024 * ly_run<BPW>(4, rot) + l16) = t.v4;
+  if constexpr (pw > 5) *reinterpret_cast<uint4 *>(lds + 1024 * ly_run<BPW>(5, rot) + l16) = t.v5;
 }
 
 // Control words of the single-launch layer at the start of the workspace:
@@ -1389,8 +1397,6 @@ layer_small(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const u
             unsigned int *ctrl) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   float *xs = reinterpret_cast<float *>(lds + ly_tab_bytes<BPW>());
-  float *red = reinterpret_cast<float *>(lds + ly_tab_bytes<BPW>() + LY_BUF_BYTES);
-  float *misc = red + GV_WAVES * 256;                 // [0..3] row sums, [8] last-workgroup flag
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 15, q = lane >> 4;
   const int64_t G = k / 8, chunks = (G + 31) / 32;
@@ -1398,8 +1404,16 @@ layer_small(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const u
   const int mk = (int)(m * k), mn = (int)(m * n);
   const int ei = ly_e(mk);
   // x~ as bf16 [m][k] after rotation: past the transpose buffer's 1024 E + 64
-  // floats when E <= 8, on top of it at E = 16
+  // floats when E <= 8, on top of it at E = 16. The reduction rows (16 waves
+  // x 256 floats) and misc follow x~ at its largest (2048 E bytes), or the
+  // upper half of the buffer at E = 16 (free once x~ is written): they are
+  // written only after the last read of the transpose buffer in the input
+  // transform, and the output transform reuses the buffer only after the
+  // last workgroup has read its flag.
   uint16_t *xb = reinterpret_cast<uint16_t *>(ei <= 8 ? xs + 1024 * ei + 64 : xs);
+  float *red = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(xs) +
+                                         (ei == 16 ? 32768 : (1024 * ei + 64) * 4 + 2048 * ei));
+  float *misc = red + GV_WAVES * 256;                 // [0..3] row sums, [8] last-workgroup flag
 
   // 1. x, the first index loads and the table copy; x~ into LDS while the
   // tables land (the barrier at its end publishes tables, x~ and row sums)
@@ -1438,10 +1452,7 @@ layer_small(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const u
       gv_unpack<BPW>(raw, i1, i2);
       Dec8<BPW> D;
       uint4 bv[8];
-      D.p1(i1, i2);
-      D.p2(i1, i2);
-      D.p3(i1, i2);
-      D.p4(bv);
+      D.run(i1, i2, bv);
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         // x~ rows past m feed output rows that are not stored; groups past k
@@ -1494,6 +1505,7 @@ layer_small(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const u
   }
   __syncthreads();
   if (misc[8] == 0.0f) return;
+  __syncthreads();                                   // every thread has read the flag (the buffer below overlaps it)
   // 5. the last workgroup: y = U^T z
 #define GLQ_LY_OUT(E, F) ly_output<E, F>(z, sign_n, (int)n, mn, logbn, xs, y, y_dt, tid)
   switch (ly_e(mn)) {
@@ -1805,23 +1817,28 @@ gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
       }
     };
 
-    // walks per step: 8 groups, two table walks each at 4 bpw
-    constexpr int NW = BPW == 4 ? 16 : 8;
+    // The decode of step s + 1, staggered over the four MFMA blocks: the
+    // records of all 8 groups in block 0; the half-vector offsets (about
+    // seven VALU operations per table walk) and reads of groups 0-3 in block
+    // 1 and of groups 4-7 in block 2; the combine of groups 0-3 in block 2
+    // and of groups 4-7 in block 3.
+    constexpr int NW = BPW == 4 ? 2 : 1;            // table walks per group
     Dec8<BPW> D;
+    uint4 bn[8];
     D.p1(q1, q2);
     mfma_block(0);
-    gm_interleave16<3, (NW + 8 + 15) / 16>();
+    gm_interleave16<2, (8 * NW + (BPW == 3 ? 8 : 0) + 8 + 15) / 16>();
     __builtin_amdgcn_sched_barrier(0);
-    D.p2(q1, q2);
+    D.template p2<0, 4>(q1, q2);
     mfma_block(1);
-    gm_interleave16<(5 * NW + 15) / 16, (NW + 8 + 15) / 16>();
+    gm_interleave16<(28 * NW + 15) / 16, (8 * NW + 8 + 15) / 16>();
     __builtin_amdgcn_sched_barrier(0);
-    D.p3(q1, q2);
+    D.template p2<4, 8>(q1, q2);
+    D.template p3<0, 4>(bn);
     mfma_block(2);
-    gm_interleave16<(9 * NW + 15) / 16, (2 * NW + 8 + 15) / 16>();
+    gm_interleave16<(28 * NW + (BPW == 2 ? 0 : 16) + 15) / 16, (8 * NW + 8 + 15) / 16>();
     __builtin_amdgcn_sched_barrier(0);
-    uint4 bn[8];
-    D.p4(bn);
+    D.template p3<4, 8>(bn);
     mfma_block(3);
     gm_store_a((s & 1) ? As0 : As1, ra, k - GM_BK * (s + 1));   // tile s + 1 (unused past the end)
     gm_load_a(xt, m, k, m0, min(s + 2, S - 1), ra);

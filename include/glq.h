@@ -327,7 +327,7 @@ const char *glq_status_string(int status);
  * until the next GPU call on the same thread. */
 const char *glq_last_error(void);
 
-/* Library and codebook-format version, e.g. 0x00020000. */
+/* Library and codebook-format version, e.g. 0x00030000. */
 uint32_t glq_version(void);
 
 #ifdef __cplusplus

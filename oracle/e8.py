@@ -17,8 +17,12 @@ R3  Stated order, ascending on the key
     values, orbit_size = 2^nnz for integer points and 128 for half-integer
     points (one sign is fixed by parity), and j is the sign counter:
       integer points: bit t of j = [t-th nonzero coordinate is negative]
-      half points:    bit t of j = [x_{t+1} < 0], t = 0..6
+      half points:    bit t of j = [x_{t+1} < 0] for t = 0, 1, 2 and
+                      [x_{t+2} < 0] for t = 3..6; the sign of x4 is the one
+                      the even-sum rule leaves
     Index i is the position in this order; the codebook is the first 65536.
+    (Format 3. Format 2 fixed x8 by parity and counted x1..x7; x4 keeps the
+    parity-fixed sign in the same half-vector as the two fastest sign bits.)
     Parity against the real glq package is unpinned (its order is not on
     the pages): the format is self-consistent, not checkpoint-compatible.
 """
@@ -80,9 +84,10 @@ def sign_counter(y: np.ndarray) -> np.ndarray:
     half = (a[:, 0] % 2) == 1
     j = np.zeros(len(y), dtype=np.int64)
     rank = np.cumsum(a != 0, axis=1) - 1           # rank among nonzeros
+    half_pos = {0: 0, 1: 1, 2: 2, 4: 3, 5: 4, 6: 5, 7: 6}    # coordinate -> bit; x4 (c = 3) by parity
     for c in range(8):
         int_bit = np.where(a[:, c] != 0, neg[:, c] << np.maximum(rank[:, c], 0), 0)
-        half_bit = (neg[:, c] << c) if c < 7 else np.zeros(len(y), dtype=np.int64)
+        half_bit = (neg[:, c] << half_pos[c]) if c in half_pos else np.zeros(len(y), dtype=np.int64)
         j += np.where(half, half_bit, int_bit)
     return j
 

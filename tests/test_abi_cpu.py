@@ -35,7 +35,7 @@ def test_status_strings_and_version():
     for s in (-1, -2, -3, -4):
         assert glq.status_string(s) != "unknown status"
     assert glq.status_string(7) == "unknown status"
-    assert glq.version() == 0x00020000
+    assert glq.version() == 0x00030000
 
 
 def test_codebook_equals_oracle():
@@ -52,50 +52,54 @@ def test_build_codebook_size_queries():
     assert lib.glq_build_codebook(7, None, 0, ctypes.byref(need)) == glq.GLQ_ERR_ARG
 
 
+# GLQ_CB_DEVICE blob layout (format 3): 256-byte header, record table of
+# 16384 uint32, then two value tables of 2048 half-vectors (8 bytes each:
+# bf16 of y/2, and uint16 0xDA40 + y), then 256 rows of 8 x uint16 0x8EC0 + y
+RT0, HALVES = 256, 2048
+HT_BF16 = RT0 + 16384 * 4
+HT_T = HT_BF16 + HALVES * 8
+R3 = HT_T + HALVES * 8
+
+
 def _walk_blob(blob: bytes):
     """Decode all 65536 indices through the device tables, written from the
     table format description (numpy, vectorised), into doubled coordinates."""
     b = np.frombuffer(blob, dtype=np.uint8)
-    ct = b[256:256 + 8192].view(np.uint16).astype(np.int64)
-    ot = b[8448:8448 + 1472 * 8].view(np.uint32).reshape(-1, 2).astype(np.int64)
-    a3 = b[8448 + 1472 * 8 + 2368 * 8: 8448 + 1472 * 8 + 2 * 2368 * 8].view(np.int16)
+    rt = b[RT0:RT0 + 16384 * 4].view(np.uint32).astype(np.int64)
+    ht = b[HT_T:HT_T + HALVES * 8].view(np.uint16).astype(np.int64)
     i = np.arange(65536, dtype=np.int64)
     ip = (i - 1) & 0xFFFF
-    e = ct[ip >> 4]
-    rec = (e >> 5) + ((ip & 15) >> (e & 31))
-    r = ot[rec]
-    r_lo, lo_off = r[:, 0] & 31, r[:, 0] >> 8
-    qw = r[:, 1] & 31
-    hi_off = r[:, 1].astype(np.uint32).view(np.int32).astype(np.int64) >> 8   # signed
-    lo = lo_off + 8 * (ip & ((1 << r_lo) - 1))
-    qsrc = ip & ((1 << qw) - 1)
-    q = np.array([bin(v).count("1") & 1 for v in qsrc])
-    hi = hi_off + 8 * (ip >> r_lo) + 64 * q
+    rec = rt[ip >> 2]
+    t_lo, lo_b = rec & 31, rec & 0xFFE0                 # low window width, low run byte offset
+    T, hi_e = (rec >> 16) & 31, rec >> 21               # high window offset, high run entry
+    lo = lo_b // 8 + (ip & ((1 << t_lo) - 1))
+    hi = hi_e + ((ip >> T) & 3)
     out = np.zeros((65536, 8), dtype=np.int64)
     for t in range(4):
-        out[:, t] = a3[(lo + 2 * t) // 2] // 2
-        out[:, 4 + t] = a3[(hi + 2 * t) // 2] // 2
+        out[:, t] = ((ht[4 * lo + t] - 0xDA40) & 0xFFFF).astype(np.uint16).view(np.int16)
+        out[:, 4 + t] = ((ht[4 * hi + t] - 0xDA40) & 0xFFFF).astype(np.uint16).view(np.int16)
     return out
 
 
 def test_device_tables_decode_every_index():
     blob = glq.build_codebook(glq.GLQ_CB_DEVICE)
+    assert np.frombuffer(blob[4:8], np.uint32)[0] == 0x00030000
     assert np.array_equal(_walk_blob(blob), e8.codebook().astype(np.int64))
     b = np.frombuffer(blob, dtype=np.uint8)
-    # value formats agree with each other: bf16 = y/2, A4 = 2 * A3, B4 = 0x4340 + y
-    base = 8448 + 1472 * 8
-    hb = b[base: base + 2368 * 8].view(np.uint16)
-    a3 = b[base + 2368 * 8: base + 2 * 2368 * 8].view(np.int16).astype(np.int64)
-    a4 = b[base + 2 * 2368 * 8: base + 3 * 2368 * 8].view(np.int16).astype(np.int64)
-    b4 = b[base + 3 * 2368 * 8: base + 4 * 2368 * 8].view(np.uint16).astype(np.int64)
-    used = int(np.frombuffer(blob[12:16], np.uint32)[0]) * 4
-    y = a3[:used] // 2
-    assert np.array_equal(a4[:used], 4 * y)
-    assert np.array_equal(b4[:used], 0x4340 + y)
+    # value formats agree with each other: bf16 = y/2 where HT_T = 0xDA40 + y
+    used = int(np.frombuffer(blob[8:12], np.uint32)[0]) * 4
+    assert 0 < used <= HALVES * 4
+    hb = b[HT_BF16:HT_BF16 + HALVES * 8].view(np.uint16)
+    y = ((b[HT_T:HT_T + HALVES * 8].view(np.uint16).astype(np.int64)[:used] - 0xDA40) & 0xFFFF)
+    y = y.astype(np.uint16).view(np.int16).astype(np.int64)
+    assert np.abs(y).max() <= 6
     f = (hb[:used].astype(np.uint32) << 16).view(np.float32)
     assert np.array_equal(f, (y / 2.0).astype(np.float32))
-    r3 = b[base + 4 * 2368 * 8: base + 4 * 2368 * 8 + 4096].view(np.uint16).astype(np.int64).reshape(256, 8)
-    assert np.array_equal(r3 - 0x4340, e8.codebook()[:256].astype(np.int64))
+    r3 = b[R3:R3 + 4096].view(np.uint16).astype(np.int64).reshape(256, 8)
+    assert np.array_equal(((r3 - 0x8EC0) & 0xFFFF).astype(np.uint16).view(np.int16), e8.codebook()[:256])
+    # the packed multiply-add of the kernels gives bf16(192 + u): 5 * 0xDA40 and
+    # 2 * 0xDA40 + 0x8EC0 are 0x4340 (bf16 192) modulo 2^16
+    assert (5 * 0xDA40) % 65536 == 0x4340 and (2 * 0xDA40 + 0x8EC0) % 65536 == 0x4340
 
 
 @pytest.mark.parametrize("bpw", [2, 3, 4])

@@ -85,9 +85,10 @@ def _py_key(y):
     size = 128 if half else 2 ** nnz
     j = 0
     if half:
-        for t in range(7):
-            if y[t] < 0:
-                j |= 1 << t
+        # bits 0..2: x1..x3; bits 3..6: x5..x8; x4 is fixed by the even sum
+        for bit, c in enumerate((0, 1, 2, 4, 5, 6, 7)):
+            if y[c] < 0:
+                j |= 1 << bit
     else:
         r = 0
         for v in y:
