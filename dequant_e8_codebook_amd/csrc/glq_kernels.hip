@@ -2494,6 +2494,74 @@ int launch_matmul(const glq_layer *L, const void *xt, glq_dtype x_dt, const floa
 }  // namespace
 }  // namespace glq
 
+// ---------------------------------------------------------------- static scratch
+// The workspace of glq_fused_linear_noalloc: one array per GPU, created with
+// the code object and held until the process ends. Host code never takes
+// this name as an address (on the host it is only a stand-in for the
+// symbol): the device address of each GPU's copy comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+static __device__ __align__(256) uint8_t scratch[GLQ_STATIC_WS_BYTES];
+
+namespace glq {
+namespace {
+
+__global__ void __launch_bounds__(256) zero_words(uint32_t *p, uint32_t count) {
+  for (uint32_t i = blockIdx.x * 256 + threadIdx.x; i < count; i += gridDim.x * 256) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+struct StaticWs {
+  std::once_flag once;
+  uint8_t *ptr = nullptr;                 // device address of this GPU's scratch
+  int rc = GLQ_OK;
+  std::atomic<bool> dirty{true};          // control words to clear before the next use
+};
+StaticWs g_static_ws[kMaxDevices];
+
+// The current device's scratch, its address looked up on the first call on
+// that device; its control words are cleared (a fill kernel on the caller's
+// stream, ordered before the layer's kernels) on first use and after a call
+// that failed in HIP.
+int static_workspace(hipStream_t st, uint8_t **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) {
+    snprintf(g_last_error, sizeof g_last_error, "glq_fused_linear_noalloc: device %d beyond %d", dev, kMaxDevices);
+    return GLQ_ERR_UNSUPPORTED;
+  }
+  StaticWs &w = g_static_ws[dev];
+  std::call_once(w.once, [&] {
+    void *p = nullptr;
+    const hipError_t err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || !p) {
+      w.rc = err != hipSuccess ? hip_status(err, "hipGetSymbolAddress(scratch)") : GLQ_ERR_HIP;
+      return;
+    }
+    w.ptr = reinterpret_cast<uint8_t *>(p);
+  });
+  if (w.rc) return w.rc;
+  if (w.dirty.exchange(false)) {
+    hipLaunchKernelGGL(zero_words, dim3(1), dim3(256), 0, st, reinterpret_cast<uint32_t *>(w.ptr),
+                       (uint32_t)(kCtrlBytes / 4));
+    const int rc = hip_status(hipGetLastError(), "zero_words");
+    if (rc) {
+      w.dirty = true;
+      return rc;
+    }
+  }
+  *out = w.ptr;
+  return GLQ_OK;
+}
+
+void static_workspace_failed() {
+  int dev = -1;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) g_static_ws[dev].dirty = true;
+}
+
+}  // namespace
+}  // namespace glq
+
 using namespace glq;
 
 extern "C" int glq_rht_apply(const void *in, glq_dtype in_dt, void *out, glq_dtype out_dt,
@@ -2617,6 +2685,29 @@ extern "C" int glq_fused_linear(const glq_layer *L, const void *x, glq_dtype x_d
   if (rc) return rc;
   if (out_rht) return launch_rht(z, mm_dt, y, y_dt, m, L->n, L->sign_n, 1, nullptr, st);
   return GLQ_OK;
+}
+
+extern "C" int glq_fused_linear_noalloc(const glq_layer *L, const void *x, glq_dtype x_dt, int64_t m, void *y,
+                                        glq_dtype y_dt, uint32_t flags, void *hip_stream) {
+  const bool in_rht = !(flags & GLQ_FLAG_NO_INPUT_RHT);
+  const bool out_rht = !(flags & GLQ_FLAG_NO_OUTPUT_RHT);
+  int rc = check_layer(L, in_rht || out_rht);
+  if (rc) return rc;
+  if (m < 0) return GLQ_ERR_ARG;
+  if (m == 0) return GLQ_OK;
+  const size_t need = ws_layout(L->n, L->k, m).total;
+  if (need > (size_t)GLQ_STATIC_WS_BYTES) {
+    snprintf(g_last_error, sizeof g_last_error,
+             "glq_fused_linear_noalloc: %zu bytes of workspace needed, the static scratch holds %zu",
+             need, (size_t)GLQ_STATIC_WS_BYTES);
+    return GLQ_ERR_WORKSPACE;
+  }
+  uint8_t *ws = nullptr;
+  rc = static_workspace(reinterpret_cast<hipStream_t>(hip_stream), &ws);
+  if (rc) return rc;
+  rc = glq_fused_linear(L, x, x_dt, m, y, y_dt, ws, (size_t)GLQ_STATIC_WS_BYTES, flags, hip_stream);
+  if (rc == GLQ_ERR_HIP) static_workspace_failed();
+  return rc;
 }
 
 extern "C" int glq_ep_decode_weights(const glq_ep_layer *L, void *w_out, glq_dtype out_dt, void *hip_stream) {

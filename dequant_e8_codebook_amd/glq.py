@@ -22,7 +22,8 @@ GLQ_CB_INT8_2X, GLQ_CB_DEVICE = 0, 1
 FLAG_NO_INPUT_RHT, FLAG_NO_OUTPUT_RHT = 1, 2
 
 EXPORTS = ("glq_build_codebook", "glq_encode_ref", "glq_encode_ldlq", "glq_rht_apply", "glq_decode_weights",
-           "glq_fused_linear_workspace", "glq_fused_linear", "glq_status_string", "glq_last_error",
+           "glq_fused_linear_workspace", "glq_fused_linear", "glq_fused_linear_noalloc", "glq_status_string",
+           "glq_last_error",
            "glq_version", "glq_ep_encode", "glq_ep_build_lut", "glq_ep_decode_weights",
            "glq_ep_fused_linear_workspace", "glq_ep_fused_linear")
 EP_LANES, EP_TABLES, EP_MAX_SYMS = 64, 5, 256
@@ -69,6 +70,8 @@ _lib.glq_fused_linear_workspace.argtypes = [ctypes.POINTER(GlqLayerStruct), _i64
 _lib.glq_fused_linear_workspace.restype = _sz
 _lib.glq_fused_linear.argtypes = [ctypes.POINTER(GlqLayerStruct), _vp, _i32, _i64, _vp, _i32, _vp, _sz,
                                   _u32, _vp]
+_lib.glq_fused_linear_noalloc.argtypes = [ctypes.POINTER(GlqLayerStruct), _vp, _i32, _i64, _vp, _i32, _u32, _vp]
+STATIC_WS_BYTES = 32 << 20
 _lib.glq_ep_encode.argtypes = [_vp, _i64, _i64, _vp, _vp, _f32, _i32, _i32, _vp, ctypes.POINTER(EpModel), _vp, _vp,
                                _vp, _i64, ctypes.POINTER(_i64)]
 _lib.glq_ep_build_lut.argtypes = [ctypes.POINTER(EpModel), _vp, _sz]
@@ -450,6 +453,24 @@ class EpLayer:
                        len(h.words), dev(ep_build_lut(h.model)),
                        None if sign_k is None else dev(np.asarray(sign_k, np.int8)),
                        None if sign_n is None else dev(np.asarray(sign_n, np.int8)))
+
+
+def fused_linear_noalloc(layer: Layer, x, y, flags: int = 0, stream=None):
+    """glq_fused_linear_noalloc: the layer with the library's static per-GPU
+    scratch instead of a caller workspace (no allocation in the call)."""
+    dev = _check_layer(layer, not (flags & FLAG_NO_INPUT_RHT), not (flags & FLAG_NO_OUTPUT_RHT))
+    torch = _torch()
+    if x.dim() != 2 or x.shape[1] != layer.k:
+        raise ValueError(f"x: shape {tuple(x.shape)}, expected (m, {layer.k})")
+    _dev_tensor(x, "x", dev, dtypes=(torch.float32, torch.bfloat16))
+    _dev_tensor(y, "y", dev, shape=(x.shape[0], layer.n), dtypes=(torch.float32, torch.bfloat16))
+    if flags & ~(FLAG_NO_INPUT_RHT | FLAG_NO_OUTPUT_RHT):
+        raise ValueError("flags: unknown bits")
+    st = layer.struct()
+    rc = _lib.glq_fused_linear_noalloc(ctypes.byref(st), x.data_ptr(), _dtype_code(x), x.shape[0], y.data_ptr(),
+                                       _dtype_code(y), flags, _stream_ptr(stream))
+    _check(rc, "glq_fused_linear_noalloc")
+    return y
 
 
 def ep_decode_weights(layer: EpLayer, out, stream=None):

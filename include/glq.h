@@ -196,14 +196,41 @@ size_t glq_fused_linear_workspace(const glq_layer *L, int64_t m);
  *                    Its first GLQ_WS_CTRL_BYTES bytes are control words
  *                    (completion counters of the single-launch layer used at
  *                    small m): they must be zero before the first call with a
- *                    workspace, every call leaves them zero, and calls that run
- *                    concurrently need separate workspaces. The rest is scratch.
+ *                    workspace, every call that returns GLQ_OK (and whose
+ *                    kernels complete) leaves them zero, and calls that run
+ *                    concurrently need separate workspaces. After a call that
+ *                    returned GLQ_ERR_HIP, or whose kernels were aborted, the
+ *                    caller must zero those GLQ_WS_CTRL_BYTES again before the
+ *                    workspace's next use. The rest is scratch.
  *   flags            GLQ_FLAG_* (0 = the full layer)
  * m == 0 is a successful no-op. x and y must not overlap the workspace.
  */
 int glq_fused_linear(const glq_layer *L, const void *x, glq_dtype x_dt, int64_t m,
                      void *y, glq_dtype y_dt, void *workspace, size_t ws_bytes,
                      uint32_t flags, void *hip_stream);
+
+/*
+ * glq_fused_linear_noalloc -- glq_fused_linear with no workspace argument,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * arguments, layouts, results and errors as glq_fused_linear (the same
+ * kernels run). Its scratch is a static device array of
+ * GLQ_STATIC_WS_BYTES bytes per GPU, created with the library's code object
+ * and held until the process ends; the call itself allocates nothing. The
+ * first call on a device looks up that GPU's copy and clears its control
+ * words with a small kernel on the given stream (also after a call that
+ * returned GLQ_ERR_HIP). All calls on one GPU share the array: calls that
+ * overlap in time on one GPU (different streams, or host threads) race and
+ * give undefined results; serialise them.
+ * Returns GLQ_ERR_WORKSPACE (glq_last_error names both sizes) when the layer
+ * at m rows needs more than GLQ_STATIC_WS_BYTES, that is when
+ * glq_fused_linear_workspace(L, m) > GLQ_STATIC_WS_BYTES (about m (k + n)
+ * 4 bytes: e.g. m <= 16 rows at any n, k <= 16384, or ~1000 rows of a
+ * 4096 x 4096 layer); GLQ_ERR_UNSUPPORTED for a device index >= 64.
+ */
+#define GLQ_STATIC_WS_BYTES (32u << 20)
+int glq_fused_linear_noalloc(const glq_layer *L, const void *x, glq_dtype x_dt, int64_t m,
+                             void *y, glq_dtype y_dt, uint32_t flags, void *hip_stream);
 
 /* ------------------------------------------------------------------------
  * Entropy-coded E8 lattice layers ("Transformers Proposes EntroPack

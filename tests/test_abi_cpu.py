@@ -486,3 +486,17 @@ def test_binding_rejects_host_tensors_before_any_call():
         glq.decode_weights(L, torch.zeros((16, 64), dtype=torch.bfloat16))
     with pytest.raises(ValueError):
         glq.rht_apply(x, x, torch.ones(64, dtype=torch.int8), False)
+
+
+def test_noalloc_rejects_oversized_layers_before_any_launch():
+    # glq_fused_linear_noalloc checks the layer's workspace against its static
+    # scratch (GLQ_STATIC_WS_BYTES) before touching a device
+    lib = glq.raw()
+    L = glq.GlqLayerStruct(16384, 4096, 3, 1, 1.0, 1, 1, 1, 1, 1)
+    assert lib.glq_fused_linear_workspace(ctypes.byref(L), 2048) > glq.STATIC_WS_BYTES
+    assert lib.glq_fused_linear_noalloc(ctypes.byref(L), 1, 1, 2048, 1, 1, 0, None) == glq.GLQ_ERR_WORKSPACE
+    assert b"static scratch" in lib.glq_last_error()
+    assert lib.glq_fused_linear_noalloc(ctypes.byref(L), 1, 1, 0, 1, 1, 0, None) == glq.GLQ_OK     # m == 0
+    assert lib.glq_fused_linear_noalloc(ctypes.byref(L), 1, 1, -1, 1, 1, 0, None) == glq.GLQ_ERR_ARG
+    bad = glq.GlqLayerStruct(16, 60, 2, 0, 1.0, 1, 0, 1, 1, 1)
+    assert lib.glq_fused_linear_noalloc(ctypes.byref(bad), 1, 1, 1, 1, 1, 0, None) == glq.GLQ_ERR_ARG
