@@ -1768,19 +1768,19 @@ gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
 
   // Software pipeline: the weights of step s + 1 are decoded while the MFMAs
   // of step s run. A wave issues in order and each SIMD holds one wave, so the
-  // table walk of all 8 groups is split into phases, one per MFMA block (chunk
-  // entries, orbit records, half-vectors, combine), and each phase's LDS reads
-  // have a whole block of MFMAs to return instead of stalling the wave.
-  uint4 bv[2][4];
+  // decode of the 8 groups is split into phases spread over the four MFMA
+  // blocks (records, half-vector offsets and reads, combine), and each
+  // phase's LDS reads have MFMAs to hide behind instead of stalling the wave.
+  // B operands of a step: group g = 4 t + u in register set [g]; two sets,
+  // the step's own and the next step's (decoded while this one runs), which
+  // trade places from one step to the next (the loop is unrolled by two).
+  uint4 B0[8], B1[8];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    bv[0][u] = gm_decode_one<BPW>(i1, i2, 0, u, lds);
-    bv[1][u] = gm_decode_one<BPW>(i1, i2, 1, u, lds);
-  }
+  for (int g = 0; g < 8; ++g) B0[g] = gm_decode_one<BPW>(i1, i2, g >> 2, g & 3, lds);
 #pragma unroll
   for (int t = 0; t < 2; ++t) { i1[t] = j1[t]; i2[t] = j2[t]; }
 
-  for (int64_t s = 0; s < S; ++s) {
+  auto kstep = [&](int64_t s, const uint4 (&bc)[8], uint4 (&bn)[8]) {
     const uint16_t *Acur = (s & 1) ? As1 : As0;
     // indices of step s + 1 (group g = 4 t + u), as i' = i - 1 mod 2^16
     uint32_t q1[8], q2[8];
@@ -1794,11 +1794,12 @@ gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
     }
     gm_load_idx<BPW, G4>(idx1, idx2, n, G, n0, c, p, min(s + 2, S - 1), i1, i2);
 
-    // A operands: those of block u + 1 are read while block u runs
-    uint4 av[8], an[8];
+    // A operands of MFMA block u in set u & 1; those of block u + 1 are read
+    // while block u runs
+    uint4 A0[8], A1[8];
 #pragma unroll
-    for (int a = 0; a < 8; ++a) av[a] = *reinterpret_cast<const uint4 *>(Acur + (32 * a + c) * GM_LDA + 32 * p);
-    auto mfma_block = [&](int u) {
+    for (int a = 0; a < 8; ++a) A0[a] = *reinterpret_cast<const uint4 *>(Acur + (32 * a + c) * GM_LDA + 32 * p);
+    auto mfma_block = [&](int u, const uint4 (&av)[8], uint4 (&an)[8]) {
       if (u < 3) {
 #pragma unroll
         for (int a = 0; a < 8; ++a)
@@ -1807,13 +1808,9 @@ gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
 #pragma unroll
       for (int a = 0; a < 8; ++a) {
         acc[a][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[a]),
-                                                            __builtin_bit_cast(bf16x8, bv[0][u]), acc[a][0], 0, 0, 0);
+                                                            __builtin_bit_cast(bf16x8, bc[u]), acc[a][0], 0, 0, 0);
         acc[a][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[a]),
-                                                            __builtin_bit_cast(bf16x8, bv[1][u]), acc[a][1], 0, 0, 0);
-      }
-      if (u < 3) {
-#pragma unroll
-        for (int a = 0; a < 8; ++a) av[a] = an[a];
+                                                            __builtin_bit_cast(bf16x8, bc[4 + u]), acc[a][1], 0, 0, 0);
       }
     };
 
@@ -1824,29 +1821,32 @@ gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
     // and of groups 4-7 in block 3.
     constexpr int NW = BPW == 4 ? 2 : 1;            // table walks per group
     Dec8<BPW> D;
-    uint4 bn[8];
     D.p1(q1, q2);
-    mfma_block(0);
+    mfma_block(0, A0, A1);
     gm_interleave16<2, (8 * NW + (BPW == 3 ? 8 : 0) + 8 + 15) / 16>();
     __builtin_amdgcn_sched_barrier(0);
     D.template p2<0, 4>(q1, q2);
-    mfma_block(1);
+    mfma_block(1, A1, A0);
     gm_interleave16<(28 * NW + 15) / 16, (8 * NW + 8 + 15) / 16>();
     __builtin_amdgcn_sched_barrier(0);
     D.template p2<4, 8>(q1, q2);
     D.template p3<0, 4>(bn);
-    mfma_block(2);
+    mfma_block(2, A0, A1);
     gm_interleave16<(28 * NW + (BPW == 2 ? 0 : 16) + 15) / 16, (8 * NW + 8 + 15) / 16>();
     __builtin_amdgcn_sched_barrier(0);
     D.template p3<4, 8>(bn);
-    mfma_block(3);
+    mfma_block(3, A1, A0);
     gm_store_a((s & 1) ? As0 : As1, ra, k - GM_BK * (s + 1));   // tile s + 1 (unused past the end)
     gm_load_a(xt, m, k, m0, min(s + 2, S - 1), ra);
     gm_interleave16<3, 1, 1, 1>();
-#pragma unroll
-    for (int g = 0; g < 8; ++g) bv[g >> 2][g & 3] = bn[g];
     __syncthreads();
+  };
+  int64_t s = 0;
+  for (; s + 1 < S; s += 2) {
+    kstep(s, B0, B1);
+    kstep(s + 1, B1, B0);
   }
+  if (s < S) kstep(s, B0, B1);
   gm_epilogue<BPW, OUT_BF16>(acc, rowsum, post, row_scale, out, m, n, m0, n0, lane, wave, vec != 0);
 }
 
