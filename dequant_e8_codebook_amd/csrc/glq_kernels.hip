@@ -158,9 +158,15 @@ __device__ __forceinline__ uint32_t pk_add16(uint32_t a, uint32_t b) {
 
 // Stage-1 and stage-2 halves into operand form: 16-bit lanes M * a + b
 // (mod 2^16), M = 2 at 3 bpw and 4 at 4 bpw (one packed multiply-add).
-template <uint16_t M>
+// MAD: the multiplier is hidden from the optimiser (an empty asm), which then
+// emits one v_pk_mad_u16 instead of a shift and an add (the decode-GEMM
+// keeps the shift and add: there the one-instruction form cost registers)
+template <uint16_t M, bool MAD = true>
 __device__ __forceinline__ uint32_t pk_comb(uint32_t a, uint32_t b) {
-  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, a) * (u16x2)(M) + __builtin_bit_cast(u16x2, b));
+  uint32_t mm = (uint32_t)M * 0x10001u;
+  if constexpr (MAD) asm("" : "+s"(mm));
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, a) * __builtin_bit_cast(u16x2, mm) +
+                                          __builtin_bit_cast(u16x2, b));
 }
 
 // Decode one group into 8 x 16-bit operand values, coordinate t in half t of
@@ -200,7 +206,7 @@ __device__ __forceinline__ uint4 decode_group(uint32_t i1, uint32_t i2, const ui
 // operand form (as decode_ip). Each phase takes a range [G0, G1) of the
 // groups, so a caller can stagger them. q1 / q2 hold the indices as
 // decode_ip takes them.
-template <int BPW>
+template <int BPW, bool MAD = true>
 struct Dec8 {
   uint32_t R1[8], R2[8];
   uint4 r3[8];
@@ -237,11 +243,11 @@ struct Dec8 {
     for (int g = G0; g < G1; ++g) {
       if constexpr (BPW == 2) out[g] = make_uint4(va[g].x, va[g].y, vb[g].x, vb[g].y);
       else if constexpr (BPW == 3)
-        out[g] = make_uint4(pk_comb<2>(va[g].x, r3[g].x), pk_comb<2>(va[g].y, r3[g].y),
-                            pk_comb<2>(vb[g].x, r3[g].z), pk_comb<2>(vb[g].y, r3[g].w));
+        out[g] = make_uint4(pk_comb<2, MAD>(va[g].x, r3[g].x), pk_comb<2, MAD>(va[g].y, r3[g].y),
+                            pk_comb<2, MAD>(vb[g].x, r3[g].z), pk_comb<2, MAD>(vb[g].y, r3[g].w));
       else
-        out[g] = make_uint4(pk_comb<4>(va[g].x, vc[g].x), pk_comb<4>(va[g].y, vc[g].y),
-                            pk_comb<4>(vb[g].x, vd[g].x), pk_comb<4>(vb[g].y, vd[g].y));
+        out[g] = make_uint4(pk_comb<4, MAD>(va[g].x, vc[g].x), pk_comb<4, MAD>(va[g].y, vc[g].y),
+                            pk_comb<4, MAD>(vb[g].x, vd[g].x), pk_comb<4, MAD>(vb[g].y, vd[g].y));
     }
   }
   // all phases at once
@@ -1820,7 +1826,7 @@ gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
     // 1 and of groups 4-7 in block 2; the combine of groups 0-3 in block 2
     // and of groups 4-7 in block 3.
     constexpr int NW = BPW == 4 ? 2 : 1;            // table walks per group
-    Dec8<BPW> D;
+    Dec8<BPW, false> D;
     D.p1(q1, q2);
     mfma_block(0, A0, A1);
     gm_interleave16<2, (8 * NW + (BPW == 3 ? 8 : 0) + 8 + 15) / 16>();
