@@ -2132,6 +2132,7 @@ __global__ __launch_bounds__(64 * kEpWaves) void ep_decode_k(const uint32_t *__r
     const uint32_t j = p * 64 + lane;
     const bool act = j < ng;
     const uint32_t gi = min(g0 + j, total_groups - 1);
+    const uint64_t actm = __builtin_amdgcn_ballot_w64(act);   // lanes with a group this round
     int32_t z[8];
     int32_t b = 0, s7 = 0;
 #pragma unroll
@@ -2152,8 +2153,9 @@ __global__ __launch_bounds__(64 * kEpWaves) void ep_decode_k(const uint32_t *__r
       } else {
         z[7] = 4 * (sym + (b ? vm4 : vm3)) + ((-s7) & 3);
       }
-      const bool need = act && x < 65536u;
-      const uint64_t mask = __builtin_amdgcn_ballot_w64(need);
+      const bool low = x < 65536u;
+      const bool need = act && low;
+      const uint64_t mask = __builtin_amdgcn_ballot_w64(low) & actm;
       const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
       const uint32_t wd = lds16(ring + ((pos + below) & (kEpRing - 1)) * 2);
@@ -2207,6 +2209,139 @@ __global__ __launch_bounds__(64 * kEpWaves) void ep_decode_k(const uint32_t *__r
     pend = ld8(f);
     __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+// The layer product on an entropy-coded weight set at batch 1, fused with
+// the decode: the same symbol decode as ep_decode_k (one wave per block, the
+// word ring in LDS), but each lane multiplies its group's 8 reconstructed
+// weights (float32, exact) with the 8 matching entries of x~ (bf16 [k])
+// instead of storing them. A lane keeps the partial sum of its current output
+// row in a register; when its next group starts another row (groups run
+// row-major) it adds the sum into the wave's row sums in LDS (the rmax rows
+// its block touches), and at the end of the block the wave adds those into z
+// (float32 [n], zeroed before the launch) with one atomic per row. The
+// decoded weights never reach memory. At batch 2 and more the decode-once
+// path wins: there every 8 weights would re-read m x 16 bytes of x~ from the
+// caches, more than writing W^ as bf16 once and streaming it through the GEMV.
+template <uint32_t kEpWaves>
+__global__ __launch_bounds__(64 * kEpWaves) void ep_gemv_k(const uint32_t *__restrict__ states,
+                                                 const uint32_t *__restrict__ offsets,
+                                                 const uint16_t *__restrict__ words, uint32_t nwords,
+                                                 const uint8_t *__restrict__ lut,
+                                                 const float *__restrict__ row_scale, float step,
+                                                 uint32_t total_groups, uint32_t gpr, uint32_t lane_groups,
+                                                 uint32_t nblocks, const uint16_t *__restrict__ xt,
+                                                 float *__restrict__ z, uint32_t rmax) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (uint32_t r = wave; r < kEpLutBytes / 1024; r += kEpWaves)
+    __builtin_amdgcn_global_load_lds((glb_void_t *)(lut + kEpLutHdr + 1024 * r + 16 * lane),
+                                     (lds_void_t *)(uintptr_t)(1024 * r), 16, 0, 0);
+  const int32_t *vm = reinterpret_cast<const int32_t *>(lut);
+  const int32_t vm0 = vm[0], vm1 = vm[1], vm2 = vm[2], vm3 = vm[3], vm4 = vm[4];
+  float *racc = reinterpret_cast<float *>(lds + ep_lds(kEpWaves)) + wave * rmax;
+  for (uint32_t e = lane; e < rmax; e += 64) racc[e] = 0.0f;
+  tables_landed();
+  __syncthreads();
+  const uint32_t blk = blockIdx.x * kEpWaves + wave;
+  if (blk >= nblocks) return;
+
+  const uint32_t ring = kEpLutBytes + wave * kEpRing * 2;   // this wave's ring (bytes)
+  const uint32_t bg = 64 * lane_groups;
+  const uint32_t g0 = blk * bg;
+  const uint32_t ng = min(bg, total_groups - g0);
+  const uint32_t rbase = g0 / gpr, rlast = (g0 + ng - 1) / gpr;
+  uint32_t x = states[(size_t)blk * 64 + lane];
+  uint32_t pos = __builtin_amdgcn_readfirstlane(offsets[blk]);
+  const uint32_t lastq = nwords > 0 ? ((nwords - 1) & ~7u) : 0u;
+  auto ld8 = [&](uint32_t at) -> uint4 {
+    return *reinterpret_cast<const uint4 *>(words + min(at + 8 * lane, lastq));
+  };
+  uint32_t f = pos & ~7u;
+  lds_st128(ring + ((f + 8 * lane) & (kEpRing - 1)) * 2, ld8(f));
+  lds_st128(ring + ((f + 512 + 8 * lane) & (kEpRing - 1)) * 2, ld8(f + 512));
+  asm volatile("" ::"v"(x));
+  f += 1024;
+  float rs = row_scale[min(g0 + lane, total_groups - 1) / gpr];
+  __builtin_amdgcn_sched_barrier(0);
+  uint4 pend = ld8(f);
+  __builtin_amdgcn_sched_barrier(0);
+
+  float acc = 0.0f;
+  uint32_t cur = 0xFFFFFFFFu;                         // row (relative to rbase) of acc
+  const uint32_t rounds = (ng + 63) / 64;
+  for (uint32_t p = 0; p < rounds; ++p) {
+    const uint32_t j = p * 64 + lane;
+    const bool act = j < ng;
+    const uint32_t gi = min(g0 + j, total_groups - 1);
+    const uint32_t row = gi / gpr, q = gi - row * gpr;
+    const uint64_t actm = __builtin_amdgcn_ballot_w64(act);   // lanes with a group this round
+    const uint4 xv = *reinterpret_cast<const uint4 *>(xt + 8 * (size_t)q);   // this group's 8 inputs
+    int32_t zz[8];
+    int32_t b = 0, s7 = 0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint32_t tb = c == 0 ? 0u : (c < 7 ? 1u + (uint32_t)b : 3u + (uint32_t)b);
+      const uint32_t e = lds32(tb * 8192u + (x & 2047u) * 4u);
+      x = ((e >> 8) & 0xFFFu) * (x >> 11) + (e >> 20);
+      const int32_t sym = (int32_t)(e & 0xFFu);
+      if (c == 0) {
+        zz[0] = sym + vm0;
+        b = zz[0] & 1;
+        s7 = zz[0];
+      } else if (c < 7) {
+        zz[c] = 2 * (sym + (b ? vm2 : vm1)) + b;
+        s7 += zz[c];
+      } else {
+        zz[7] = 4 * (sym + (b ? vm4 : vm3)) + ((-s7) & 3);
+      }
+      const bool low = x < 65536u;
+      const bool need = act && low;
+      const uint64_t mask = __builtin_amdgcn_ballot_w64(low) & actm;
+      const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+      const uint32_t wd = lds16(ring + ((pos + below) & (kEpRing - 1)) * 2);
+      x = need ? ((x << 16) | wd) : x;
+      pos += (uint32_t)__popcll(mask);
+    }
+    const float er = __fmul_rn(step, rs);
+    float v[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[c] = __fmul_rn(er, (float)zz[c] * 0.5f);
+    const uint32_t w4[4] = {xv.x, xv.y, xv.z, xv.w};
+    float d = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      d = fmaf(v[2 * c], __uint_as_float(w4[c] << 16), d);
+      d = fmaf(v[2 * c + 1], __uint_as_float(w4[c] & 0xFFFF0000u), d);
+    }
+    if (act) {
+      const uint32_t rr = row - rbase;
+      if (rr != cur) {
+        if (cur != 0xFFFFFFFFu)
+          __hip_atomic_fetch_add(racc + cur, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        acc = 0.0f;
+        cur = rr;
+      }
+      acc += d;
+    }
+    const uint32_t rsi = min(g0 + j + 64, total_groups - 1) / gpr;
+    const uint32_t fn = min(f + 512, (pos & ~7u) + 1024);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_st128(ring + ((f + 8 * lane) & (kEpRing - 1)) * 2, pend);
+    rs = row_scale[rsi];
+    __builtin_amdgcn_sched_barrier(0);
+    f = fn;
+    pend = ld8(f);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (cur != 0xFFFFFFFFu)
+    __hip_atomic_fetch_add(racc + cur, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  // the wave's LDS atomics are done before its lanes read the sums back
+  __builtin_amdgcn_s_waitcnt(0xC07F);                // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  for (uint32_t rr = lane; rr <= rlast - rbase; rr += 64)
+    __hip_atomic_fetch_add(z + rbase + rr, racc[rr], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------- host helpers
@@ -2767,13 +2902,76 @@ int launch_gemm_w(const uint16_t *w, const uint16_t *xt, int64_t m, int64_t n, i
   return hip_status(hipGetLastError());
 }
 
-// Workspace of the entropy-coded layer: decoded W^ (bf16), x~ (bf16), z.
-struct EpWs { size_t w, xt, z, total; };
+// LDS bytes of ep_gemv_k for this layer at `waves` waves per workgroup, or 0
+// where the fused batch-1 product does not apply: m != 1, k / 8 < 64 (a block
+// of groups would span too many rows for the LDS row sums), or a layer of
+// 2^31 groups or more.
+size_t ep_gemv_shm(const glq_ep_layer *L, int64_t m, uint32_t waves) {
+  if (m != 1 || L->k < 512 || L->k % 8 != 0 || L->n < 1 || L->lane_groups < 1 || L->lane_groups > (1 << 20))
+    return 0;
+  if ((double)L->n * (double)L->k / 8.0 >= 2147483648.0) return 0;
+  const uint64_t gpr = (uint64_t)(L->k / 8), bg = 64ull * (uint64_t)L->lane_groups;
+  const uint64_t rmax = (bg + gpr - 2) / gpr + 1;      // rows a block of bg groups can touch
+  const uint64_t shm = ep_lds(waves) + (uint64_t)waves * rmax * 4;
+  return shm <= 160 * 1024 ? (size_t)shm : 0;
+}
 
-EpWs ep_ws_layout(int64_t n, int64_t k, int64_t m) {
+__global__ void __launch_bounds__(256) f32_to_bf16_k(const float *__restrict__ in, uint16_t *__restrict__ out,
+                                                     uint32_t count) {
+  for (uint32_t i = blockIdx.x * 256 + threadIdx.x; i < count; i += gridDim.x * 256)
+    out[i] = f32_to_bf16_rne(in[i]);
+}
+
+// The batch-1 product fused with the decode (ep_gemv_shm(L, m, 8) != 0): x~
+// (bf16) from the input transform (or x itself), z zeroed, then ep_gemv_k
+// summing into z (float32 [n]).
+int launch_ep_gemv(const glq_ep_layer *L, const void *x, glq_dtype x_dt, bool in_rht, int64_t m, uint16_t *xt,
+                   float *z, hipStream_t st) {
+  if (!(L->step > 0.0f) || !std::isfinite(L->step)) return GLQ_ERR_ARG;
+  if (!L->row_scale || !L->states || !L->offsets || !L->lut) return GLQ_ERR_ARG;
+  if (L->nwords < 0 || L->nwords > 0xFFFFFFF0ll || !L->words) return GLQ_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(L->lut) & 15) || (reinterpret_cast<uintptr_t>(L->words) & 15)) return GLQ_ERR_ARG;
+  const uint32_t gpr = (uint32_t)(L->k / 8);
+  const uint32_t total = (uint32_t)(L->n * gpr);
+  const uint64_t bg = 64ull * (uint64_t)L->lane_groups;
+  const uint32_t nblocks = (uint32_t)((total + bg - 1) / bg);
+  const uint32_t rmax = (uint32_t)((bg + gpr - 2) / gpr + 1);
+  // as in the decode: 4-wave workgroups while one wave per SIMD covers the
+  // layer, 8 beyond
+  const bool wide = nblocks > (uint32_t)cu_count() * 4;
+  const uint32_t waves = wide ? 8 : 4;
+  const size_t shm = ep_gemv_shm(L, m, waves);
+  if (!shm) return GLQ_ERR_UNSUPPORTED;
+  const uint16_t *xt_use = reinterpret_cast<const uint16_t *>(x);
+  int rc;
+  if (in_rht) {
+    rc = launch_rht(x, x_dt, xt, GLQ_BF16, m, L->k, L->sign_k, 0, nullptr, st);
+    if (rc) return rc;
+    xt_use = xt;
+  }
+  const uint32_t zw = (uint32_t)(m * L->n);
+  hipLaunchKernelGGL(zero_words, dim3((zw + 255) / 256 < 1024 ? (zw + 255) / 256 : 1024), dim3(256), 0, st,
+                     reinterpret_cast<uint32_t *>(z), zw);
+  rc = hip_status(hipGetLastError(), "zero_words");
+  if (rc) return rc;
+  const uint32_t grid = (nblocks + waves - 1) / waves;
+  auto kern = wide ? ep_gemv_k<8> : ep_gemv_k<4>;
+  rc = allow_lds(kern, shm);
+  if (rc) return rc;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * waves), shm, st, L->states, L->offsets, L->words, (uint32_t)L->nwords,
+                     reinterpret_cast<const uint8_t *>(L->lut), L->row_scale, L->step, total, gpr,
+                     (uint32_t)L->lane_groups, nblocks, xt_use, z, rmax);
+  return hip_status(hipGetLastError(), "ep_gemv_k");
+}
+
+// Workspace of the entropy-coded layer: decoded W^ (bf16; absent where the
+// fused batch-1 product applies), x~ (bf16), z (float32).
+struct EpWs { size_t w, xt, z, total; };
+EpWs ep_ws_layout(const glq_ep_layer *L, int64_t m) {
+  const int64_t n = L->n, k = L->k;
   EpWs e;
   e.w = 0;
-  e.xt = align256((size_t)n * (size_t)k * 2);
+  e.xt = ep_gemv_shm(L, m, 8) ? 0 : align256((size_t)n * (size_t)k * 2);
   e.z = e.xt + align256((size_t)m * (size_t)k * 2);
   e.total = e.z + align256((size_t)m * (size_t)n * 4);
   return e;
@@ -2781,7 +2979,7 @@ EpWs ep_ws_layout(int64_t n, int64_t k, int64_t m) {
 
 extern "C" size_t glq_ep_fused_linear_workspace(const glq_ep_layer *L, int64_t m) {
   if (!L || m <= 0 || L->n < 1 || L->k < 8) return 0;
-  return ep_ws_layout(L->n, L->k, m).total;
+  return ep_ws_layout(L, m).total;
 }
 
 extern "C" int glq_ep_fused_linear(const glq_ep_layer *L, const void *x, glq_dtype x_dt, int64_t m, void *y,
@@ -2797,14 +2995,27 @@ extern "C" int glq_ep_fused_linear(const glq_ep_layer *L, const void *x, glq_dty
   if (in_rht && log2_block(L->k) > kMaxLogBlock) return GLQ_ERR_UNSUPPORTED;
   if (out_rht && log2_block(L->n) > kMaxLogBlock) return GLQ_ERR_UNSUPPORTED;
   if (L->n < 1 || L->k < 8 || L->k % 8 != 0) return GLQ_ERR_ARG;
-  const EpWs ws = ep_ws_layout(L->n, L->k, m);
+  const EpWs ws = ep_ws_layout(L, m);
   if (!workspace || ws_bytes < ws.total || (reinterpret_cast<uintptr_t>(workspace) & 255)) return GLQ_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
   uint8_t *wsb = reinterpret_cast<uint8_t *>(workspace);
   uint16_t *w = reinterpret_cast<uint16_t *>(wsb + ws.w);
   uint16_t *xt = reinterpret_cast<uint16_t *>(wsb + ws.xt);
   void *z = wsb + ws.z;
-  int rc = glq_ep_decode_weights(L, w, GLQ_BF16, hip_stream);
+  int rc;
+  if (ep_gemv_shm(L, m, 8)) {
+    // batch 1: the decode fused into the product (ep_gemv_k), summed in
+    // float32 into z, or straight into a float32 y without the output transform
+    const bool direct = !out_rht && y_dt == GLQ_F32 && !(reinterpret_cast<uintptr_t>(y) & 3);
+    rc = launch_ep_gemv(L, x, x_dt, in_rht, m, xt, reinterpret_cast<float *>(direct ? y : z), st);
+    if (rc || direct) return rc;
+    if (out_rht) return launch_rht(z, GLQ_F32, y, y_dt, m, L->n, L->sign_n, 1, nullptr, st);
+    const uint32_t cnt = (uint32_t)(m * L->n);
+    hipLaunchKernelGGL(f32_to_bf16_k, dim3((cnt + 255) / 256 < 1024 ? (cnt + 255) / 256 : 1024), dim3(256), 0, st,
+                       reinterpret_cast<const float *>(z), reinterpret_cast<uint16_t *>(y), cnt);
+    return hip_status(hipGetLastError(), "f32_to_bf16_k");
+  }
+  rc = glq_ep_decode_weights(L, w, GLQ_BF16, hip_stream);
   if (rc) return rc;
   const uint16_t *xt_use = reinterpret_cast<const uint16_t *>(x);
   if (in_rht) {

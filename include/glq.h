@@ -329,18 +329,26 @@ int glq_ep_decode_weights(const glq_ep_layer *L, void *w_out, glq_dtype out_dt, 
 
 /*
  * glq_ep_fused_linear -- the layer on an entropy-coded weight set:
- * y = U^T (W^ (V x)) with W^ from glq_ep_decode_weights (the weights carry
- * their row scales and step), computed as: W^ decoded to bf16 in the
- * workspace, x~ = V x rounded to bf16, z = x~ W^T on bf16 matrix cores with
- * float32 accumulation (kept in float32, or bf16 for bf16 y when m > 16), then
- * y = U^T z. Flags, dtypes and m as in glq_fused_linear; with
+ * y = U^T (W^ (V x)) with W^ as glq_ep_decode_weights gives it (the weights
+ * carry their row scales and step). x~ = V x is rounded to bf16. Then:
+ *   m = 1, k >= 512 and a block's rows fit the kernel's LDS row sums
+ *     (always for lane_groups <= 128): the decode is fused into the product.
+ *     Each group's 8 weights are reconstructed in float32 (exactly as the
+ *     decode gives them) and multiplied into z = x~ W^T with float32 sums;
+ *     W^ is never stored. Sums from different blocks of groups meet in
+ *     float32 atomic adds, so z (and y) can differ between calls in the
+ *     last bits.
+ *   otherwise: W^ is decoded to bf16 in the workspace and z = x~ W^T runs on
+ *     bf16 matrix cores with float32 accumulation (z kept in float32, or bf16
+ *     for bf16 y when m > 16).
+ * Then y = U^T z. Flags, dtypes and m as in glq_fused_linear; with
  * GLQ_FLAG_NO_INPUT_RHT, x must be bf16 and 16-byte aligned
  * (GLQ_ERR_UNSUPPORTED otherwise).
- *   workspace   device, >= glq_ep_fused_linear_workspace(L, m) bytes (2 n k +
- *               2 m k + 4 m n, each part 256-byte aligned), 256-byte aligned;
- *               owned by the caller, overwritten on every call, and must not
- *               overlap x or y (calls that share one workspace on concurrent
- *               streams race)
+ *   workspace   device, >= glq_ep_fused_linear_workspace(L, m) bytes (2 n k,
+ *               unless the fused batch-1 product applies, + 2 m k + 4 m n,
+ *               each part 256-byte aligned), 256-byte aligned; owned by the
+ *               caller, overwritten on every call, and must not overlap x or y
+ *               (calls that share one workspace on concurrent streams race)
  */
 size_t glq_ep_fused_linear_workspace(const glq_ep_layer *L, int64_t m);
 int glq_ep_fused_linear(const glq_ep_layer *L, const void *x, glq_dtype x_dt, int64_t m, void *y,

@@ -701,6 +701,62 @@ def test_ep_fused_linear_flags(G, flags):
     assert og.relative_error(y, ref) <= TOL_BF16
 
 
+@pytest.mark.parametrize("n,k,m,lg,x_dt,y_dt", [(4096, 4096, 1, 32, "bf16", "bf16"), (4096, 4096, 1, 8, "bf16", "f32"),
+                                               (1000, 1024, 1, 8, "f32", "f32"), (513, 512, 1, 5, "bf16", "f32"),
+                                               (257, 768, 1, 3, "f32", "bf16"), (96, 4096, 1, 64, "bf16", "f32"),
+                                               (4096, 4096, 2, 8, "bf16", "f32"), (1000, 1024, 7, 8, "f32", "f32"),
+                                               (512, 2048, 16, 32, "bf16", "bf16")])
+def test_ep_fused_small_batch(G, n, k, m, lg, x_dt, y_dt):
+    # m = 1 with k / 8 >= 64 takes the decode fused into the product (the
+    # weights never stored): block sizes that end mid-row, blocks spanning
+    # several rows (lg = 3, 5), 4- and 8-wave launches (4096 x 4096 at lg 8
+    # has 4096 blocks); m = 2 .. 16 the decode + GEMV path
+    L, w32, sn, sk = _ep_layer_case(G, n, k, 0.3, 13 * n + k + m, lane_groups=lg)
+    x = np.random.default_rng(n + 3 * m).standard_normal((m, k)).astype(np.float32)
+    if x_dt == "bf16":
+        x = workloads.bf16_round_trip(x)
+    y = _ep_run(G, L, x, x_dt, y_dt)
+    ref = rht.rht_transpose(rht.rht_forward(x.astype(np.float64), sk) @ w32.T, sn)
+    assert og.relative_error(y, ref) <= TOL_BF16
+    # every row checked on its own (a row summed into the wrong output row
+    # would move the total error little)
+    for i in range(m):
+        assert og.relative_error(y[i], ref[i]) <= TOL_BF16
+
+
+@pytest.mark.parametrize("flags,y_dt", [(1, "f32"), (2, "f32"), (3, "f32"), (2, "bf16"), (3, "bf16")])
+def test_ep_fused_small_batch_flags(G, flags, y_dt):
+    # at m = 1 without the output transform a float32 y is summed into
+    # directly, a bf16 y converted from the float32 sums
+    n, k, m = 384, 1024, 1
+    L, w32, sn, sk = _ep_layer_case(G, n, k, 0.25, 78 + flags)
+    x = workloads.bf16_round_trip(np.random.default_rng(flags).standard_normal((m, k)).astype(np.float32))
+    y = _ep_run(G, L, x, "bf16", y_dt, flags)
+    xt = x.astype(np.float64) if flags & 1 else rht.rht_forward(x.astype(np.float64), sk)
+    ref = xt @ w32.T
+    if not flags & 2:
+        ref = rht.rht_transpose(ref, sn)
+    assert og.relative_error(y, ref) <= TOL_BF16
+
+
+def test_ep_fused_small_batch_repeat_clears(G):
+    # the float32 sums start from zero on every call (no carry-over between
+    # calls sharing a workspace or an output)
+    n, k, m = 256, 1024, 1
+    L, w32, sn, sk = _ep_layer_case(G, n, k, 0.3, 5)
+    x = workloads.bf16_round_trip(np.random.default_rng(9).standard_normal((m, k)).astype(np.float32))
+    xt = _t(x, torch.bfloat16)
+    ws = torch.zeros(G.ep_workspace_bytes(L, m), device="cuda", dtype=torch.uint8)
+    ref = rht.rht_forward(x.astype(np.float64), sk) @ w32.T
+    for flags in (0, 2):
+        y = torch.full((m, n), 7.0, device="cuda", dtype=torch.float32)
+        for _ in range(3):
+            G.ep_fused_linear(L, xt, y, ws, flags)
+        torch.cuda.synchronize()
+        want = ref if flags & 2 else rht.rht_transpose(ref, sn)
+        assert og.relative_error(y.cpu().numpy(), want) <= TOL_BF16
+
+
 def test_ep_fused_linear_full_size_sampled(G):
     # the prefill up-projection shape, 16384 x 4096 at m = 2048: sampled rows
     # of y against the oracle (row r of y needs only row r of x)
@@ -724,6 +780,15 @@ def test_ep_decode_zero_layer(G):
     assert not out.any()
     y = _ep_run(G, L, np.ones((3, 256), np.float32), "f32", "f32")
     assert not np.any(y)
+    # the same at k = 512, where m = 1 takes the fused decode-product
+    w = np.zeros((64, 512), np.float32)
+    sk = workloads.signs(512, 4)
+    h = G.ep_encode(w, sn, sk, 0.25, 4)
+    assert len(h.words) == 0
+    L = G.EpLayer.from_host(h, sign_k=sk, sign_n=sn)
+    for m in (1, 3, 16):
+        y = _ep_run(G, L, np.ones((m, 512), np.float32), "f32", "f32")
+        assert not np.any(y)
 
 
 @pytest.mark.parametrize("m,x_dt,y_dt,bpw", [(1, "bf16", "bf16", 2), (3, "f32", "f32", 2), (16, "bf16", "f32", 4),
