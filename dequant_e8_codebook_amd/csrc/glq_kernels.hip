@@ -12,11 +12,13 @@
 //                   float32 in LDS (x~ = V x on inputs, y = U^T z on outputs);
 //                   optionally rounds to bf16 and records each row's sum of the
 //                   rounded values (needed by the biased 3/4 bpw operands).
-//   rht_rows_vec,   the same for 16-byte aligned rows, out of place: radix-16
-//   rht_rows_reg    passes through LDS (thousands of rows of several blocks,
-//                   3072 or 12288), or butterflies in registers and lane
-//                   exchanges with one LDS transpose (rows that are one block
-//                   of 1024 .. 16384, and a few rows of any width).
+//   rht_rows_blk,   the same for 16-byte aligned rows, out of place: rows of
+//   rht_rows_reg,   whole blocks of 1024 .. 16384 with one wave per 1024
+//   rht_rows_vec    elements (butterflies in registers and DPP lane stages,
+//                   one LDS transpose above the wave); a few rows of any width
+//                   on 1024 threads; the rest in radix-16 passes through LDS.
+//   ep_gemv_k       entropy-coded layers at batch 1: the symbol decode fused
+//                   into the product.
 //   decode_weights  indices -> W^ (rotated basis) as float32 or bf16.
 //   gemv_bf16       m <= 16: one 16-row weight tile per workgroup, 16 waves split
 //                   k, bf16 MFMA 16x16x32 with x~ rows as the M side (the few
@@ -682,7 +684,7 @@ row_sums_bf16(const uint16_t *x, int64_t rows, int64_t n, float *rowsum) {
 template <int E, int NW = 16> struct LyF {
   static constexpr int LE = E == 1 ? 0 : E == 2 ? 1 : E == 4 ? 2 : E == 8 ? 3 : 4;
   static constexpr int L = LE + 6;
-  static constexpr int WB = NW == 4 ? 2 : NW == 8 ? 3 : 4;
+  static constexpr int WB = NW == 1 ? 0 : NW == 2 ? 1 : NW == 4 ? 2 : NW == 8 ? 3 : 4;
   static constexpr int LPC = E < NW ? NW / E : 1;  // lanes per column after the transpose
   static constexpr int CPT = E < NW ? 1 : E / NW;  // columns per thread after the transpose
 };
@@ -743,28 +745,12 @@ __device__ __forceinline__ void ly_stage_swap(float (&v)[E]) {
   }
 }
 
-// FULL: the block is all 64 NW E elements (logb = L + log2 NW), so that every
-// stage runs and none is tested at run time.
-template <int E, int NW = 16, bool FULL = false>
-__device__ __forceinline__ bool ly_fwht(float (&v)[E], float *buf, int logb_rt, int tid) {
+// The stages above the wave (labels L .. logb - 1, logb > L): an LDS transpose
+// to the layout of ly_elem(., ., true), then the butterflies there.
+template <int E, int NW>
+__device__ __forceinline__ void ly_fwht_cross(float (&v)[E], float *buf, int logb, int tid) {
   using F = LyF<E, NW>;
   constexpr int LE = F::LE, L = F::L;
-  const int logb = FULL ? L + F::WB : logb_rt;
-  const int lane = tid & 63;
-#pragma unroll
-  for (int s = 0; s < LE; ++s)
-    if (s < logb) ly_stage_regs<E>(v, s);
-#pragma unroll
-  for (int s = 0; s < 6; ++s) {
-    if (LE + s < logb) {
-      if constexpr (E >= 2) {
-        if (s == 4) { ly_stage_swap<E, true>(v); continue; }
-        if (s == 5) { ly_stage_swap<E, false>(v); continue; }
-      }
-      ly_stage_lanes<E>(v, 1 << s, (lane >> s) & 1);
-    }
-  }
-  if (logb <= L) return false;
   {
     float *w = buf + E * tid + 4 * (tid >> 6);         // element E tid + i at e + 4 (e >> L)
     if constexpr (E >= 4) {
@@ -801,8 +787,34 @@ __device__ __forceinline__ bool ly_fwht(float (&v)[E], float *buf, int logb_rt, 
       ly_stage_regs<E>(v, h);
     }
   }
+}
+
+// FULL: the block is all 64 NW E elements (logb = L + log2 NW), so that every
+// stage runs and none is tested at run time.
+template <int E, int NW = 16, bool FULL = false>
+__device__ __forceinline__ bool ly_fwht(float (&v)[E], float *buf, int logb_rt, int tid) {
+  using F = LyF<E, NW>;
+  constexpr int LE = F::LE, L = F::L;
+  const int logb = FULL ? L + F::WB : logb_rt;
+  const int lane = tid & 63;
+#pragma unroll
+  for (int s = 0; s < LE; ++s)
+    if (s < logb) ly_stage_regs<E>(v, s);
+#pragma unroll
+  for (int s = 0; s < 6; ++s) {
+    if (LE + s < logb) {
+      if constexpr (E >= 2) {
+        if (s == 4) { ly_stage_swap<E, true>(v); continue; }
+        if (s == 5) { ly_stage_swap<E, false>(v); continue; }
+      }
+      ly_stage_lanes<E>(v, 1 << s, (lane >> s) & 1);
+    }
+  }
+  if (logb <= L) return false;
+  ly_fwht_cross<E, NW>(v, buf, logb, tid);
   return true;
 }
+
 
 __device__ __forceinline__ int ly_e(int count) {    // elements per thread for count <= 16384 elements
   int e = 1;
@@ -1002,6 +1014,227 @@ rht_rows_reg(const void *in, void *out, int64_t rows, int n, int logb, const int
     default: GLQ_RR(16); break;
   }
 #undef GLQ_RR
+}
+
+// RHT of rows of nb blocks of B = 1024 NW elements (n = nb B, B the Hadamard
+// block, nb NW <= 16): one workgroup of nb NW waves per row (grid-stride over
+// rows), NW waves per block with 16 elements per lane, the FWHT over each
+// wave's 1024 elements in registers and lane exchanges (rb_fwht_wave: no
+// LDS), then for NW > 1 one LDS transpose for the top log2 NW bits
+// (ly_fwht_cross) and one back, so that loads and stores are whole 16-byte
+// vectors. It replaces the LDS radix-16 kernel on rows of several blocks
+// (3072 = 3 x 1024, 12288 = 3 x 4096), whose three to four LDS passes per
+// element held it to about 3 TB/s. The next row's inputs are in flight during
+// the current row's transform; the row sum of the rounded outputs is reduced
+// over the workgroup (deterministic).
+//
+// Labels: thread t of a block, register i carries label p = 16 t + i, which
+// stands for element rb_elem(p) of the block: label bits 0..2 are element
+// bits 0..2, label bit 3 is element bit 9, label bits 4..9 (the lane l)
+// are element bits 3..8 after the lane relabelling rb_ell, and bits 10 and
+// up (the wave) are the same. Lane l of a wave then holds elements
+// 8 rb_ell(l) + 0..7 and 512 + 8 rb_ell(l) + 0..7 of its 1024-element chunk,
+// so each 16-byte load or store of the wave covers one contiguous KiB.
+//
+// The lane stages of rb_fwht_wave pair lanes l and l ^ m for m = 1, 2, 7, 8:
+// each partner read is a single DPP permutation (quad_perm for 1 and 2, the
+// half-row mirror for 7, a rotation by 8 within 16-lane rows for 8), folded
+// into one fused multiply-add per element. Stage j transforms bit j of
+// rb_ell(l) (its pairs differ in exactly that bit), which makes the four
+// stages the Hadamard transform over element bits 3..6. The lower member of
+// a pair (bit j of rb_ell(l) clear) keeps a + b, the upper one a - b instead
+// of b - a: the upper lane's value is then the negated result, a factor
+// rb_sgn(l) = (-1)^popcount(rb_ell(l) & 15) that every later stage carries
+// along unchanged (partners share it) and the output scale removes.
+__device__ __forceinline__ int rb_ell(int l) { return l ^ (((l >> 2) & 1) * 3); }
+__device__ __forceinline__ float rb_sgn(int l) { return (__popc(rb_ell(l) & 15) & 1) ? -1.0f : 1.0f; }
+__device__ __forceinline__ int rb_elem(int p) {
+  return (p & ~1023) | (p & 7) | (((p >> 3) & 1) << 9) | (rb_ell((p >> 4) & 63) << 3);
+}
+
+// One lane stage on 16 registers: v[i] += s * v[i] of the partner lane, the
+// partner read by the DPP control CTRL of a v_fmac_f32_dpp (one VALU
+// operation per element; the compiler does not fold a DPP move into a
+// multiply-add). The leading s_nop gives the two wait states a DPP read needs
+// after a VALU write of its source, which the compiler cannot see through the
+// asm; inside the block each instruction reads its own register only.
+#define RB_FMAC16(CTRL, S)                                                                                  \
+  asm volatile("s_nop 1\n\t"                                                                                \
+               "v_fmac_f32_dpp %0, %0, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                          \
+               "v_fmac_f32_dpp %1, %1, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                          \
+               "v_fmac_f32_dpp %2, %2, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                          \
+               "v_fmac_f32_dpp %3, %3, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                          \
+               "v_fmac_f32_dpp %4, %4, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                          \
+               "v_fmac_f32_dpp %5, %5, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                          \
+               "v_fmac_f32_dpp %6, %6, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                          \
+               "v_fmac_f32_dpp %7, %7, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                          \
+               "v_fmac_f32_dpp %8, %8, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                          \
+               "v_fmac_f32_dpp %9, %9, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                          \
+               "v_fmac_f32_dpp %10, %10, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                        \
+               "v_fmac_f32_dpp %11, %11, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                        \
+               "v_fmac_f32_dpp %12, %12, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                        \
+               "v_fmac_f32_dpp %13, %13, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                        \
+               "v_fmac_f32_dpp %14, %14, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                        \
+               "v_fmac_f32_dpp %15, %15, %16 " CTRL " row_mask:0xf bank_mask:0xf"                            \
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]),         \
+                 "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]),     \
+                 "+v"(v[14]), "+v"(v[15])                                                                    \
+               : "v"(S))
+
+// The FWHT over a wave's 1024 labels (E = 16 registers a lane): registers,
+// then the four DPP lane stages, then lane bits 4 and 5 by lane swaps.
+__device__ __forceinline__ void rb_fwht_wave(float (&v)[16], int lane) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) ly_stage_regs<16>(v, s);
+  const int ell = rb_ell(lane);
+  const float s0 = (ell & 1) ? -1.0f : 1.0f, s1 = (ell & 2) ? -1.0f : 1.0f;
+  const float s2 = (ell & 4) ? -1.0f : 1.0f, s3 = (ell & 8) ? -1.0f : 1.0f;
+  RB_FMAC16("quad_perm:[1,0,3,2]", s0);   // lane ^ 1
+  RB_FMAC16("quad_perm:[2,3,0,1]", s1);   // lane ^ 2
+  RB_FMAC16("row_half_mirror", s2);       // lane ^ 7
+  RB_FMAC16("row_ror:8", s3);             // lane ^ 8
+  asm volatile("s_nop 1" ::);
+  ly_stage_swap<16, true>(v);
+  ly_stage_swap<16, false>(v);
+}
+#undef RB_FMAC16
+
+template <bool IN_BF16>
+__device__ __forceinline__ void rb_fetch(const void *in, size_t base, uint4 (&r)[IN_BF16 ? 2 : 4]) {
+  if constexpr (IN_BF16) {
+    const uint16_t *p = reinterpret_cast<const uint16_t *>(in) + base;
+    r[0] = *reinterpret_cast<const uint4 *>(p);
+    r[1] = *reinterpret_cast<const uint4 *>(p + 512);
+  } else {
+    const float *p = reinterpret_cast<const float *>(in) + base;
+    r[0] = *reinterpret_cast<const uint4 *>(p);
+    r[1] = *reinterpret_cast<const uint4 *>(p + 4);
+    r[2] = *reinterpret_cast<const uint4 *>(p + 512);
+    r[3] = *reinterpret_cast<const uint4 *>(p + 516);
+  }
+}
+
+template <bool IN_BF16>
+__device__ __forceinline__ void rb_unpack(const uint4 (&r)[IN_BF16 ? 2 : 4], float (&v)[16]) {
+  if constexpr (IN_BF16) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t w[4] = {r[h].x, r[h].y, r[h].z, r[h].w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        v[8 * h + 2 * t] = __uint_as_float(w[t] << 16);
+        v[8 * h + 2 * t + 1] = __uint_as_float(w[t] & 0xFFFF0000u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[4 * q] = __uint_as_float(r[q].x);
+      v[4 * q + 1] = __uint_as_float(r[q].y);
+      v[4 * q + 2] = __uint_as_float(r[q].z);
+      v[4 * q + 3] = __uint_as_float(r[q].w);
+    }
+  }
+}
+
+template <int NW, bool IN_BF16, bool OUT_BF16, bool TRANSPOSE>
+__global__ void __launch_bounds__(1024)
+rht_rows_blk(const void *in, void *out, int64_t rows, int n, int nb, const int8_t *signs, float *rowsum) {
+  constexpr int E = 16, B = 64 * NW * E;
+  using F = LyF<E, NW>;
+  constexpr int logb = F::L + F::WB;
+  static_assert((1 << logb) == B, "block size");
+  extern __shared__ __attribute__((aligned(16))) float rb_buf[];   // nb (B + 64) floats when NW > 1
+  __shared__ float red[16];
+  const int tid = threadIdx.x;
+  const int blk = tid / (64 * NW), tl = tid - blk * 64 * NW;
+  float *buf = rb_buf + blk * (B + 64);
+  const int eb = blk * B;
+  const int el = 1024 * (tl >> 6) + 8 * rb_ell(tl & 63);   // element of register 0 (8.. at el + 512)
+  const float inv = 1.0f / sqrtf((float)B);      // exact for even log2 B
+  constexpr bool tr = NW > 1;                     // the labels are transposed iff the wave stages used LDS
+  // sg: input signs (applied before the transform); sc: output scale, the
+  // sign after the transform or 1 / sqrt(B), times rb_sgn of the label's lane
+  float sg[E], sc[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const int p = tr ? ly_elem<E, NW>(tl, i, true) : 16 * tl + i;
+    sc[i] = rb_sgn((p >> 4) & 63) * (TRANSPOSE ? (float)signs[eb + rb_elem(p)] * inv : inv);
+    sg[i] = TRANSPOSE ? 1.0f : (float)signs[eb + el + (i & 7) + 512 * (i >> 3)];
+  }
+  uint4 raw[IN_BF16 ? 2 : 4];
+  if ((int64_t)blockIdx.x < rows) rb_fetch<IN_BF16>(in, (size_t)blockIdx.x * n + eb + el, raw);
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    const size_t base = (size_t)row * n + eb;
+    float v[E];
+    rb_unpack<IN_BF16>(raw, v);
+    if (row + gridDim.x < rows) rb_fetch<IN_BF16>(in, base + (size_t)gridDim.x * n + el, raw);   // next row
+    if (!TRANSPOSE) {
+#pragma unroll
+      for (int i = 0; i < E; ++i) v[i] *= sg[i];
+    }
+    rb_fwht_wave(v, tl & 63);
+    if constexpr (NW > 1) {
+      __syncthreads();                              // the previous row is out of buf
+      ly_fwht_cross<E, NW>(v, buf, logb, tl);
+    }
+    float x[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) x[i] = v[i] * sc[i];
+    if constexpr (tr) {
+      // back to the thread's own labels 16 tl + i through LDS, so that the
+      // stores below are whole 16-byte vectors (the layout of ly_fwht_cross's
+      // buffer: label p at p + 4 (p >> 10))
+      __syncthreads();                              // every lane is done reading buf
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        const int p = ly_elem<E, NW>(tl, i, true);
+        buf[p + 4 * (p >> 10)] = x[i];
+      }
+      __syncthreads();
+      const float *r = buf + 16 * tl + 4 * (tl >> 6);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 f = reinterpret_cast<const float4 *>(r)[q];
+        x[4 * q] = f.x; x[4 * q + 1] = f.y; x[4 * q + 2] = f.z; x[4 * q + 3] = f.w;
+      }
+    }
+    float rs = 0.0f;
+    if constexpr (OUT_BF16) {
+      uint32_t w[E / 2];
+#pragma unroll
+      for (int i = 0; i < E; i += 2) w[i / 2] = bf16x2_rne(x[i], x[i + 1]);
+      if (rowsum) {
+#pragma unroll
+        for (int i = 0; i < E / 2; ++i) rs += __uint_as_float(w[i] << 16) + __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+      uint16_t *o = reinterpret_cast<uint16_t *>(out) + base + el;
+      *reinterpret_cast<uint4 *>(o) = make_uint4(w[0], w[1], w[2], w[3]);
+      *reinterpret_cast<uint4 *>(o + 512) = make_uint4(w[4], w[5], w[6], w[7]);
+    } else {
+      if (rowsum) {
+#pragma unroll
+        for (int i = 0; i < E; ++i) rs += x[i];
+      }
+      float *o = reinterpret_cast<float *>(out) + base + el;
+      reinterpret_cast<float4 *>(o)[0] = make_float4(x[0], x[1], x[2], x[3]);
+      reinterpret_cast<float4 *>(o)[1] = make_float4(x[4], x[5], x[6], x[7]);
+      reinterpret_cast<float4 *>(o + 512)[0] = make_float4(x[8], x[9], x[10], x[11]);
+      reinterpret_cast<float4 *>(o + 512)[1] = make_float4(x[12], x[13], x[14], x[15]);
+    }
+    if (rowsum) {
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) rs += lane_xor(rs, off);
+      if (NW == 1) __syncthreads();                 // (NW > 1: the barriers above) red is free
+      if ((tid & 63) == 0) red[tid >> 6] = rs;
+      __syncthreads();
+      if (tid == 0) {
+        float t = 0.0f;
+        for (int w = 0; w < NW * nb; ++w) t += red[w];
+        rowsum[row] = t;
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------- decode only
@@ -2442,6 +2675,34 @@ int launch_rht_reg_nw(const void *in, void *out, int64_t rows, int64_t n, int lb
   return hip_status(hipGetLastError());
 }
 
+// rows of nb > 1 blocks of B = 1024, 2048 or 4096 (rht_rows_blk)
+template <int NW, bool IB, bool OB, bool TR>
+int launch_rht_blk_nw(const void *in, void *out, int64_t rows, int64_t n, const int8_t *signs, float *rowsum,
+                      hipStream_t st) {
+  constexpr int B = 1024 * NW;
+  const int nb = (int)(n / B);
+  const size_t shm = NW > 1 ? sizeof(float) * (size_t)nb * (B + 64) : 0;
+  const int64_t cap = (int64_t)cu_count() * (24 / (nb * NW) > 1 ? 24 / (nb * NW) : 1);
+  const int64_t grid = rows < cap ? rows : cap;
+  const int rc = allow_lds(rht_rows_blk<NW, IB, OB, TR>, shm + 64);
+  if (rc) return rc;
+  hipLaunchKernelGGL((rht_rows_blk<NW, IB, OB, TR>), dim3((unsigned)grid), dim3(64 * NW * nb), shm, st, in, out, rows,
+                     (int)n, nb, signs, rowsum);
+  return hip_status(hipGetLastError());
+}
+
+template <bool IB, bool OB, bool TR>
+int launch_rht_blk(const void *in, void *out, int64_t rows, int64_t n, int lb, const int8_t *signs, float *rowsum,
+                   hipStream_t st) {
+  switch (lb) {
+    case 10: return launch_rht_blk_nw<1, IB, OB, TR>(in, out, rows, n, signs, rowsum, st);
+    case 11: return launch_rht_blk_nw<2, IB, OB, TR>(in, out, rows, n, signs, rowsum, st);
+    case 12: return launch_rht_blk_nw<4, IB, OB, TR>(in, out, rows, n, signs, rowsum, st);
+    case 13: return launch_rht_blk_nw<8, IB, OB, TR>(in, out, rows, n, signs, rowsum, st);
+    default: return launch_rht_blk_nw<16, IB, OB, TR>(in, out, rows, n, signs, rowsum, st);
+  }
+}
+
 // x~ of at most 16 rows written in the small-batch GEMV's operand layout
 // (tile16_index): bf16 in and out, n a multiple of 256 and at most 16384,
 // 16-byte aligned pointers, in != out (rht_tile16_ok).
@@ -2470,13 +2731,28 @@ int launch_rht(const void *in, glq_dtype in_dt, void *out, glq_dtype out_dt, int
   if (lb > kMaxLogBlock) return GLQ_ERR_UNSUPPORTED;
   const bool aligned = ((reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out) |
                          reinterpret_cast<uintptr_t>(signs)) & 15) == 0;
-  // the register kernel where it measured faster: rows that are one whole
-  // block of 1024 .. 16384 (its full-block variant; level with the LDS kernel
-  // at 4096, faster at 1024, 2048, 8192 and 16384), and a few rows
-  // (decode-time batches, latency-bound: 1024 threads per row); the LDS
-  // radix-16 kernel below for thousands of rows of several blocks (3072,
-  // 12288)
+  // the block kernel for rows of whole blocks of 1024 .. 16384 (one
+  // workgroup of at most 16 waves per row); the register kernel for a few
+  // rows (decode-time batches, latency-bound: 1024 threads per row) and for
+  // one-block rows the block kernel does not take; the LDS radix-16 kernel
+  // for the remaining aligned rows
   const bool few = rows <= 64 && n % 8 == 0 && n <= 16384;
+  // rows of whole blocks of 1024 .. 16384 (at most 16 waves a row): one
+  // workgroup per row, the blocks' FWHTs in registers (rht_rows_blk)
+  const int64_t nblk = n >> lb;
+  if (lb >= 10 && lb <= 14 && (nblk << (lb - 10)) <= 16 && (nblk > 1 || !few) && aligned && in != out) {
+    const bool ib = in_dt == GLQ_BF16, ob = out_dt == GLQ_BF16;
+    if (transpose) {
+      if (ib) return ob ? launch_rht_blk<true, true, true>(in, out, rows, n, lb, signs, rowsum, st)
+                        : launch_rht_blk<true, false, true>(in, out, rows, n, lb, signs, rowsum, st);
+      return ob ? launch_rht_blk<false, true, true>(in, out, rows, n, lb, signs, rowsum, st)
+                : launch_rht_blk<false, false, true>(in, out, rows, n, lb, signs, rowsum, st);
+    }
+    if (ib) return ob ? launch_rht_blk<true, true, false>(in, out, rows, n, lb, signs, rowsum, st)
+                      : launch_rht_blk<true, false, false>(in, out, rows, n, lb, signs, rowsum, st);
+    return ob ? launch_rht_blk<false, true, false>(in, out, rows, n, lb, signs, rowsum, st)
+              : launch_rht_blk<false, false, false>(in, out, rows, n, lb, signs, rowsum, st);
+  }
   const bool one_block = n >= 1024 && n <= 16384 && (n & (n - 1)) == 0;
   if ((one_block || few) && aligned && in != out) {
     const bool ib = in_dt == GLQ_BF16, ob = out_dt == GLQ_BF16;

@@ -158,9 +158,9 @@ def test_rht_few_rows_whole_block(G, n, rows, transpose, dt):
 @pytest.mark.parametrize("n", [3072, 4096, 16384, 8200, 1024, 8192])
 @pytest.mark.parametrize("transpose", [0, 1])
 def test_rht_many_rows(G, n, transpose):
-    # more rows than the few-row path takes: the LDS radix-16 kernel (3072,
-    # 8200) and the full-block register kernel on 256 .. 1024 threads (1024,
-    # 4096, 8192, 16384)
+    # more rows than the few-row path takes: the block kernel (3072), the LDS
+    # radix-16 kernel (8200) and the full-block register kernel on 256 .. 1024
+    # threads (1024, 4096, 8192, 16384)
     rows = 96
     rng = np.random.default_rng(n + transpose)
     x = rng.standard_normal((rows, n)).astype(np.float32)
@@ -175,8 +175,7 @@ def test_rht_many_rows(G, n, transpose):
 @pytest.mark.parametrize("n", [3072, 12288])
 @pytest.mark.parametrize("transpose", [0, 1])
 def test_rht_many_rows_bf16(G, n, transpose):
-    # the LDS kernel on bf16 rows of several blocks: 2 pieces a thread (3072)
-    # and 8 (12288, compile-time pass strides under a 3-wave register cap)
+    # bf16 rows of several blocks (the block kernel: 3 x 1024, 3 x 4096)
     rows = 96
     x = workloads.bf16_round_trip(np.random.default_rng(n + 7 * transpose).standard_normal((rows, n)).astype(np.float32))
     sig = workloads.signs(n, n + 9)
@@ -186,6 +185,33 @@ def test_rht_many_rows_bf16(G, n, transpose):
     ref = (rht.rht_transpose if transpose else rht.rht_forward)(x.astype(np.float64), sig)
     got = out.float().cpu().numpy()
     assert np.max(np.abs(got - ref) / np.maximum(np.abs(ref), 1e-3)) <= 2.0 ** -8   # one bf16 rounding
+
+
+@pytest.mark.parametrize("n,rows", [(3072, 2600), (12288, 600), (6144, 300), (5120, 40), (15360, 70),
+                                    (10240, 33), (20480, 9)])
+@pytest.mark.parametrize("transpose", [0, 1])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_rht_multi_block_rows(G, n, rows, transpose, dt):
+    # rows of several Hadamard blocks of 1024 (3072, 5120, 15360), 2048 (6144,
+    # 10240) or 4096 (12288): one workgroup per row, one to four waves per
+    # block; more rows than resident workgroups at 3072 and 12288 (the
+    # grid-stride loop with the next row in flight); 20480 = 5 x 4096 needs
+    # 20 waves and takes the LDS kernel
+    x = np.random.default_rng(n + rows + transpose).standard_normal((rows, n)).astype(np.float32)
+    if dt == "bf16":
+        x = workloads.bf16_round_trip(x)
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    sig = workloads.signs(n, n + 13)
+    out = torch.full((rows, n), float("nan"), device="cuda", dtype=tdt)
+    G.rht_apply(_t(x, tdt), out, _t(sig), bool(transpose))
+    torch.cuda.synchronize()
+    ref = (rht.rht_transpose if transpose else rht.rht_forward)(x.astype(np.float64), sig)
+    got = out.float().cpu().numpy()
+    assert np.isfinite(got).all()
+    if dt == "f32":
+        assert np.max(np.abs(got - ref)) <= 1e-6 * np.max(np.abs(ref)) * np.log2(rht.block_size(n))
+    else:
+        assert np.max(np.abs(got - ref) / np.maximum(np.abs(ref), 1e-3)) <= 2.0 ** -8   # one bf16 rounding
 
 
 def test_rht_bf16_in_out(G):
