@@ -1628,6 +1628,95 @@ __device__ __forceinline__ void ly_output(const float *z, const int8_t *sign_n, 
   }
 }
 
+// Output side for one row of n = 1024 NW (the Hadamard block is all of n):
+// waves 0 .. NW - 1 hold 16 elements a lane, lane l of wave w the elements
+// 1024 w + 256 j + 4 rb_ell(l) + 0..3 (j = 0..3, registers 4 j ..), so that z
+// comes in as four 16-byte coherent loads a lane, each covering one
+// contiguous KiB of the wave (per-element loads fetched every line 16 times),
+// and y goes out in 8- or 16-byte stores. The FWHT over a wave's 1024
+// elements is rb_fwht_wave (register bits are element bits 0, 1, 8, 9, the
+// relabelled lane bits element bits 2..7), the bits above the wave one LDS
+// transpose (ly_fwht_cross) and one back. Every thread of the workgroup
+// takes part in the barriers.
+__device__ __forceinline__ int lo_elem(int p) {
+  return (p & ~1023) | (p & 3) | (((p >> 2) & 3) << 8) | (rb_ell((p >> 4) & 63) << 2);
+}
+
+template <int NW>
+__device__ __forceinline__ void ly_output_rb(const float *z, const int8_t *sign_n, int n, float *buf, void *y,
+                                             glq_dtype y_dt, int tid) {
+  constexpr int B = 1024 * NW;
+  const bool act = tid < 64 * NW;                    // whole waves
+  const int lane = tid & 63;
+  const int el = 1024 * (tid >> 6) + 4 * rb_ell(lane);   // element of register 0 (4 j + t at el + 256 j + t)
+  float v[16];
+  if (act) {
+    // coherent (sc1) loads, as the relaxed agent-scope loads of z elsewhere
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)z, 0, 4 * B, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 u = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, 4 * (el + 256 * j), 0, 16));
+      v[4 * j] = __uint_as_float(u.x); v[4 * j + 1] = __uint_as_float(u.y);
+      v[4 * j + 2] = __uint_as_float(u.z); v[4 * j + 3] = __uint_as_float(u.w);
+    }
+    rb_fwht_wave(v, lane);
+  }
+  const float inv = 1.0f / sqrtf((float)B);
+  if constexpr (NW > 1) {
+    // the bits above the wave, then back to the thread's own labels 16 tid + i
+    if (act) {
+      float *w = buf + 16 * tid + 4 * (tid >> 6);
+#pragma unroll
+      for (int i = 0; i < 16; i += 4) *reinterpret_cast<float4 *>(w + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+    }
+    __syncthreads();
+    if (act) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int hi = i % NW;
+        v[i] = buf[tid + 64 * NW * (i / NW) + (hi << 10) + 4 * hi];
+      }
+#pragma unroll
+      for (int h = 0; h < LyF<16, NW>::WB; ++h) ly_stage_regs<16>(v, h);
+    }
+    __syncthreads();                                 // every lane is done reading buf
+    if (act) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int p = ly_elem<16, NW>(tid, i, true);
+        buf[p + 4 * (p >> 10)] = v[i] * (inv * rb_sgn((p >> 4) & 63));
+      }
+    }
+    __syncthreads();
+    if (act) {
+      const float *r = buf + 16 * tid + 4 * (tid >> 6);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 f = reinterpret_cast<const float4 *>(r)[q];
+        v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+      }
+    }
+  } else {
+    const float c = inv * rb_sgn(lane);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] *= c;
+  }
+  if (!act) return;
+  // labels 16 tid + i are elements el + 256 j + t (i = 4 j + t): signs, store
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = el + 256 * j;
+    const uint32_t sw = *reinterpret_cast<const uint32_t *>(sign_n + e);
+    float o[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) o[t] = v[4 * j + t] * (float)(int8_t)((sw >> (8 * t)) & 0xFFu);
+    if (y_dt == GLQ_BF16)
+      *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(y) + e) = make_uint2(bf16x2_rne(o[0], o[1]), bf16x2_rne(o[2], o[3]));
+    else
+      *reinterpret_cast<float4 *>(reinterpret_cast<float *>(y) + e) = make_float4(o[0], o[1], o[2], o[3]);
+  }
+}
+
 template <int BPW>
 __global__ void __launch_bounds__(LY_THREADS, 1)
 layer_small(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uint16_t *x,
@@ -1747,6 +1836,20 @@ layer_small(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const u
   __syncthreads();                                   // every thread has read the flag (the buffer below overlaps it)
   // 5. the last workgroup: y = U^T z
 #define GLQ_LY_OUT(E, F) ly_output<E, F>(z, sign_n, (int)n, mn, logbn, xs, y, y_dt, tid)
+  // one row whose Hadamard block is all of n = 8192 or 16384, aligned y and
+  // signs: 16-byte coherent loads of z, vector stores of y (16384: the tail
+  // 10.4 -> 4.2 us; at n = 4096 the 16-wave path below measured level)
+  const bool rb = m == 1 && n >= 8192 && (1 << logbn) == n &&
+                  ((reinterpret_cast<uintptr_t>(y) | reinterpret_cast<uintptr_t>(sign_n)) & 15) == 0;
+  if (rb) {
+    switch (n >> 10) {
+      case 1: ly_output_rb<1>(z, sign_n, (int)n, xs, y, y_dt, tid); return;
+      case 2: ly_output_rb<2>(z, sign_n, (int)n, xs, y, y_dt, tid); return;
+      case 4: ly_output_rb<4>(z, sign_n, (int)n, xs, y, y_dt, tid); return;
+      case 8: ly_output_rb<8>(z, sign_n, (int)n, xs, y, y_dt, tid); return;
+      default: ly_output_rb<16>(z, sign_n, (int)n, xs, y, y_dt, tid); return;
+    }
+  }
   switch (ly_e(mn)) {
     case 1: GLQ_LY_OUT(1, false); break;
     case 2: GLQ_LY_OUT(2, false); break;

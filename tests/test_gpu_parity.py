@@ -477,6 +477,29 @@ def test_one_row_whole_block_layers(G, cb, n, k, bpw):
     assert og.relative_error(y, ref) <= TOL_BF16
 
 
+@pytest.mark.parametrize("n", [1024, 2048, 4096, 8192, 16384])
+@pytest.mark.parametrize("y_dt", ["bf16", "f32"])
+def test_one_row_output_tail(G, cb, n, y_dt):
+    # one row whose output Hadamard block is all of n: at 8192 and 16384 the
+    # last workgroup's 16-byte loads of z and vector stores of y (8 or 16
+    # waves of 1024 elements), below that the 16-wave path (NaN-filled y:
+    # every element must be written)
+    k, bpw = 512, 2
+    i1, i2 = _random_layer(n, k, bpw, 7100 + n)
+    s = np.float32(0.02)
+    sn, sk = workloads.signs(n, 53), workloads.signs(k, 54)
+    x = workloads.bf16_round_trip(np.random.default_rng(n).standard_normal((1, k)).astype(np.float32))
+    L = G.Layer.from_numpy(i1, i2, s, sn, sk, cb)
+    ws = torch.zeros(G.workspace_bytes(L, 1), device="cuda", dtype=torch.uint8)
+    y = torch.full((1, n), float("nan"), device="cuda", dtype=torch.float32 if y_dt == "f32" else torch.bfloat16)
+    G.fused_linear(L, _t(x, torch.bfloat16), y, ws)
+    torch.cuda.synchronize()
+    got = y.float().cpu().numpy()
+    assert np.isfinite(got).all()
+    ref = og.layer_reference(x, i1, i2, bpw, s, sn, sk)
+    assert og.relative_error(got, ref) <= TOL_BF16
+
+
 # ------------------------------------------------------ per-row scales ----
 
 def _row_scale_layer(n, k, bpw, seed, scale=0.75):
