@@ -1771,10 +1771,15 @@ layer_small(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const u
   // 3. decode-GEMV over this workgroup's tiles
   const uint16_t *xrow = xb + (size_t)min((int64_t)j, m - 1) * k;
   for (; tile < tiles; tile += gridDim.x) {
-    const int64_t row = min(tile * 16 + j, n - 1);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (c = wave; c < chunks; c += GV_WAVES) {
-      if (!(tile == (int64_t)blockIdx.x && c == wave)) raw = gv_load_raw<BPW, true>(idx1, idx2, row, G, 32 * c + 8 * q);
+      // the indices of this wave's next chunk (this tile's, else the next
+      // tile's first) are in flight while this one decodes; past the last
+      // chunk the clamped addresses load indices that are never used
+      const bool wrap = c + GV_WAVES >= chunks;
+      const int64_t cn = wrap ? wave : c + GV_WAVES, tn = wrap ? tile + gridDim.x : tile;
+      const GvRaw rawn = gv_load_raw<BPW, true>(idx1, idx2, min(tn * 16 + j, n - 1), G,
+                                                32 * min(cn, chunks - 1) + 8 * q);
       const int64_t g0 = 32 * c + 8 * q;
       uint32_t i1[8], i2[8];
       gv_unpack<BPW>(raw, i1, i2);
@@ -1790,6 +1795,7 @@ layer_small(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const u
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
                                                       __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
       }
+      raw = rawn;
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) red[(wave * 16 + 4 * q + t) * 16 + j] = acc[t];
