@@ -364,7 +364,7 @@ def cpu_baseline_layer(built, budget_s):
     n_done = 0
     t0 = time.perf_counter()
     while True:
-        og.layer_reference(x[:rows], i1, i2, spec.bpw, s, sn, sk)
+        ref = og.layer_reference(x[:rows], i1, i2, spec.bpw, s, sn, sk)
         n_done += 1
         if time.perf_counter() - t0 >= budget_s:
             break
@@ -372,7 +372,8 @@ def cpu_baseline_layer(built, budget_s):
     comp = i1.size * 2 + (0 if i2 is None else i2.size * i2.itemsize) + (4 * np.size(s) if np.ndim(s) else 0)
     return {"value": round(n_done * comp / dt / 1e9, 5), "unit": "GB/s", "cores": _blas_threads(), "kind": "oracle",
             "sample": f"{n_done} layer forwards of {spec.n}x{spec.k} at {spec.bpw} bpw, {rows} activation row(s) "
-                      f"each (decode + float64 RHTs + matmul), {dt:.1f} s; compressed bytes per second"}
+                      f"each (decode + float64 RHTs + matmul), {dt:.1f} s; compressed bytes per second",
+            "accuracy": [_accuracy(og, b, ref)]}
 
 
 def cpu_baseline_block(built, rows):
@@ -381,19 +382,31 @@ def cpu_baseline_block(built, rows):
     the matrix product all inside the timed region), in TFLOP/s of 2 rows n k."""
     from oracle import glq as og
     fl, t = 0.0, 0.0
+    acc = []
     for b in built:
         spec = b["spec"]
         i1, i2, s, sn, sk = b["idx"]
         x = b["xnp"][:rows]
         t0 = time.perf_counter()
-        og.layer_reference(x, i1, i2, spec.bpw, s, sn, sk)
+        ref = og.layer_reference(x, i1, i2, spec.bpw, s, sn, sk)
         t += time.perf_counter() - t0
         fl += 2.0 * len(x) * spec.n * spec.k
+        acc.append(_accuracy(og, b, ref))
     names = ", ".join(f"{b['spec'].n}x{b['spec'].k}" for b in built)
     return {"value": round(fl / t / 1e12, 6), "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
             "sample": f"{rows} of {built[0]['spec'].m} activation rows through each linear ({names}) at "
                       f"{built[0]['spec'].bpw} bpw: decode + float64 RHTs + matmul, {t:.1f} s",
-            "cpu_model": _cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0))}
+            "cpu_model": _cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0)), "accuracy": acc}
+
+
+def _accuracy(og, b, ref):
+    """The timed runs' own output (y of the last replay; every copy of a
+    linear holds the same indices) against the oracle on the sampled rows:
+    max|y - y_ref| / max|y_ref| and its row-normalised maximum."""
+    y = b["y"][:len(ref)].float().cpu().numpy()
+    return {"layer": f"{b['spec'].n}x{b['spec'].k}", "rows": len(ref),
+            "rel_max": float(f"{og.relative_error(y, ref):.3e}"),
+            "row_rel_max": float(f"{og.row_relative_error(y, ref):.3e}"), "tolerance": 1e-2}
 
 
 def _blas_threads():

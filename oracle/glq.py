@@ -309,6 +309,18 @@ def deserialise_layer(blob: bytes, n: int, k: int, bpw: int):
     return idx1, idx2, scale, signs[0], signs[1]
 
 
+def row_relative_error(y: np.ndarray, y_ref: np.ndarray) -> float:
+    """The row-normalised maximum: max over output rows r of
+    max|y_r - y_ref_r| / max|y_ref_r| (a row of zeros in y_ref contributes its
+    absolute error). Reported beside relative_error, which a few large rows
+    can dominate."""
+    y = np.atleast_2d(np.asarray(y, dtype=np.float64))
+    y_ref = np.atleast_2d(np.asarray(y_ref, dtype=np.float64))
+    num = np.max(np.abs(y - y_ref), axis=-1)
+    den = np.max(np.abs(y_ref), axis=-1)
+    return float(np.max(np.where(den > 0, num / np.where(den > 0, den, 1.0), num)))
+
+
 def relative_error(y: np.ndarray, y_ref: np.ndarray) -> float:
     """max|y - y_ref| / max|y_ref| over the whole output (the tolerance
     measure for layer outputs)."""

@@ -258,6 +258,19 @@ def test_relative_error_measure():
     assert glq.relative_error(np.array([1.5, 2.0]), np.array([1.0, 2.0])) == 0.25
 
 
+def test_row_relative_error_measure():
+    # hand-computed: row 0 error 0.5 of max 2 (0.25), row 1 error 0.1 of max
+    # 0.2 (0.5); the global measure sees 0.5 / 2 = 0.25
+    ref = np.array([[1.0, 2.0], [0.1, 0.2]])
+    got = np.array([[1.5, 2.0], [0.1, 0.1]])
+    assert glq.row_relative_error(got, ref) == pytest.approx(0.5)
+    assert glq.relative_error(got, ref) == pytest.approx(0.25)
+    # one row: the two measures agree; an all-zero reference row counts its
+    # absolute error
+    assert glq.row_relative_error(got[:1], ref[:1]) == glq.relative_error(got[:1], ref[:1])
+    assert glq.row_relative_error(np.array([[0.0, 0.3]]), np.zeros((1, 2))) == pytest.approx(0.3)
+
+
 # -------------------------------------------------------- per-row scales ----
 
 def test_row_scales_equal_norm_rows_reduce_to_global_scale():
