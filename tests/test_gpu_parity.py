@@ -660,6 +660,40 @@ def test_ep_decode_graph_replays(G):
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
 
 
+@pytest.mark.parametrize("m", [1, 16])
+def test_ep_fused_linear_graph_replays(G, m):
+    # a captured entropy-coded layer (m = 1: the fill kernel that clears z and
+    # the fused decode-product with its atomic row sums; m = 16: decode then
+    # GEMV), replayed with eager calls in between: every replay within the
+    # tolerance of the oracle and close to the eager result (float32 atomics
+    # may sum in another order)
+    n, k = 768, 1024
+    L, w32, sn, sk = _ep_layer_case(G, n, k, 0.27, 31 + m)
+    x = workloads.bf16_round_trip(np.random.default_rng(m).standard_normal((m, k)).astype(np.float32))
+    xt = _t(x, torch.bfloat16)
+    ref = rht.rht_transpose(rht.rht_forward(x.astype(np.float64), sk) @ w32.T, sn)
+    ws = torch.zeros(G.ep_workspace_bytes(L, m), device="cuda", dtype=torch.uint8)
+    y = torch.empty((m, n), device="cuda", dtype=torch.float32)
+    eager = torch.empty_like(y)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        G.ep_fused_linear(L, xt, y, ws, stream=s)
+        s.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            G.ep_fused_linear(L, xt, y, ws, stream=s)
+    for _ in range(3):
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        G.ep_fused_linear(L, xt, eager, ws)
+        torch.cuda.synchronize()
+        got = y.cpu().numpy()
+        assert og.relative_error(got, ref) <= TOL_BF16
+        assert og.relative_error(got, eager.cpu().numpy()) <= 1e-5
+
+
 @pytest.mark.parametrize("m,bpw", [(1, 2), (3, 4), (16, 4), (40, 3)])
 def test_fused_graph_replays(G, cb, m, bpw):
     # a captured layer forward (single launch with its completion tickets at
