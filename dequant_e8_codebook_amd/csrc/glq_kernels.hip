@@ -2241,21 +2241,27 @@ gemm_w_bf16(const uint16_t *w, const uint16_t *xt, int64_t m, int64_t n, int64_t
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][t][e] = 0.f;
 
+  // One k-step: four MFMA blocks (sub-steps u of 16 inputs); the A and B
+  // operands of block u + 1 are read from LDS while block u runs, into the
+  // other of two register sets (no copies), and the reads are spread between
+  // the MFMAs; the next tiles go to LDS and the ones after them are loaded
+  // during the last block.
   for (int64_t st = 0; st < S; ++st) {
     const uint16_t *Acur = (st & 1) ? As1 : As0;
     const uint16_t *Bcur = ((st & 1) ? Bs1 : Bs0) + (64 * wave) * GM_LDA;
-    uint4 av[8], an[8], bv[2];
+    uint4 A0[8], A1[8], B0[2], B1[2];
 #pragma unroll
-    for (int a = 0; a < 8; ++a) av[a] = *reinterpret_cast<const uint4 *>(Acur + (32 * a + c) * GM_LDA + 32 * p);
+    for (int a = 0; a < 8; ++a) A0[a] = *reinterpret_cast<const uint4 *>(Acur + (32 * a + c) * GM_LDA + 32 * p);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-        bv[t] = *reinterpret_cast<const uint4 *>(Bcur + (32 * t + c) * GM_LDA + 32 * p + 8 * u);
+    for (int t = 0; t < 2; ++t) B0[t] = *reinterpret_cast<const uint4 *>(Bcur + (32 * t + c) * GM_LDA + 32 * p);
+    auto block = [&](int u, const uint4 (&av)[8], const uint4 (&bv)[2], uint4 (&an)[8], uint4 (&bn)[2]) {
       if (u < 3) {
 #pragma unroll
         for (int a = 0; a < 8; ++a)
           an[a] = *reinterpret_cast<const uint4 *>(Acur + (32 * a + c) * GM_LDA + 32 * p + 8 * (u + 1));
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          bn[t] = *reinterpret_cast<const uint4 *>(Bcur + (32 * t + c) * GM_LDA + 32 * p + 8 * (u + 1));
       }
 #pragma unroll
       for (int a = 0; a < 8; ++a) {
@@ -2264,16 +2270,23 @@ gemm_w_bf16(const uint16_t *w, const uint16_t *xt, int64_t m, int64_t n, int64_t
         acc[a][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[a]),
                                                             __builtin_bit_cast(bf16x8, bv[1]), acc[a][1], 0, 0, 0);
       }
-      if (u < 3) {
-#pragma unroll
-        for (int a = 0; a < 8; ++a) av[a] = an[a];
-      }
-    }
+    };
+    block(0, A0, B0, A1, B1);
+    gm_interleave16<0, 1>();
+    __builtin_amdgcn_sched_barrier(0);
+    block(1, A1, B1, A0, B0);
+    gm_interleave16<0, 1>();
+    __builtin_amdgcn_sched_barrier(0);
+    block(2, A0, B0, A1, B1);
+    gm_interleave16<0, 1>();
+    __builtin_amdgcn_sched_barrier(0);
+    block(3, A1, B1, A0, B0);
     const int64_t kv = k - GM_BK * (st + 1);
     gm_store_a((st & 1) ? As0 : As1, ra, kv);          // tiles st + 1 (unused past the end)
     gm_store_a((st & 1) ? Bs0 : Bs1, rb, kv);
     gm_load_a(xt, m, k, m0, min(st + 2, S - 1), ra);
     gm_load_a(w, n, k, nb0, min(st + 2, S - 1), rb);
+    gm_interleave16<1, 0, 1, 1>();
     __syncthreads();
   }
   gm_epilogue<2, OUT_BF16>(acc, nullptr, post, nullptr, out, m, n, m0, n0, lane, wave, vec != 0);
