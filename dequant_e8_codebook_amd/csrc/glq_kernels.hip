@@ -2200,6 +2200,100 @@ gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
 
 // Dense GEMM z = post * x~ W^T with the weights already in memory as bf16
 // [n][k] row-major (the entropy-coded layers' decoded weights): the tiling,
+// x~ staging, operand pipeline and epilogue of gemm_bf16, with the B
+// operands loaded from memory instead of decoded: lane (c, p) of wave w takes
+// inputs 32 p + 8 u .. + 7 of weight row nb0 + 64 w + 32 t + c in MFMA block
+// u (the order in which it reads its A operands: the k order inside a step
+// is a permutation shared by A and B), eight 16-byte loads a step, issued a
+// step ahead into the other of two register sets. k is a multiple of 64
+// (every step whole); other shapes take gemm_w_bf16_lds.
+template <bool OUT_BF16>
+__global__ void __launch_bounds__(256, 1)
+gemm_w_bf16(const uint16_t *w, const uint16_t *xt, int64_t m, int64_t n, int64_t k, float post, void *out,
+            int vec, int64_t mblocks, int64_t tiles) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  uint16_t *As0 = reinterpret_cast<uint16_t *>(lds);
+  uint16_t *As1 = As0 + GM_BM * GM_LDA;
+  int64_t tile = blockIdx.x;
+  if (tiles % 8 == 0) tile = (blockIdx.x % 8) * (tiles / 8) + blockIdx.x / 8;
+  const int64_t m0 = (tile % mblocks) * GM_BM;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 31, p = lane >> 5;
+  const int64_t n0 = (tile / mblocks) * GM_BN + 64 * wave;
+  const int64_t S = k / GM_BK;
+  // weight rows of this lane (clamped: rows past n feed outputs never stored)
+  const uint16_t *wr0 = w + (size_t)min(n0 + c, n - 1) * k + 32 * p;
+  const uint16_t *wr1 = w + (size_t)min(n0 + 32 + c, n - 1) * k + 32 * p;
+  auto load_b = [&](int64_t st, uint4 (&b)[8]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      b[u] = *reinterpret_cast<const uint4 *>(wr0 + GM_BK * st + 8 * u);
+      b[4 + u] = *reinterpret_cast<const uint4 *>(wr1 + GM_BK * st + 8 * u);
+    }
+  };
+
+  uint4 ra[8];
+  uint4 B0[8], B1[8];
+  gm_load_a(xt, m, k, m0, 0, ra);
+  load_b(0, B0);
+  gm_store_a(As0, ra, k);
+  gm_load_a(xt, m, k, m0, min((int64_t)1, S - 1), ra);
+  __syncthreads();
+
+  f32x16 acc[8][2];
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][t][e] = 0.f;
+
+  auto kstep = [&](int64_t st, const uint4 (&bc)[8], uint4 (&bn)[8]) {
+    const uint16_t *Acur = (st & 1) ? As1 : As0;
+    load_b(min(st + 1, S - 1), bn);                  // next step's weights
+    uint4 A0[8], A1[8];
+#pragma unroll
+    for (int a = 0; a < 8; ++a) A0[a] = *reinterpret_cast<const uint4 *>(Acur + (32 * a + c) * GM_LDA + 32 * p);
+    auto block = [&](int u, const uint4 (&av)[8], uint4 (&an)[8]) {
+      if (u < 3) {
+#pragma unroll
+        for (int a = 0; a < 8; ++a)
+          an[a] = *reinterpret_cast<const uint4 *>(Acur + (32 * a + c) * GM_LDA + 32 * p + 8 * (u + 1));
+      }
+#pragma unroll
+      for (int a = 0; a < 8; ++a) {
+        acc[a][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[a]),
+                                                            __builtin_bit_cast(bf16x8, bc[u]), acc[a][0], 0, 0, 0);
+        acc[a][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[a]),
+                                                            __builtin_bit_cast(bf16x8, bc[4 + u]), acc[a][1], 0, 0, 0);
+      }
+    };
+    block(0, A0, A1);
+    gm_interleave16<0, 1>();
+    __builtin_amdgcn_sched_barrier(0);
+    block(1, A1, A0);
+    gm_interleave16<0, 1>();
+    __builtin_amdgcn_sched_barrier(0);
+    block(2, A0, A1);
+    gm_interleave16<0, 1>();
+    __builtin_amdgcn_sched_barrier(0);
+    block(3, A1, A0);
+    gm_store_a((st & 1) ? As0 : As1, ra, GM_BK);      // tile st + 1 (unused past the end)
+    gm_load_a(xt, m, k, m0, min(st + 2, S - 1), ra);
+    gm_interleave16<1, 0, 1, 1>();
+    __syncthreads();
+  };
+  int64_t st = 0;
+  for (; st + 1 < S; st += 2) {
+    kstep(st, B0, B1);
+    kstep(st + 1, B1, B0);
+  }
+  if (st < S) kstep(st, B0, B1);
+  gm_epilogue<2, OUT_BF16>(acc, nullptr, post, nullptr, out, m, n, m0, n0, lane, wave, vec != 0);
+}
+
+// Dense GEMM z = post * x~ W^T with the weights already in memory as bf16
+// [n][k] row-major (the entropy-coded layers' decoded weights): the tiling,
 // x~ staging and epilogue of gemm_bf16. The 256 x 64 weight tile of a step
 // has the shape of the x~ tile, so it is staged the same way (loaded into
 // registers one step ahead, stored to a second double-buffered LDS tile);
@@ -2208,7 +2302,7 @@ gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
 // is a permutation shared by A and B). Past k both tiles are zero.
 template <bool OUT_BF16>
 __global__ void __launch_bounds__(256, 1)
-gemm_w_bf16(const uint16_t *w, const uint16_t *xt, int64_t m, int64_t n, int64_t k, float post, void *out,
+gemm_w_bf16_lds(const uint16_t *w, const uint16_t *xt, int64_t m, int64_t n, int64_t k, float post, void *out,
             int vec, int64_t mblocks, int64_t tiles) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   uint16_t *As0 = reinterpret_cast<uint16_t *>(lds);
@@ -3290,10 +3384,14 @@ int launch_gemm_w(const uint16_t *w, const uint16_t *xt, int64_t m, int64_t n, i
   const int64_t mb = (m + GM_BM - 1) / GM_BM, nb = (n + GM_BN - 1) / GM_BN;
   const int64_t tiles = mb * nb;
   if (tiles > 0x7FFFFFFF) return GLQ_ERR_UNSUPPORTED;
-  const size_t shm = 4 * GM_A_BYTES;                 // x~ and W tiles, double-buffered
+  // k a multiple of 64: weight operands straight from memory into registers
+  // (x~ tiles double-buffered in LDS); otherwise both tiles through LDS
+  const bool direct = k % GM_BK == 0;
+  const size_t shm = (direct ? 2 : 4) * GM_A_BYTES;
   const bool ob = out_dt == GLQ_BF16;
   const int vec = ((n * (ob ? 2 : 4)) % 16 == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0) ? 1 : 0;
-  auto kern = ob ? gemm_w_bf16<true> : gemm_w_bf16<false>;
+  auto kern = direct ? (ob ? gemm_w_bf16<true> : gemm_w_bf16<false>)
+                     : (ob ? gemm_w_bf16_lds<true> : gemm_w_bf16_lds<false>);
   int rc = allow_lds(kern, shm);
   if (rc) return rc;
   hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(256), shm, st, w, xt, m, n, k, 1.0f, out, vec, mb, tiles);
