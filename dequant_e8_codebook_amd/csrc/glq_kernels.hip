@@ -161,8 +161,9 @@ __device__ __forceinline__ uint32_t pk_add16(uint32_t a, uint32_t b) {
 // Stage-1 and stage-2 halves into operand form: 16-bit lanes M * a + b
 // (mod 2^16), M = 2 at 3 bpw and 4 at 4 bpw (one packed multiply-add).
 // MAD: the multiplier is hidden from the optimiser (an empty asm), which then
-// emits one v_pk_mad_u16 instead of a shift and an add (the decode-GEMM
-// keeps the shift and add: there the one-instruction form cost registers)
+// emits one v_pk_mad_u16 instead of a shift and an add (the decode-GEMM with
+// partial x~ tiles keeps the shift and add: there the one-instruction form
+// cost registers)
 template <uint16_t M, bool MAD = true>
 __device__ __forceinline__ uint32_t pk_comb(uint32_t a, uint32_t b) {
   uint32_t mm = (uint32_t)M * 0x10001u;
@@ -1885,9 +1886,11 @@ constexpr size_t GM_A_BYTES = (size_t)GM_BM * GM_LDA * 2;   // one buffer
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // Index planes for k-step s: rows nrow0 + 32 t + c (t = 0, 1), groups
-// 8 s + 4 p .. +3, returned as i' = i - 1 mod 2^16 (stage 1, stage 2 at 4 bpw). Addresses are clamped into the planes instead of
-// branching: out-of-range rows are never stored, out-of-range groups meet
-// zero activations, and any index decodes to finite values. G4: k/8 is a
+// 8 s + 4 p .. +3, returned as stored (gm_dec_idx turns them into
+// i' = i - 1 mod 2^16 where they are used, so nothing waits for the loads
+// early). Addresses are clamped into the planes instead of branching:
+// out-of-range rows are never stored, out-of-range groups meet zero
+// activations, and any index decodes to finite values. G4: k/8 is a
 // multiple of 4, so the 4 indices are one aligned 8-byte load.
 template <int BPW, bool G4>
 __device__ __forceinline__ void gm_load_idx(const uint16_t *idx1, const void *idx2, int64_t n,
@@ -1898,13 +1901,9 @@ __device__ __forceinline__ void gm_load_idx(const uint16_t *idx1, const void *id
     const int64_t row = min(nrow0 + 32 * t + c, n - 1);
     if constexpr (G4) {
       const int64_t off = row * G + min(8 * s + 4 * p, G - 4);
-      const uint2 a = *reinterpret_cast<const uint2 *>(idx1 + off);
-      i1[t] = make_uint2(pk_dec16(a.x), pk_dec16(a.y));
+      i1[t] = *reinterpret_cast<const uint2 *>(idx1 + off);
       if constexpr (BPW == 3) i2[t] = make_uint2(*reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint8_t *>(idx2) + off), 0u);
-      if constexpr (BPW == 4) {
-        const uint2 b = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(idx2) + off);
-        i2[t] = make_uint2(pk_dec16(b.x), pk_dec16(b.y));
-      }
+      if constexpr (BPW == 4) i2[t] = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(idx2) + off);
       if constexpr (BPW == 2) i2[t] = make_uint2(0u, 0u);
     } else {
       uint32_t w1[4], w2[4];
@@ -1914,10 +1913,20 @@ __device__ __forceinline__ void gm_load_idx(const uint16_t *idx1, const void *id
         w1[u] = idx1[o];
         w2[u] = BPW > 2 ? load_idx2(idx2, o, BPW) : 0u;
       }
-      i1[t] = make_uint2(pk_dec16(w1[0] | (w1[1] << 16)), pk_dec16(w1[2] | (w1[3] << 16)));
+      i1[t] = make_uint2(w1[0] | (w1[1] << 16), w1[2] | (w1[3] << 16));
       if constexpr (BPW == 3) i2[t] = make_uint2(w2[0] | (w2[1] << 8) | (w2[2] << 16) | (w2[3] << 24), 0u);
-      else i2[t] = make_uint2(pk_dec16(w2[0] | (w2[1] << 16)), pk_dec16(w2[2] | (w2[3] << 16)));
+      else i2[t] = make_uint2(w2[0] | (w2[1] << 16), w2[2] | (w2[3] << 16));
     }
+  }
+}
+
+// stored indices -> i' = i - 1 mod 2^16 (stage 1; stage 2 at 4 bpw)
+template <int BPW>
+__device__ __forceinline__ void gm_dec_idx(uint2 (&i1)[2], uint2 (&i2)[2]) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    i1[t] = make_uint2(pk_dec16(i1[t].x), pk_dec16(i1[t].y));
+    if constexpr (BPW == 4) i2[t] = make_uint2(pk_dec16(i2[t].x), pk_dec16(i2[t].y));
   }
 }
 
@@ -2073,7 +2082,65 @@ __device__ __forceinline__ void gm_interleave16() {
   }
 }
 
-template <int BPW, bool G4, bool OUT_BF16>
+// Buffer-load forms of the k-loop's global reads, used when k is a multiple
+// of 64 (every x~ tile whole). Each lane's byte offsets inside the block's
+// rows are fixed for the whole loop; the step enters as the scalar offset,
+// so a load is one instruction with no address arithmetic. Reads past the
+// descriptor's size return zeros: rows past m (accumulator rows that are
+// never stored) and weight rows past n (outputs never stored).
+struct GmBuf {
+  __amdgpu_buffer_rsrc_t xa, i1, i2;
+  uint32_t va;           // x~ piece 0 of this lane; piece u is 32 u rows further
+  uint32_t vi, vi8;      // index row t = 0 of this lane (2-byte, 1-byte planes)
+  int sa, si;            // bytes of 32 x~ rows, of 32 index rows (2-byte plane)
+};
+
+template <int BPW>
+__device__ __forceinline__ void gm_buf_init(GmBuf &b, const uint16_t *idx1, const void *idx2, const uint16_t *xt,
+                                            int64_t m, int64_t n, int64_t k, int64_t m0, int64_t nrow0, int c,
+                                            int p) {
+  const int64_t G = k / 8;
+  const int64_t rows_a = min(m - m0, (int64_t)GM_BM);
+  b.xa = __builtin_amdgcn_make_buffer_rsrc((void *)(xt + m0 * k), 0, (int)(rows_a * k * 2), 0x00020000);
+  const int64_t rows_w = max(min(n - nrow0, (int64_t)64), (int64_t)0);
+  b.i1 = __builtin_amdgcn_make_buffer_rsrc((void *)(idx1 + nrow0 * G), 0, (int)(rows_w * G * 2), 0x00020000);
+  if constexpr (BPW == 3)
+    b.i2 = __builtin_amdgcn_make_buffer_rsrc((void *)(reinterpret_cast<const uint8_t *>(idx2) + nrow0 * G), 0,
+                                             (int)(rows_w * G), 0x00020000);
+  else if constexpr (BPW == 4)
+    b.i2 = __builtin_amdgcn_make_buffer_rsrc((void *)(reinterpret_cast<const uint16_t *>(idx2) + nrow0 * G), 0,
+                                             (int)(rows_w * G * 2), 0x00020000);
+  else
+    b.i2 = b.i1;
+  b.va = (uint32_t)((threadIdx.x >> 3) * k * 2 + 16 * (threadIdx.x & 7));
+  b.vi = (uint32_t)(c * G * 2 + 8 * p);
+  b.vi8 = (uint32_t)(c * G + 4 * p);
+  b.sa = (int)(32 * k * 2);
+  b.si = (int)(32 * G * 2);
+}
+
+__device__ __forceinline__ void gm_buf_load_a(const GmBuf &b, int64_t s, uint4 (&ra)[8]) {
+  const int so = (int)(2 * GM_BK * s);
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    ra[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(b.xa, b.va, so + u * b.sa, 0));
+}
+
+template <int BPW>
+__device__ __forceinline__ void gm_buf_load_idx(const GmBuf &b, int64_t s, uint2 (&i1)[2], uint2 (&i2)[2]) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int so = (int)(16 * s) + t * b.si;
+    i1[t] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(b.i1, b.vi, so, 0));
+    if constexpr (BPW == 3)
+      i2[t] = make_uint2(__builtin_amdgcn_raw_buffer_load_b32(b.i2, b.vi8, (int)(8 * s) + t * (b.si >> 1), 0), 0u);
+    if constexpr (BPW == 4)
+      i2[t] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(b.i2, b.vi, so, 0));
+    if constexpr (BPW == 2) i2[t] = make_uint2(0u, 0u);
+  }
+}
+
+template <int BPW, bool G4, bool K64, bool OUT_BF16>
 __global__ void __launch_bounds__(256, 1)
 gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uint16_t *xt,
           const float *rowsum, int64_t m, int64_t n, int64_t k, float post, const float *row_scale,
@@ -2087,23 +2154,35 @@ gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
   int64_t tile = blockIdx.x;
   if (tiles % 8 == 0) tile = (blockIdx.x % 8) * (tiles / 8) + blockIdx.x / 8;
   const int64_t m0 = (tile % mblocks) * GM_BM;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // wave index as a scalar: the buffer descriptors built from it must be uniform
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 31, p = lane >> 5;
   const int64_t n0 = (tile / mblocks) * GM_BN + 64 * wave;
   const int64_t G = k / 8;
   const int64_t S = (k + GM_BK - 1) / GM_BK;
 
+  GmBuf gb;
+  if constexpr (K64) gm_buf_init<BPW>(gb, idx1, idx2, xt, m, n, k, m0, n0, c, p);
+  auto load_a = [&](int64_t s, uint4 (&ra)[8]) {
+    if constexpr (K64) gm_buf_load_a(gb, s, ra);
+    else gm_load_a(xt, m, k, m0, s, ra);
+  };
+  auto load_idx = [&](int64_t s, uint2 (&a)[2], uint2 (&b)[2]) {
+    if constexpr (K64) gm_buf_load_idx<BPW>(gb, s, a, b);
+    else gm_load_idx<BPW, G4>(idx1, idx2, n, G, n0, c, p, s, a, b);
+  };
+
   load_tables<BPW>(lds, blob);
   uint4 ra[8];
-  gm_load_a(xt, m, k, m0, 0, ra);
+  load_a(0, ra);
   uint2 i1[2], i2[2], j1[2], j2[2];
-  gm_load_idx<BPW, G4>(idx1, idx2, n, G, n0, c, p, 0, i1, i2);
+  load_idx(0, i1, i2);
   tables_landed();                                   // tables, x~ tile 0, step-0 indices
   gm_store_a(As0, ra, k);
   // indices of step 1, then x~ tile 1: the same issue order as in the loop,
   // so that the loop-entry wait for the indices does not cover the tile
-  gm_load_idx<BPW, G4>(idx1, idx2, n, G, n0, c, p, min((int64_t)1, S - 1), j1, j2);
-  gm_load_a(xt, m, k, m0, min((int64_t)1, S - 1), ra);
+  load_idx(min((int64_t)1, S - 1), j1, j2);
+  load_a(min((int64_t)1, S - 1), ra);
   __syncthreads();                                   // tables and x~ tile 0 in LDS
 
   f32x16 acc[8][2];
@@ -2123,36 +2202,46 @@ gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
   // the step's own and the next step's (decoded while this one runs), which
   // trade places from one step to the next (the loop is unrolled by two).
   uint4 B0[8], B1[8];
+  gm_dec_idx<BPW>(i1, i2);
 #pragma unroll
   for (int g = 0; g < 8; ++g) B0[g] = gm_decode_one<BPW>(i1, i2, g >> 2, g & 3, lds);
 #pragma unroll
   for (int t = 0; t < 2; ++t) { i1[t] = j1[t]; i2[t] = j2[t]; }
 
+  // A operands of MFMA block u sit in set u & 1 and those of block u + 1 are
+  // read while block u runs; block 3 reads block 0 of the next tile, so the
+  // step's barrier sits between blocks 2 and 3: by then every wave has read
+  // its last operands of tile s and written tile s + 1 (into the buffer tile
+  // s - 1 used), and after it block 3's MFMAs cover the first reads of tile
+  // s + 1. Nothing waits for an operand read at the start of a step.
+  uint4 A0[8], A1[8];
+#pragma unroll
+  for (int a = 0; a < 8; ++a) A0[a] = *reinterpret_cast<const uint4 *>(As0 + (32 * a + c) * GM_LDA + 32 * p);
+
   auto kstep = [&](int64_t s, const uint4 (&bc)[8], uint4 (&bn)[8]) {
     const uint16_t *Acur = (s & 1) ? As1 : As0;
+    uint16_t *Anext = (s & 1) ? As0 : As1;
     // indices of step s + 1 (group g = 4 t + u), as i' = i - 1 mod 2^16
     uint32_t q1[8], q2[8];
+    {
+      uint2 d1[2] = {i1[0], i1[1]}, d2[2] = {i2[0], i2[1]};
+      gm_dec_idx<BPW>(d1, d2);
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      const int t = g >> 2, u = g & 3;
-      q1[g] = ((u < 2 ? i1[t].x : i1[t].y) >> (16 * (u & 1))) & 0xFFFFu;
-      if constexpr (BPW == 3) q2[g] = (i2[t].x >> (8 * u)) & 0xFFu;
-      else if constexpr (BPW == 4) q2[g] = ((u < 2 ? i2[t].x : i2[t].y) >> (16 * (u & 1))) & 0xFFFFu;
-      else q2[g] = 0u;
-    }
-    gm_load_idx<BPW, G4>(idx1, idx2, n, G, n0, c, p, min(s + 2, S - 1), i1, i2);
-
-    // A operands of MFMA block u in set u & 1; those of block u + 1 are read
-    // while block u runs
-    uint4 A0[8], A1[8];
-#pragma unroll
-    for (int a = 0; a < 8; ++a) A0[a] = *reinterpret_cast<const uint4 *>(Acur + (32 * a + c) * GM_LDA + 32 * p);
-    auto mfma_block = [&](int u, const uint4 (&av)[8], uint4 (&an)[8]) {
-      if (u < 3) {
-#pragma unroll
-        for (int a = 0; a < 8; ++a)
-          an[a] = *reinterpret_cast<const uint4 *>(Acur + (32 * a + c) * GM_LDA + 32 * p + 8 * (u + 1));
+      for (int g = 0; g < 8; ++g) {
+        const int t = g >> 2, u = g & 3;
+        q1[g] = ((u < 2 ? d1[t].x : d1[t].y) >> (16 * (u & 1))) & 0xFFFFu;
+        if constexpr (BPW == 3) q2[g] = (d2[t].x >> (8 * u)) & 0xFFu;
+        else if constexpr (BPW == 4) q2[g] = ((u < 2 ? d2[t].x : d2[t].y) >> (16 * (u & 1))) & 0xFFFFu;
+        else q2[g] = 0u;
       }
+    }
+    load_idx(min(s + 2, S - 1), i1, i2);
+
+    auto mfma_block = [&](int u, const uint4 (&av)[8], uint4 (&an)[8]) {
+#pragma unroll
+      for (int a = 0; a < 8; ++a)
+        an[a] = u < 3 ? *reinterpret_cast<const uint4 *>(Acur + (32 * a + c) * GM_LDA + 32 * p + 8 * (u + 1))
+                      : *reinterpret_cast<const uint4 *>(Anext + (32 * a + c) * GM_LDA + 32 * p);
 #pragma unroll
       for (int a = 0; a < 8; ++a) {
         acc[a][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[a]),
@@ -2166,12 +2255,14 @@ gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
     // records of all 8 groups in block 0; the half-vector offsets (about
     // seven VALU operations per table walk) and reads of groups 0-3 in block
     // 1 and of groups 4-7 in block 2; the combine of groups 0-3 in block 2
-    // and of groups 4-7 in block 3.
+    // and of groups 4-7 in block 3. x~ tile s + 1 goes to LDS and tile s + 2
+    // is requested during block 2.
     constexpr int NW = BPW == 4 ? 2 : 1;            // table walks per group
-    Dec8<BPW, false> D;
+    constexpr int LA = K64 ? 0 : 1;                 // address arithmetic of a pointer-based load
+    Dec8<BPW, K64> D;
     D.p1(q1, q2);
     mfma_block(0, A0, A1);
-    gm_interleave16<2, (8 * NW + (BPW == 3 ? 8 : 0) + 8 + 15) / 16>();
+    gm_interleave16<2 + LA, (8 * NW + (BPW == 3 ? 8 : 0) + 8 + 15) / 16>();
     __builtin_amdgcn_sched_barrier(0);
     D.template p2<0, 4>(q1, q2);
     mfma_block(1, A1, A0);
@@ -2179,15 +2270,17 @@ gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
     __builtin_amdgcn_sched_barrier(0);
     D.template p2<4, 8>(q1, q2);
     D.template p3<0, 4>(bn);
+    if constexpr (K64) gm_store_a(Anext, ra, GM_BK);
+    else gm_store_a(Anext, ra, k - GM_BK * (s + 1));   // tile s + 1 (unused past the end)
+    load_a(min(s + 2, S - 1), ra);
     mfma_block(2, A0, A1);
-    gm_interleave16<(28 * NW + (BPW == 2 ? 0 : 16) + 15) / 16, (8 * NW + 8 + 15) / 16>();
+    gm_interleave16<(28 * NW + (BPW == 2 ? 0 : 16) + 15) / 16 + LA, (8 * NW + 8 + 15) / 16, 1, 1>();
     __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
     D.template p3<4, 8>(bn);
     mfma_block(3, A1, A0);
-    gm_store_a((s & 1) ? As0 : As1, ra, k - GM_BK * (s + 1));   // tile s + 1 (unused past the end)
-    gm_load_a(xt, m, k, m0, min(s + 2, S - 1), ra);
-    gm_interleave16<3, 1, 1, 1>();
-    __syncthreads();
+    gm_interleave16<1, 1>();
+    __builtin_amdgcn_sched_barrier(0);
   };
   int64_t s = 0;
   for (; s + 1 < S; s += 2) {
@@ -2195,6 +2288,7 @@ gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
     kstep(s + 1, B1, B0);
   }
   if (s < S) kstep(s, B0, B1);
+  __syncthreads();                                   // the epilogue reuses the x~ buffers
   gm_epilogue<BPW, OUT_BF16>(acc, rowsum, post, row_scale, out, m, n, m0, n0, lane, wave, vec != 0);
 }
 
@@ -3112,10 +3206,13 @@ int launch_matmul(const glq_layer *L, const void *xt, glq_dtype x_dt, const floa
     if (tiles > 0x7FFFFFFF) return GLQ_ERR_UNSUPPORTED;
     const size_t shm = tab + 2 * GM_A_BYTES;
     const bool even_g = ((L->k / 8) % 4) == 0;
+    // whole x~ tiles and 32-bit buffer offsets (256 rows of x~, 64 index rows)
+    const bool k64 = L->k % GM_BK == 0 && (int64_t)GM_BM * L->k * 2 < 0x7FFFFFFF;
     const bool ob = out_dt == GLQ_BF16;
     const int vec = ((L->n * (ob ? 2 : 4)) % 16 == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0) ? 1 : 0;
-    auto kern = even_g ? (ob ? gemm_bf16<BPW, true, true> : gemm_bf16<BPW, true, false>)
-                       : (ob ? gemm_bf16<BPW, false, true> : gemm_bf16<BPW, false, false>);
+    auto kern = k64 ? (ob ? gemm_bf16<BPW, true, true, true> : gemm_bf16<BPW, true, true, false>)
+              : even_g ? (ob ? gemm_bf16<BPW, true, false, true> : gemm_bf16<BPW, true, false, false>)
+                       : (ob ? gemm_bf16<BPW, false, false, true> : gemm_bf16<BPW, false, false, false>);
     int rc = allow_lds(kern, shm);
     if (rc) return rc;
     hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(256), shm, st, L->idx1, L->idx2, blob, xb, rowsum, m,
