@@ -136,7 +136,10 @@ def dominant_kernel(spec):
         return f"gemv_f32<{spec.bpw}>"
     if single_launch(spec):
         return f"layer_small<{spec.bpw}>"
-    return f"gemv_bf16<{spec.bpw}>" if spec.m <= 16 else f"gemm_bf16<{spec.bpw}>"
+    if spec.m <= 16:
+        return f"gemv_bf16<{spec.bpw}>"
+    # k a multiple of 64: the 8-wave GEMM; other k: the 4-wave one
+    return f"gemm8_bf16<{spec.bpw}>" if spec.k % 64 == 0 else f"gemm_bf16<{spec.bpw}>"
 
 
 def _event():

@@ -24,8 +24,11 @@
 //                   k, bf16 MFMA 16x16x32 with x~ rows as the M side (the few
 //                   activation rows are padded to 16) and weights decoded
 //                   straight into the B operand registers.
-//   gemm_bf16       m > 16: 256 x 256 output tiles, x~ double-buffered in LDS,
-//                   weights decoded per wave straight into MFMA B operands.
+//   gemm8_bf16      m > 16, k a multiple of 64: 256 x 256 output tiles, 8
+//                   waves (two per SIMD, 32 weight rows each), x~
+//                   double-buffered in LDS, weights decoded per wave straight
+//                   into MFMA B operands.
+//   gemm_bf16       m > 16, other k: the same tile with 4 waves of 64 rows.
 //   gemv_f32        float32 path: exact float32 weights, float32 FMAs.
 //   layer_small     m <= 4: the whole layer (both transforms and the
 //                   decode-GEMV) in one launch.
@@ -1980,28 +1983,26 @@ __device__ __forceinline__ uint4 gm_decode_one(const uint2 (&i1)[2], const uint2
 // GEMM epilogue: z = post * acc + cz(row) with cz = -post * bias * rowsum(x~),
 // staged through LDS (free once the k-loop has ended) so that every lane
 // stores 16 contiguous bytes of an output row. Each wave stages its own
-// 256 x 64 tile in chunks of CH 32-row blocks. vec: 16-byte stores are
+// 256 x 32 NT tile in chunks of CH 32-row blocks. vec: 16-byte stores are
 // aligned (n * element size % 16 == 0 and an aligned output pointer).
-template <int BPW, bool OUT_BF16>
-__device__ __forceinline__ void gm_epilogue(const f32x16 (&acc)[8][2], const float *rowsum, float post,
+template <int BPW, bool OUT_BF16, int NT = 2>
+__device__ __forceinline__ void gm_epilogue(const f32x16 (&acc)[8][NT], const float *rowsum, float post,
                                             const float *row_scale, void *out, int64_t m, int64_t n, int64_t m0,
                                             int64_t n0, int lane, int wave, bool vec) {
   constexpr int ES = OUT_BF16 ? 2 : 4;              // bytes per output value
   constexpr int CH = OUT_BF16 ? 4 : 2;              // 32-row blocks per chunk
-  constexpr uint32_t SB = 64 * ES + 16;             // padded LDS row stride (bytes)
+  constexpr uint32_t SB = 32 * NT * ES + 16;        // padded LDS row stride (bytes)
   constexpr uint32_t WAVE_BYTES = 32 * CH * SB;
-  constexpr int CPR = 64 * ES / 16;                 // 16-byte pieces per row
+  constexpr int CPR = 32 * NT * ES / 16;            // 16-byte pieces per row
   constexpr int RPI = 64 / CPR;                     // rows per pass of the wave
   constexpr int EPP = 16 / ES;                      // values per piece
   const int c = lane & 31, p = lane >> 5;
   const uint32_t wbase = wave * WAVE_BYTES;
   const int64_t rlast4 = ((m - 1) >> 2) << 2;
   // per output column (weight row) n0 + 32 t + c: post, times its row scale
-  float pt[2] = {post, post};
-  if (row_scale) {
+  float pt[NT];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) pt[t] = post * row_scale[min(n0 + 32 * t + c, n - 1)];
-  }
+  for (int t = 0; t < NT; ++t) pt[t] = row_scale ? post * row_scale[min(n0 + 32 * t + c, n - 1)] : post;
 #pragma unroll
   for (int a0 = 0; a0 < 8; a0 += CH) {
 #pragma unroll
@@ -2018,7 +2019,7 @@ __device__ __forceinline__ void gm_epilogue(const f32x16 (&acc)[8][2], const flo
           cz[0] = f * rs.x; cz[1] = f * rs.y; cz[2] = f * rs.z; cz[3] = f * rs.w;
         }
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < NT; ++t) {
           const uint32_t base = wbase + (32 * (a - a0) + 8 * q + 4 * p) * SB + (32 * t + c) * ES;
           float v[4];
 #pragma unroll
@@ -2082,65 +2083,7 @@ __device__ __forceinline__ void gm_interleave16() {
   }
 }
 
-// Buffer-load forms of the k-loop's global reads, used when k is a multiple
-// of 64 (every x~ tile whole). Each lane's byte offsets inside the block's
-// rows are fixed for the whole loop; the step enters as the scalar offset,
-// so a load is one instruction with no address arithmetic. Reads past the
-// descriptor's size return zeros: rows past m (accumulator rows that are
-// never stored) and weight rows past n (outputs never stored).
-struct GmBuf {
-  __amdgpu_buffer_rsrc_t xa, i1, i2;
-  uint32_t va;           // x~ piece 0 of this lane; piece u is 32 u rows further
-  uint32_t vi, vi8;      // index row t = 0 of this lane (2-byte, 1-byte planes)
-  int sa, si;            // bytes of 32 x~ rows, of 32 index rows (2-byte plane)
-};
-
-template <int BPW>
-__device__ __forceinline__ void gm_buf_init(GmBuf &b, const uint16_t *idx1, const void *idx2, const uint16_t *xt,
-                                            int64_t m, int64_t n, int64_t k, int64_t m0, int64_t nrow0, int c,
-                                            int p) {
-  const int64_t G = k / 8;
-  const int64_t rows_a = min(m - m0, (int64_t)GM_BM);
-  b.xa = __builtin_amdgcn_make_buffer_rsrc((void *)(xt + m0 * k), 0, (int)(rows_a * k * 2), 0x00020000);
-  const int64_t rows_w = max(min(n - nrow0, (int64_t)64), (int64_t)0);
-  b.i1 = __builtin_amdgcn_make_buffer_rsrc((void *)(idx1 + nrow0 * G), 0, (int)(rows_w * G * 2), 0x00020000);
-  if constexpr (BPW == 3)
-    b.i2 = __builtin_amdgcn_make_buffer_rsrc((void *)(reinterpret_cast<const uint8_t *>(idx2) + nrow0 * G), 0,
-                                             (int)(rows_w * G), 0x00020000);
-  else if constexpr (BPW == 4)
-    b.i2 = __builtin_amdgcn_make_buffer_rsrc((void *)(reinterpret_cast<const uint16_t *>(idx2) + nrow0 * G), 0,
-                                             (int)(rows_w * G * 2), 0x00020000);
-  else
-    b.i2 = b.i1;
-  b.va = (uint32_t)((threadIdx.x >> 3) * k * 2 + 16 * (threadIdx.x & 7));
-  b.vi = (uint32_t)(c * G * 2 + 8 * p);
-  b.vi8 = (uint32_t)(c * G + 4 * p);
-  b.sa = (int)(32 * k * 2);
-  b.si = (int)(32 * G * 2);
-}
-
-__device__ __forceinline__ void gm_buf_load_a(const GmBuf &b, int64_t s, uint4 (&ra)[8]) {
-  const int so = (int)(2 * GM_BK * s);
-#pragma unroll
-  for (int u = 0; u < 8; ++u)
-    ra[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(b.xa, b.va, so + u * b.sa, 0));
-}
-
-template <int BPW>
-__device__ __forceinline__ void gm_buf_load_idx(const GmBuf &b, int64_t s, uint2 (&i1)[2], uint2 (&i2)[2]) {
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int so = (int)(16 * s) + t * b.si;
-    i1[t] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(b.i1, b.vi, so, 0));
-    if constexpr (BPW == 3)
-      i2[t] = make_uint2(__builtin_amdgcn_raw_buffer_load_b32(b.i2, b.vi8, (int)(8 * s) + t * (b.si >> 1), 0), 0u);
-    if constexpr (BPW == 4)
-      i2[t] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(b.i2, b.vi, so, 0));
-    if constexpr (BPW == 2) i2[t] = make_uint2(0u, 0u);
-  }
-}
-
-template <int BPW, bool G4, bool K64, bool OUT_BF16>
+template <int BPW, bool G4, bool OUT_BF16>
 __global__ void __launch_bounds__(256, 1)
 gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uint16_t *xt,
           const float *rowsum, int64_t m, int64_t n, int64_t k, float post, const float *row_scale,
@@ -2154,22 +2097,15 @@ gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
   int64_t tile = blockIdx.x;
   if (tiles % 8 == 0) tile = (blockIdx.x % 8) * (tiles / 8) + blockIdx.x / 8;
   const int64_t m0 = (tile % mblocks) * GM_BM;
-  // wave index as a scalar: the buffer descriptors built from it must be uniform
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 31, p = lane >> 5;
   const int64_t n0 = (tile / mblocks) * GM_BN + 64 * wave;
   const int64_t G = k / 8;
   const int64_t S = (k + GM_BK - 1) / GM_BK;
 
-  GmBuf gb;
-  if constexpr (K64) gm_buf_init<BPW>(gb, idx1, idx2, xt, m, n, k, m0, n0, c, p);
-  auto load_a = [&](int64_t s, uint4 (&ra)[8]) {
-    if constexpr (K64) gm_buf_load_a(gb, s, ra);
-    else gm_load_a(xt, m, k, m0, s, ra);
-  };
+  auto load_a = [&](int64_t s, uint4 (&ra)[8]) { gm_load_a(xt, m, k, m0, s, ra); };
   auto load_idx = [&](int64_t s, uint2 (&a)[2], uint2 (&b)[2]) {
-    if constexpr (K64) gm_buf_load_idx<BPW>(gb, s, a, b);
-    else gm_load_idx<BPW, G4>(idx1, idx2, n, G, n0, c, p, s, a, b);
+    gm_load_idx<BPW, G4>(idx1, idx2, n, G, n0, c, p, s, a, b);
   };
 
   load_tables<BPW>(lds, blob);
@@ -2258,8 +2194,8 @@ gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
     // and of groups 4-7 in block 3. x~ tile s + 1 goes to LDS and tile s + 2
     // is requested during block 2.
     constexpr int NW = BPW == 4 ? 2 : 1;            // table walks per group
-    constexpr int LA = K64 ? 0 : 1;                 // address arithmetic of a pointer-based load
-    Dec8<BPW, K64> D;
+    constexpr int LA = 1;                           // address arithmetic of a pointer-based load
+    Dec8<BPW, false> D;
     D.p1(q1, q2);
     mfma_block(0, A0, A1);
     gm_interleave16<2 + LA, (8 * NW + (BPW == 3 ? 8 : 0) + 8 + 15) / 16>();
@@ -2270,8 +2206,7 @@ gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
     __builtin_amdgcn_sched_barrier(0);
     D.template p2<4, 8>(q1, q2);
     D.template p3<0, 4>(bn);
-    if constexpr (K64) gm_store_a(Anext, ra, GM_BK);
-    else gm_store_a(Anext, ra, k - GM_BK * (s + 1));   // tile s + 1 (unused past the end)
+    gm_store_a(Anext, ra, k - GM_BK * (s + 1));     // tile s + 1 (unused past the end)
     load_a(min(s + 2, S - 1), ra);
     mfma_block(2, A0, A1);
     gm_interleave16<(28 * NW + (BPW == 2 ? 0 : 16) + 15) / 16 + LA, (8 * NW + 8 + 15) / 16, 1, 1>();
@@ -2290,6 +2225,219 @@ gemm_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uin
   if (s < S) kstep(s, B0, B1);
   __syncthreads();                                   // the epilogue reuses the x~ buffers
   gm_epilogue<BPW, OUT_BF16>(acc, rowsum, post, row_scale, out, m, n, m0, n0, lane, wave, vec != 0);
+}
+
+// Issue pattern of N MFMAs with up to V VALU, D LDS-read, W LDS-write and M
+// global-load instructions placed after each (gm_interleave16 for any N).
+template <int N, int V, int D, int W = 0, int M = 0>
+__device__ __forceinline__ void gm_interleave() {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (D > 0) __builtin_amdgcn_sched_group_barrier(0x100, D, 0);
+    if constexpr (V > 0) __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+    if constexpr (W > 0) __builtin_amdgcn_sched_group_barrier(0x200, W, 0);
+    if constexpr (M > 0) __builtin_amdgcn_sched_group_barrier(0x020, M, 0);
+  }
+}
+
+// ---------------------------------------------------------------- 8-wave decode-GEMM
+// gemm8_bf16 (m > 16, k a multiple of 64): the tile, the x~ staging and the
+// epilogue of gemm_bf16 with 8 waves, two per SIMD. Wave w owns weight rows
+// n0 + 32 w .. + 31 for all 256 activation rows (8 MFMA 32x32x16 tiles, 128
+// accumulators), so every weight is still decoded once per workgroup, while
+// each SIMD now interleaves two instruction streams: one wave's decode
+// (VALU and table reads) and operand reads issue while the other wave's
+// MFMAs run. Lane (c, p) of a wave decodes groups 8 s + 4 p + u (u = 0..3)
+// of weight row n0 + 32 w + c: the B operand of MFMA k-step u, and the x~
+// columns the A operands read for that step. A k-step is eight half-blocks
+// of four MFMAs (k-step u = h >> 1, activation tiles 4 (h & 1) .. + 3); the
+// operands of half-block h + 1 are read during h, and the last half-block
+// reads the first of the next x~ tile, after the step's barrier.
+constexpr int G8_THREADS = 512;
+
+struct G8Buf {
+  __amdgpu_buffer_rsrc_t xa, i1, i2;
+  uint32_t va;           // x~ piece 0 of this thread; piece u is 64 u rows further
+  uint32_t vi, vi8;      // this lane's index row (2-byte, 1-byte planes)
+  int sa;                // bytes of 64 x~ rows
+};
+
+template <int BPW>
+__device__ __forceinline__ void g8_buf_init(G8Buf &b, const uint16_t *idx1, const void *idx2, const uint16_t *xt,
+                                            int64_t m, int64_t n, int64_t k, int64_t m0, int64_t nrow0, int c,
+                                            int p) {
+  const int64_t G = k / 8;
+  const int64_t rows_a = min(m - m0, (int64_t)GM_BM);
+  b.xa = __builtin_amdgcn_make_buffer_rsrc((void *)(xt + m0 * k), 0, (int)(rows_a * k * 2), 0x00020000);
+  const int64_t rows_w = max(min(n - nrow0, (int64_t)32), (int64_t)0);
+  b.i1 = __builtin_amdgcn_make_buffer_rsrc((void *)(idx1 + nrow0 * G), 0, (int)(rows_w * G * 2), 0x00020000);
+  if constexpr (BPW == 3)
+    b.i2 = __builtin_amdgcn_make_buffer_rsrc((void *)(reinterpret_cast<const uint8_t *>(idx2) + nrow0 * G), 0,
+                                             (int)(rows_w * G), 0x00020000);
+  else if constexpr (BPW == 4)
+    b.i2 = __builtin_amdgcn_make_buffer_rsrc((void *)(reinterpret_cast<const uint16_t *>(idx2) + nrow0 * G), 0,
+                                             (int)(rows_w * G * 2), 0x00020000);
+  else
+    b.i2 = b.i1;
+  b.va = (uint32_t)((threadIdx.x >> 3) * k * 2 + 16 * (threadIdx.x & 7));
+  b.vi = (uint32_t)(c * G * 2 + 8 * p);
+  b.vi8 = (uint32_t)(c * G + 4 * p);
+  b.sa = (int)(64 * k * 2);
+}
+
+__device__ __forceinline__ void g8_load_a(const G8Buf &b, int64_t s, uint4 (&ra)[4]) {
+  const int so = (int)(2 * GM_BK * s);
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    ra[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(b.xa, b.va, so + u * b.sa, 0));
+}
+
+// indices of k-step s as stored (i1: 4 stage-1 indices; i2: stage 2)
+template <int BPW>
+__device__ __forceinline__ void g8_load_idx(const G8Buf &b, int64_t s, uint2 &i1, uint2 &i2) {
+  i1 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(b.i1, b.vi, (int)(16 * s), 0));
+  if constexpr (BPW == 3) i2 = make_uint2(__builtin_amdgcn_raw_buffer_load_b32(b.i2, b.vi8, (int)(8 * s), 0), 0u);
+  else if constexpr (BPW == 4) i2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(b.i2, b.vi, (int)(16 * s), 0));
+  else i2 = make_uint2(0u, 0u);
+}
+
+// stored indices -> decode inputs of groups u = 0..3 (as decode_ip takes them)
+template <int BPW>
+__device__ __forceinline__ void g8_split(uint2 i1, uint2 i2, uint32_t (&q1)[8], uint32_t (&q2)[8]) {
+  const uint2 d1 = make_uint2(pk_dec16(i1.x), pk_dec16(i1.y));
+  const uint2 d2 = BPW == 4 ? make_uint2(pk_dec16(i2.x), pk_dec16(i2.y)) : i2;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    q1[u] = ((u < 2 ? d1.x : d1.y) >> (16 * (u & 1))) & 0xFFFFu;
+    if constexpr (BPW == 3) q2[u] = (d2.x >> (8 * u)) & 0xFFu;
+    else if constexpr (BPW == 4) q2[u] = ((u < 2 ? d2.x : d2.y) >> (16 * (u & 1))) & 0xFFFFu;
+    else q2[u] = 0u;
+  }
+}
+
+template <int BPW, bool OUT_BF16>
+__global__ void __launch_bounds__(G8_THREADS, 1)
+gemm8_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uint16_t *xt,
+           const float *rowsum, int64_t m, int64_t n, int64_t k, float post, const float *row_scale,
+           void *out, int vec, int64_t mblocks, int64_t tiles) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  uint16_t *As0 = reinterpret_cast<uint16_t *>(lds + lds_table_bytes<BPW>());
+  uint16_t *As1 = As0 + GM_BM * GM_LDA;
+  // XCD-aware tile order, as in gemm_bf16
+  int64_t tile = blockIdx.x;
+  if (tiles % 8 == 0) tile = (blockIdx.x % 8) * (tiles / 8) + blockIdx.x / 8;
+  const int64_t m0 = (tile % mblocks) * GM_BM;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 31, p = lane >> 5;
+  const int64_t n0 = (tile / mblocks) * GM_BN + 32 * wave;
+  const int64_t S = k / GM_BK;
+
+  G8Buf gb;
+  g8_buf_init<BPW>(gb, idx1, idx2, xt, m, n, k, m0, n0, c, p);
+  // x~ piece u of this thread: row (tid >> 3) + 64 u, 16-byte column tid & 7
+  auto store_a = [&](uint16_t *As, const uint4 (&ra)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int pc = threadIdx.x + G8_THREADS * u;
+      *reinterpret_cast<uint4 *>(As + (pc >> 3) * GM_LDA + 8 * (pc & 7)) = ra[u];
+    }
+  };
+
+  load_tables<BPW, G8_THREADS>(lds, blob);
+  uint4 ra[4];
+  g8_load_a(gb, 0, ra);
+  uint2 i1, i2, j1, j2;
+  g8_load_idx<BPW>(gb, 0, i1, i2);
+  tables_landed();                                   // tables, x~ tile 0, step-0 indices
+  store_a(As0, ra);
+  g8_load_idx<BPW>(gb, min((int64_t)1, S - 1), j1, j2);
+  g8_load_a(gb, min((int64_t)1, S - 1), ra);
+  __syncthreads();                                   // tables and x~ tile 0 in LDS
+
+  f32x16 acc[8][1];
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[a][0][e] = 0.f;
+
+  uint4 B0[8], B1[8];                                // groups u = 0..3 used
+  {
+    uint32_t q1[8], q2[8];
+    g8_split<BPW>(i1, i2, q1, q2);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) B0[u] = decode_ip<BPW>(q1[u], q2[u]);
+  }
+  i1 = j1;
+  i2 = j2;
+
+  uint4 H0[4], H1[4];                                // A operands of even / odd half-blocks
+#pragma unroll
+  for (int a = 0; a < 4; ++a) H0[a] = *reinterpret_cast<const uint4 *>(As0 + (32 * a + c) * GM_LDA + 32 * p);
+
+  auto kstep = [&](int64_t s, const uint4 (&bc)[8], uint4 (&bn)[8]) {
+    const uint16_t *Acur = (s & 1) ? As1 : As0;
+    uint16_t *Anext = (s & 1) ? As0 : As1;
+    uint32_t q1[8], q2[8];
+    g8_split<BPW>(i1, i2, q1, q2);                   // indices of step s + 1
+    g8_load_idx<BPW>(gb, min(s + 2, S - 1), i1, i2);
+
+    // half-block h: MFMAs of k-step u = h >> 1 on activation tiles 4 (h & 1) + a,
+    // reading the operands of half-block h + 1 (of the next tile for h = 7)
+    auto half = [&](int h, const uint4 (&av)[4], uint4 (&an)[4]) {
+      const int hn = h + 1, un = (hn >> 1) & 3, tn = 4 * (hn & 1);
+      const uint16_t *Ab = h < 7 ? Acur : Anext;
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        an[a] = *reinterpret_cast<const uint4 *>(Ab + (32 * (tn + a) + c) * GM_LDA + 32 * p + 8 * un);
+      const int u = h >> 1, t0 = 4 * (h & 1);
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        acc[t0 + a][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[a]),
+                                                                 __builtin_bit_cast(bf16x8, bc[u]), acc[t0 + a][0],
+                                                                 0, 0, 0);
+    };
+    constexpr int NW = BPW == 4 ? 2 : 1;             // table walks per group
+    Dec8<BPW, true> D;
+    D.template p1<0, 4>(q1, q2);
+    half(0, H0, H1);
+    gm_interleave<4, 3, (4 * NW + (BPW == 3 ? 4 : 0) + 4 + 3) / 4>();
+    __builtin_amdgcn_sched_barrier(0);
+    D.template p2<0, 2>(q1, q2);
+    half(1, H1, H0);
+    gm_interleave<4, (14 * NW + 3) / 4, (4 * NW + 4 + 3) / 4>();
+    __builtin_amdgcn_sched_barrier(0);
+    D.template p2<2, 4>(q1, q2);
+    half(2, H0, H1);
+    gm_interleave<4, (14 * NW + 3) / 4, (4 * NW + 4 + 3) / 4>();
+    __builtin_amdgcn_sched_barrier(0);
+    D.template p3<0, 2>(bn);
+    half(3, H1, H0);
+    gm_interleave<4, 2, 1>();
+    __builtin_amdgcn_sched_barrier(0);
+    D.template p3<2, 4>(bn);
+    store_a(Anext, ra);                              // tile s + 1 (unused past the end)
+    half(4, H0, H1);
+    gm_interleave<4, 2, 1, 1>();
+    __builtin_amdgcn_sched_barrier(0);
+    g8_load_a(gb, min(s + 2, S - 1), ra);
+    half(5, H1, H0);
+    gm_interleave<4, 0, 1, 0, 1>();
+    __builtin_amdgcn_sched_barrier(0);
+    half(6, H0, H1);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    half(7, H1, H0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int64_t s = 0;
+  for (; s + 1 < S; s += 2) {
+    kstep(s, B0, B1);
+    kstep(s + 1, B1, B0);
+  }
+  if (s < S) kstep(s, B0, B1);
+  __syncthreads();                                   // the epilogue reuses the x~ buffers
+  gm_epilogue<BPW, OUT_BF16, 1>(acc, rowsum, post, row_scale, out, m, n, m0, n0, lane, wave, vec != 0);
 }
 
 // Dense GEMM z = post * x~ W^T with the weights already in memory as bf16
@@ -3206,17 +3354,17 @@ int launch_matmul(const glq_layer *L, const void *xt, glq_dtype x_dt, const floa
     if (tiles > 0x7FFFFFFF) return GLQ_ERR_UNSUPPORTED;
     const size_t shm = tab + 2 * GM_A_BYTES;
     const bool even_g = ((L->k / 8) % 4) == 0;
-    // whole x~ tiles and 32-bit buffer offsets (256 rows of x~, 64 index rows)
+    // gemm8_bf16: whole x~ tiles and 32-bit buffer offsets (256 rows of x~)
     const bool k64 = L->k % GM_BK == 0 && (int64_t)GM_BM * L->k * 2 < 0x7FFFFFFF;
     const bool ob = out_dt == GLQ_BF16;
     const int vec = ((L->n * (ob ? 2 : 4)) % 16 == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0) ? 1 : 0;
-    auto kern = k64 ? (ob ? gemm_bf16<BPW, true, true, true> : gemm_bf16<BPW, true, true, false>)
-              : even_g ? (ob ? gemm_bf16<BPW, true, false, true> : gemm_bf16<BPW, true, false, false>)
-                       : (ob ? gemm_bf16<BPW, false, false, true> : gemm_bf16<BPW, false, false, false>);
+    auto kern = k64 ? (ob ? gemm8_bf16<BPW, true> : gemm8_bf16<BPW, false>)
+              : even_g ? (ob ? gemm_bf16<BPW, true, true> : gemm_bf16<BPW, true, false>)
+                       : (ob ? gemm_bf16<BPW, false, true> : gemm_bf16<BPW, false, false>);
     int rc = allow_lds(kern, shm);
     if (rc) return rc;
-    hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(256), shm, st, L->idx1, L->idx2, blob, xb, rowsum, m,
-                       L->n, L->k, post, L->row_scale, out, vec, mb, tiles);
+    hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(k64 ? G8_THREADS : 256), shm, st, L->idx1, L->idx2,
+                       blob, xb, rowsum, m, L->n, L->k, post, L->row_scale, out, vec, mb, tiles);
   }
   return hip_status(hipGetLastError());
 }

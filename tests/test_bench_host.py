@@ -32,9 +32,10 @@ def test_dominant_kernel_per_workload():
     b = _bench()
     kern = {name: b.dominant_kernel(workloads.layer_specs(name)[0]) for name in workloads.WORKLOADS}
     # batch 1 at 4096^2 fits the single-launch layer; 16 rows take the GEMV;
-    # 2048 and 4096 rows the GEMM; the float32 workload its own kernel
+    # 2048 and 4096 rows the 8-wave GEMM (k a multiple of 64); the float32
+    # workload its own kernel
     assert kern == {"small": "gemv_f32<2>", "gemv": "layer_small<2>", "batch16": "gemv_bf16<4>",
-                    "prefill_up": "gemm_bf16<3>", "dit_block": "gemm_bf16<4>"}
+                    "prefill_up": "gemm8_bf16<3>", "dit_block": "gemm8_bf16<4>"}
     assert b.single_launch(workloads.layer_specs("gemv")[0])
     assert not b.single_launch(workloads.layer_specs("batch16")[0])
     assert b.operand_layout(workloads.layer_specs("batch16")[0])
