@@ -312,6 +312,25 @@ def test_prefill_tiles(G, cb, bpw, m, n, k):
         assert og.relative_error(y, ref) <= TOL_BF16
 
 
+@pytest.mark.parametrize("bpw", [2, 3, 4])
+@pytest.mark.parametrize("m,n,k", [(17, 300, 64), (40, 1000, 128), (257, 33, 192), (520, 600, 1088)])
+def test_gemm_whole_k_steps(G, cb, bpw, m, n, k):
+    # k a multiple of 64 (the 8-wave GEMM, 32 weight rows a wave): one, two and
+    # an odd number of k-steps; n not a multiple of 32, so one wave's rows end
+    # inside it and whole waves lie past n; m just above the GEMV range, a
+    # single activation row in the last tile, and several tiles both ways
+    i1, i2 = _random_layer(n, k, bpw, 7000 + m + n + k)
+    s = np.float32(0.019)
+    sn, sk = workloads.signs(n, 71), workloads.signs(k, 72)
+    x = workloads.bf16_round_trip(np.random.default_rng(m * k).standard_normal((m, k)).astype(np.float32))
+    ref = og.layer_reference(x, i1, i2, bpw, s, sn, sk)
+    for y_dt in ("bf16", "f32"):
+        y = _run_linear(G, cb, i1, i2, s, sn, sk, x, "bf16", y_dt)
+        assert np.isfinite(y).all()
+        assert og.relative_error(y, ref) <= TOL_BF16
+        assert og.row_relative_error(y, ref) <= TOL_BF16
+
+
 _LDS_ORDER_SCRIPT = r"""
 import numpy as np, torch
 from dequant_e8_codebook_amd import glq
