@@ -2255,6 +2255,11 @@ __device__ __forceinline__ void gm_interleave() {
 // operands of half-block h + 1 are read during h, and the last half-block
 // reads the first of the next x~ tile, after the step's barrier.
 constexpr int G8_THREADS = 512;
+// LDS the 8-wave epilogue stages through: per wave 4 blocks of 32 rows of 32
+// bf16 values padded to 80 bytes (the float32 form, 2 blocks of 144-byte
+// rows, is smaller)
+constexpr size_t G8_EPI_BYTES = (size_t)(G8_THREADS / 64) * 4 * 32 * (32 * 2 + 16);
+static_assert(lds_table_bytes<2>() + 2 * GM_A_BYTES >= G8_EPI_BYTES, "decode-GEMM LDS holds the epilogue");
 
 struct G8Buf {
   __amdgpu_buffer_rsrc_t xa, i1, i2;
@@ -2490,18 +2495,21 @@ gemm_w_bf16(const uint16_t *w, const uint16_t *xt, int64_t m, int64_t n, int64_t
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][t][e] = 0.f;
 
+  // A operands of block 0 of tile 0; the loop reads those of tile st + 1 in
+  // block 3 of step st, after the step's barrier (placed as in gemm_bf16)
+  uint4 A0[8], A1[8];
+#pragma unroll
+  for (int a = 0; a < 8; ++a) A0[a] = *reinterpret_cast<const uint4 *>(As0 + (32 * a + c) * GM_LDA + 32 * p);
+
   auto kstep = [&](int64_t st, const uint4 (&bc)[8], uint4 (&bn)[8]) {
     const uint16_t *Acur = (st & 1) ? As1 : As0;
+    uint16_t *Anext = (st & 1) ? As0 : As1;
     load_b(min(st + 1, S - 1), bn);                  // next step's weights
-    uint4 A0[8], A1[8];
-#pragma unroll
-    for (int a = 0; a < 8; ++a) A0[a] = *reinterpret_cast<const uint4 *>(Acur + (32 * a + c) * GM_LDA + 32 * p);
     auto block = [&](int u, const uint4 (&av)[8], uint4 (&an)[8]) {
-      if (u < 3) {
 #pragma unroll
-        for (int a = 0; a < 8; ++a)
-          an[a] = *reinterpret_cast<const uint4 *>(Acur + (32 * a + c) * GM_LDA + 32 * p + 8 * (u + 1));
-      }
+      for (int a = 0; a < 8; ++a)
+        an[a] = u < 3 ? *reinterpret_cast<const uint4 *>(Acur + (32 * a + c) * GM_LDA + 32 * p + 8 * (u + 1))
+                      : *reinterpret_cast<const uint4 *>(Anext + (32 * a + c) * GM_LDA + 32 * p);
 #pragma unroll
       for (int a = 0; a < 8; ++a) {
         acc[a][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[a]),
@@ -2516,14 +2524,15 @@ gemm_w_bf16(const uint16_t *w, const uint16_t *xt, int64_t m, int64_t n, int64_t
     block(1, A1, A0);
     gm_interleave16<0, 1>();
     __builtin_amdgcn_sched_barrier(0);
+    gm_store_a(Anext, ra, GM_BK);                    // tile st + 1 (unused past the end)
+    gm_load_a(xt, m, k, m0, min(st + 2, S - 1), ra);
     block(2, A0, A1);
+    gm_interleave16<1, 1, 1, 1>();
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    block(3, A1, A0);
     gm_interleave16<0, 1>();
     __builtin_amdgcn_sched_barrier(0);
-    block(3, A1, A0);
-    gm_store_a((st & 1) ? As0 : As1, ra, GM_BK);      // tile st + 1 (unused past the end)
-    gm_load_a(xt, m, k, m0, min(st + 2, S - 1), ra);
-    gm_interleave16<1, 0, 1, 1>();
-    __syncthreads();
   };
   int64_t st = 0;
   for (; st + 1 < S; st += 2) {
@@ -2531,6 +2540,7 @@ gemm_w_bf16(const uint16_t *w, const uint16_t *xt, int64_t m, int64_t n, int64_t
     kstep(st + 1, B1, B0);
   }
   if (st < S) kstep(st, B0, B1);
+  __syncthreads();                                   // the epilogue reuses the x~ buffers
   gm_epilogue<2, OUT_BF16>(acc, nullptr, post, nullptr, out, m, n, m0, n0, lane, wave, vec != 0);
 }
 
@@ -3352,7 +3362,7 @@ int launch_matmul(const glq_layer *L, const void *xt, glq_dtype x_dt, const floa
     const int64_t mb = (m + GM_BM - 1) / GM_BM, nb = (L->n + GM_BN - 1) / GM_BN;
     const int64_t tiles = mb * nb;
     if (tiles > 0x7FFFFFFF) return GLQ_ERR_UNSUPPORTED;
-    const size_t shm = tab + 2 * GM_A_BYTES;
+    const size_t shm = tab + 2 * GM_A_BYTES;       // >= G8_EPI_BYTES: the 8-wave epilogue fits
     const bool even_g = ((L->k / 8) % 4) == 0;
     // gemm8_bf16: whole x~ tiles and 32-bit buffer offsets (256 rows of x~)
     const bool k64 = L->k % GM_BK == 0 && (int64_t)GM_BM * L->k * 2 < 0x7FFFFFFF;

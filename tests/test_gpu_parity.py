@@ -777,7 +777,7 @@ def _ep_run(G, L, x, x_dt, y_dt, flags=0):
 @pytest.mark.parametrize("n,k,m,x_dt,y_dt", [(256, 512, 1, "bf16", "bf16"), (256, 512, 16, "f32", "f32"),
                                             (300, 264, 5, "bf16", "f32"), (40, 8, 3, "f32", "f32"),
                                             (300, 264, 37, "bf16", "f32"), (1024, 4096, 300, "bf16", "bf16"),
-                                            (520, 3072, 257, "f32", "bf16")])
+                                            (520, 3072, 257, "f32", "bf16"), (600, 1024, 40, "bf16", "f32")])
 def test_ep_fused_linear(G, n, k, m, x_dt, y_dt):
     # y = U^T W^ (V x) on entropy-coded weights: bf16 matrix cores against
     # the float64 product of the oracle's weights and transforms
