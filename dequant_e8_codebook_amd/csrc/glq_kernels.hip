@@ -3150,7 +3150,11 @@ int launch_rht_blk_nw(const void *in, void *out, int64_t rows, int64_t n, const 
   constexpr int B = 1024 * NW;
   const int nb = (int)(n / B);
   const size_t shm = NW > 1 ? sizeof(float) * (size_t)nb * (B + 64) : 0;
-  const int64_t cap = (int64_t)cu_count() * (24 / (nb * NW) > 1 ? 24 / (nb * NW) : 1);
+  // about 24 waves a CU; a whole row of 16 waves (at most 64 VGPRs, 66 KiB of
+  // LDS) gets two workgroups a CU, which keeps two rows in flight per CU
+  // (2048 x 16384: 39 -> 34 us; wider grids measured no better elsewhere)
+  const int wpc = nb * NW == 16 ? 32 : 24;
+  const int64_t cap = (int64_t)cu_count() * (wpc / (nb * NW) > 1 ? wpc / (nb * NW) : 1);
   const int64_t grid = rows < cap ? rows : cap;
   const int rc = allow_lds(rht_rows_blk<NW, IB, OB, TR>, shm + 64);
   if (rc) return rc;
