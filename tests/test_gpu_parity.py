@@ -331,6 +331,22 @@ def test_gemm_whole_k_steps(G, cb, bpw, m, n, k):
         assert og.row_relative_error(y, ref) <= TOL_BF16
 
 
+@pytest.mark.parametrize("bpw", [3, 4])
+def test_gemm_long_k(G, cb, bpw):
+    # 384 whole k-steps (k = 3 x 8192): the loop's buffer offsets reach
+    # 48 KiB per index row and 12 MiB across the x~ tile
+    m, n, k = 20, 96, 24576
+    i1, i2 = _random_layer(n, k, bpw, 7700 + bpw)
+    s = np.float32(0.011)
+    sn, sk = workloads.signs(n, 77), workloads.signs(k, 78)
+    x = workloads.bf16_round_trip(np.random.default_rng(bpw).standard_normal((m, k)).astype(np.float32))
+    ref = og.layer_reference(x, i1, i2, bpw, s, sn, sk)
+    y = _run_linear(G, cb, i1, i2, s, sn, sk, x, "bf16", "f32")
+    assert np.isfinite(y).all()
+    assert og.relative_error(y, ref) <= TOL_BF16
+    assert og.row_relative_error(y, ref) <= TOL_BF16
+
+
 _LDS_ORDER_SCRIPT = r"""
 import numpy as np, torch
 from dequant_e8_codebook_amd import glq
