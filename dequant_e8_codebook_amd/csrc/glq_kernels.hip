@@ -34,8 +34,9 @@
 //                   decode-GEMV) in one launch.
 //   ep_decode_k     entropy-coded layers: rANS symbol decode and weight
 //                   reconstruction, one wave per 64-lane block.
-//   gemm_w_bf16,    entropy-coded layers: the product on decoded bf16 weights
-//   gemv_w_bf16     (m > 16 / m <= 16).
+//   gemm_w2_bf16,   entropy-coded layers: the product on decoded bf16 weights
+//   gemm_w_bf16_lds, (m > 16: k a multiple of 64 / other k; m <= 16).
+//   gemv_w_bf16
 //
 // Every kernel that decodes first copies its decode tables (glq_tables.h, or
 // the entropy-coded layer's symbol tables) from the caller's buffer into LDS.
@@ -1983,10 +1984,10 @@ __device__ __forceinline__ uint4 gm_decode_one(const uint2 (&i1)[2], const uint2
 // GEMM epilogue: z = post * acc + cz(row) with cz = -post * bias * rowsum(x~),
 // staged through LDS (free once the k-loop has ended) so that every lane
 // stores 16 contiguous bytes of an output row. Each wave stages its own
-// 256 x 32 NT tile in chunks of CH 32-row blocks. vec: 16-byte stores are
+// 32 MB x 32 NT tile in chunks of CH 32-row blocks. vec: 16-byte stores are
 // aligned (n * element size % 16 == 0 and an aligned output pointer).
-template <int BPW, bool OUT_BF16, int NT = 2>
-__device__ __forceinline__ void gm_epilogue(const f32x16 (&acc)[8][NT], const float *rowsum, float post,
+template <int BPW, bool OUT_BF16, int NT = 2, int MB = 8>
+__device__ __forceinline__ void gm_epilogue(const f32x16 (&acc)[MB][NT], const float *rowsum, float post,
                                             const float *row_scale, void *out, int64_t m, int64_t n, int64_t m0,
                                             int64_t n0, int lane, int wave, bool vec) {
   constexpr int ES = OUT_BF16 ? 2 : 4;              // bytes per output value
@@ -2004,7 +2005,7 @@ __device__ __forceinline__ void gm_epilogue(const f32x16 (&acc)[8][NT], const fl
 #pragma unroll
   for (int t = 0; t < NT; ++t) pt[t] = row_scale ? post * row_scale[min(n0 + 32 * t + c, n - 1)] : post;
 #pragma unroll
-  for (int a0 = 0; a0 < 8; a0 += CH) {
+  for (int a0 = 0; a0 < MB; a0 += CH) {
 #pragma unroll
     for (int a = a0; a < a0 + CH; ++a) {
 #pragma unroll
@@ -2445,103 +2446,123 @@ gemm8_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const ui
   gm_epilogue<BPW, OUT_BF16, 1>(acc, rowsum, post, row_scale, out, m, n, m0, n0, lane, wave, vec != 0);
 }
 
-// Dense GEMM z = post * x~ W^T with the weights already in memory as bf16
-// [n][k] row-major (the entropy-coded layers' decoded weights): the tiling,
-// x~ staging, operand pipeline and epilogue of gemm_bf16, with the B
-// operands loaded from memory instead of decoded: lane (c, p) of wave w takes
-// inputs 32 p + 8 u .. + 7 of weight row nb0 + 64 w + 32 t + c in MFMA block
-// u (the order in which it reads its A operands: the k order inside a step
-// is a permutation shared by A and B), eight 16-byte loads a step, issued a
-// step ahead into the other of two register sets. k is a multiple of 64
-// (every step whole); other shapes take gemm_w_bf16_lds.
+// Dense GEMM z = post * x~ W^T on bf16 weights in memory [n][k] (the
+// entropy-coded layers' decoded weights), k a multiple of 64: 256 x 256
+// tiles with both operand tiles double-buffered in LDS ([256][64 + 8] each)
+// and 4 waves in a 2 x 2 grid of 128 x 128 wave tiles (4 x 4 MFMA 32x32x16
+// tiles, 256 accumulators), so every operand read from LDS feeds four MFMAs.
+// Tiles are fetched with buffer loads at fixed per-thread offsets (the step is
+// the scalar offset; rows past m or n read as zeros) one step ahead into
+// registers and written to LDS during the step before their use; the step's
+// barrier sits before the last MFMA block, whose MFMAs cover the first
+// operand reads of the next tile (as in gemm_bf16).
 template <bool OUT_BF16>
 __global__ void __launch_bounds__(256, 1)
-gemm_w_bf16(const uint16_t *w, const uint16_t *xt, int64_t m, int64_t n, int64_t k, float post, void *out,
-            int vec, int64_t mblocks, int64_t tiles) {
+gemm_w2_bf16(const uint16_t *w, const uint16_t *xt, int64_t m, int64_t n, int64_t k, float post, void *out,
+             int vec, int64_t mblocks, int64_t tiles) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   uint16_t *As0 = reinterpret_cast<uint16_t *>(lds);
   uint16_t *As1 = As0 + GM_BM * GM_LDA;
+  uint16_t *Bs0 = As1 + GM_BM * GM_LDA;
+  uint16_t *Bs1 = Bs0 + GM_BN * GM_LDA;
   int64_t tile = blockIdx.x;
   if (tiles % 8 == 0) tile = (blockIdx.x % 8) * (tiles / 8) + blockIdx.x / 8;
   const int64_t m0 = (tile % mblocks) * GM_BM;
+  const int64_t nb0 = (tile / mblocks) * GM_BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 31, p = lane >> 5;
-  const int64_t n0 = (tile / mblocks) * GM_BN + 64 * wave;
+  const int wm = wave & 1, wn = wave >> 1;            // wave tile: rows 128 wm, columns 128 wn
   const int64_t S = k / GM_BK;
-  // weight rows of this lane (clamped: rows past n feed outputs never stored)
-  const uint16_t *wr0 = w + (size_t)min(n0 + c, n - 1) * k + 32 * p;
-  const uint16_t *wr1 = w + (size_t)min(n0 + 32 + c, n - 1) * k + 32 * p;
-  auto load_b = [&](int64_t st, uint4 (&b)[8]) {
+
+  const int64_t rows_a = min(m - m0, (int64_t)GM_BM), rows_w = min(n - nb0, (int64_t)GM_BN);
+  const __amdgpu_buffer_rsrc_t ra_rs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(xt + m0 * k), 0, (int)(rows_a * k * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb_rs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(w + nb0 * k), 0, (int)(rows_w * k * 2), 0x00020000);
+  // piece u of this thread: tile row (tid >> 3) + 32 u, 16-byte column tid & 7
+  const uint32_t voff = (uint32_t)((threadIdx.x >> 3) * k * 2 + 16 * (threadIdx.x & 7));
+  const int s32 = (int)(32 * k * 2);
+  auto load = [&](const __amdgpu_buffer_rsrc_t &rs, int64_t st, uint4 (&r)[8]) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      b[u] = *reinterpret_cast<const uint4 *>(wr0 + GM_BK * st + 8 * u);
-      b[4 + u] = *reinterpret_cast<const uint4 *>(wr1 + GM_BK * st + 8 * u);
+    for (int u = 0; u < 8; ++u)
+      r[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (int)(2 * GM_BK * st) + u * s32, 0));
+  };
+  auto store = [&](uint16_t *T, const uint4 (&r)[8]) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int pc = threadIdx.x + 256 * u;
+      *reinterpret_cast<uint4 *>(T + (pc >> 3) * GM_LDA + 8 * (pc & 7)) = r[u];
     }
   };
 
-  uint4 ra[8];
-  uint4 B0[8], B1[8];
-  gm_load_a(xt, m, k, m0, 0, ra);
-  load_b(0, B0);
-  gm_store_a(As0, ra, k);
-  gm_load_a(xt, m, k, m0, min((int64_t)1, S - 1), ra);
+  uint4 ra[8], rb[8];
+  load(ra_rs, 0, ra);
+  load(rb_rs, 0, rb);
+  store(As0, ra);
+  store(Bs0, rb);
+  load(ra_rs, min((int64_t)1, S - 1), ra);
+  load(rb_rs, min((int64_t)1, S - 1), rb);
   __syncthreads();
 
-  f32x16 acc[8][2];
+  f32x16 acc[4][4];
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][t][e] = 0.f;
 
-  // A operands of block 0 of tile 0; the loop reads those of tile st + 1 in
-  // block 3 of step st, after the step's barrier (placed as in gemm_bf16)
-  uint4 A0[8], A1[8];
+  // operands of MFMA block u (k-step sub-step u): A rows 128 wm + 32 a + c,
+  // B rows 128 wn + 32 t + c, inputs 32 p + 8 u .. + 7 (the k order inside a
+  // step is a permutation shared by A and B)
+  auto rd = [&](const uint16_t *T, int base, int u, uint4 (&v)[4]) {
 #pragma unroll
-  for (int a = 0; a < 8; ++a) A0[a] = *reinterpret_cast<const uint4 *>(As0 + (32 * a + c) * GM_LDA + 32 * p);
+    for (int a = 0; a < 4; ++a) v[a] = *reinterpret_cast<const uint4 *>(T + (base + 32 * a + c) * GM_LDA + 32 * p + 8 * u);
+  };
+  uint4 A0[4], A1[4], B0[4], B1[4];
+  rd(As0, 128 * wm, 0, A0);
+  rd(Bs0, 128 * wn, 0, B0);
 
-  auto kstep = [&](int64_t st, const uint4 (&bc)[8], uint4 (&bn)[8]) {
-    const uint16_t *Acur = (st & 1) ? As1 : As0;
-    uint16_t *Anext = (st & 1) ? As0 : As1;
-    load_b(min(st + 1, S - 1), bn);                  // next step's weights
-    auto block = [&](int u, const uint4 (&av)[8], uint4 (&an)[8]) {
-#pragma unroll
-      for (int a = 0; a < 8; ++a)
-        an[a] = u < 3 ? *reinterpret_cast<const uint4 *>(Acur + (32 * a + c) * GM_LDA + 32 * p + 8 * (u + 1))
-                      : *reinterpret_cast<const uint4 *>(Anext + (32 * a + c) * GM_LDA + 32 * p);
-#pragma unroll
-      for (int a = 0; a < 8; ++a) {
-        acc[a][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[a]),
-                                                            __builtin_bit_cast(bf16x8, bc[u]), acc[a][0], 0, 0, 0);
-        acc[a][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[a]),
-                                                            __builtin_bit_cast(bf16x8, bc[4 + u]), acc[a][1], 0, 0, 0);
+  auto kstep = [&](int64_t st) {
+    const uint16_t *Acur = (st & 1) ? As1 : As0, *Bcur = (st & 1) ? Bs1 : Bs0;
+    uint16_t *Anext = (st & 1) ? As0 : As1, *Bnext = (st & 1) ? Bs0 : Bs1;
+    auto block = [&](int u, const uint4 (&av)[4], const uint4 (&bv)[4], uint4 (&an)[4], uint4 (&bn)[4]) {
+      if (u < 3) {
+        rd(Acur, 128 * wm, u + 1, an);
+        rd(Bcur, 128 * wn, u + 1, bn);
+      } else {
+        rd(Anext, 128 * wm, 0, an);
+        rd(Bnext, 128 * wn, 0, bn);
       }
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          acc[a][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[a]),
+                                                              __builtin_bit_cast(bf16x8, bv[t]), acc[a][t], 0, 0, 0);
     };
-    block(0, A0, A1);
+    block(0, A0, B0, A1, B1);
     gm_interleave16<0, 1>();
     __builtin_amdgcn_sched_barrier(0);
-    block(1, A1, A0);
-    gm_interleave16<0, 1>();
+    store(Anext, ra);                                // tiles st + 1 (unused past the end)
+    load(ra_rs, min(st + 2, S - 1), ra);
+    block(1, A1, B1, A0, B0);
+    gm_interleave16<0, 1, 1, 1>();
     __builtin_amdgcn_sched_barrier(0);
-    gm_store_a(Anext, ra, GM_BK);                    // tile st + 1 (unused past the end)
-    gm_load_a(xt, m, k, m0, min(st + 2, S - 1), ra);
-    block(2, A0, A1);
-    gm_interleave16<1, 1, 1, 1>();
+    store(Bnext, rb);
+    load(rb_rs, min(st + 2, S - 1), rb);
+    block(2, A0, B0, A1, B1);
+    gm_interleave16<0, 1, 1, 1>();
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
-    block(3, A1, A0);
+    block(3, A1, B1, A0, B0);
     gm_interleave16<0, 1>();
     __builtin_amdgcn_sched_barrier(0);
   };
-  int64_t st = 0;
-  for (; st + 1 < S; st += 2) {
-    kstep(st, B0, B1);
-    kstep(st + 1, B1, B0);
-  }
-  if (st < S) kstep(st, B0, B1);
-  __syncthreads();                                   // the epilogue reuses the x~ buffers
-  gm_epilogue<2, OUT_BF16>(acc, nullptr, post, nullptr, out, m, n, m0, n0, lane, wave, vec != 0);
+  for (int64_t st = 0; st < S; ++st) kstep(st);
+  __syncthreads();                                   // the epilogue reuses the operand buffers
+  gm_epilogue<2, OUT_BF16, 4, 4>(acc, nullptr, post, nullptr, out, m, n, m0 + 128 * wm, nb0 + 128 * wn, lane, wave,
+                                 vec != 0);
 }
 
 // Dense GEMM z = post * x~ W^T with the weights already in memory as bf16
@@ -3643,14 +3664,22 @@ int launch_gemm_w(const uint16_t *w, const uint16_t *xt, int64_t m, int64_t n, i
   const int64_t mb = (m + GM_BM - 1) / GM_BM, nb = (n + GM_BN - 1) / GM_BN;
   const int64_t tiles = mb * nb;
   if (tiles > 0x7FFFFFFF) return GLQ_ERR_UNSUPPORTED;
-  // k a multiple of 64: weight operands straight from memory into registers
-  // (x~ tiles double-buffered in LDS); otherwise both tiles through LDS
+  // k a multiple of 64: gemm_w2_bf16; otherwise gemm_w_bf16_lds (4 waves of
+  // 64 weight rows, pointer loads, partial last tile)
   const bool direct = k % GM_BK == 0;
-  const size_t shm = (direct ? 2 : 4) * GM_A_BYTES;
+  const size_t shm = 4 * GM_A_BYTES;
   const bool ob = out_dt == GLQ_BF16;
   const int vec = ((n * (ob ? 2 : 4)) % 16 == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0) ? 1 : 0;
-  auto kern = direct ? (ob ? gemm_w_bf16<true> : gemm_w_bf16<false>)
-                     : (ob ? gemm_w_bf16_lds<true> : gemm_w_bf16_lds<false>);
+  if (direct && (int64_t)GM_BM * k * 2 < 0x7FFFFFFF) {
+    // 2 x 2 wave tiles, both operands through LDS (buffer loads, 32-bit offsets)
+    auto k2 = ob ? gemm_w2_bf16<true> : gemm_w2_bf16<false>;
+    const size_t shm2 = 4 * GM_A_BYTES;
+    int rc = allow_lds(k2, shm2);
+    if (rc) return rc;
+    hipLaunchKernelGGL(k2, dim3((unsigned)tiles), dim3(256), shm2, st, w, xt, m, n, k, 1.0f, out, vec, mb, tiles);
+    return hip_status(hipGetLastError());
+  }
+  auto kern = ob ? gemm_w_bf16_lds<true> : gemm_w_bf16_lds<false>;
   int rc = allow_lds(kern, shm);
   if (rc) return rc;
   hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(256), shm, st, w, xt, m, n, k, 1.0f, out, vec, mb, tiles);
