@@ -1210,8 +1210,10 @@ rht_rows_blk(const void *in, void *out, int64_t rows, int n, int nb, const int8_
 #pragma unroll
       for (int i = 0; i < E; i += 2) w[i / 2] = bf16x2_rne(x[i], x[i + 1]);
       if (rowsum) {
+        // both halves of each packed word in one dot product with (1, 1)
+        const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
 #pragma unroll
-        for (int i = 0; i < E / 2; ++i) rs += __uint_as_float(w[i] << 16) + __uint_as_float(w[i] & 0xFFFF0000u);
+        for (int i = 0; i < E / 2; ++i) rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[i]), one, rs, false);
       }
       uint16_t *o = reinterpret_cast<uint16_t *>(out) + base + el;
       *reinterpret_cast<uint4 *>(o) = make_uint4(w[0], w[1], w[2], w[3]);
