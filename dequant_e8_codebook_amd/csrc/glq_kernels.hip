@@ -1088,9 +1088,35 @@ __device__ __forceinline__ int rb_elem(int p) {
 
 // The FWHT over a wave's 1024 labels (E = 16 registers a lane): registers,
 // then the four DPP lane stages, then lane bits 4 and 5 by lane swaps.
-__device__ __forceinline__ void rb_fwht_wave(float (&v)[16], int lane) {
+// Lane bits 4 and 5 (element bits 7 and 8) without the swap back: register
+// pairs (p, p + 8) trade lane bit 4, then lane bit 5, for register bit 3, and
+// the butterfly results stay where the trade left them. Afterwards register
+// bit 3 holds element bit 8, lane bit 5 element bit 7 and lane bit 4 element
+// bit 9 (rb_elem_out); register bits 0..2 are still element bits 0..2, so a
+// lane's 8 registers of one half are 8 consecutive elements.
+template <bool R16>
+__device__ __forceinline__ void rb_stage_swap_keep(float (&v)[16]) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) ly_stage_regs<16>(v, s);
+  for (int p = 0; p < 8; ++p) {
+    const auto r = R16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(v[p]), __float_as_uint(v[p + 8]), false, false)
+                       : __builtin_amdgcn_permlane32_swap(__float_as_uint(v[p]), __float_as_uint(v[p + 8]), false, false);
+    const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+    v[p] = a + b;
+    v[p + 8] = a - b;
+  }
+}
+
+// element of register i of lane l after rb_fwht_wave<., true>
+__device__ __forceinline__ int rb_elem_out(int l, int i) {
+  return (i & 7) | ((rb_ell(l) & 15) << 3) | (((l >> 5) & 1) << 7) | (((i >> 3) & 1) << 8) | (((l >> 4) & 1) << 9);
+}
+
+template <int FIRST = 0, bool KEEP = false>
+__device__ __forceinline__ void rb_fwht_wave(float (&v)[16], int lane) {
+  // FIRST = 1: the caller has done register stage 0 (element bit 0);
+  // KEEP: the last two stages leave the layout of rb_elem_out
+#pragma unroll
+  for (int s = FIRST; s < 4; ++s) ly_stage_regs<16>(v, s);
   const int ell = rb_ell(lane);
   const float s0 = (ell & 1) ? -1.0f : 1.0f, s1 = (ell & 2) ? -1.0f : 1.0f;
   const float s2 = (ell & 4) ? -1.0f : 1.0f, s3 = (ell & 8) ? -1.0f : 1.0f;
@@ -1099,8 +1125,13 @@ __device__ __forceinline__ void rb_fwht_wave(float (&v)[16], int lane) {
   RB_FMAC16("row_half_mirror", s2);       // lane ^ 7
   RB_FMAC16("row_ror:8", s3);             // lane ^ 8
   asm volatile("s_nop 1" ::);
-  ly_stage_swap<16, true>(v);
-  ly_stage_swap<16, false>(v);
+  if constexpr (KEEP) {
+    rb_stage_swap_keep<true>(v);
+    rb_stage_swap_keep<false>(v);
+  } else {
+    ly_stage_swap<16, true>(v);
+    ly_stage_swap<16, false>(v);
+  }
 }
 #undef RB_FMAC16
 
@@ -1158,34 +1189,77 @@ rht_rows_blk(const void *in, void *out, int64_t rows, int n, int nb, const int8_
   const int el = 1024 * (tl >> 6) + 8 * rb_ell(tl & 63);   // element of register 0 (8.. at el + 512)
   const float inv = 1.0f / sqrtf((float)B);      // exact for even log2 B
   constexpr bool tr = NW > 1;                     // the labels are transposed iff the wave stages used LDS
-  // sg: input signs (applied before the transform); sc: output scale, the
-  // sign after the transform or 1 / sqrt(B), times rb_sgn of the label's lane
-  float sg[E], sc[E];
+  // sc: output scale, the sign after the transform or 1 / sqrt(B), times
+  // rb_sgn of the label's lane. Input signs (applied before the transform):
+  // float factors sg for float32 input; for bf16 input, the bf16 pairs
+  // (s0, s1) and (s0, -s1) of the two elements of each packed word, so that
+  // two dot products per word apply the signs and the first butterfly stage
+  // (register stage 0 pairs exactly those two elements) with no unpacking
+  // XO (bf16 in and out, one wave a block, B = 1024): the pairs carry
+  // 1 / sqrt(B) = 2^-5 as well (an exact power of two: the sums are the same
+  // values scaled), and sc reduces to a sign per element, applied to the
+  // packed output words as sign-bit masks xm
+  constexpr bool XO = IN_BF16 && OUT_BF16 && NW == 1;
+  // one wave a block: the lane-swap stages keep their layout, and the
+  // stores (and the output signs) follow rb_elem_out: register half h of
+  // lane l is elements eo + 256 h .. + 7
+  constexpr bool KEEP = NW == 1;
+  const int eo = KEEP ? rb_elem_out(tl & 63, 0) : el;
+  constexpr uint32_t ONE = XO ? (uint32_t)(127 - logb / 2) << 7 : 0x3F80u;   // bf16 2^-5 or 1
+  float sg[IN_BF16 ? 1 : E], sc[E];
+  uint32_t sp[IN_BF16 ? 8 : 1], sq[IN_BF16 ? 8 : 1], xm[XO ? 8 : 1];
 #pragma unroll
   for (int i = 0; i < E; ++i) {
     const int p = tr ? ly_elem<E, NW>(tl, i, true) : 16 * tl + i;
-    sc[i] = rb_sgn((p >> 4) & 63) * (TRANSPOSE ? (float)signs[eb + rb_elem(p)] * inv : inv);
-    sg[i] = TRANSPOSE ? 1.0f : (float)signs[eb + el + (i & 7) + 512 * (i >> 3)];
+    const int pe = KEEP ? eo + (i & 7) + 256 * (i >> 3) : rb_elem(p);   // the element register i ends as
+    sc[i] = rb_sgn((p >> 4) & 63) * (TRANSPOSE ? (float)signs[eb + pe] * inv : inv);
+    const bool neg = !TRANSPOSE && signs[eb + el + (i & 7) + 512 * (i >> 3)] < 0;
+    if constexpr (IN_BF16) {
+      const uint32_t b = (neg ? 0x8000u : 0u) | ONE;   // bf16 -+1 (times 2^-5 under XO)
+      if (i & 1) {
+        sp[i >> 1] |= b << 16;
+        sq[i >> 1] |= (b ^ 0x8000u) << 16;
+      } else {
+        sp[i >> 1] = b;
+        sq[i >> 1] = b;
+      }
+    } else {
+      sg[i] = neg ? -1.0f : 1.0f;
+    }
+    if constexpr (XO) {
+      const uint32_t mb = sc[i] < 0.0f ? 0x8000u << (16 * (i & 1)) : 0u;
+      xm[i >> 1] = (i & 1) ? xm[i >> 1] | mb : mb;
+    }
   }
   uint4 raw[IN_BF16 ? 2 : 4];
   if ((int64_t)blockIdx.x < rows) rb_fetch<IN_BF16>(in, (size_t)blockIdx.x * n + eb + el, raw);
   for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
     const size_t base = (size_t)row * n + eb;
     float v[E];
-    rb_unpack<IN_BF16>(raw, v);
-    if (row + gridDim.x < rows) rb_fetch<IN_BF16>(in, base + (size_t)gridDim.x * n + el, raw);   // next row
-    if (!TRANSPOSE) {
+    if constexpr (IN_BF16) {
+      const uint32_t w[8] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y, raw[1].z, raw[1].w};
 #pragma unroll
-      for (int i = 0; i < E; ++i) v[i] *= sg[i];
+      for (int j = 0; j < 8; ++j) {
+        const bf16x2_t x2 = __builtin_bit_cast(bf16x2_t, w[j]);
+        v[2 * j] = __builtin_amdgcn_fdot2_f32_bf16(x2, __builtin_bit_cast(bf16x2_t, sp[j]), 0.0f, false);
+        v[2 * j + 1] = __builtin_amdgcn_fdot2_f32_bf16(x2, __builtin_bit_cast(bf16x2_t, sq[j]), 0.0f, false);
+      }
+    } else {
+      rb_unpack<IN_BF16>(raw, v);
+      if (!TRANSPOSE) {
+#pragma unroll
+        for (int i = 0; i < E; ++i) v[i] *= sg[i];
+      }
     }
-    rb_fwht_wave(v, tl & 63);
+    if (row + gridDim.x < rows) rb_fetch<IN_BF16>(in, base + (size_t)gridDim.x * n + el, raw);   // next row
+    rb_fwht_wave<IN_BF16 ? 1 : 0, KEEP>(v, tl & 63);
     if constexpr (NW > 1) {
       __syncthreads();                              // the previous row is out of buf
       ly_fwht_cross<E, NW>(v, buf, logb, tl);
     }
     float x[E];
 #pragma unroll
-    for (int i = 0; i < E; ++i) x[i] = v[i] * sc[i];
+    for (int i = 0; i < E; ++i) x[i] = XO ? v[i] : v[i] * sc[i];
     if constexpr (tr) {
       // back to the thread's own labels 16 tl + i through LDS, so that the
       // stores below are whole 16-byte vectors (the layout of ly_fwht_cross's
@@ -1208,26 +1282,30 @@ rht_rows_blk(const void *in, void *out, int64_t rows, int n, int nb, const int8_
     if constexpr (OUT_BF16) {
       uint32_t w[E / 2];
 #pragma unroll
-      for (int i = 0; i < E; i += 2) w[i / 2] = bf16x2_rne(x[i], x[i + 1]);
+      for (int i = 0; i < E; i += 2) {
+        w[i / 2] = bf16x2_rne(x[i], x[i + 1]);
+        if constexpr (XO) w[i / 2] ^= xm[i / 2];
+      }
       if (rowsum) {
         // both halves of each packed word in one dot product with (1, 1)
         const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
 #pragma unroll
         for (int i = 0; i < E / 2; ++i) rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[i]), one, rs, false);
       }
-      uint16_t *o = reinterpret_cast<uint16_t *>(out) + base + el;
+      uint16_t *o = reinterpret_cast<uint16_t *>(out) + base + eo;
       *reinterpret_cast<uint4 *>(o) = make_uint4(w[0], w[1], w[2], w[3]);
-      *reinterpret_cast<uint4 *>(o + 512) = make_uint4(w[4], w[5], w[6], w[7]);
+      *reinterpret_cast<uint4 *>(o + (KEEP ? 256 : 512)) = make_uint4(w[4], w[5], w[6], w[7]);
     } else {
       if (rowsum) {
 #pragma unroll
         for (int i = 0; i < E; ++i) rs += x[i];
       }
-      float *o = reinterpret_cast<float *>(out) + base + el;
+      float *o = reinterpret_cast<float *>(out) + base + eo;
+      constexpr int H1 = KEEP ? 256 : 512;
       reinterpret_cast<float4 *>(o)[0] = make_float4(x[0], x[1], x[2], x[3]);
       reinterpret_cast<float4 *>(o)[1] = make_float4(x[4], x[5], x[6], x[7]);
-      reinterpret_cast<float4 *>(o + 512)[0] = make_float4(x[8], x[9], x[10], x[11]);
-      reinterpret_cast<float4 *>(o + 512)[1] = make_float4(x[12], x[13], x[14], x[15]);
+      reinterpret_cast<float4 *>(o + H1)[0] = make_float4(x[8], x[9], x[10], x[11]);
+      reinterpret_cast<float4 *>(o + H1)[1] = make_float4(x[12], x[13], x[14], x[15]);
     }
     if (rowsum) {
 #pragma unroll
