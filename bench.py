@@ -315,30 +315,44 @@ def time_workload(name, steps, warmup, copies, row_scale=False, kernel_launches=
         "roofline": roof,
     }
     if one_kernel:
-        res["single_call_us"] = single_call_us(built[0])
-        res["single_call_note"] = ("median of isolated launches (host waits for each), each on a different "
-                                   "layer copy; the sustained rate (value) is over back-to-back launches")
+        res["single_call_us"], res["single_call_host_us"] = single_call_us(built[0])
+        res["single_call_note"] = ("medians of isolated calls (host waits for each), each on a different layer "
+                                   "copy: single_call_us is the call's own GPU time (events enqueued behind a "
+                                   "spin kernel), single_call_host_us adds the binding and launch submission; "
+                                   "the sustained rate (value) is over back-to-back launches")
     return res, built
 
 
 def single_call_us(b, calls=200):
-    """Median duration of one isolated whole-layer call (HIP events around
-    the launch, host synchronised before and after each)."""
+    """One isolated whole-layer call, each on another layer copy, the host
+    synchronised before and after each: (GPU, host) medians in microseconds.
+    GPU: a spin kernel (~100 us) holds the stream while the host enqueues
+    event, call, event, so the events bracket the call alone, started on an
+    idle GPU with nothing else in flight. Host: the events recorded around
+    the Python call on an idle GPU, so the binding's marshalling and the
+    launch submission are inside."""
     import statistics
     import torch
     from dequant_e8_codebook_amd import glq
-    out = []
+    gpu, host = [], []
     Ls = b["layers"]
     for i in range(calls):
         L = Ls[i % len(Ls)]
         e0, e1 = _event(), _event()
         torch.cuda.synchronize()
+        torch.cuda._sleep(200000)
         e0.record()
         glq.fused_linear(L, b["x"], b["y"], b["ws"])
         e1.record()
         torch.cuda.synchronize()
-        out.append(e0.elapsed_time(e1) * 1e3)
-    return round(statistics.median(out), 3)
+        gpu.append(e0.elapsed_time(e1) * 1e3)
+        e0, e1 = _event(), _event()
+        e0.record()
+        glq.fused_linear(L, b["x"], b["y"], b["ws"])
+        e1.record()
+        torch.cuda.synchronize()
+        host.append(e0.elapsed_time(e1) * 1e3)
+    return round(statistics.median(gpu), 3), round(statistics.median(host), 3)
 
 
 def bf16_matmul_step_ms(built, reps=20):
