@@ -797,6 +797,9 @@ def main():
     if args.pmc_summary:
         pmc_summary(args)
         return 0
+    if args.steps < 1 or args.warmup < 0 or args.warm_seconds < 0:
+        print("bench.py: --steps must be at least 1, --warmup and --warm-seconds at least 0", file=sys.stderr)
+        return 2
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(rows of x or output features would shard across GPUs with no exchange).",

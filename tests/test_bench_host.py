@@ -90,3 +90,11 @@ def test_pmc_summary_scales_by_the_copy_and_takes_medians(tmp_path, monkeypatch)
     assert b.read_traffic("unit", "other<4>") is None
     monkeypatch.setattr(b, "kernel_source_hash", lambda: "0" * 16)
     assert b.read_traffic("unit", "k<4>") is None
+
+
+def test_invalid_step_counts_exit_with_a_message():
+    for args in (["--steps", "0"], ["--warmup", "-1"], ["--warm-seconds", "-0.5"]):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")] + args, capture_output=True,
+                           text=True, timeout=120)
+        assert r.returncode == 2, args
+        assert "--steps" in r.stderr
