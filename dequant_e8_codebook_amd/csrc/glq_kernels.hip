@@ -2402,22 +2402,107 @@ __device__ __forceinline__ void g8_split(uint2 i1, uint2 i2, uint32_t (&q1)[8], 
   }
 }
 
-template <int BPW, bool OUT_BF16>
+// k split of the decode-GEMM for layers with fewer 256 x 256 tiles than CUs
+// and long rows (the 3072 x 12288 down projection at 4,096 tokens: 192 tiles
+// on 256 CUs, 192 k-steps). Tile t's k-steps 0 .. s_main - 1 run on
+// workgroup t (its main part), the remaining ones (its remainder) on
+// workgroup tiles + t; the remainders start on the CUs the main parts leave
+// free and follow one another there (3 on each at 192 tiles: the main parts
+// run 144 of 192 steps, the remainders 48). The two parts of a tile meet through float32
+// partial sums in the workspace and a counter in the control words; neither
+// part ever waits for the other: a part that finds the other's partial
+// complete adds it and runs the epilogue, otherwise it publishes its own
+// partial (write-through stores, completed before the counter is taken) and
+// the other part, arriving second, finishes the tile and clears the counter.
+// The main part checks the counter before publishing, so a remainder that
+// finished earlier costs it no partial of its own.
+struct G8Split {
+  float *part;            // [tiles][2][512 threads x 128 accumulators] (main part, remainder)
+  unsigned int *ctrl;     // control words: tile t's counter in a dword the single-launch layer leaves unused
+  int64_t s_main;         // k-steps of a main part (even)
+};
+
+// counter of tile t: dwords 1 .. 63 of the sixteen 256-byte control lines
+// (dword 0 of each is a group counter of the single-launch layer), t < 1008
+__device__ __forceinline__ unsigned int *g8_tile_counter(unsigned int *ctrl, int64_t t) {
+  return ctrl + 64 * (t % 16) + 1 + t / 16;
+}
+
+// Join the two parts of tile t (every thread of the workgroup calls it):
+// returns true when acc now holds the tile's whole sum (this part finishes
+// the tile), false when this part has published its partial for the other.
+__device__ __forceinline__ bool g8_split_join(f32x16 (&acc)[8][1], const G8Split &sp, int64_t t, bool main_part,
+                                              int *flag) {
+  unsigned int *cnt = g8_tile_counter(sp.ctrl, t);
+  const __amdgpu_buffer_rsrc_t mine = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(sp.part + ((size_t)t * 2 + (main_part ? 0 : 1)) * 65536), 0, 65536 * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t other = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(sp.part + ((size_t)t * 2 + (main_part ? 1 : 0)) * 65536), 0, 65536 * 4, 0x00020000);
+  // accumulator block (a, e) of thread tid at floats 4 ((4 a + e) 512 + tid): 16 bytes a thread, whole
+  // 2 KiB runs a wave
+  int done = 0;
+  if (main_part) {
+    if (threadIdx.x == 0) *flag = (int)__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    done = *flag;
+    __syncthreads();
+  }
+  if (!done) {
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f32x4 v = {acc[a][0][4 * e], acc[a][0][4 * e + 1], acc[a][0][4 * e + 2], acc[a][0][4 * e + 3]};
+        // sc1: written through to the memory side, where the other part reads it
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), mine,
+                                               16 * ((4 * a + e) * G8_THREADS + (int)threadIdx.x), 0, 16);
+      }
+    __builtin_amdgcn_s_waitcnt(0);                   // the partial is at the memory side
+    __syncthreads();
+    if (threadIdx.x == 0) *flag = (int)__hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    done = *flag;
+    __syncthreads();
+    if (!done) return false;                         // first: the other part finishes the tile
+  }
+  // one accumulator tile (16 floats) in flight at a time: the k-loop's
+  // registers are free here, but all 128 loads at once would not fit
+#pragma unroll
+  for (int a = 0; a < 8; ++a) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    other, 16 * ((4 * a + e) * G8_THREADS + (int)threadIdx.x), 0, 16));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[a][0][4 * e + j] += v[j];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
+template <int BPW, bool OUT_BF16, bool SPLIT = false>
 __global__ void __launch_bounds__(G8_THREADS, 1)
 gemm8_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const uint16_t *xt,
            const float *rowsum, int64_t m, int64_t n, int64_t k, float post, const float *row_scale,
-           void *out, int vec, int64_t mblocks, int64_t tiles) {
+           void *out, int vec, int64_t mblocks, int64_t tiles, G8Split sp) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   uint16_t *As0 = reinterpret_cast<uint16_t *>(lds + lds_table_bytes<BPW>());
   uint16_t *As1 = As0 + GM_BM * GM_LDA;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 31, p = lane >> 5;
+  const int64_t S = k / GM_BK;
+  // work: workgroup b < tiles runs a main part (unsplit: the whole tile),
+  // workgroup tiles + t the remainder of tile t
+  const bool main_part = !SPLIT || (int64_t)blockIdx.x < tiles;
+  const int64_t s0 = SPLIT && !main_part ? sp.s_main : 0, s1 = SPLIT && main_part ? sp.s_main : S;
   // XCD-aware tile order, as in gemm_bf16
   int64_t tile = blockIdx.x;
   if (tiles % 8 == 0) tile = (blockIdx.x % 8) * (tiles / 8) + blockIdx.x / 8;
+  if (SPLIT && !main_part) tile = (int64_t)blockIdx.x - tiles;
   const int64_t m0 = (tile % mblocks) * GM_BM;
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c = lane & 31, p = lane >> 5;
   const int64_t n0 = (tile / mblocks) * GM_BN + 32 * wave;
-  const int64_t S = k / GM_BK;
 
   G8Buf gb;
   g8_buf_init<BPW>(gb, idx1, idx2, xt, m, n, k, m0, n0, c, p);
@@ -2432,14 +2517,14 @@ gemm8_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const ui
 
   load_tables<BPW, G8_THREADS>(lds, blob);
   uint4 ra[4];
-  g8_load_a(gb, 0, ra);
+  g8_load_a(gb, s0, ra);
   uint2 i1, i2, j1, j2;
-  g8_load_idx<BPW>(gb, 0, i1, i2);
-  tables_landed();                                   // tables, x~ tile 0, step-0 indices
-  store_a(As0, ra);
-  g8_load_idx<BPW>(gb, min((int64_t)1, S - 1), j1, j2);
-  g8_load_a(gb, min((int64_t)1, S - 1), ra);
-  __syncthreads();                                   // tables and x~ tile 0 in LDS
+  g8_load_idx<BPW>(gb, s0, i1, i2);
+  tables_landed();                                   // tables, x~ tile s0, step-s0 indices
+  store_a(As0, ra);                                  // (s0 is even)
+  g8_load_idx<BPW>(gb, min(s0 + 1, s1 - 1), j1, j2);
+  g8_load_a(gb, min(s0 + 1, s1 - 1), ra);
+  __syncthreads();                                   // tables and x~ tile s0 in LDS
 
   f32x16 acc[8][1];
 #pragma unroll
@@ -2466,7 +2551,7 @@ gemm8_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const ui
     uint16_t *Anext = (s & 1) ? As0 : As1;
     uint32_t q1[8], q2[8];
     g8_split<BPW>(i1, i2, q1, q2);                   // indices of step s + 1
-    g8_load_idx<BPW>(gb, min(s + 2, S - 1), i1, i2);
+    g8_load_idx<BPW>(gb, min(s + 2, s1 - 1), i1, i2);
 
     // half-block h: MFMAs of k-step u = h >> 1 on activation tiles 4 (h & 1) + a,
     // reading the operands of half-block h + 1 (of the next tile for h = 7)
@@ -2506,7 +2591,7 @@ gemm8_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const ui
     half(4, H0, H1);
     gm_interleave<4, 2, 1, 1>();
     __builtin_amdgcn_sched_barrier(0);
-    g8_load_a(gb, min(s + 2, S - 1), ra);
+    g8_load_a(gb, min(s + 2, s1 - 1), ra);
     half(5, H1, H0);
     gm_interleave<4, 0, 1, 0, 1>();
     __builtin_amdgcn_sched_barrier(0);
@@ -2516,13 +2601,17 @@ gemm8_bf16(const uint16_t *idx1, const void *idx2, const uint8_t *blob, const ui
     half(7, H1, H0);
     __builtin_amdgcn_sched_barrier(0);
   };
-  int64_t s = 0;
-  for (; s + 1 < S; s += 2) {
+  int64_t s = s0;
+  for (; s + 1 < s1; s += 2) {
     kstep(s, B0, B1);
     kstep(s + 1, B1, B0);
   }
-  if (s < S) kstep(s, B0, B1);
+  if (s < s1) kstep(s, B0, B1);
   __syncthreads();                                   // the epilogue reuses the x~ buffers
+  if constexpr (SPLIT) {
+    // the join's flag word lives in the x~ buffer, free after the k-loop
+    if (!g8_split_join(acc, sp, tile, main_part, reinterpret_cast<int *>(As0))) return;
+  }
   gm_epilogue<BPW, OUT_BF16, 1>(acc, rowsum, post, row_scale, out, m, n, m0, n0, lane, wave, vec != 0);
 }
 
@@ -3382,10 +3471,42 @@ int check_layer(const glq_layer *L, bool need_signs) {
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-// Workspace: [0, kCtrlBytes) control words (the whole-layer kernel's ticket
-// counters: zero before first use, left zero by every call), then x~, row sums
-// of x~ and z = s W^ x~.
-struct WsLayout { size_t ctrl, xt, rowsum, z, total; };
+// The decode-GEMM's k split (gemm8_bf16<., ., true>): used when a layer has
+// fewer 256 x 256 tiles than CUs and long rows (remainders of at least 32
+// k-steps). The E = CUs - tiles
+// free CUs run q = ceil(tiles / E) remainders each (at most 4), so a
+// remainder of r = S / (q + 1) steps balances a main part's S - r against
+// q r; s_main = S - r is made even (the x~ double buffer starts on its first
+// half).
+struct G8Plan { bool split = false; int64_t s_main = 0; int64_t grid = 0; };
+
+G8Plan g8_plan(int64_t m, int64_t n, int64_t k) {
+  G8Plan pl;
+  if (m <= 16 || k % GM_BK != 0) return pl;
+  const int64_t tiles = ((m + GM_BM - 1) / GM_BM) * ((n + GM_BN - 1) / GM_BN);
+  const int64_t S = k / GM_BK, cus = cu_count();
+  if (tiles >= cus || S < 64 || tiles >= 1008) return pl;
+  const int64_t extra = cus - tiles;
+  const int64_t q = (tiles + extra - 1) / extra;
+  if (q > 4) return pl;
+  int64_t r = S / (q + 1);
+  if ((S - r) % 2) ++r;
+  // a remainder pays the table copy, its prologue and the partial sums: below
+  // 32 k-steps that outweighs the CUs it brings (3072^2 at 4,096 tokens, 12
+  // steps: 87 -> 104 us; the 3072 x 12288 down projection, 48: 334 -> 315 us)
+  if (r < 32 || S - r < 2) return pl;
+  pl.split = true;
+  pl.s_main = S - r;
+  pl.grid = 2 * tiles;
+  return pl;
+}
+
+// Workspace: control words (GLQ_WS_CTRL_BYTES; the single-launch layer's
+// counters and the k split's tile counters: zero before first use, left zero
+// by every call), then x~, row sums of x~, z = s W^ x~, and the k split's
+// float32 partial sums (two 256 KiB halves per tile, only for layers the
+// split applies to).
+struct WsLayout { size_t ctrl, xt, rowsum, z, part, total; };
 
 WsLayout ws_layout(int64_t n, int64_t k, int64_t m) {
   WsLayout w;
@@ -3395,7 +3516,10 @@ WsLayout ws_layout(int64_t n, int64_t k, int64_t m) {
   const size_t xt_bytes = (size_t)(m <= 16 ? 16 : m) * (size_t)k * 4;
   w.rowsum = w.xt + align256(xt_bytes);
   w.z = w.rowsum + align256((size_t)m * 4);
-  w.total = w.z + align256((size_t)m * (size_t)n * 4);
+  w.part = w.z + align256((size_t)m * (size_t)n * 4);
+  const G8Plan pl = g8_plan(m, n, k);
+  const int64_t tiles = ((m + GM_BM - 1) / GM_BM) * ((n + GM_BN - 1) / GM_BN);
+  w.total = w.part + (pl.split ? (size_t)tiles * 2 * 65536 * 4 : 0);
   return w;
 }
 
@@ -3426,7 +3550,8 @@ int gv_row_tiles(int bpw, int64_t tiles) { return bpw == 2 && tiles >= 1024 ? 4 
 
 template <int BPW>
 int launch_matmul(const glq_layer *L, const void *xt, glq_dtype x_dt, const float *rowsum, int64_t m,
-                  void *out, glq_dtype out_dt, hipStream_t st, bool tiled = false) {
+                  void *out, glq_dtype out_dt, hipStream_t st, bool tiled = false, unsigned int *ctrl = nullptr,
+                  float *part = nullptr) {
   const uint8_t *blob = reinterpret_cast<const uint8_t *>(L->cb);
   const size_t tab = lds_table_bytes<BPW>();
   if (x_dt == GLQ_F32) {
@@ -3473,13 +3598,23 @@ int launch_matmul(const glq_layer *L, const void *xt, glq_dtype x_dt, const floa
     const bool k64 = L->k % GM_BK == 0 && (int64_t)GM_BM * L->k * 2 < 0x7FFFFFFF;
     const bool ob = out_dt == GLQ_BF16;
     const int vec = ((L->n * (ob ? 2 : 4)) % 16 == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0) ? 1 : 0;
-    auto kern = k64 ? (ob ? gemm8_bf16<BPW, true> : gemm8_bf16<BPW, false>)
-              : even_g ? (ob ? gemm_bf16<BPW, true, true> : gemm_bf16<BPW, true, false>)
-                       : (ob ? gemm_bf16<BPW, false, true> : gemm_bf16<BPW, false, false>);
-    int rc = allow_lds(kern, shm);
-    if (rc) return rc;
-    hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(k64 ? G8_THREADS : 256), shm, st, L->idx1, L->idx2,
-                       blob, xb, rowsum, m, L->n, L->k, post, L->row_scale, out, vec, mb, tiles);
+    if (k64) {
+      const G8Plan pl = part && ctrl ? g8_plan(m, L->n, L->k) : G8Plan{};
+      G8Split sp{part, ctrl, pl.s_main};
+      auto kern = pl.split ? (ob ? gemm8_bf16<BPW, true, true> : gemm8_bf16<BPW, false, true>)
+                           : (ob ? gemm8_bf16<BPW, true, false> : gemm8_bf16<BPW, false, false>);
+      int rc = allow_lds(kern, shm);
+      if (rc) return rc;
+      hipLaunchKernelGGL(kern, dim3((unsigned)(pl.split ? pl.grid : tiles)), dim3(G8_THREADS), shm, st, L->idx1,
+                         L->idx2, blob, xb, rowsum, m, L->n, L->k, post, L->row_scale, out, vec, mb, tiles, sp);
+    } else {
+      auto kern = even_g ? (ob ? gemm_bf16<BPW, true, true> : gemm_bf16<BPW, true, false>)
+                         : (ob ? gemm_bf16<BPW, false, true> : gemm_bf16<BPW, false, false>);
+      int rc = allow_lds(kern, shm);
+      if (rc) return rc;
+      hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(256), shm, st, L->idx1, L->idx2, blob, xb, rowsum, m,
+                         L->n, L->k, post, L->row_scale, out, vec, mb, tiles);
+    }
   }
   return hip_status(hipGetLastError());
 }
@@ -3609,6 +3744,8 @@ extern "C" int glq_fused_linear(const glq_layer *L, const void *x, glq_dtype x_d
   void *xt = wsb + ws.xt;
   float *rowsum = reinterpret_cast<float *>(wsb + ws.rowsum);
   float *z = reinterpret_cast<float *>(wsb + ws.z);
+  unsigned int *ctrl_w = reinterpret_cast<unsigned int *>(wsb + ws.ctrl);
+  float *part = ws.total > ws.part ? reinterpret_cast<float *>(wsb + ws.part) : nullptr;
 
   // whole layer in one launch at decode-time batch sizes
   if (x_dt == GLQ_BF16 && in_rht && out_rht && m <= 4 && m * L->k <= LY_MAXE && m * L->n <= LY_MAXE &&
@@ -3671,9 +3808,9 @@ extern "C" int glq_fused_linear(const glq_layer *L, const void *x, glq_dtype x_d
   void *mm_out = out_rht ? (void *)z : y;
   const glq_dtype mm_dt = !out_rht ? y_dt : (x_dt == GLQ_BF16 && y_dt == GLQ_BF16 && m > 16) ? GLQ_BF16 : GLQ_F32;
   switch (L->bpw) {
-    case 2: rc = launch_matmul<2>(L, xt_use, x_dt, rowsum, m, mm_out, mm_dt, st, tiled); break;
-    case 3: rc = launch_matmul<3>(L, xt_use, x_dt, rowsum, m, mm_out, mm_dt, st, tiled); break;
-    default: rc = launch_matmul<4>(L, xt_use, x_dt, rowsum, m, mm_out, mm_dt, st, tiled); break;
+    case 2: rc = launch_matmul<2>(L, xt_use, x_dt, rowsum, m, mm_out, mm_dt, st, tiled, ctrl_w, part); break;
+    case 3: rc = launch_matmul<3>(L, xt_use, x_dt, rowsum, m, mm_out, mm_dt, st, tiled, ctrl_w, part); break;
+    default: rc = launch_matmul<4>(L, xt_use, x_dt, rowsum, m, mm_out, mm_dt, st, tiled, ctrl_w, part); break;
   }
   if (rc) return rc;
   if (out_rht) return launch_rht(z, mm_dt, y, y_dt, m, L->n, L->sign_n, 1, nullptr, st);

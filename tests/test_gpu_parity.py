@@ -347,6 +347,36 @@ def test_gemm_long_k(G, cb, bpw):
     assert og.row_relative_error(y, ref) <= TOL_BF16
 
 
+@pytest.mark.parametrize("bpw", [3, 4])
+def test_gemm_k_split(G, cb, bpw):
+    # long rows and fewer 256 x 256 tiles than CUs: every tile's k-steps are
+    # split between two workgroups that meet through partial sums and a tile
+    # counter in the control words (12 ragged tiles, 128 k-steps, remainders
+    # of 64); all rows checked, both output types, and a repeat call on the
+    # same workspace (the counters must be back at zero) bit-identical
+    m, n, k = 600, 1000, 8192
+    i1, i2 = _random_layer(n, k, bpw, 8100 + bpw)
+    s = np.float32(0.013)
+    sn, sk = workloads.signs(n, 81), workloads.signs(k, 82)
+    x = workloads.bf16_round_trip(np.random.default_rng(bpw + 81).standard_normal((m, k)).astype(np.float32))
+    ref = og.layer_reference(x, i1, i2, bpw, s, sn, sk)
+    L = G.Layer.from_numpy(i1, i2, s, sn, sk, cb)
+    xt = _t(x, torch.bfloat16)
+    ws = torch.zeros(G.workspace_bytes(L, m), device="cuda", dtype=torch.uint8)
+    for y_dt in (torch.bfloat16, torch.float32):
+        outs = []
+        for _ in range(2):
+            y = torch.full((m, n), float("nan"), device="cuda", dtype=y_dt)
+            G.fused_linear(L, xt, y, ws)
+            torch.cuda.synchronize()
+            outs.append(y.float().cpu().numpy())
+        assert np.isfinite(outs[0]).all()
+        assert og.relative_error(outs[0], ref) <= TOL_BF16
+        assert og.row_relative_error(outs[0], ref) <= TOL_BF16
+        assert np.array_equal(outs[0], outs[1])
+    assert not ws[:4352].any().item()                 # control words left zero
+
+
 _LDS_ORDER_SCRIPT = r"""
 import numpy as np, torch
 from dequant_e8_codebook_amd import glq
