@@ -100,42 +100,3 @@ def test_kept_layout_stores_whole_16_byte_pieces():
                         for l in range(16 * row, 16 * row + 16))
         assert starts == list(range(starts[0], starts[0] + 128, 8))
 
-
-def wave_transform_64(x):
-    # 64 registers a lane, a 4096-element block in one wave: registers 8 h + 0..7
-    # hold elements 8 ell(l) + 512 h + 0..7 (register bits 3..5 = element
-    # bits 9..11); the same lane stages, the swaps kept in place within each
-    # group of 16 registers
-    v = np.zeros((64, 64))
-    for l in range(64):
-        for i in range(64):
-            v[i, l] = x[8 * ell(l) + (i & 7) + 512 * (i >> 3)]
-    for s in range(6):
-        for i in range(64):
-            if not i & (1 << s):
-                a, b = v[i].copy(), v[i + (1 << s)].copy()
-                v[i], v[i + (1 << s)] = a + b, a - b
-    partners = [lambda l: l ^ 1, lambda l: l ^ 2, lambda l: (l & ~7) | (7 - (l & 7)),
-                lambda l: (l & ~15) | ((l + 8) & 15)]
-    for j, perm in enumerate(partners):
-        s = np.array([-1.0 if (ell(l) >> j) & 1 else 1.0 for l in range(64)])
-        v = v + s[None, :] * v[:, [perm(l) for l in range(64)]]
-    for sw in (swap16, swap32):
-        for g in range(4):
-            for p in range(8):
-                a, b = sw(v[16 * g + p], v[16 * g + p + 8])
-                v[16 * g + p], v[16 * g + p + 8] = a + b, a - b
-    y = np.full(4096, np.nan)
-    for l in range(64):
-        for i in range(64):
-            e = ((i & 7) | ((ell(l) & 15) << 3) | (((l >> 5) & 1) << 7) | (((i >> 3) & 1) << 8)
-                 | (((l >> 4) & 1) << 9) | ((i >> 4) << 10))
-            assert np.isnan(y[e])
-            y[e] = v[i, l] * lane_sign(l) / 64.0
-    return y
-
-
-def test_one_wave_4096_block_gives_the_hadamard_transform():
-    rng = np.random.default_rng(12)
-    x = rng.standard_normal(4096)
-    assert np.allclose(wave_transform_64(x), hadamard(4096) @ x / 64.0, rtol=0, atol=1e-11)
