@@ -195,7 +195,9 @@ size_t glq_fused_linear_workspace(const glq_layer *L, int64_t m);
  *   workspace        device, >= glq_fused_linear_workspace(L, m) bytes, 256-byte aligned.
  *                    Its first GLQ_WS_CTRL_BYTES bytes are control words
  *                    (completion counters of the single-launch layer used at
- *                    small m): they must be zero before the first call with a
+ *                    small m, and the tile counters of the k-split GEMM used
+ *                    for long rows with fewer output tiles than CUs): they
+ *                    must be zero before the first call with a
  *                    workspace, every call that returns GLQ_OK (and whose
  *                    kernels complete) leaves them zero, and calls that run
  *                    concurrently need separate workspaces. After a call that
