@@ -53,11 +53,14 @@ def _call_both(G, L, x):
 
 
 # (n, k, bpw, m): the single-launch small-batch layer, then the multi-kernel
-# paths (16-row GEMV and the decode-GEMM), each pair ending with a smaller call
+# paths (16-row GEMV, the decode-GEMM, and the decode-GEMM split along k,
+# whose tile counters live in the static scratch's control words), each pair
+# ending with a smaller call
 @pytest.mark.parametrize("first,second", [
     ((4096, 4096, 4, 3), (1024, 1024, 2, 1)),
     ((1000, 768, 3, 12), (300, 256, 4, 5)),
     ((640, 1024, 2, 300), (264, 160, 3, 40)),
+    ((512, 4096, 4, 300), (300, 8192, 3, 100)),
 ])
 def test_noalloc_matches_workspace_entry_point(G, first, second):
     cb = G.device_codebook("cuda")
