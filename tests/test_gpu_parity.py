@@ -347,7 +347,7 @@ def test_gemm_long_k(G, cb, bpw):
     assert og.row_relative_error(y, ref) <= TOL_BF16
 
 
-@pytest.mark.parametrize("bpw", [3, 4])
+@pytest.mark.parametrize("bpw", [2, 3, 4])
 def test_gemm_k_split(G, cb, bpw):
     # long rows and fewer 256 x 256 tiles than CUs: every tile's k-steps are
     # split between two workgroups that meet through partial sums and a tile
@@ -606,6 +606,26 @@ def test_fused_row_scales(G, cb, bpw, m, x_dt):
         G.fused_linear(L, xt, y, ws)
         torch.cuda.synchronize()
         assert og.relative_error(y.float().cpu().numpy(), ref) <= (TOL_F32 if x_dt == "f32" else TOL_BF16)
+
+
+@pytest.mark.parametrize("bpw", [2, 4])
+def test_fused_row_scales_k_split(G, cb, bpw):
+    # per-row scales through the epilogue of the decode-GEMM split along k
+    # (two 256-row tiles with a ragged second, 96 k-steps: remainders of 48)
+    m, n, k = 300, 272, 6144
+    i1, i2, s, rs = _row_scale_layer(n, k, bpw, 690 + bpw)
+    sn, sk = workloads.signs(n, 69), workloads.signs(k, 70)
+    x = workloads.bf16_round_trip(np.random.default_rng(bpw + 69).standard_normal((m, k)).astype(np.float32))
+    L = G.Layer.from_numpy(i1, i2, s, sn, sk, cb, row_scale=rs)
+    ref = og.layer_reference(x, i1, i2, bpw, og.effective_scale(s, rs), sn, sk)
+    y = torch.full((m, n), float("nan"), device="cuda", dtype=torch.bfloat16)
+    ws = torch.zeros(G.workspace_bytes(L, m), device="cuda", dtype=torch.uint8)
+    G.fused_linear(L, _t(x, torch.bfloat16), y, ws)
+    torch.cuda.synchronize()
+    yn = y.float().cpu().numpy()
+    assert np.isfinite(yn).all()
+    assert og.relative_error(yn, ref) <= TOL_BF16
+    assert og.row_relative_error(yn, ref) <= TOL_BF16
 
 
 def test_fused_row_scales_oracle_encoded(G, cb):
