@@ -3475,9 +3475,9 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 // fewer 256 x 256 tiles than CUs and long rows (remainders of at least 32
 // k-steps). The E = CUs - tiles
 // free CUs run q = ceil(tiles / E) remainders each (at most 4), so a
-// remainder of r = S / (q + 1) steps balances a main part's S - r against
-// q r; s_main = S - r is made even (the x~ double buffer starts on its first
-// half).
+// remainder of r = (S - 2 q) / (q + 1) steps balances a main part's S - r
+// against q (r + 2); s_main = S - r is made even (the x~ double buffer starts
+// on its first half).
 struct G8Plan { bool split = false; int64_t s_main = 0; int64_t grid = 0; };
 
 G8Plan g8_plan(int64_t m, int64_t n, int64_t k) {
@@ -3489,7 +3489,9 @@ G8Plan g8_plan(int64_t m, int64_t n, int64_t k) {
   const int64_t extra = cus - tiles;
   const int64_t q = (tiles + extra - 1) / extra;
   if (q > 4) return pl;
-  int64_t r = S / (q + 1);
+  // each remainder also pays about two k-steps of fixed cost (its table
+  // copy, prologue and partial sums), which the q in a row on one CU add up
+  int64_t r = (S - 2 * q) / (q + 1);
   if ((S - r) % 2) ++r;
   // a remainder pays the table copy, its prologue and the partial sums: below
   // 32 k-steps that outweighs the CUs it brings (3072^2 at 4,096 tokens, 12
