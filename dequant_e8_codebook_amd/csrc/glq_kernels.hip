@@ -2408,7 +2408,7 @@ __device__ __forceinline__ void g8_split(uint2 i1, uint2 i2, uint32_t (&q1)[8], 
 // workgroup t (its main part), the remaining ones (its remainder) on
 // workgroup tiles + t; the remainders start on the CUs the main parts leave
 // free and follow one another there (3 on each at 192 tiles: the main parts
-// run 144 of 192 steps, the remainders 48). The two parts of a tile meet through float32
+// run 146 of 192 steps, the remainders 46). The two parts of a tile meet through float32
 // partial sums in the workspace and a counter in the control words; neither
 // part ever waits for the other: a part that finds the other's partial
 // complete adds it and runs the epilogue, otherwise it publishes its own
